@@ -1,0 +1,136 @@
+"""Pins for the oracle's format decoders (CPU only).
+
+Each check ties oracle.formats to something other than itself: the table the
+NVFP4 page prints, the closed form of e2m1, torch's float8_e4m3fn decode,
+ldexp, hand-built GPTQ words, and the group counts the pages state.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    rows = []
+    for ln in open(os.path.join(GOLDEN, name)):
+        ln = ln.split("#", 1)[0].strip()
+        if ln:
+            rows.append(ln.split())
+    return rows
+
+
+def test_e2m1_table_matches_page():
+    printed = np.array([float(v) for v in _golden_rows("e2m1_table.txt")[0]])
+    assert printed.shape == (16,)
+    np.testing.assert_array_equal(F.E2M1_TABLE, printed)
+    # signed zero at code 8 as printed
+    assert np.signbit(F.E2M1_TABLE[8]) and not np.signbit(F.E2M1_TABLE[0])
+
+
+def test_e2m1_table_matches_closed_form():
+    # e2m1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit; e = 0 is subnormal.
+    for code in range(16):
+        s = -1.0 if code & 8 else 1.0
+        e, m = (code >> 1) & 3, code & 1
+        v = s * (m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2))
+        assert F.E2M1_TABLE[code] == v, code
+
+
+def test_e4m3fn_all_bytes_match_torch():
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    np.testing.assert_array_equal(np.isnan(F.E4M3FN_TABLE), nan)
+    np.testing.assert_array_equal(F.E4M3FN_TABLE[~nan], ref[~nan])
+    assert F.E4M3FN_TABLE[0x7E] == 448.0 and F.E4M3FN_TABLE[0x01] == 2.0 ** -9
+
+
+def test_e8m0_is_power_of_two():
+    for b in range(255):
+        assert F.E8M0_TABLE[b] == np.ldexp(1.0, b - 127)
+    assert np.isnan(F.E8M0_TABLE[255])
+
+
+def test_bf16_and_fp16_decode():
+    vals = np.array([0.0, 1.0, -2.5, 3.140625, 1e-3], dtype=np.float32)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    got = F.bf16_to_f64(bits)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).double().numpy()
+    # the chosen values are exact in bf16 except 1e-3, which truncation and RNE
+    # round the same way here
+    np.testing.assert_array_equal(got[:4], ref[:4])
+    h = np.array([1.0, 0.0999755859375, -65504.0], dtype=np.float16)
+    np.testing.assert_array_equal(F.fp16_to_f64(h), h.astype(np.float64))
+
+
+def test_nvfp4_decode_nibble_order_and_scales():
+    # one row, K = 32: byte j holds codes for k = 2j (low) and 2j+1 (high)
+    codes = np.array([(k * 5 + 3) % 16 for k in range(32)], dtype=np.uint8)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, :]
+    scales = np.array([[0x38, 0x40]], dtype=np.uint8)   # e4m3 1.0 and 2.0
+    W = F.decode_nvfp4(packed, scales, 0.5, 16)
+    for k in range(32):
+        s = 1.0 if k < 16 else 2.0
+        assert W[0, k] == F.E2M1_TABLE[codes[k]] * s * 0.5
+
+
+def test_mxfp4_decode():
+    codes = np.arange(32, dtype=np.uint8) % 16
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, :]
+    W = F.decode_mxfp4(packed, np.array([[127 - 3]], dtype=np.uint8), 32)
+    np.testing.assert_array_equal(W[0], F.E2M1_TABLE[codes] / 8.0)
+
+
+def test_gptq_decode_hand_built_words():
+    # K = 64 (one group), N = 8: q[k, n] = (k + n) % 16, z[n] = n, s[n] = 0.5 * (n + 1)
+    K, N, G = 64, 8, 64
+    q = np.array([[(k + n) % 16 for n in range(N)] for k in range(K)], dtype=np.int64)
+    qw = np.zeros((K // 8, N), dtype=np.int64)
+    for k in range(K):
+        qw[k // 8] |= q[k] << (4 * (k % 8))
+    zw = np.zeros((1, 1), dtype=np.int64)
+    for n in range(N):
+        zw[0, 0] |= n << (4 * n)
+    s = np.array([[0.5 * (n + 1) for n in range(N)]], dtype=np.float16)
+    W = F.decode_gptq(qw.astype(np.uint32).view(np.int32), zw.astype(np.uint32).view(np.int32), s, G)
+    assert W.shape == (N, K)
+    for n in range(N):
+        for k in range(K):
+            assert W[n, k] == (q[k, n] - n) * 0.5 * (n + 1)
+    # an all-ones word (nibble 15 everywhere) with zero point 15 decodes to 0
+    W0 = F.decode_gptq(np.full((8, 8), -1, dtype=np.int32), np.full((1, 1), -1, dtype=np.int32),
+                       np.ones((1, 8), dtype=np.float16), 64)
+    assert not W0.any()
+
+
+@pytest.mark.parametrize("row", _golden_rows("group_counts.txt"))
+def test_group_counts_from_pages(row):
+    """Each stated group count is the number of distinct scale groups decode uses.
+
+    Every scale group gets a distinctive power-of-two scale; decoding an all-
+    ones code row must show exactly the stated number of distinct groups, the
+    last one covering the tail, with nothing read past the real groups.
+    """
+    K, G, ngroups = int(row[0]), int(row[1]), int(row[2])
+    assert K // G == ngroups and K % G == 0
+    if G == 16:   # NVFP4
+        codes = np.full((1, K // 2), 0x22, dtype=np.uint8)       # both nibbles = 1.0
+        sc = np.array([[0x38 + 8 * (g % 4) for g in range(ngroups)]], dtype=np.uint8)  # 1,2,4,8
+        W = F.decode_nvfp4(codes, sc, 1.0, G)
+        for g in range(ngroups):
+            assert np.all(W[0, g * G:(g + 1) * G] == 2.0 ** (g % 4))
+        with pytest.raises(AssertionError):
+            F.decode_nvfp4(codes, np.concatenate([sc, sc[:, :8]], axis=1), 1.0, G)  # padded groups
+    else:         # GPTQ
+        N = 8
+        qw = np.full((K // 8, N), 0x11111111, dtype=np.int64).astype(np.uint32).view(np.int32)
+        zw = np.zeros((ngroups, 1), dtype=np.int32)
+        s = np.array([[2.0 ** (g % 5)] * N for g in range(ngroups)], dtype=np.float16)
+        W = F.decode_gptq(qw, zw, s, G)
+        for g in range(ngroups):
+            assert np.all(W[:, g * G:(g + 1) * G] == 2.0 ** (g % 5))
