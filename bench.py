@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Throughput of the fused W4A16 MoE layer on one MI355X.
+
+Workload: the gpt-oss-20b-shaped MoE layer -- E=32 experts, top-4, hidden =
+intermediate = 2880, NVFP4 (e2m1 + e4m3 scale per 16 + fp32 global scale)
+weights, per-expert biases, swigluoai, routing weight applied in GEMM2's
+epilogue -- on synthetic inputs (seeded; see synthetic/).  One step is one
+moe_forward call (route -> align -> GEMM1 -> GEMM2 -> sum) over a batch of T
+tokens with everything already resident in HBM.  The headline line is at
+T = 4096; the same JSON line carries the other token counts of the sweep.
+
+Weight copies are rotated between calls so that no call finds its weights in
+the 256 MB last-level cache left behind by the previous one.
+
+Prints ONE JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def alg_bytes_per_expert(L) -> int:
+    """Bytes one touched expert must stream: 4-bit codes, scales, global scale, biases."""
+    tot = 0
+    for w in (L.w13, L.w2):
+        tot += w.qweight[0].nbytes + w.scales[0].nbytes
+        if w.zeros is not None:
+            tot += w.zeros[0].nbytes
+        if w.global_scale is not None:
+            tot += 4
+        if w.bias is not None:
+            tot += w.bias[0].nbytes
+    return tot
+
+
+def algorithmic(L, T, ids):
+    """(bytes, flops) the layer must move / compute for T tokens with routing ids."""
+    touched = len(np.unique(ids[(ids >= 0) & (ids < L.E)]))
+    nbytes = touched * alg_bytes_per_expert(L) + T * L.H * 2 * 2 + T * L.E * 4
+    n1 = L.N1
+    flops = 2 * T * L.top_k * L.H * (n1 + L.I)
+    return nbytes, flops, touched
+
+
+def gemm1_alg(L, T, ids):
+    touched = len(np.unique(ids))
+    w = L.w13
+    b = touched * (w.qweight[0].nbytes + w.scales[0].nbytes + 4 + (w.bias[0].nbytes if w.bias is not None else 0))
+    b += T * L.H * 2 + T * L.top_k * L.I * 2
+    f = 2 * T * L.top_k * L.H * L.N1
+    return b, f
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--tokens", type=int, default=4096)
+    ap.add_argument("--sweep", default="1,8,64,512,4096")
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--cpu-sample", type=int, default=64, help="tokens the oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer "
+              "is not sharded across GPUs in this build.", file=sys.stderr)
+        return 2
+
+    import torch
+    import synthetic as S
+    import bit_weight_expert_amd as M
+
+    M.lib()  # fails loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+
+    sweep = sorted(set(int(t) for t in args.sweep.split(",") if t) | {args.tokens})
+    t_max = max(sweep)
+    t0 = time.time()
+    L = S.make_config(2)
+    assert L.T >= t_max
+    log(f"generated config 2 inputs in {time.time() - t0:.1f}s")
+
+    dev = torch.device("cuda")
+    x = torch.from_numpy(L.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    logits = torch.from_numpy(L.logits).to(dev)
+    copies = []
+    for r in range(args.copies):
+        w13 = M.QuantWeights.from_arrays(L.w13.fmt, L.w13.group, L.w13.N, L.w13.K, L.w13.qweight,
+                                         L.w13.scales, None, L.w13.global_scale, L.w13.bias)
+        w2 = M.QuantWeights.from_arrays(L.w2.fmt, L.w2.group, L.w2.N, L.w2.K, L.w2.qweight,
+                                        L.w2.scales, None, L.w2.global_scale, L.w2.bias)
+        copies.append((w13, w2))
+    ws = torch.empty((M.moe_forward_workspace_bytes(t_max, L.E, L.top_k, L.H, L.I),),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((t_max, L.H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def fwd(T, i):
+        w13, w2 = copies[i % len(copies)]
+        M.moe_forward(x[:T], logits[:T], L.top_k, L.I, w13, w2, act=L.act, route=L.route,
+                      renormalize=L.renormalize, alpha=L.alpha, beta=L.beta, limit=L.limit,
+                      mul_topk_weights=L.mul_topk_weights, workspace=ws, out=out[:T])
+
+    def time_calls(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(steps):
+            fn(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps  # ms per call
+
+    # routing ids of the batch (for the algorithmic byte counts: touched experts)
+    ids_all = M.moe_route(logits, L.top_k, L.route, None, L.renormalize)[0].cpu().numpy()
+
+    results = {}
+    for T in sweep:
+        steps = args.steps if T == args.tokens else max(args.steps, 50)
+        ms = time_calls(lambda i: fwd(T, i), steps, args.warmup)
+        nb, fl, touched = algorithmic(L, T, ids_all[:T])
+        t_hbm = nb / (HBM_PEAK_GBS * 1e9)
+        t_mfma = fl / (BF16_PEAK_TFLOPS * 1e12)
+        bound = "hbm" if t_hbm >= t_mfma else "mfma"
+        results[T] = dict(T=T, ms=ms, tokens_per_s=T / (ms * 1e-3), touched_experts=touched,
+                          alg_bytes=nb, alg_flops=fl, GBps=nb / (ms * 1e-3) / 1e9,
+                          TFLOPs=fl / (ms * 1e-3) / 1e12, bound=bound,
+                          roofline_frac=max(t_hbm, t_mfma) / (ms * 1e-3))
+        log(f"T={T}: {ms * 1e3:.1f} us/step, {results[T]['tokens_per_s']:.0f} tok/s, "
+            f"{results[T]['GBps']:.0f} GB/s, {results[T]['TFLOPs']:.1f} TFLOP/s, "
+            f"{bound} roofline {results[T]['roofline_frac'] * 100:.1f}%")
+
+    # dominant kernel at the headline T: GEMM1, timed alone on the same stream
+    T = args.tokens
+    bm = M.moe_forward_block_m(T, L.top_k, L.E)
+    ids_t, w_t = M.moe_route(logits[:T], L.top_k, L.route, None, L.renormalize)
+    si, ei, npp = M.moe_align(ids_t, L.E, bm)
+    act_buf = torch.empty((T * L.top_k, L.I), dtype=torch.bfloat16, device=dev)
+
+    def g1(i):
+        w13 = copies[i % len(copies)][0]
+        M.moe_w4a16_gemm1(x[:T], L.top_k, w13, L.act, L.alpha, L.beta, L.limit, si, ei, npp, bm,
+                          out=act_buf)
+
+    g1_ms = time_calls(g1, args.steps, args.warmup)
+    gb, gf = gemm1_alg(L, T, ids_all[:T])
+    g_bound = "hbm" if gb / (HBM_PEAK_GBS * 1e9) >= gf / (BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    if g_bound == "mfma":
+        achieved, peak, unit = gf / (g1_ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = gb / (g1_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    log(f"gemm1 alone at T={T}: {g1_ms * 1e3:.1f} us, {achieved:.1f} {unit} ({achieved / peak * 100:.1f}%)")
+
+    # headline: the timed K steps at T = args.tokens, bracketed by synchronisation
+    head = results[args.tokens]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import moe as O
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            blas_threads = 1
+        n = min(args.cpu_sample, T)
+        t0 = time.time()
+        O.forward(L.take(n))
+        dt = time.time() - t0
+        cpu = {"value": n / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+               "sample": f"first {n} tokens of the T={T} batch, whole layer (route, align, float64 "
+                         f"dequant of every touched expert, both GEMMs, sum); {dt:.1f}s wall"}
+        log(f"oracle: {n} tokens in {dt:.1f}s")
+
+    line = {
+        "metric": "fused W4A16 MoE layer tokens/s + % HBM/MFMA roofline, E32 top4 h2880",
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gpt-oss-20b-shaped MoE layer: E=32, top_k=4, hidden=2880, "
+                               "intermediate=2880, NVFP4 g16 weights + bias, swigluoai, "
+                               f"T={args.tokens} tokens",
+                   "tokens": args.tokens, "block_m": bm, "weight_copies_rotated": args.copies},
+        "roofline": {"kernel": "grouped_gemm (GEMM1, w13 + swigluoai)", "bound": g_bound,
+                     "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+                     "traffic": None, "kernel_us": g1_ms * 1e3},
+        "layer_roofline": {"bound": head["bound"], "frac": head["roofline_frac"],
+                           "GBps": head["GBps"], "TFLOPs": head["TFLOPs"]},
+        "cpu_baseline": cpu,
+        "sweep": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in results[t].items()}
+                  for t in sweep],
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

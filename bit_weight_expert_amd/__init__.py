@@ -1,0 +1,14 @@
+"""Fused W4A16 Mixture-of-Experts layer for MI355X (gfx950).
+
+Thin Python binding over the C-ABI library libmoe_w4a16.so (declared in
+include/moe_w4a16.h).  The binding only marshals arguments: torch tensors
+provide device memory and the current HIP stream; every step of the layer
+runs in the library's HIP kernels.  There is no fallback: if the library is
+missing, every call raises.
+"""
+from ._binding import (  # noqa: F401
+    ACT, FMT, ROUTE, QuantWeights, MoeError, lib, library_path,
+    moe_align, moe_align_capacity, moe_forward, moe_forward_block_m,
+    moe_forward_workspace_bytes,
+    moe_route, moe_w4a16_gemm1, moe_w4a16_gemm2,
+)

@@ -1,0 +1,245 @@
+"""ctypes marshalling for libmoe_w4a16.so.  Argument checking beyond what the
+library does itself is limited to dtype/device/contiguity of tensors."""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmoe_w4a16.so"
+
+FMT = {"nvfp4": 0, "mxfp4": 1, "gptq": 2}
+ACT = {"swigluoai": 0, "relu2": 1, "none": 2}
+ROUTE = {"softmax": 0, "sigmoid_bias": 1}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({_status_str(status)})")
+
+
+class _Wq(ctypes.Structure):
+    _fields_ = [
+        ("fmt", ctypes.c_int),
+        ("group_size", ctypes.c_int),
+        ("qweight", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("zeros", ctypes.c_void_p),
+        ("global_scale", ctypes.c_void_p),
+        ("g_idx", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (built in-tree by bit_weight_expert_amd.build)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run python -m bit_weight_expert_amd.build")
+        L = ctypes.CDLL(path)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        wq = ctypes.POINTER(_Wq)
+        L.moe_align_capacity.argtypes = [i, i, i, i]
+        L.moe_align_capacity.restype = sz
+        L.moe_forward_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.moe_forward_workspace_bytes.restype = sz
+        L.moe_forward_block_m.argtypes = [i, i, i]
+        L.moe_forward_block_m.restype = i
+        L.moe_status_str.argtypes = [i]
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_route.argtypes = [vp, i, i, i, i, vp, i, vp, vp, vp]
+        L.moe_route.restype = i
+        L.moe_align.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
+        L.moe_align.restype = i
+        L.moe_w4a16_gemm1.argtypes = [vp, i, i, i, i, i, wq, i, f, f, f, vp, vp, vp, i, vp, vp]
+        L.moe_w4a16_gemm1.restype = i
+        L.moe_w4a16_gemm2.argtypes = [vp, i, i, i, i, wq, vp, i, vp, vp, vp, i, vp, vp]
+        L.moe_w4a16_gemm2.restype = i
+        L.moe_forward.argtypes = [vp, vp, i, i, i, i, i, i, vp, i, wq, wq, i, f, f, f, i, vp, sz,
+                                  vp, vp]
+        L.moe_forward.restype = i
+        _lib = L
+    return _lib
+
+
+def _status_str(s: int) -> str:
+    try:
+        return lib().moe_status_str(s).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise MoeError(status, what)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name}: expected a contiguous {dtype} CUDA tensor, got {t.dtype} "
+                        f"on {t.device} (contiguous={t.is_contiguous()})")
+    return t
+
+
+@dataclasses.dataclass
+class QuantWeights:
+    """Device-resident 4-bit weights of all experts; logical W_e is [N][K]."""
+    fmt: str
+    group: int
+    N: int
+    K: int
+    qweight: torch.Tensor
+    scales: torch.Tensor
+    zeros: torch.Tensor | None = None
+    global_scale: torch.Tensor | None = None
+    bias: torch.Tensor | None = None
+
+    @classmethod
+    def from_arrays(cls, fmt, group, N, K, qweight, scales, zeros=None, global_scale=None,
+                    bias=None, device="cuda"):
+        """Upload host arrays (numpy) holding the storage bytes."""
+        def up(a, dt):
+            if a is None:
+                return None
+            return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+        sdt = np.float16 if fmt == "gptq" else np.uint8
+        return cls(fmt=fmt, group=group, N=N, K=K,
+                   qweight=up(qweight, np.int32 if fmt == "gptq" else np.uint8),
+                   scales=up(scales, sdt), zeros=up(zeros, np.int32),
+                   global_scale=up(global_scale, np.float32), bias=up(bias, np.int16))
+
+    def struct(self) -> _Wq:
+        return _Wq(FMT[self.fmt], self.group, _ptr(self.qweight), _ptr(self.scales),
+                   _ptr(self.zeros), _ptr(self.global_scale), None, _ptr(self.bias))
+
+    @property
+    def E(self) -> int:
+        return self.qweight.shape[0]
+
+
+def moe_align_capacity(T: int, top_k: int, E: int, block_m: int) -> int:
+    return lib().moe_align_capacity(T, top_k, E, block_m)
+
+
+def moe_forward_block_m(T: int, top_k: int, E: int) -> int:
+    return lib().moe_forward_block_m(T, top_k, E)
+
+
+def moe_forward_workspace_bytes(T: int, E: int, top_k: int, hidden: int, inter: int) -> int:
+    return lib().moe_forward_workspace_bytes(T, E, top_k, hidden, inter)
+
+
+def moe_route(logits: torch.Tensor, top_k: int, kind: str = "softmax", expert_bias=None,
+              renormalize: bool = True, topk_ids=None, topk_w=None):
+    """-> (topk_ids int32 [T,k], topk_w float32 [T,k])."""
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    if expert_bias is not None:
+        _dev(expert_bias, torch.float32, "expert_bias")
+    _check(lib().moe_route(_ptr(logits), T, E, top_k, ROUTE[kind], _ptr(expert_bias),
+                           int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_w), _stream()),
+           "moe_route")
+    return topk_ids, topk_w
+
+
+def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, sorted_ids=None, expert_ids=None,
+              num_post_pad=None):
+    """-> (sorted_ids int32 [cap], expert_ids int32 [cap/block_m], num_post_pad int32 [1])."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    cap = moe_align_capacity(T, k, E, block_m)
+    dev = topk_ids.device
+    if sorted_ids is None:
+        sorted_ids = torch.empty((cap,), dtype=torch.int32, device=dev)
+    if expert_ids is None:
+        expert_ids = torch.empty((cap // block_m if block_m else 0,), dtype=torch.int32, device=dev)
+    if num_post_pad is None:
+        num_post_pad = torch.zeros((1,), dtype=torch.int32, device=dev)
+    _check(lib().moe_align(_ptr(topk_ids), T, k, E, block_m, _ptr(sorted_ids), _ptr(expert_ids),
+                           _ptr(num_post_pad), _stream()), "moe_align")
+    return sorted_ids, expert_ids, num_post_pad
+
+
+def moe_w4a16_gemm1(x: torch.Tensor, top_k: int, w13: QuantWeights, act: str, alpha: float,
+                    beta: float, limit: float, sorted_ids, expert_ids, num_post_pad,
+                    block_m: int, out=None):
+    """x bf16 [size_m, K] -> out bf16 [size_m*top_k, N/2 (gated) or N]."""
+    _dev(x, torch.bfloat16, "x")
+    size_m, K = x.shape
+    n_out = w13.N // 2 if act == "swigluoai" else w13.N
+    if out is None:
+        out = torch.zeros((size_m * top_k, n_out), dtype=torch.bfloat16, device=x.device)
+    s = w13.struct()
+    _check(lib().moe_w4a16_gemm1(_ptr(x), size_m, top_k, K, w13.N, w13.E, ctypes.byref(s),
+                                 ACT[act], alpha, beta, limit, _ptr(sorted_ids), _ptr(expert_ids),
+                                 _ptr(num_post_pad), block_m, _ptr(out), _stream()),
+           "moe_w4a16_gemm1")
+    return out
+
+
+def moe_w4a16_gemm2(a: torch.Tensor, w2: QuantWeights, topk_w, mul_topk_weights: bool,
+                    sorted_ids, expert_ids, num_post_pad, block_m: int, out=None):
+    """a bf16 [size_m, K] (one row per flat slot) -> y bf16 [size_m, N]."""
+    _dev(a, torch.bfloat16, "a")
+    size_m, K = a.shape
+    if out is None:
+        out = torch.zeros((size_m, w2.N), dtype=torch.bfloat16, device=a.device)
+    s = w2.struct()
+    _check(lib().moe_w4a16_gemm2(_ptr(a), size_m, K, w2.N, w2.E, ctypes.byref(s),
+                                 _ptr(topk_w), int(bool(mul_topk_weights)), _ptr(sorted_ids),
+                                 _ptr(expert_ids), _ptr(num_post_pad), block_m, _ptr(out),
+                                 _stream()), "moe_w4a16_gemm2")
+    return out
+
+
+def moe_forward(x: torch.Tensor, logits: torch.Tensor, top_k: int, inter: int,
+                w13: QuantWeights, w2: QuantWeights, act: str = "swigluoai",
+                route: str = "softmax", expert_bias=None, renormalize: bool = True,
+                alpha: float = 1.702, beta: float = 1.0, limit: float = 7.0,
+                mul_topk_weights: bool = True, workspace=None, out=None):
+    """The whole layer: x bf16 [T, hidden], logits f32 [T, E] -> out bf16 [T, hidden]."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(logits, torch.float32, "logits")
+    T, hidden = x.shape
+    E = logits.shape[1]
+    need = moe_forward_workspace_bytes(T, E, top_k, hidden, inter)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
+    s13, s2 = w13.struct(), w2.struct()
+    _check(lib().moe_forward(_ptr(x), _ptr(logits), T, E, top_k, hidden, inter, ROUTE[route],
+                             _ptr(expert_bias), int(bool(renormalize)), ctypes.byref(s13),
+                             ctypes.byref(s2), ACT[act], alpha, beta, limit,
+                             int(bool(mul_topk_weights)), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _ptr(out), _stream()),
+           "moe_forward")
+    return out

@@ -1,0 +1,280 @@
+// C-ABI of the fused W4A16 MoE library: host-side validation and dispatch.
+// Every entry point checks its arguments before enqueueing anything and
+// returns a status; nothing here allocates, synchronises or reads device
+// memory.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_w4a16.h"
+#include "common.h"
+
+extern "C" hipError_t moe_launch_route(const float*, int, int, int, int, const float*, int,
+                                       int32_t*, float*, hipStream_t);
+extern "C" hipError_t moe_launch_align(const int32_t*, int, int, int, int, int32_t*, int32_t*,
+                                       int32_t*, hipStream_t);
+extern "C" hipError_t moe_launch_gemm(int, int, int, int, const uint16_t*, int, int, int, int, int,
+                                      const moe::WeightArgs*, const int32_t*, const int32_t*,
+                                      const int32_t*, const float*, int, float, float, float,
+                                      uint16_t*, int, hipStream_t);
+extern "C" hipError_t moe_launch_sum(const uint16_t*, const int32_t*, int, int, int, int,
+                                     uint16_t*, hipStream_t);
+
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxTopK = 16;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_block_m(int b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+
+size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Validate one weight family for logical [N][K] and build the kernel view.
+moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out) {
+  if (w == nullptr || w->qweight == nullptr || w->scales == nullptr) return MOE_ERR_NULL;
+  if (K <= 0 || N <= 0 || K % 32 != 0 || N % 16 != 0) return MOE_ERR_SHAPE;
+  switch (w->fmt) {
+    case MOE_W_NVFP4:
+      if (w->group_size != 16) return MOE_ERR_UNSUPPORTED;
+      if (w->global_scale == nullptr) return MOE_ERR_NULL;
+      break;
+    case MOE_W_MXFP4:
+      if (w->group_size != 32) return MOE_ERR_UNSUPPORTED;
+      break;
+    case MOE_W_INT4_GPTQ:
+      if (w->group_size != 32 && w->group_size != 64 && w->group_size != 128)
+        return MOE_ERR_UNSUPPORTED;
+      if (K % w->group_size != 0) return MOE_ERR_SHAPE;
+      if (w->zeros == nullptr) return MOE_ERR_NULL;
+      if (w->g_idx != nullptr) return MOE_ERR_UNSUPPORTED;
+      break;
+    default:
+      return MOE_ERR_UNSUPPORTED;
+  }
+  if (!aligned16(w->qweight)) return MOE_ERR_ALIGN;
+  if (w->fmt == MOE_W_NVFP4 && (reinterpret_cast<uintptr_t>(w->scales) & 1u)) return MOE_ERR_ALIGN;
+  if (w->fmt == MOE_W_INT4_GPTQ &&
+      ((reinterpret_cast<uintptr_t>(w->scales) & 1u) || (reinterpret_cast<uintptr_t>(w->zeros) & 3u)))
+    return MOE_ERR_ALIGN;
+  if (w->bias != nullptr && (reinterpret_cast<uintptr_t>(w->bias) & 1u)) return MOE_ERR_ALIGN;
+  out->qweight = static_cast<const uint8_t*>(w->qweight);
+  out->scales = static_cast<const uint8_t*>(w->scales);
+  out->zeros = static_cast<const uint32_t*>(w->zeros);
+  out->global_scale = w->global_scale;
+  out->bias = w->bias;
+  out->group = w->group_size;
+  return MOE_OK;
+}
+
+int epi_of(moe_act_t act) {
+  switch (act) {
+    case MOE_ACT_SWIGLUOAI: return moe::EPI_SWIGLU;
+    case MOE_ACT_RELU2: return moe::EPI_RELU2;
+    case MOE_ACT_NONE: return moe::EPI_NONE;
+    default: return -1;
+  }
+}
+
+// block_m for moe_forward: the smallest tile that the average expert load fills.
+int pick_block_m(int T, int top_k, int E) {
+  const long avg = ((long)T * top_k + E - 1) / E;
+  if (avg <= 16) return 16;
+  if (avg <= 32) return 32;
+  if (avg <= 64) return 64;
+  return 128;
+}
+
+struct WsLayout {
+  size_t ids, w, sorted, eids, npp, act, y, total;
+};
+
+WsLayout ws_layout(int T, int E, int top_k, int hidden, int inter, int block_m) {
+  WsLayout L;
+  const size_t n = (size_t)T * top_k;
+  const size_t cap = moe_align_capacity(T, top_k, E, block_m);
+  size_t o = 0;
+  L.ids = o; o = round_up(o + n * 4, 256);
+  L.w = o; o = round_up(o + n * 4, 256);
+  L.sorted = o; o = round_up(o + cap * 4, 256);
+  L.eids = o; o = round_up(o + (cap / block_m) * 4, 256);
+  L.npp = o; o = round_up(o + 4, 256);
+  L.act = o; o = round_up(o + n * (size_t)inter * 2, 256);
+  L.y = o; o = round_up(o + n * (size_t)hidden * 2, 256);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_align_capacity(int T, int top_k, int E, int block_m) {
+  if (T <= 0 || top_k <= 0 || E <= 0 || block_m <= 0) return 0;
+  const size_t n = (size_t)T * top_k;
+  const size_t hit = n < (size_t)E ? n : (size_t)E;
+  return round_up(n + hit * (size_t)(block_m - 1), (size_t)block_m);
+}
+
+const char* moe_status_str(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "required pointer is NULL";
+    case MOE_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case MOE_ERR_UNSUPPORTED: return "unsupported format/activation/option";
+    case MOE_ERR_ALIGN: return "pointer not sufficiently aligned";
+    case MOE_ERR_HIP: return "HIP launch error";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_route(const float* logits, int T, int E, int top_k, moe_route_t kind,
+                       const float* expert_bias, int renormalize, int32_t* topk_ids, float* topk_w,
+                       moe_stream_t stream) {
+  if (T < 0 || E <= 0 || E > kMaxE || top_k < 1 || top_k > E || top_k > kMaxTopK)
+    return MOE_ERR_SHAPE;
+  if (kind != MOE_ROUTE_SOFTMAX && kind != MOE_ROUTE_SIGMOID_BIAS) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (logits == nullptr || topk_ids == nullptr || topk_w == nullptr) return MOE_ERR_NULL;
+  if (kind == MOE_ROUTE_SIGMOID_BIAS && expert_bias == nullptr) return MOE_ERR_NULL;
+  return hip_status(moe_launch_route(logits, T, E, top_k, (int)kind, expert_bias, renormalize ? 1 : 0,
+                                     topk_ids, topk_w, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
+                       int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_post_pad,
+                       moe_stream_t stream) {
+  if (T < 0 || top_k < 1 || E <= 0 || E > kMaxE || !valid_block_m(block_m)) return MOE_ERR_SHAPE;
+  if ((long long)T * top_k >= (1LL << 24)) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (topk_ids == nullptr || sorted_ids == nullptr || expert_ids == nullptr ||
+      num_post_pad == nullptr)
+    return MOE_ERR_NULL;
+  const int cap = (int)moe_align_capacity(T, top_k, E, block_m);
+  return hip_status(moe_launch_align(topk_ids, T * top_k, E, block_m, cap, sorted_ids, expert_ids,
+                                     num_post_pad, static_cast<hipStream_t>(stream)));
+}
+
+static moe_status_t gemm_common_checks(int size_m, int top_k, int E, int block_m) {
+  if (size_m < 0 || top_k < 1 || E <= 0 || E > kMaxE || !valid_block_m(block_m))
+    return MOE_ERR_SHAPE;
+  if ((long long)size_m * top_k >= (1LL << 24)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+moe_status_t moe_w4a16_gemm1(const uint16_t* x, int size_m, int top_k, int K, int N, int E,
+                             const moe_wq_t* w13, moe_act_t act, float alpha, float beta,
+                             float limit, const int32_t* sorted_ids, const int32_t* expert_ids,
+                             const int32_t* num_post_pad, int block_m, uint16_t* out,
+                             moe_stream_t stream) {
+  moe_status_t st = gemm_common_checks(size_m, top_k, E, block_m);
+  if (st != MOE_OK) return st;
+  const int epi = epi_of(act);
+  if (epi < 0) return MOE_ERR_UNSUPPORTED;
+  moe::WeightArgs W;
+  st = check_weights(w13, N, K, &W);
+  if (st != MOE_OK) return st;
+  if (epi == moe::EPI_SWIGLU && N % 32 != 0) return MOE_ERR_SHAPE;
+  if (size_m == 0) return MOE_OK;
+  if (x == nullptr || sorted_ids == nullptr || expert_ids == nullptr || num_post_pad == nullptr ||
+      out == nullptr)
+    return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
+  const int cap = (int)moe_align_capacity(size_m, top_k, E, block_m);
+  const int out_ld = (epi == moe::EPI_SWIGLU) ? N / 2 : N;
+  return hip_status(moe_launch_gemm((int)w13->fmt, epi, block_m, cap, x, top_k, size_m * top_k, K, N, E,
+                                    &W, sorted_ids, expert_ids, num_post_pad, nullptr, 0, alpha,
+                                    beta, limit, out, out_ld, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_w4a16_gemm2(const uint16_t* a, int size_m, int K, int N, int E,
+                             const moe_wq_t* w2, const float* topk_w, int mul_topk_weights,
+                             const int32_t* sorted_ids, const int32_t* expert_ids,
+                             const int32_t* num_post_pad, int block_m, uint16_t* y,
+                             moe_stream_t stream) {
+  moe_status_t st = gemm_common_checks(size_m, 1, E, block_m);
+  if (st != MOE_OK) return st;
+  moe::WeightArgs W;
+  st = check_weights(w2, N, K, &W);
+  if (st != MOE_OK) return st;
+  if (size_m == 0) return MOE_OK;
+  if (a == nullptr || sorted_ids == nullptr || expert_ids == nullptr || num_post_pad == nullptr ||
+      y == nullptr)
+    return MOE_ERR_NULL;
+  if (mul_topk_weights && topk_w == nullptr) return MOE_ERR_NULL;
+  if (!aligned16(a) || !aligned16(y)) return MOE_ERR_ALIGN;
+  const int cap = (int)moe_align_capacity(size_m, 1, E, block_m);
+  return hip_status(moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, a, 1, size_m, K, N, E, &W,
+                                    sorted_ids, expert_ids, num_post_pad, topk_w,
+                                    mul_topk_weights ? 1 : 0, 0.f, 0.f, 0.f, y, N,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward_block_m(int T, int top_k, int E) {
+  if (T <= 0 || top_k <= 0 || E <= 0) return 16;
+  return pick_block_m(T, top_k, E);
+}
+
+size_t moe_forward_workspace_bytes(int T, int E, int top_k, int hidden, int inter) {
+  if (T <= 0 || E <= 0 || top_k <= 0 || hidden <= 0 || inter <= 0) return 0;
+  return ws_layout(T, E, top_k, hidden, inter, pick_block_m(T, top_k, E)).total;
+}
+
+moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, int top_k,
+                         int hidden, int inter, moe_route_t kind, const float* expert_bias,
+                         int renormalize, const moe_wq_t* w13, const moe_wq_t* w2, moe_act_t act,
+                         float alpha, float beta, float limit, int mul_topk_weights,
+                         void* workspace, size_t workspace_bytes, uint16_t* out,
+                         moe_stream_t stream) {
+  if (T < 0 || E <= 0 || E > kMaxE || top_k < 1 || top_k > E || top_k > kMaxTopK)
+    return MOE_ERR_SHAPE;
+  if ((long long)T * top_k >= (1LL << 24)) return MOE_ERR_SHAPE;
+  if (kind != MOE_ROUTE_SOFTMAX && kind != MOE_ROUTE_SIGMOID_BIAS) return MOE_ERR_UNSUPPORTED;
+  const int epi = epi_of(act);
+  if (epi != moe::EPI_SWIGLU && epi != moe::EPI_RELU2) return MOE_ERR_UNSUPPORTED;
+  const int n1 = (epi == moe::EPI_SWIGLU) ? 2 * inter : inter;
+  moe::WeightArgs W13, W2;
+  moe_status_t st = check_weights(w13, n1, hidden, &W13);
+  if (st != MOE_OK) return st;
+  st = check_weights(w2, hidden, inter, &W2);
+  if (st != MOE_OK) return st;
+  if (epi == moe::EPI_SWIGLU && n1 % 32 != 0) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || logits == nullptr || out == nullptr || workspace == nullptr) return MOE_ERR_NULL;
+  if (kind == MOE_ROUTE_SIGMOID_BIAS && expert_bias == nullptr) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return MOE_ERR_ALIGN;
+  const int block_m = pick_block_m(T, top_k, E);
+  const WsLayout L = ws_layout(T, E, top_k, hidden, inter, block_m);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  float* tw = reinterpret_cast<float*>(ws + L.w);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* eids = reinterpret_cast<int32_t*>(ws + L.eids);
+  int32_t* npp = reinterpret_cast<int32_t*>(ws + L.npp);
+  uint16_t* actb = reinterpret_cast<uint16_t*>(ws + L.act);
+  uint16_t* yb = reinterpret_cast<uint16_t*>(ws + L.y);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n = T * top_k;
+  const int cap = (int)moe_align_capacity(T, top_k, E, block_m);
+
+  hipError_t e = moe_launch_route(logits, T, E, top_k, (int)kind, expert_bias, renormalize ? 1 : 0,
+                                  ids, tw, s);
+  if (e == hipSuccess) e = moe_launch_align(ids, n, E, block_m, cap, sorted, eids, npp, s);
+  if (e == hipSuccess)
+    e = moe_launch_gemm((int)w13->fmt, epi, block_m, cap, x, top_k, n, hidden, n1, E, &W13, sorted, eids,
+                        npp, nullptr, 0, alpha, beta, limit, actb, inter, s);
+  if (e == hipSuccess)
+    e = moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, actb, 1, n, inter, hidden, E, &W2,
+                        sorted, eids, npp, tw, mul_topk_weights ? 1 : 0, 0.f, 0.f, 0.f, yb, hidden,
+                        s);
+  if (e == hipSuccess) e = moe_launch_sum(yb, ids, T, top_k, hidden, E, out, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

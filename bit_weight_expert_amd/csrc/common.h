@@ -1,0 +1,44 @@
+// Internal helpers shared by the HIP sources of the library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+
+// Weight formats and epilogues (values match the public enums).
+enum { FMT_NVFP4 = 0, FMT_MXFP4 = 1, FMT_GPTQ = 2 };
+enum { EPI_SWIGLU = 0, EPI_RELU2 = 1, EPI_NONE = 2, EPI_DOWN = 3 };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// float -> bf16 bits, round to nearest even (inputs here are finite or NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = (__bf16)f;
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Parameters of one weight family as the kernels see them.
+struct WeightArgs {
+  const uint8_t* qweight;      // NVFP4/MXFP4: [E][N][K/2]; GPTQ: int32 words [E][K/8][N]
+  const uint8_t* scales;       // e4m3 / e8m0 bytes, or fp16 [E][K/G][N]
+  const uint32_t* zeros;       // GPTQ zero words [E][K/G][N/8]
+  const float* global_scale;   // NVFP4 [E]
+  const uint16_t* bias;        // bf16 [E][N] or null
+  int group;
+};
+
+}  // namespace moe

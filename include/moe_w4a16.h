@@ -1,0 +1,199 @@
+/*
+ * moe_w4a16.h -- fused Mixture-of-Experts layer with 4-bit expert weights and
+ * bf16 activations (W4A16) for AMD MI355X (gfx950).
+ *
+ * The layer, step by step (the steps of the fused MoE call that the
+ * "moe_wna16_marlin_gemm applies wrong per-row topk weights" page replays):
+ *
+ *   moe_route        router logits -> top-k expert ids and routing weights
+ *   moe_align        flat slots sorted by expert, each expert padded to block_m
+ *   moe_w4a16_gemm1  grouped GEMM with the gate/up weights (w13), bias and the
+ *                    swigluoai or ReLU^2 activation fused in the epilogue
+ *   moe_w4a16_gemm2  grouped GEMM with the down weights (w2), bias and the
+ *                    per-row routing weight fused in the epilogue
+ *   moe_forward      all of the above plus the sum of each token's top-k rows
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is device memory owned by the caller (global
+ *   memory of the GPU current on the calling thread), contiguous, row-major.
+ *   The library allocates nothing, never synchronises, never reads device
+ *   memory from the host and keeps no state between calls: all work is
+ *   enqueued on `stream` (a hipStream_t; NULL is the default stream).
+ * - bf16 values are passed as uint16_t bit patterns.
+ * - A "flat slot" is f = t*top_k + j (token t, choice j).  The padding id in
+ *   sorted_ids is the sentinel size_m*top_k.
+ * - Every call validates its arguments on the host before launching
+ *   anything and returns a status; no C++ exception crosses this boundary.
+ *   A non-MOE_OK status means nothing was enqueued, except MOE_ERR_HIP,
+ *   which reports a launch failure (work enqueued before it may have run).
+ * - Device data conventions: expert ids outside [0, E) are not routed (align
+ *   gives them no slot; the sum skips them).  NaN scales propagate.
+ * - Sizes: K (the reduction length) must be a multiple of 32 and of the
+ *   group size; N must be a multiple of 16 (32 for the gated GEMM1, whose
+ *   rows pair up).  K and N tails are handled exactly: no buffer is padded
+ *   (hidden 2880 stays 2880; "gpt-oss-120b MXFP4 + --enable-expert-parallel
+ *   crashes", root cause: the op's output is the unpadded width).
+ * - Base pointers of qweight, x/a and outputs must be 16-byte aligned.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* a hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* sizes are inconsistent or out of range */
+  MOE_ERR_UNSUPPORTED = 3, /* a format / activation / option combination that is not built */
+  MOE_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned */
+  MOE_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
+  MOE_ERR_WORKSPACE = 6    /* workspace smaller than moe_forward_workspace_bytes() */
+} moe_status_t;
+
+/* 4-bit weight storage formats.
+ * NVFP4: e2m1 codes + fp8-e4m3fn scale per 16 along K + fp32 global scale per
+ *   expert; w = e2m1 * scale * global ("moe_wna16_marlin_gemm applies wrong
+ *   per-row topk weights", minimal repro: ModelOpt NVFP4 layout and its
+ *   dequantised reference).
+ * MXFP4: e2m1 codes + e8m0 shared exponent per 32 along K; w = e2m1 * 2^(s-127)
+ *   ("gpt-oss-120b MXFP4 ..." page names the format; the block layout is the
+ *   OCP microscaling one).
+ * INT4_GPTQ: asymmetric uint4 with uint4 zero points and fp16 scales per
+ *   group along K; w = (q - z) * s (OneCompression "GPT-OSS (mixed_gptq)",
+ *   sections 1 and "Why GPT-OSS needs special handling": group size 64 for
+ *   hidden 2880, 45 groups). */
+typedef enum { MOE_W_NVFP4 = 0, MOE_W_MXFP4 = 1, MOE_W_INT4_GPTQ = 2 } moe_wfmt_t;
+
+/* Epilogue of GEMM1.
+ * SWIGLUOAI: gpt-oss clamped SwiGLU over interleaved rows (row 2i = gate,
+ *   2i+1 = up): g = min(gate, limit), u = clamp(up, -limit, limit),
+ *   a = g * sigmoid(alpha * g) * (u + beta) ("gpt-oss-20b NVFP4 inference is
+ *   broken", Gap 3: alpha/beta/clamp limit, biases, interleaved gate/up).
+ * RELU2: non-gated a = max(h, 0)^2 (Nemotron-3-Nano page, summary and
+ *   environment: non-gated ReLU^2 MoE).
+ * NONE: a = h (the raw pre-activation; for testing GEMM1 alone). */
+typedef enum { MOE_ACT_SWIGLUOAI = 0, MOE_ACT_RELU2 = 1, MOE_ACT_NONE = 2 } moe_act_t;
+
+/* Router.
+ * SOFTMAX: topk(softmax(logits)) ("moe_wna16_marlin_gemm ..." repro, routing
+ *   step); selection on the raw logits, descending, ties to the lower id.
+ * SIGMOID_BIAS: score = sigmoid(l) + bias[e] in fp32 (sigmoid evaluated in
+ *   double and rounded once), top-k of the scores with n_group = 1, weights =
+ *   the selected *unbiased* sigmoids (Nemotron-3-Nano page, Analysis item 3). */
+typedef enum { MOE_ROUTE_SOFTMAX = 0, MOE_ROUTE_SIGMOID_BIAS = 1 } moe_route_t;
+
+/* One family of 4-bit expert weights; logical W_e is [N][K] (out x reduce). */
+typedef struct {
+  moe_wfmt_t fmt;
+  int group_size;             /* NVFP4: 16, MXFP4: 32, GPTQ: 32/64/128; must divide K */
+  const void* qweight;        /* NVFP4/MXFP4: uint8 [E][N][K/2], even k in the low nibble.
+                                 GPTQ: int32 [E][K/8][N], nibble i holds k%8 == i */
+  const void* scales;         /* NVFP4: e4m3fn uint8 [E][N][K/16]; MXFP4: e8m0 uint8 [E][N][K/32];
+                                 GPTQ: fp16 [E][K/G][N] */
+  const void* zeros;          /* GPTQ: int32 [E][K/G][N/8], nibble i holds n%8 == i. Else NULL */
+  const float* global_scale;  /* NVFP4: fp32 [E]. Else NULL */
+  const int32_t* g_idx;       /* GPTQ act-order map; must be NULL (identity) */
+  const uint16_t* bias;       /* bf16 [E][N], or NULL for no bias */
+} moe_wq_t;
+
+/* Length of sorted_ids for T tokens: T*top_k + min(E, T*top_k)*(block_m-1),
+ * rounded up to block_m (every expert that can receive a slot pads to
+ * block_m).  expert_ids has moe_align_capacity()/block_m entries. */
+size_t moe_align_capacity(int T, int top_k, int E, int block_m);
+
+/* Route T tokens over E experts.
+ *   logits      fp32 [T][E]
+ *   expert_bias fp32 [E] for SIGMOID_BIAS, ignored (may be NULL) for SOFTMAX
+ *   renormalize 1: weights divided by their sum over the selected k
+ *   topk_ids    out int32 [T][top_k], descending score, ties to lower id
+ *   topk_w      out fp32 [T][top_k]
+ * Limits: 1 <= top_k <= min(E, 16), E <= 1024, T >= 0 (T = 0 is a no-op). */
+moe_status_t moe_route(const float* logits, int T, int E, int top_k, moe_route_t kind,
+                       const float* expert_bias, int renormalize,
+                       int32_t* topk_ids, float* topk_w, moe_stream_t stream);
+
+/* Stable sort of the T*top_k flat slots by expert id, each expert's run
+ * padded to a multiple of block_m with the sentinel T*top_k ("moe_align_block_size"
+ * in the repro; the reference loop reads blocks with expert id < 0 as empty).
+ *   topk_ids     int32 [T*top_k]
+ *   sorted_ids   out int32 [moe_align_capacity()]: experts ascending, slots
+ *                ascending within an expert, sentinel in padding and past the end
+ *   expert_ids   out int32 [capacity/block_m]: expert of each block, -1 past the end
+ *   num_post_pad out int32 [1]: padded length actually used
+ * block_m in {16, 32, 64, 128}; E <= 1024; T*top_k < 2^24. */
+moe_status_t moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
+                       int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_post_pad,
+                       moe_stream_t stream);
+
+/* Grouped GEMM1 over aligned blocks.  For every real entry f of block b
+ * (expert e = expert_ids[b]):
+ *   h   = W13_e . x[f / top_k] (+ bias13_e)           fp32 accumulate
+ *   out[f][:] = act(h)  bf16 (round to nearest even)
+ *   x    bf16 [size_m][K]
+ *   N    rows of W13 (2*intermediate when gated, intermediate for RELU2/NONE)
+ *   out  bf16 [size_m*top_k][N/2] for SWIGLUOAI, [size_m*top_k][N] otherwise;
+ *        rows of slots that no block covers are left untouched.
+ * sorted_ids / expert_ids / num_post_pad come from moe_align with the same
+ * block_m, size_m and top_k. */
+moe_status_t moe_w4a16_gemm1(const uint16_t* x, int size_m, int top_k, int K, int N, int E,
+                             const moe_wq_t* w13, moe_act_t act, float alpha, float beta,
+                             float limit, const int32_t* sorted_ids, const int32_t* expert_ids,
+                             const int32_t* num_post_pad, int block_m, uint16_t* out,
+                             moe_stream_t stream);
+
+/* Grouped GEMM2 in the top_k = 1 view: A rows are already one per flat slot.
+ * For every real entry f of block b (expert e):
+ *   y[f][:] = (W2_e . a[f] (+ bias2_e)) * (mul_topk_weights ? topk_w[f] : 1)
+ * The routing weight is read from topk_w at the row's own flat slot ("moe_wna16_marlin_gemm
+ * applies wrong per-row topk weights": the fix is exactly that each row gets its
+ * own weight).
+ *   a      bf16 [size_m][K]         (size_m = T*top_k)
+ *   topk_w fp32 [size_m]            (may be NULL when mul_topk_weights = 0)
+ *   y      bf16 [size_m][N]; rows no block covers are left untouched. */
+moe_status_t moe_w4a16_gemm2(const uint16_t* a, int size_m, int K, int N, int E,
+                             const moe_wq_t* w2, const float* topk_w, int mul_topk_weights,
+                             const int32_t* sorted_ids, const int32_t* expert_ids,
+                             const int32_t* num_post_pad, int block_m, uint16_t* y,
+                             moe_stream_t stream);
+
+/* The block_m moe_forward uses for T tokens (the smallest of 16/32/64/128
+ * that covers the average number of slots per expert, T*top_k/E); callers
+ * that run the steps one by one can use it to get the same tiling. */
+int moe_forward_block_m(int T, int top_k, int E);
+
+/* Bytes of scratch moe_forward needs (routing results, align metadata and
+ * the two intermediates act [T*top_k][inter] and y [T*top_k][hidden] in bf16). */
+size_t moe_forward_workspace_bytes(int T, int E, int top_k, int hidden, int inter);
+
+/* The whole layer: route -> align -> gemm1 -> gemm2 -> sum over each token's
+ * top_k rows (fp32, j ascending, one bf16 rounding).
+ *   x          bf16 [T][hidden]
+ *   logits     fp32 [T][E]
+ *   w13        N = 2*inter (SWIGLUOAI) or inter (RELU2), K = hidden
+ *   w2         N = hidden, K = inter
+ *   workspace  device scratch of at least moe_forward_workspace_bytes(), 256-byte aligned
+ *   out        bf16 [T][hidden] (the unpadded width)
+ * block_m is chosen by the library from T*top_k/E. */
+moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, int top_k,
+                         int hidden, int inter, moe_route_t kind, const float* expert_bias,
+                         int renormalize, const moe_wq_t* w13, const moe_wq_t* w2,
+                         moe_act_t act, float alpha, float beta, float limit,
+                         int mul_topk_weights, void* workspace, size_t workspace_bytes,
+                         uint16_t* out, moe_stream_t stream);
+
+/* Static description of a status code. */
+const char* moe_status_str(moe_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

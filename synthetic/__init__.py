@@ -19,17 +19,20 @@ Workload shapes follow the pages:
     sigmoid+bias grouped top-k with n_group=1 ("NVFP4 MoE monolithic backend
     ... Nemotron-3-Nano", environment section).
 
-Recipe (applies to every config): NumPy PCG64 seeded with 1000*cfg+7; draw
-order logits -> per-expert offsets / router bias -> x -> W13 (expert by
-expert) -> b13 -> W2 (expert by expert) -> b2.  x and logits are drawn at the
-largest token count and smaller T take the leading rows.  Weights are
+Recipe (applies to every config): NumPy PCG64 streams spawned from
+SeedSequence(1000*cfg+7) -- child 0 draws the logits, then the per-expert
+logit offsets or router bias; child 1 draws x; children 2 and 3 draw W13 and
+W2, one grandchild stream per expert plus one for the bias.  x and logits are
+drawn at the largest token count and smaller T take the leading rows.  Weights are
 N(0, 0.02) float32 (0.02 is the standard deviation) and quantised as below;
 biases N(0, 0.02) rounded to bf16; activations N(0, 1) rounded to bf16;
 logits N(0, 1) float32.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+
 import numpy as np
 
 # --------------------------------------------------------------------------
@@ -202,40 +205,56 @@ class Layer:
         return dataclasses.replace(self, logits=self.logits[:T], x=self.x[:T])
 
 
-def _make_weights(rng, fmt, group, E, N, K, bias, interleave_from=None):
-    """Draw E experts of W[N, K] ~ N(0, 0.02), quantise each, then the bias."""
-    buf = np.empty((N, K), dtype=np.float32)
+def _make_weights(ss, fmt, group, E, N, K, bias, threads=8):
+    """Draw E experts of W[N, K] ~ N(0, 0.02), quantise each, then the bias.
+
+    Expert e draws from its own child stream ss.spawn(E+1)[e] (the last child
+    draws the bias), so experts can be generated in parallel and the bytes do
+    not depend on the thread count.
+    """
+    kids = ss.spawn(E + 1)
     if fmt in ("nvfp4", "mxfp4"):
         qweight = np.empty((E, N, K // 2), dtype=np.uint8)
         scales = np.empty((E, N, K // group), dtype=np.uint8)
+        zeros = None
     else:
         qweight = np.empty((E, K // 8, N), dtype=np.int32)
         scales = np.empty((E, K // group, N), dtype=np.float16)
         zeros = np.empty((E, K // group, N // 8), dtype=np.int32)
     gscale = np.empty((E,), dtype=np.float32) if fmt == "nvfp4" else None
-    for e in range(E):
-        rng.standard_normal(out=buf, dtype=np.float32)
-        buf *= np.float32(0.02)
+
+    def one(e):
+        w = np.random.Generator(np.random.PCG64(kids[e])).standard_normal((N, K), dtype=np.float32)
+        w *= np.float32(0.02)
         if fmt == "nvfp4":
-            qweight[e], scales[e], gscale[e] = quantize_nvfp4(buf, group)
+            qweight[e], scales[e], gscale[e] = quantize_nvfp4(w, group)
         elif fmt == "mxfp4":
-            qweight[e], scales[e] = quantize_mxfp4(buf, group)
+            qweight[e], scales[e] = quantize_mxfp4(w, group)
         else:
-            qweight[e], zeros[e], scales[e] = quantize_gptq(buf, group)
+            qweight[e], zeros[e], scales[e] = quantize_gptq(w, group)
+
+    if threads > 1 and E > 1:
+        with concurrent.futures.ThreadPoolExecutor(min(threads, E)) as ex:
+            list(ex.map(one, range(E)))
+    else:
+        for e in range(E):
+            one(e)
     b = None
     if bias:
-        b = f32_to_bf16_bits(rng.standard_normal((E, N), dtype=np.float32) * np.float32(0.02))
+        rb = np.random.Generator(np.random.PCG64(kids[E]))
+        b = f32_to_bf16_bits(rb.standard_normal((E, N), dtype=np.float32) * np.float32(0.02))
     return Weights(fmt=fmt, group=group, N=N, K=K, qweight=qweight, scales=scales,
-                   zeros=zeros if fmt == "gptq" else None, global_scale=gscale, bias=b)
+                   zeros=zeros, global_scale=gscale, bias=b)
 
 
 def make_layer(*, E, top_k, H, I, fmt, act="swigluoai", route="softmax", T,
                seed, group=None, bias=True, skew_std=0.0, router_bias_std=0.0,
                renormalize=True, mul_topk_weights=True, alpha=1.702, beta=1.0,
-               limit=7.0, x_std=1.0) -> Layer:
+               limit=7.0, x_std=1.0, threads=8) -> Layer:
     """Draw one synthetic MoE layer (see the module docstring for the recipe)."""
     group = group or DEFAULT_GROUP[fmt]
-    rng = np.random.Generator(np.random.PCG64(seed))
+    ss_router, ss_x, ss_w13, ss_w2 = np.random.SeedSequence(seed).spawn(4)
+    rng = np.random.Generator(np.random.PCG64(ss_router))
     logits = rng.standard_normal((T, E), dtype=np.float32)
     expert_bias = None
     if skew_std > 0:
@@ -243,10 +262,11 @@ def make_layer(*, E, top_k, H, I, fmt, act="swigluoai", route="softmax", T,
         logits = (logits + off[None, :]).astype(np.float32)
     if route == "sigmoid_bias":
         expert_bias = rng.standard_normal((E,), dtype=np.float32) * np.float32(router_bias_std)
-    x = f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32) * np.float32(x_std))
+    rx = np.random.Generator(np.random.PCG64(ss_x))
+    x = f32_to_bf16_bits(rx.standard_normal((T, H), dtype=np.float32) * np.float32(x_std))
     n1 = 2 * I if act == "swigluoai" else I
-    w13 = _make_weights(rng, fmt, group, E, n1, H, bias)
-    w2 = _make_weights(rng, fmt, group, E, H, I, bias)
+    w13 = _make_weights(ss_w13, fmt, group, E, n1, H, bias, threads)
+    w2 = _make_weights(ss_w2, fmt, group, E, H, I, bias, threads)
     return Layer(E=E, top_k=top_k, H=H, I=I, act=act, route=route,
                  renormalize=renormalize, mul_topk_weights=mul_topk_weights,
                  alpha=alpha, beta=beta, limit=limit, logits=logits,
@@ -288,3 +308,26 @@ def make_config(cfg: int, T: int | None = None) -> Layer:
     if T is not None:
         layer = layer.take(T)
     return layer
+
+
+def make_router_inputs(cfg: int, T: int | None = None):
+    """Only the router inputs of a config: (logits f32 [T, E], expert_bias f32 [E] or None).
+
+    Same seed and draw order as make_config (logits and the per-expert
+    offsets / router bias are the first draws), so the values are identical.
+    """
+    c = CONFIGS[cfg]
+    ss_router = np.random.SeedSequence(config_seed(cfg)).spawn(4)[0]
+    rng = np.random.Generator(np.random.PCG64(ss_router))
+    t_draw = max(c["T"])
+    E = c["E"]
+    logits = rng.standard_normal((t_draw, E), dtype=np.float32)
+    if c.get("skew_std", 0.0) > 0:
+        off = rng.standard_normal((E,), dtype=np.float32) * np.float32(c["skew_std"])
+        logits = (logits + off[None, :]).astype(np.float32)
+    bias = None
+    if c["route"] == "sigmoid_bias":
+        bias = rng.standard_normal((E,), dtype=np.float32) * np.float32(c["router_bias_std"])
+    if T is not None:
+        logits = logits[:T]
+    return logits, bias

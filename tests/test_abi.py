@@ -1,0 +1,125 @@
+"""The C-ABI library: it loads, exports every function include/moe_w4a16.h declares,
+and rejects invalid arguments on the host before any launch (CPU only: no call
+here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_weight_expert_amd as M
+from bit_weight_expert_amd._binding import _Wq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w4a16.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, HIP, WS = range(7)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(M.library_path()):
+        pytest.skip("library not built")
+    return M.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert set(names) >= {"moe_route", "moe_align", "moe_w4a16_gemm1", "moe_w4a16_gemm2",
+                          "moe_forward", "moe_align_capacity", "moe_forward_workspace_bytes",
+                          "moe_status_str", "moe_forward_block_m"}
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in the header but not exported"
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert len(L.moe_status_str(s)) > 0
+
+
+def test_capacity_and_workspace(L):
+    assert L.moe_align_capacity(1, 4, 32, 16) == 64          # 4 slots, each may open a block
+    assert L.moe_align_capacity(4096, 4, 32, 128) == 16384 + 32 * 128
+    assert L.moe_align_capacity(0, 4, 32, 16) == 0
+    assert L.moe_forward_workspace_bytes(0, 32, 4, 2880, 2880) == 0
+    ws = L.moe_forward_workspace_bytes(64, 32, 4, 2880, 2880)
+    assert ws >= 64 * 4 * (2880 + 2880) * 2
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _wq(fmt=0, group=16, qweight=FAKE, scales=FAKE, zeros=None, gs=FAKE, g_idx=None, bias=None):
+    return _Wq(fmt, group, qweight, scales, zeros, gs, g_idx, bias)
+
+
+def test_route_rejects(L):
+    assert L.moe_route(FAKE, 4, 8, 9, 0, None, 1, FAKE, FAKE, None) == SHAPE      # top_k > E
+    assert L.moe_route(FAKE, 4, 2048, 4, 0, None, 1, FAKE, FAKE, None) == SHAPE   # E too large
+    assert L.moe_route(FAKE, 4, 64, 17, 0, None, 1, FAKE, FAKE, None) == SHAPE    # top_k > 16
+    assert L.moe_route(None, 4, 8, 2, 0, None, 1, FAKE, FAKE, None) == NULL
+    assert L.moe_route(FAKE, 4, 8, 2, 1, None, 1, FAKE, FAKE, None) == NULL       # bias needed
+    assert L.moe_route(FAKE, 4, 8, 2, 7, None, 1, FAKE, FAKE, None) == UNSUP
+    assert L.moe_route(None, 0, 8, 2, 0, None, 1, None, None, None) == OK         # T = 0: no-op
+
+
+def test_align_rejects(L):
+    assert L.moe_align(FAKE, 4, 2, 8, 48, FAKE, FAKE, FAKE, None) == SHAPE       # block_m
+    assert L.moe_align(FAKE, 4, 2, 0, 16, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.moe_align(FAKE, 1 << 23, 4, 8, 16, FAKE, FAKE, FAKE, None) == SHAPE  # too many slots
+    assert L.moe_align(FAKE, 4, 2, 8, 16, FAKE, None, FAKE, None) == NULL
+    assert L.moe_align(None, 0, 2, 8, 16, None, None, None, None) == OK
+
+
+def _g1(L, w, K=2880, N=5760, act=0, x=FAKE, out=FAKE, block_m=16):
+    return L.moe_w4a16_gemm1(x, 8, 4, K, N, 32, ctypes.byref(w), act, 1.702, 1.0, 7.0,
+                             FAKE, FAKE, FAKE, block_m, out, None)
+
+
+def test_gemm1_rejects(L):
+    assert _g1(L, _wq(), K=2880 + 16) == SHAPE           # K % 32
+    assert _g1(L, _wq(), N=5760 + 8) == SHAPE            # N % 16
+    assert _g1(L, _wq(), N=5760 + 16) == SHAPE           # gated N % 32
+    assert _g1(L, _wq(group=32)) == UNSUP                # NVFP4 is group 16
+    assert _g1(L, _wq(fmt=1, group=16)) == UNSUP         # MXFP4 is group 32
+    assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE), K=2880 + 32) == SHAPE   # K % group
+    assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, g_idx=FAKE)) == UNSUP    # act-order
+    assert _g1(L, _wq(fmt=2, group=64)) == NULL          # zeros missing
+    assert _g1(L, _wq(gs=None)) == NULL                  # NVFP4 global scale missing
+    assert _g1(L, _wq(fmt=9)) == UNSUP
+    assert _g1(L, _wq(), act=5) == UNSUP
+    assert _g1(L, _wq(qweight=FAKE + 8)) == ALIGN
+    assert _g1(L, _wq(), x=FAKE + 2) == ALIGN
+    assert _g1(L, _wq(), x=None) == NULL
+    assert _g1(L, _wq(), block_m=8) == SHAPE
+
+
+def test_gemm2_rejects(L):
+    w = _wq()
+    g2 = lambda **kw: L.moe_w4a16_gemm2(kw.get("a", FAKE), 32, 2880, 2880, 32, ctypes.byref(kw.get("w", w)),
+                                        kw.get("tw", FAKE), kw.get("mul", 1), FAKE, FAKE, FAKE,
+                                        kw.get("bm", 16), kw.get("y", FAKE), None)
+    assert g2(tw=None) == NULL                           # weights needed when multiplying
+    assert g2(bm=256) == SHAPE
+    assert g2(y=None) == NULL
+    assert g2(w=_wq(scales=None)) == NULL
+
+
+def test_forward_rejects(L):
+    w13, w2 = _wq(), _wq()
+    f = lambda **kw: L.moe_forward(FAKE, FAKE, kw.get("T", 8), 32, kw.get("k", 4), 2880, 2880,
+                                   kw.get("kind", 0), None, 1, ctypes.byref(w13), ctypes.byref(w2),
+                                   kw.get("act", 0), 1.702, 1.0, 7.0, 1, kw.get("ws", FAKE * 16),
+                                   kw.get("wsb", 0), FAKE, None)
+    assert f() == WS                                     # workspace too small
+    assert f(ws=FAKE + 16, wsb=1 << 40) == ALIGN         # workspace must be 256-byte aligned
+    assert f(act=2) == UNSUP                             # forward needs a real activation
+    assert f(k=33) == SHAPE
+    assert f(kind=1) == NULL                             # sigmoid routing needs the bias
+    assert f(T=0) == OK

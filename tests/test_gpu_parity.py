@@ -1,0 +1,195 @@
+"""GPU parity: every step of the HIP path against the float64 oracle, through the C-ABI.
+
+Integer results (routing ids, sorted ids, expert ids, padded length) must be
+bit-exact; float results within 5e-3 per-row relative error with no NaN/Inf.
+Shapes here are small enough for the oracle to finish in seconds but span
+several tiles and ragged K / N tails (K = 320 = 2*128 + 64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from oracle import moe as O
+
+pytestmark = pytest.mark.gpu
+
+M = pytest.importorskip("bit_weight_expert_amd")
+from gpu_util import (TOL, assert_rows_close, dev_bf16, gpu_forward, host_bf16,  # noqa: E402
+                      upload, upload_weights)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    M.lib()  # the HIP library must load; no fallback exists
+
+
+# ------------------------------------------------------------------ routing --
+
+@pytest.mark.parametrize("cfg", [1, 2, 4, 5])
+def test_route_bitexact_full_size(cfg):
+    logits, bias = S.make_router_inputs(cfg)
+    c = S.CONFIGS[cfg]
+    ids_ref, w_ref = O.route(logits, c["top_k"], c["route"], bias, True)
+    ids, w = M.moe_route(torch.from_numpy(logits).cuda(), c["top_k"], c["route"],
+                         None if bias is None else torch.from_numpy(bias).cuda(), True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=2e-6, atol=0)
+
+
+@pytest.mark.parametrize("E,k,kind,renorm", [(8, 2, "softmax", False), (130, 5, "sigmoid_bias", True),
+                                             (1024, 16, "softmax", True), (3, 3, "softmax", True)])
+def test_route_shapes(E, k, kind, renorm):
+    rng = np.random.default_rng(E)
+    T = 37
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[0, :] = 0.25                       # all tied: lowest ids win
+    bias = (rng.standard_normal(E) * 0.1).astype(np.float32) if kind == "sigmoid_bias" else None
+    ids_ref, w_ref = O.route(logits, k, kind, bias, renorm)
+    ids, w = M.moe_route(torch.from_numpy(logits).cuda(), k, kind,
+                         None if bias is None else torch.from_numpy(bias).cuda(), renorm)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=2e-6)
+
+
+# -------------------------------------------------------------------- align --
+
+@pytest.mark.parametrize("T,k,E,B", [(1, 4, 32, 16), (13, 2, 8, 16), (64, 4, 32, 64), (511, 6, 128, 32),
+                                      (4096, 4, 32, 128), (8192, 4, 128, 64), (3, 3, 1024, 16)])
+def test_align_bitexact(T, k, E, B):
+    rng = np.random.default_rng(T + E + B)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if T > 3:
+        ids[2, 0] = E + 7          # not routed
+        ids[3, k - 1] = -2
+    ref = O.align(ids, E, B)
+    got = M.moe_align(torch.from_numpy(ids).cuda(), E, B)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got[0].cpu().numpy(), ref[0])
+    np.testing.assert_array_equal(got[1].cpu().numpy(), ref[1])
+    assert int(got[2].item()) == int(ref[2])
+
+
+def test_align_skewed_routing_full_size():
+    logits, _ = S.make_router_inputs(4)          # E=128, T=8192, per-expert offsets
+    ids_ref, _ = O.route(logits, 4, "softmax", None, True)
+    for B in (16, 64, 128):
+        ref = O.align(ids_ref, 128, B)
+        got = M.moe_align(torch.from_numpy(ids_ref).cuda(), 128, B)
+        np.testing.assert_array_equal(got[0].cpu().numpy(), ref[0])
+        np.testing.assert_array_equal(got[1].cpu().numpy(), ref[1])
+        assert int(got[2].item()) == int(ref[2])
+
+
+# -------------------------------------------------------------------- GEMMs --
+
+def _small(fmt, act="swigluoai", E=4, k=2, H=320, I=192, T=13, seed=21, **kw):
+    route = "sigmoid_bias" if act == "relu2" else "softmax"
+    return S.make_layer(E=E, top_k=k, H=H, I=I, fmt=fmt, act=act, route=route, T=T, seed=seed,
+                        router_bias_std=0.1 if route == "sigmoid_bias" else 0.0, **kw)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "gptq"])
+@pytest.mark.parametrize("act", ["none", "swigluoai", "relu2"])
+@pytest.mark.parametrize("B", [16, 64])
+def test_gemm1_parity(fmt, act, B):
+    L = _small(fmt, "relu2" if act == "relu2" else "swigluoai", x_std=12.0)
+    D = upload(L)
+    ids, w = O.route(L)
+    si, ei, npp = O.align(ids, L.E, B)
+    ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, act, L.alpha, L.beta, L.limit, si, ei, npp, B)
+    dsi, dei, dnpp = (torch.from_numpy(a).cuda() for a in (si, ei, np.array([npp], np.int32)))
+    out = M.moe_w4a16_gemm1(D["x"], L.top_k, D["w13"], act, L.alpha, L.beta, L.limit, dsi, dei,
+                            dnpp, B)
+    assert_rows_close(host_bf16(out), ref, rows=cov, what=f"gemm1 {fmt} {act} B{B}")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "gptq"])
+@pytest.mark.parametrize("B", [16, 32, 128])
+def test_gemm2_parity_and_mul_flag(fmt, B):
+    L = _small(fmt, E=5, k=3, T=11)
+    D = upload(L)
+    ids, w = O.route(L)
+    si, ei, npp = O.align(ids, L.E, B)
+    n = L.T * L.top_k
+    rng = np.random.default_rng(3)
+    a_bits = S.f32_to_bf16_bits(rng.standard_normal((n, L.I)).astype(np.float32))
+    tw = w.reshape(-1).astype(np.float32)
+    ref1, cov = O.gemm2(a_bits, n, L.w2, tw, True, si, ei, npp, B)
+    dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
+    a = dev_bf16(a_bits)
+    dtw = torch.from_numpy(tw).cuda()
+    y1 = M.moe_w4a16_gemm2(a, D["w2"], dtw, True, dsi, dei, dnpp, B)
+    y0 = M.moe_w4a16_gemm2(a, D["w2"], dtw, False, dsi, dei, dnpp, B)
+    assert_rows_close(host_bf16(y1), ref1, rows=cov, what=f"gemm2 {fmt} B{B}")
+    # forensic check: the multiplier each row received is its own weight
+    g1, g0 = host_bf16(y1), host_bf16(y0)
+    ratio = (g1 * g0).sum(1) / np.maximum((g0 * g0).sum(1), 1e-30)
+    np.testing.assert_allclose(ratio[cov], tw[cov], rtol=5e-3)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_gemm2_power_of_two_weights_bitwise(fmt):
+    """With routing weights 2^-m the in-kernel multiply equals the external one bit for bit."""
+    L = _small(fmt, E=4, k=4, T=9)
+    D = upload(L)
+    ids, _ = O.route(L)
+    si, ei, npp = O.align(ids, L.E, 16)
+    n = L.T * L.top_k
+    tw = np.ldexp(np.ones(n, np.float32), -(np.arange(n) % 5)).astype(np.float32)
+    rng = np.random.default_rng(4)
+    a = dev_bf16(S.f32_to_bf16_bits(rng.standard_normal((n, L.I)).astype(np.float32)))
+    dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
+    dtw = torch.from_numpy(tw).cuda()
+    y1 = M.moe_w4a16_gemm2(a, D["w2"], dtw, True, dsi, dei, dnpp, 16)
+    y0 = M.moe_w4a16_gemm2(a, D["w2"], dtw, False, dsi, dei, dnpp, 16)
+    ext = (y0.float() * dtw[:, None]).to(torch.bfloat16)
+    assert torch.equal(y1.view(torch.int16), ext.view(torch.int16))
+
+
+# ------------------------------------------------------------------ forward --
+
+@pytest.mark.parametrize("fmt,act", [("nvfp4", "swigluoai"), ("mxfp4", "swigluoai"),
+                                     ("gptq", "swigluoai"), ("nvfp4", "relu2")])
+@pytest.mark.parametrize("T", [1, 13, 100])
+def test_forward_parity_small(fmt, act, T):
+    L = _small(fmt, act, E=6, k=3, T=T, skew_std=1.0)
+    D = upload(L)
+    out = gpu_forward(L, D)
+    ref = O.forward(L)["out"]
+    assert_rows_close(host_bf16(out), ref, what=f"forward {fmt} {act} T{T}")
+
+
+def test_forward_config1_full():
+    L = S.make_config(1)
+    D = upload(L)
+    out = gpu_forward(L, D)
+    ref = O.forward(L)["out"]
+    assert_rows_close(host_bf16(out), ref, what="config 1")
+
+
+def test_forward_deterministic_bitwise():
+    L = _small("nvfp4", E=6, k=3, T=100)
+    D = upload(L)
+    a = gpu_forward(L, D)
+    b = gpu_forward(L, D)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_forward_t0_is_noop():
+    L = _small("nvfp4", T=4)
+    D = upload(L)
+    x0 = D["x"][:0]
+    out = M.moe_forward(x0, D["logits"][:0], L.top_k, L.I, D["w13"], D["w2"])
+    assert out.shape == (0, L.H)
+
+
+def test_forward_top_k_equals_e():
+    L = _small("mxfp4", E=3, k=3, T=7)
+    D = upload(L)
+    out = gpu_forward(L, D)
+    assert_rows_close(host_bf16(out), O.forward(L)["out"], what="top_k = E")
