@@ -27,8 +27,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return b;
 }
 
+// Two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  const f32x2 v = {lo, hi};
+  const bf16x2 r = __builtin_convertvector(v, bf16x2);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
 }
 
 // Parameters of one weight family as the kernels see them.
