@@ -470,7 +470,6 @@ __global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(GemmArgs ga, Weigh
 // decode kernel
 // --------------------------------------------------------------------------
 
-constexpr int kDcWaves = 4;
 constexpr int kDcBK = 256;
 
 // One wave's share of a K chunk: weights of NF fragments plus its A fragments.
@@ -480,16 +479,21 @@ struct DcChunk {
   uint4 a[MI][C / 32];
 };
 
+// A rows of padding slots are not read (their lanes keep stale values, which
+// only reach accumulator rows the epilogue skips).
 template <int FMT, int C, int MI, int NF>
 __device__ __forceinline__ void dc_load(DcChunk<FMT, C, MI, NF>& d, const WeightArgs& W,
                                         const GemmArgs& ga, const uint16_t* const (&arow)[MI],
-                                        const int (&nrow)[NF], int e, int k0, int g) {
+                                        const bool (&aon)[MI], const int (&nrow)[NF], int e, int k0,
+                                        int g) {
   load_frags<FMT, C, NF>(d.b, W, e, nrow, ga.N, ga.K, k0, g);
 #pragma unroll
   for (int i = 0; i < MI; ++i)
+    if (aon[i]) {
 #pragma unroll
-    for (int s = 0; s < C / 32; ++s)
-      d.a[i][s] = *reinterpret_cast<const uint4*>(arow[i] + k0 + g * (C / 4) + 8 * s);
+      for (int s = 0; s < C / 32; ++s)
+        d.a[i][s] = *reinterpret_cast<const uint4*>(arow[i] + k0 + g * (C / 4) + 8 * s);
+    }
 }
 
 template <int FMT, int C, int MI, int NF>
@@ -509,25 +513,47 @@ __device__ __forceinline__ void dc_compute(f32x4 (&acc)[MI][NF], const DcChunk<F
   }
 }
 
-// Workgroup = 16*MI rows x 16*NF columns; the four waves split K and add their
-// partial sums through LDS in wave order.
-template <int FMT, int EPI, int MI, int NF>
-__global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
+template <int FMT, int C, int MI, int NF>
+__device__ __forceinline__ void dc_chunk(f32x4 (&acc)[MI][NF], const WeightArgs& W,
+                                         const GemmArgs& ga, const uint16_t* const (&arow)[MI],
+                                         const bool (&aon)[MI], const int (&nrow)[NF], int e,
+                                         int k0, int g) {
+  DcChunk<FMT, C, MI, NF> d;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int s = 0; s < C / 32; ++s) d.a[i][s] = uint4{0u, 0u, 0u, 0u};
+  dc_load(d, W, ga, arow, aon, nrow, e, k0, g);
+  dc_compute(acc, d);
+}
+
+// Workgroup = 16*MI rows x 16*NF columns and one wave per 256-wide K chunk
+// (blockDim.x / 64 waves, at most MAXT / 64): every chunk of the tile is in
+// flight at once, which is what a weight-streaming GEMV needs.  The waves'
+// partial sums are added through LDS in wave order (deterministic).
+template <int FMT, int EPI, int MI, int NF, int MAXT>
+__global__ void __launch_bounds__(MAXT) gemm_decode_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
   constexpr int BM = 16 * MI;
-  __shared__ f32x4 red[kDcWaves][MI][NF][64];
+  extern __shared__ f32x4 red[];  // [nw][MI][NF][64]
 
   const int mb = blockIdx.x / ga.n_ntiles, nt = blockIdx.x % ga.n_ntiles;
   if (mb * BM >= ga.num_post_pad[0]) return;
   const int e = ga.expert_ids[mb];
   if (e < 0 || e >= ga.E) return;
 
+  const int nw = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
   const int n0 = nt * NF * 16;
 
   const uint16_t* arow[MI];
+  bool aon[MI];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) arow[i] = a_row(ga, ga.sorted_ids[mb * BM + i * 16 + c16]);
+  for (int i = 0; i < MI; ++i) {
+    const int sid = ga.sorted_ids[mb * BM + i * 16 + c16];
+    aon[i] = sid < ga.n_slots;
+    arow[i] = a_row(ga, sid);
+  }
   int nrow[NF];
 #pragma unroll
   for (int j = 0; j < NF; ++j) nrow[j] = frag_on<EPI>(n0, j, ga.N) ? frag_row<EPI>(n0, j, c16) : 0;
@@ -538,71 +564,58 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // wave w takes full chunks w, w+4, ... (two register sets, ping-pong)
   const int nfull = ga.K / kDcBK;
-  {
-    DcChunk<FMT, kDcBK, MI, NF> d0, d1;
-    int c = wave;
-    if (c < nfull) dc_load(d0, W, ga, arow, nrow, e, c * kDcBK, g);
-    while (c < nfull) {
-      const int cn = c + kDcWaves;
-      if (cn < nfull) dc_load(d1, W, ga, arow, nrow, e, cn * kDcBK, g);
-      dc_compute(acc, d0);
-      if (cn >= nfull) break;
-      const int cn2 = cn + kDcWaves;
-      if (cn2 < nfull) dc_load(d0, W, ga, arow, nrow, e, cn2 * kDcBK, g);
-      dc_compute(acc, d1);
-      c = cn2;
-    }
-  }
-  // tail (K % 256) in 128/64/32-wide chunks, one wave each, starting after the last owner
+  for (int c = wave; c < nfull; c += nw)
+    dc_chunk<FMT, kDcBK, MI, NF>(acc, W, ga, arow, aon, nrow, e, c * kDcBK, g);
+  // tail (K % 256) in 128/64/32-wide pieces, one wave each, after the last chunk owner
   int k0 = nfull * kDcBK;
-  int tw = nfull % kDcWaves;
-  auto tail = [&](auto cw_tag) {
-    constexpr int CW = decltype(cw_tag)::value;
-    if (wave == tw) {
-      DcChunk<FMT, CW, MI, NF> d;
-      dc_load(d, W, ga, arow, nrow, e, k0, g);
-      dc_compute(acc, d);
-    }
-    k0 += CW;
-    tw = (tw + 1) % kDcWaves;
-  };
-  if (ga.K - k0 >= 128) tail(std::integral_constant<int, 128>{});
-  if (ga.K - k0 >= 64) tail(std::integral_constant<int, 64>{});
-  if (ga.K - k0 >= 32) tail(std::integral_constant<int, 32>{});
+  int tw = nfull % nw;
+  if (ga.K - k0 >= 128) {
+    if (wave == tw) dc_chunk<FMT, 128, MI, NF>(acc, W, ga, arow, aon, nrow, e, k0, g);
+    k0 += 128;
+    tw = (tw + 1) % nw;
+  }
+  if (ga.K - k0 >= 64) {
+    if (wave == tw) dc_chunk<FMT, 64, MI, NF>(acc, W, ga, arow, aon, nrow, e, k0, g);
+    k0 += 64;
+    tw = (tw + 1) % nw;
+  }
+  if (ga.K - k0 >= 32) {
+    if (wave == tw) dc_chunk<FMT, 32, MI, NF>(acc, W, ga, arow, aon, nrow, e, k0, g);
+  }
 
-  // reduce the four partial sums in wave order
+  // reduce the partial sums in wave order
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NF; ++j) red[wave][i][j][lane] = acc[i][j];
+    for (int j = 0; j < NF; ++j) red[((wave * MI + i) * NF + j) * 64 + lane] = acc[i][j];
   __syncthreads();
-  // wave w finishes fragment group w: one fragment (plain) or one gate/up pair (gated)
+  // wave w finishes fragment groups w, w + nw, ...: one fragment (plain) or one
+  // gate/up pair (gated) each
   constexpr int GF = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int kGroups = NF / GF;
-  if (wave >= kGroups) return;
-  f32x4 fin[MI][GF];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int q = 0; q < GF; ++q) {
-      const int j = wave * GF + q;
-      f32x4 s = red[0][i][j][lane];
-#pragma unroll
-      for (int w2 = 1; w2 < kDcWaves; ++w2) {
-        const f32x4 t = red[w2][i][j][lane];
-        s[0] += t[0];
-        s[1] += t[1];
-        s[2] += t[2];
-        s[3] += t[3];
-      }
-      fin[i][q] = s;
-    }
   EpiArgs a = ea;
   a.row0 = mb * BM;
-  // the fragment group as its own "wave" starting at weight row n0 + 16*GF*wave
-  epilogue<EPI, FMT, MI, GF>(fin, a, W, e, n0 + 16 * GF * wave, lane);
+  for (int grp = wave; grp < kGroups; grp += nw) {
+    f32x4 fin[MI][GF];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int q = 0; q < GF; ++q) {
+        const int j = grp * GF + q;
+        f32x4 s = red[(i * NF + j) * 64 + lane];
+        for (int w2 = 1; w2 < nw; ++w2) {
+          const f32x4 t = red[((w2 * MI + i) * NF + j) * 64 + lane];
+          s[0] += t[0];
+          s[1] += t[1];
+          s[2] += t[2];
+          s[3] += t[3];
+        }
+        fin[i][q] = s;
+      }
+    // the fragment group as its own "wave" starting at weight row n0 + 16*GF*grp
+    epilogue<EPI, FMT, MI, GF>(fin, a, W, e, n0 + 16 * GF * grp, lane);
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -642,14 +655,24 @@ __global__ void __launch_bounds__(256) moe_sum_kernel(const uint16_t* __restrict
 // launch
 // --------------------------------------------------------------------------
 
+template <int FMT, int EPI, int MI, int NF, int MAXT>
+static void launch_decode_nw(const GemmArgs& ga, const WeightArgs& W, const EpiArgs& ea,
+                             hipStream_t st) {
+  const int chunks = ga.K / kDcBK + (ga.K % kDcBK ? 1 : 0);
+  const int nw = chunks < MAXT / 64 ? chunks : MAXT / 64;
+  const size_t lds = (size_t)nw * MI * NF * 64 * sizeof(f32x4);
+  gemm_decode_kernel<FMT, EPI, MI, NF, MAXT>
+      <<<dim3(ga.n_mblocks * ga.n_ntiles), dim3(64 * nw), lds, st>>>(ga, W, ea);
+}
+
 template <int FMT, int EPI, int MI>
 static void launch_decode(int nf, const GemmArgs& ga, const WeightArgs& W, const EpiArgs& ea,
                           hipStream_t st) {
-  const dim3 grid(ga.n_mblocks * ga.n_ntiles);
+  constexpr int kMaxT = MI == 1 ? 768 : 512;
   if (nf == 2)
-    gemm_decode_kernel<FMT, EPI, MI, 2><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+    launch_decode_nw<FMT, EPI, MI, 2, kMaxT>(ga, W, ea, st);
   else
-    gemm_decode_kernel<FMT, EPI, MI, 4><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+    launch_decode_nw<FMT, EPI, MI, 4, kMaxT>(ga, W, ea, st);
 }
 
 template <int FMT, int EPI>

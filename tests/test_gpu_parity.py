@@ -193,3 +193,22 @@ def test_forward_top_k_equals_e():
     D = upload(L)
     out = gpu_forward(L, D)
     assert_rows_close(host_bf16(out), O.forward(L)["out"], what="top_k = E")
+
+
+@pytest.mark.parametrize("K", [32, 96, 224, 256, 288, 480, 544, 4128])
+@pytest.mark.parametrize("B", [16, 32, 64, 128])
+def test_gemm2_k_tails(K, B):
+    """Every K tail decomposition (256-chunks + 128/64/32 pieces) in both kernels."""
+    fmt = "mxfp4" if K % 64 else "nvfp4"
+    L = _small(fmt, E=3, k=2, H=96, I=K, T=40)
+    D = upload(L)
+    ids, w = O.route(L)
+    si, ei, npp = O.align(ids, L.E, B)
+    n = L.T * L.top_k
+    rng = np.random.default_rng(K)
+    a_bits = S.f32_to_bf16_bits(rng.standard_normal((n, K)).astype(np.float32))
+    tw = w.reshape(-1).astype(np.float32)
+    ref, cov = O.gemm2(a_bits, n, L.w2, tw, True, si, ei, npp, B)
+    dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
+    y = M.moe_w4a16_gemm2(dev_bf16(a_bits), D["w2"], torch.from_numpy(tw).cuda(), True, dsi, dei, dnpp, B)
+    assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 K={K} B{B}")
