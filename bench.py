@@ -67,6 +67,26 @@ def gemm1_alg(L, T, ids):
     return b, f
 
 
+def profiled_traffic():
+    """GEMM1 HBM bytes per launch from the committed counter summary, or None.
+
+    The summary records the GEMM source it was taken on; if the source has
+    changed since, the figure no longer describes this kernel and None is
+    returned.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm1_nvfp4_e32_t4096_traffic.md")
+    src = os.path.join(ROOT, "bit_weight_expert_amd", "csrc", "gemm.hip")
+    try:
+        fields = dict(ln.split(":", 1) for ln in open(path) if ln.startswith(("traffic_", "kernel_")))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if not sha.startswith(fields["kernel_source_sha256_prefix"].strip()):
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -75,8 +95,11 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=4096)
     ap.add_argument("--sweep", default="1,8,64,512,4096")
     ap.add_argument("--copies", type=int, default=8)
-    ap.add_argument("--cpu-sample", type=int, default=64, help="tokens the oracle is timed on")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay timings")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -136,19 +159,43 @@ def main() -> int:
     # routing ids of the batch (for the algorithmic byte counts: touched experts)
     ids_all = M.moe_route(logits, L.top_k, L.route, None, L.renormalize)[0].cpu().numpy()
 
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def graph_ms(T, steps):
+        """Per-call time of moe_forward replayed from hipGraphs (one graph per weight copy)."""
+        graphs = []
+        for r in range(len(copies)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fwd(T, r)
+            graphs.append(g)
+        ms = time_calls(lambda i: graphs[i % len(graphs)].replay(), steps, args.warmup)
+        del graphs
+        return ms
+
     results = {}
     for T in sweep:
         steps = args.steps if T == args.tokens else max(args.steps, 50)
         ms = time_calls(lambda i: fwd(T, i), steps, args.warmup)
+        g_ms = None if args.no_graph else graph_ms(T, steps)
         nb, fl, touched = algorithmic(L, T, ids_all[:T])
         t_hbm = nb / (HBM_PEAK_GBS * 1e9)
         t_mfma = fl / (BF16_PEAK_TFLOPS * 1e12)
         bound = "hbm" if t_hbm >= t_mfma else "mfma"
         results[T] = dict(T=T, ms=ms, tokens_per_s=T / (ms * 1e-3), touched_experts=touched,
+                          graph_ms=g_ms,
+                          graph_roofline_frac=None if g_ms is None else max(t_hbm, t_mfma) / (g_ms * 1e-3),
                           alg_bytes=nb, alg_flops=fl, GBps=nb / (ms * 1e-3) / 1e9,
                           TFLOPs=fl / (ms * 1e-3) / 1e12, bound=bound,
                           roofline_frac=max(t_hbm, t_mfma) / (ms * 1e-3))
-        log(f"T={T}: {ms * 1e3:.1f} us/step, {results[T]['tokens_per_s']:.0f} tok/s, "
+        log(f"T={T}: {ms * 1e3:.1f} us/step (graph {('%.1f' % (g_ms * 1e3)) if g_ms else '-'}), "
+            f"{results[T]['tokens_per_s']:.0f} tok/s, "
             f"{results[T]['GBps']:.0f} GB/s, {results[T]['TFLOPs']:.1f} TFLOP/s, "
             f"{bound} roofline {results[T]['roofline_frac'] * 100:.1f}%")
 
@@ -212,7 +259,7 @@ def main() -> int:
                    "tokens": args.tokens, "block_m": bm, "weight_copies_rotated": args.copies},
         "roofline": {"kernel": "grouped_gemm (GEMM1, w13 + swigluoai)", "bound": g_bound,
                      "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
-                     "traffic": None, "kernel_us": g1_ms * 1e3},
+                     "traffic": profiled_traffic(), "kernel_us": g1_ms * 1e3},
         "layer_roofline": {"bound": head["bound"], "frac": head["roofline_frac"],
                            "GBps": head["GBps"], "TFLOPs": head["TFLOPs"]},
         "cpu_baseline": cpu,

@@ -270,9 +270,11 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiAr
 #define MOE_PF_NF128 4
 #endif
 constexpr int kPfWaves = 4;
-template <int BM>
+template <int BM, int FMT>
 struct PfShape {
-  static constexpr int NF = BM >= 128 ? MOE_PF_NF128 : MOE_PF_NF64;
+  // GPTQ needs more registers per fragment (words, scale and zero); it keeps
+  // 32-column waves at every block size.
+  static constexpr int NF = (BM >= 128 && FMT != FMT_GPTQ) ? MOE_PF_NF128 : MOE_PF_NF64;
   static constexpr int BN = kPfWaves * NF * 16;  // columns per workgroup
 };
 constexpr int kPfBK = 128;                    // K chunk staged in LDS
@@ -392,7 +394,7 @@ __device__ __forceinline__ void pf_tail(f32x4 (&acc)[BM / 16][NF], uint4 (*As)[k
 template <int FMT, int EPI, int BM>
 __global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
   constexpr int MI = BM / 16;
-  constexpr int NF = PfShape<BM>::NF;
+  constexpr int NF = PfShape<BM, FMT>::NF;
   constexpr int kPasses = BM / 16;  // 16 rows staged per pass (4 per wave)
   __shared__ uint4 As[2][BM][kPfSlots];
 
@@ -404,7 +406,7 @@ __global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(GemmArgs ga, Weigh
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int n0 = nt * PfShape<BM>::BN + wave * NF * 16;
+  const int n0 = nt * PfShape<BM, FMT>::BN + wave * NF * 16;
   const bool wave_on = n0 < ga.N;
 
   // A rows this lane stages (see pf_issue_a)
@@ -695,7 +697,7 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
     else
       launch_decode<FMT, EPI, 2>(nf, ga, W, ea, st);
   } else {
-    const int bn = block_m == 64 ? PfShape<64>::BN : PfShape<128>::BN;
+    const int bn = block_m == 64 ? PfShape<64, FMT>::BN : PfShape<128, FMT>::BN;
     ga.n_ntiles = (ga.N + bn - 1) / bn;
     const int total = ga.n_mblocks * ga.n_ntiles;
     const dim3 grid((total + 7) / 8 * 8);
