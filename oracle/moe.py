@@ -271,31 +271,39 @@ def forward(layer, block_m: int = 16, topk=None):
 
 
 def forward_tokens(layer, tokens, topk=None):
-    """The layer's output for a subset of tokens, computed one token at a time.
+    """The layer's output for a subset of tokens (same definition as forward()).
 
-    Used to check full-size runs on sampled rows: it touches only the
-    experts those tokens route to.
+    Used to check full-size runs on sampled rows: only the experts those
+    tokens route to are decoded, one at a time, so memory stays at one
+    expert's float64 weights.  Each (token, choice) row is computed on its
+    own; the rows are then summed over the choices j in ascending order.
     Returns float64 [len(tokens), H].
     """
     L = layer
     ids, w = route(L) if topk is None else topk
-    out = np.zeros((len(tokens), L.H), dtype=np.float64)
-    cache13, cache2 = {}, {}
+    tokens = list(tokens)
     x = bf16_to_f64(L.x)
+    y = np.zeros((len(tokens), L.top_k, L.H), dtype=np.float64)
+    by_expert = {}
     for i, t in enumerate(tokens):
         for j in range(L.top_k):
             e = int(ids[t, j])
-            if not (0 <= e < L.E):
-                continue
-            if e not in cache13:
-                cache13[e] = decode_expert(L.w13, e)
-                cache2[e] = decode_expert(L.w2, e)
-            h = cache13[e] @ x[t] + _bias_f64(L.w13, e)
+            if 0 <= e < L.E:
+                by_expert.setdefault(e, []).append((i, t, j))
+    for e, items in sorted(by_expert.items()):
+        W13 = decode_expert(L.w13, e)
+        W2 = decode_expert(L.w2, e)
+        for i, t, j in items:
+            h = W13 @ x[t] + _bias_f64(L.w13, e)
             a = activation(h, L.act, L.alpha, L.beta, L.limit)
-            yv = cache2[e] @ a + _bias_f64(L.w2, e)
+            yv = W2 @ a + _bias_f64(L.w2, e)
             if L.mul_topk_weights:
                 yv = yv * float(w[t, j])
-            out[i] += yv
+            y[i, j] = yv
+        del W13, W2
+    out = np.zeros((len(tokens), L.H), dtype=np.float64)
+    for j in range(L.top_k):
+        out += y[:, j]
     return out
 
 

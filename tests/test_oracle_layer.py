@@ -221,3 +221,11 @@ def test_sum_skips_invalid_ids_and_keeps_j_order():
     np.testing.assert_array_equal(out[0], y[0] + y[1])
     np.testing.assert_array_equal(out[1], y[3])
     np.testing.assert_array_equal(out[2], y[4])
+
+
+def test_forward_tokens_matches_forward():
+    """The sampled-token path used at full sizes equals the whole-batch definition."""
+    L = _tiny_layer("nvfp4", E=5, k=3, T=9, H=64, I=64)
+    full = O.forward(L)["out"]
+    rows = [0, 3, 8]
+    np.testing.assert_allclose(O.forward_tokens(L, rows), full[rows], rtol=1e-12, atol=1e-15)
