@@ -17,20 +17,23 @@
 // buffer is read or written (hidden 2880 = 11*256 + 64 = 22*128 + 64).
 //
 // Two kernels share the chunk loaders, the dequantisers and the epilogue:
-//   prefill  many rows per expert.  Workgroup = BM (64/128) rows x 256
-//            columns; four waves split the columns, 64 each, so every weight
+//   prefill  many rows per expert.  Workgroup = BM (64/128) rows x 128
+//            columns; four waves split the columns, 32 each, so every weight
 //            is fetched and dequantised once per workgroup and no LDS is spent
-//            on weights.  A is staged through a double-buffered LDS tile
-//            (128-wide chunks); the next chunk's A and weights are loaded
-//            while the current one is multiplied.  Tiles are ordered expert-
-//            block-major within groups of 4 column tiles and handed out so
-//            that each XCD works on a contiguous run, keeping a weight tile
-//            and an A block in one XCD's L2 while they are reused.
+//            on weights.  A is staged by LDS-DMA into a double-buffered,
+//            XOR-swizzled LDS tile (128-wide chunks); the next chunk's A and
+//            weight codes (raw scale words included, decoded only when used,
+//            so no wait for the load is forced early) are in flight while the
+//            current chunk is multiplied.  Tiles are ordered expert-block-major
+//            within groups of 4 column tiles and handed out so that each XCD
+//            works on a contiguous run, keeping a weight tile and an A block
+//            in one XCD's L2 while they are reused.
 //   decode   a few rows per expert: the weight stream is the whole cost.
-//            Workgroup = 16*MI rows x 64 columns; the four waves split K
-//            (256-wide chunks, two 16-byte code loads per lane per fragment,
-//            next chunk prefetched), read A straight from global memory, and
-//            add their partial sums through LDS in wave order (deterministic).
+//            Workgroup = 16*MI rows x 16*NF columns; each wave owns one or
+//            more 256-wide K chunks (up to 12 waves for one row block, 8 for
+//            two), reads A straight from global memory, and the waves add
+//            their partial sums through LDS in wave order (deterministic);
+//            the epilogue is then spread over the waves.
 //
 // Dequantisation:
 //   NVFP4  e2m1 -> f32 with the gfx950 fp4 convert (unit scale), times the
@@ -60,12 +63,15 @@ namespace moe {
 template <int FMT, int C>
 struct BChunk {
   static constexpr int kSteps = C / 32;  // MFMA steps (8 k each) in the lane's C/4 range
-  static constexpr int kScales = FMT == FMT_NVFP4 ? (C / 64 > 0 ? C / 64 : 1)
-                                 : FMT == FMT_MXFP4 ? (C / 128 > 0 ? C / 128 : 1)
-                                                    : 1;
+  // raw scale words exactly as loaded (decoded only when a step uses them, so
+  // a prefetched chunk never makes the wave wait for its loads early):
+  //   NVFP4  C=256: two u16 (4 group scales); C=128: one u16; else one u8
+  //   MXFP4  C=256: two u8 (2 group scales); else one u8
+  //   GPTQ   [0] = fp16 scale bits, [1] = the packed zero-point word
+  static constexpr int kRaw = FMT == FMT_GPTQ ? 2 : (C == 256 ? 2 : 1);
   uint32_t q[kSteps];
-  float s[kScales];
-  float zs;  // GPTQ: z * s
+  uint32_t sr[kRaw];
+  int zsh;  // GPTQ: bit offset of this column's zero point in sr[1]
 };
 
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
@@ -79,8 +85,8 @@ __device__ __forceinline__ void zero_chunk(BChunk<FMT, C>& b) {
 #pragma unroll
   for (int i = 0; i < BChunk<FMT, C>::kSteps; ++i) b.q[i] = 0u;
 #pragma unroll
-  for (int i = 0; i < BChunk<FMT, C>::kScales; ++i) b.s[i] = 0.f;
-  b.zs = 0.f;
+  for (int i = 0; i < BChunk<FMT, C>::kRaw; ++i) b.sr[i] = 0u;
+  b.zsh = 0;
 }
 
 // Load the lane's k range [kl, kl + C/4) of weight row n of expert e.
@@ -108,14 +114,20 @@ __device__ __forceinline__ void load_chunk(BChunk<FMT, C>& b, const WeightArgs& 
       b.q[0] = *reinterpret_cast<const uint32_t*>(p);
     }
     if (FMT == FMT_NVFP4) {
+      // K % 32 == 0 makes K/16 even, so scale pairs are 2-byte aligned
       const uint8_t* sp = W.scales + row * (size_t)(K / 16) + kl / 16;
-#pragma unroll
-      for (int i = 0; i < BChunk<FMT, C>::kScales; ++i)
-        b.s[i] = __builtin_amdgcn_cvt_f32_fp8((int)sp[i], 0);
+      if (C == 256) {
+        b.sr[0] = *reinterpret_cast<const uint16_t*>(sp);
+        b.sr[1] = *reinterpret_cast<const uint16_t*>(sp + 2);
+      } else if (C == 128) {
+        b.sr[0] = *reinterpret_cast<const uint16_t*>(sp);
+      } else {
+        b.sr[0] = *sp;
+      }
     } else {
       const uint8_t* sp = W.scales + row * (size_t)(K / 32) + kl / 32;
-#pragma unroll
-      for (int i = 0; i < BChunk<FMT, C>::kScales; ++i) b.s[i] = __uint_as_float((uint32_t)sp[i] << 23);
+      b.sr[0] = sp[0];
+      if (C == 256) b.sr[1] = sp[1];
     }
   } else {
     const uint32_t* qw = reinterpret_cast<const uint32_t*>(W.qweight);
@@ -123,10 +135,9 @@ __device__ __forceinline__ void load_chunk(BChunk<FMT, C>& b, const WeightArgs& 
 #pragma unroll
     for (int i = 0; i < S; ++i) b.q[i] = qw[base + (size_t)i * N];
     const size_t gi = (size_t)e * (K / W.group) + kl / W.group;
-    const float s = half_bits_to_f32(reinterpret_cast<const uint16_t*>(W.scales)[gi * N + n]);
-    const uint32_t z = (W.zeros[gi * (N / 8) + n / 8] >> (4 * (n & 7))) & 15u;
-    b.s[0] = s;
-    b.zs = (float)z * s;
+    b.sr[0] = reinterpret_cast<const uint16_t*>(W.scales)[gi * N + n];
+    b.sr[1] = W.zeros[gi * (N / 8) + n / 8];
+    b.zsh = 4 * (n & 7);
   }
 }
 
@@ -136,7 +147,10 @@ __device__ __forceinline__ bf16x8 deq_step(const BChunk<FMT, C>& b, int st) {
   const uint32_t w = b.q[st];
   uint4 r;
   if (FMT == FMT_NVFP4) {
-    const float s = b.s[(st * 8) / 16];
+    const int grp = (st * 8) / 16;  // 16-k group inside the lane's range
+    const uint32_t raw = (C == 256) ? b.sr[grp >> 1] : b.sr[0];
+    const float s = (grp & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)raw, 1)
+                              : __builtin_amdgcn_cvt_f32_fp8((int)raw, 0);
     f32x2 p;
     p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
     r.x = pack_bf16x2(p[0] * s, p[1] * s);
@@ -147,7 +161,9 @@ __device__ __forceinline__ bf16x8 deq_step(const BChunk<FMT, C>& b, int st) {
     p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
     r.w = pack_bf16x2(p[0] * s, p[1] * s);
   } else if (FMT == FMT_MXFP4) {
-    const float s = b.s[(st * 8) / 32];
+    const int grp = (st * 8) / 32;
+    const uint32_t raw = (C == 256) ? b.sr[grp] : b.sr[0];
+    const float s = __uint_as_float((raw & 0xffu) << 23);
     bf16x2 p;
     p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
     __builtin_memcpy(&r.x, &p, 4);
@@ -158,9 +174,11 @@ __device__ __forceinline__ bf16x8 deq_step(const BChunk<FMT, C>& b, int st) {
     p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
     __builtin_memcpy(&r.w, &p, 4);
   } else {
+    const float s = half_bits_to_f32((uint16_t)b.sr[0]);
+    const float zs = (float)((b.sr[1] >> b.zsh) & 15u) * s;
     float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = fmaf((float)((w >> (4 * i)) & 15u), b.s[0], -b.zs);
+    for (int i = 0; i < 8; ++i) v[i] = fmaf((float)((w >> (4 * i)) & 15u), s, -zs);
     r.x = pack_bf16x2(v[0], v[1]);
     r.y = pack_bf16x2(v[2], v[3]);
     r.z = pack_bf16x2(v[4], v[5]);
@@ -175,6 +193,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;
   __builtin_memcpy(&r, &v, 16);
   return r;
+}
+
+// sigmoid(x) with the hardware exp2 and reciprocal (about 1 ulp each; the result
+// is rounded to bf16 afterwards).  x -> -inf gives 0, x -> +inf gives 1.
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
 }
 
 // --------------------------------------------------------------------------
@@ -233,7 +257,7 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiAr
           float up = acc[i][2 * p + 1][r] * gsc + bias[2 * p + 1];
           gate = fminf(gate, a.limit);
           up = fminf(fmaxf(up, -a.limit), a.limit);
-          const float v = gate / (1.f + expf(-a.alpha * gate)) * (up + a.beta);
+          const float v = gate * sigmoid_fast(a.alpha * gate) * (up + a.beta);
           orow[n0 / 2 + 16 * p + c16] = f32_to_bf16_bits(v);
         }
       } else {
@@ -260,21 +284,17 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiAr
 // prefill kernel
 // --------------------------------------------------------------------------
 
-// Fragments (16 columns each) per wave of the prefill kernel, by block_m:
-// 64-row blocks use 32-column waves (more workgroups for mid-size batches),
-// 128-row blocks 64-column waves (half the LDS reads per MFMA).
-#ifndef MOE_PF_NF64
-#define MOE_PF_NF64 2
-#endif
-#ifndef MOE_PF_NF128
-#define MOE_PF_NF128 4
+// Fragments (16 columns each) per wave of the prefill kernel.  Two (32-column
+// waves, 128-column workgroups) at both block sizes: with four the software
+// pipeline of a 128-row block (next fragments' codes and raw scales in flight
+// while the current ones are multiplied) no longer fits in 256 VGPRs and spills.
+#ifndef MOE_PF_NF
+#define MOE_PF_NF 2
 #endif
 constexpr int kPfWaves = 4;
 template <int BM, int FMT>
 struct PfShape {
-  // GPTQ needs more registers per fragment (words, scale and zero); it keeps
-  // 32-column waves at every block size.
-  static constexpr int NF = (BM >= 128 && FMT != FMT_GPTQ) ? MOE_PF_NF128 : MOE_PF_NF64;
+  static constexpr int NF = MOE_PF_NF;
   static constexpr int BN = kPfWaves * NF * 16;  // columns per workgroup
 };
 constexpr int kPfBK = 128;                    // K chunk staged in LDS
@@ -335,17 +355,30 @@ __device__ __forceinline__ void load_frags(BChunk<FMT, C> (&b)[NF], const Weight
 template <int FMT, int C, int MI, int NF>
 __device__ __forceinline__ void pf_compute(f32x4 (&acc)[MI][NF], const uint4 (*As)[kPfSlots],
                                            const BChunk<FMT, C> (&b)[NF], int c16, int g) {
+  // Software-pipelined: the weights of step s+1 are dequantised (VALU) while
+  // the MFMAs of step s run, so the matrix core and the vector ALU can work at
+  // the same time.
+  constexpr int S = C / 32;
+  bf16x8 bcur[NF];
 #pragma unroll
-  for (int s = 0; s < C / 32; ++s) {
-    bf16x8 bf[NF];
+  for (int j = 0; j < NF; ++j) bcur[j] = deq_step<FMT, C>(b[j], 0);
 #pragma unroll
-    for (int j = 0; j < NF; ++j) bf[j] = deq_step<FMT, C>(b[j], s);
+  for (int s = 0; s < S; ++s) {
+    bf16x8 bnext[NF];
+    if (s + 1 < S) {
+#pragma unroll
+      for (int j = 0; j < NF; ++j) bnext[j] = deq_step<FMT, C>(b[j], s + 1);
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const bf16x8 af = as_bf16x8(As[i * 16 + c16][(g * (C / 32) + s) ^ c16]);
+      const bf16x8 af = as_bf16x8(As[i * 16 + c16][(g * S + s) ^ c16]);
 #pragma unroll
       for (int j = 0; j < NF; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bcur[j], acc[i][j], 0, 0, 0);
+    }
+    if (s + 1 < S) {
+#pragma unroll
+      for (int j = 0; j < NF; ++j) bcur[j] = bnext[j];
     }
   }
 }
@@ -396,7 +429,11 @@ __global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(GemmArgs ga, Weigh
   constexpr int MI = BM / 16;
   constexpr int NF = PfShape<BM, FMT>::NF;
   constexpr int kPasses = BM / 16;  // 16 rows staged per pass (4 per wave)
-  __shared__ uint4 As[2][BM][kPfSlots];
+  // two separate LDS objects (not one [2][..] array), so the compiler can see
+  // that the LDS-DMA filling one buffer never aliases the reads of the other
+  // and need not wait for the DMA before every LDS read
+  __shared__ uint4 As0[BM][kPfSlots];
+  __shared__ uint4 As1[BM][kPfSlots];
 
   int mb, nt;
   if (!prefill_tile(ga, mb, nt)) return;
@@ -433,34 +470,34 @@ __global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(GemmArgs ga, Weigh
   // two chunks per trip: even chunks use LDS buffer 0 and b0, odd ones buffer 1 and b1;
   // each chunk's MFMAs overlap the loads of the next
   if (nfull > 0) {
-    pf_issue_a<kPasses>(As[0], arow, 0, wave_u);
+    pf_issue_a<kPasses>(As0, arow, 0, wave_u);
     if (wave_on) load_frags<FMT, kPfBK, NF>(b0, W, e, nrow, ga.N, ga.K, 0, g);
   }
   pf_sync();
   for (int c = 0; c < nfull; c += 2) {
     const bool m1 = c + 1 < nfull;
     if (m1) {
-      pf_issue_a<kPasses>(As[1], arow, (c + 1) * kPfBK, wave_u);
+      pf_issue_a<kPasses>(As1, arow, (c + 1) * kPfBK, wave_u);
       if (wave_on) load_frags<FMT, kPfBK, NF>(b1, W, e, nrow, ga.N, ga.K, (c + 1) * kPfBK, g);
     }
-    if (wave_on) pf_compute<FMT, kPfBK, MI, NF>(acc, As[0], b0, c16, g);
+    if (wave_on) pf_compute<FMT, kPfBK, MI, NF>(acc, As0, b0, c16, g);
     pf_sync();
     if (!m1) break;
     const bool m2 = c + 2 < nfull;
     if (m2) {
-      pf_issue_a<kPasses>(As[0], arow, (c + 2) * kPfBK, wave_u);
+      pf_issue_a<kPasses>(As0, arow, (c + 2) * kPfBK, wave_u);
       if (wave_on) load_frags<FMT, kPfBK, NF>(b0, W, e, nrow, ga.N, ga.K, (c + 2) * kPfBK, g);
     }
-    if (wave_on) pf_compute<FMT, kPfBK, MI, NF>(acc, As[1], b1, c16, g);
+    if (wave_on) pf_compute<FMT, kPfBK, MI, NF>(acc, As1, b1, c16, g);
     pf_sync();
   }
 
   int k0 = nfull * kPfBK;
   if (ga.K - k0 >= 64) {
-    pf_tail<FMT, 64, BM, NF>(acc, As[0], ga, W, e, mb, nrow, wave_on, k0, tid, c16, g);
+    pf_tail<FMT, 64, BM, NF>(acc, As0, ga, W, e, mb, nrow, wave_on, k0, tid, c16, g);
     k0 += 64;
   }
-  if (ga.K - k0 >= 32) pf_tail<FMT, 32, BM, NF>(acc, As[0], ga, W, e, mb, nrow, wave_on, k0, tid, c16, g);
+  if (ga.K - k0 >= 32) pf_tail<FMT, 32, BM, NF>(acc, As0, ga, W, e, mb, nrow, wave_on, k0, tid, c16, g);
 
   if (!wave_on) return;
   EpiArgs a = ea;
