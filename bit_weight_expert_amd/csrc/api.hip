@@ -54,11 +54,8 @@ moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out
     default:
       return MOE_ERR_UNSUPPORTED;
   }
-  if (!aligned16(w->qweight)) return MOE_ERR_ALIGN;
-  if (w->fmt == MOE_W_NVFP4 && (reinterpret_cast<uintptr_t>(w->scales) & 1u)) return MOE_ERR_ALIGN;
-  if (w->fmt == MOE_W_INT4_GPTQ &&
-      ((reinterpret_cast<uintptr_t>(w->scales) & 1u) || (reinterpret_cast<uintptr_t>(w->zeros) & 3u)))
-    return MOE_ERR_ALIGN;
+  if (!aligned16(w->qweight) || !aligned16(w->scales)) return MOE_ERR_ALIGN;
+  if (w->fmt == MOE_W_INT4_GPTQ && !aligned16(w->zeros)) return MOE_ERR_ALIGN;
   if (w->bias != nullptr && (reinterpret_cast<uintptr_t>(w->bias) & 1u)) return MOE_ERR_ALIGN;
   out->qweight = static_cast<const uint8_t*>(w->qweight);
   out->scales = static_cast<const uint8_t*>(w->scales);

@@ -6,34 +6,24 @@
 // in the NVFP4 repro); its A rows are x[sorted_id / top_k] for GEMM1 and the
 // intermediate row of the slot itself for GEMM2 (the top_k = 1 view).
 //
-// MFMA mapping (v_mfma_f32_16x16x32_bf16).  Lane l works on column l%16 of a
-// 16-column fragment and on k-group g = l/16.  A K chunk of width C is split
-// in four: the lane owns the C/4 consecutive k at [k0 + g*C/4, k0 + (g+1)*C/4),
-// holds their 4-bit codes in registers and dequantises 8 of them per MFMA
-// step; step s reads the A fragment with the same k assignment, so every k
-// is reduced exactly once (the order of a reduction is free).  C = 256/128
-// for full chunks; the K tail is cut into 128/64/32-wide chunks, so K need
-// only be a multiple of 32 and no MFMA step is spent on padding.  No padded
-// buffer is read or written (hidden 2880 = 11*256 + 64 = 22*128 + 64).
-//
-// Two kernels share the chunk loaders, the dequantisers and the epilogue:
-//   prefill  many rows per expert.  Workgroup = BM (64/128) rows x 128
-//            columns; four waves split the columns, 32 each, so every weight
-//            is fetched and dequantised once per workgroup and no LDS is spent
-//            on weights.  A is staged by LDS-DMA into a double-buffered,
-//            XOR-swizzled LDS tile (128-wide chunks); the next chunk's A and
-//            weight codes (raw scale words included, decoded only when used,
-//            so no wait for the load is forced early) are in flight while the
-//            current chunk is multiplied.  Tiles are ordered expert-block-major
-//            within groups of 4 column tiles and handed out so that each XCD
-//            works on a contiguous run, keeping a weight tile and an A block
-//            in one XCD's L2 while they are reused.
+// Two kernels share the weight decoders and the routing-weight epilogue rule:
+//   prefill  many rows per expert (blocks of 64/128 slots).  Workgroup = BM
+//            rows x 256 weight rows; four waves split the weight rows, so
+//            every weight is dequantised once per workgroup.  A rows and the
+//            4-bit codes stream through a 4-deep LDS ring filled by gfx950
+//            LDS-DMA, the tile's scales for the whole K sit in LDS, MFMA is
+//            v_mfma_f32_32x32x16_bf16 (details at the kernel).
 //   decode   a few rows per expert: the weight stream is the whole cost.
-//            Workgroup = 16*MI rows x 16*NF columns; each wave owns one or
-//            more 256-wide K chunks (up to 12 waves for one row block, 8 for
-//            two), reads A straight from global memory, and the waves add
-//            their partial sums through LDS in wave order (deterministic);
-//            the epilogue is then spread over the waves.
+//            Workgroup = 16*MI rows x 16*NF columns with v_mfma_f32_16x16x32:
+//            lane l works on column l%16 of a 16-column fragment and on
+//            k-group g = l/16; each wave owns one or more 256-wide K chunks
+//            (up to 12 waves for one row block, 8 for two), reads its codes
+//            and A straight from global memory, and the waves add their
+//            partial sums through LDS in wave order (deterministic); the
+//            epilogue is then spread over the waves.
+// Both handle K tails exactly (K need only be a multiple of 32; no MFMA step
+// is spent on padding) and N tails per fragment: no padded buffer is read or
+// written (hidden 2880 = 45*64 = 11*256 + 64).
 //
 // Dequantisation:
 //   NVFP4  e2m1 -> f32 with the gfx950 fp4 convert (unit scale), times the
@@ -283,30 +273,39 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiAr
 // --------------------------------------------------------------------------
 // prefill kernel
 // --------------------------------------------------------------------------
-
-// Fragments (16 columns each) per wave of the prefill kernel.  Two (32-column
-// waves, 128-column workgroups) at both block sizes: with four the software
-// pipeline of a 128-row block (next fragments' codes and raw scales in flight
-// while the current ones are multiplied) no longer fits in 256 VGPRs and spills.
-#ifndef MOE_PF_NF
-#define MOE_PF_NF 2
-#endif
-constexpr int kPfWaves = 4;
-template <int BM, int FMT>
-struct PfShape {
-  static constexpr int NF = MOE_PF_NF;
-  static constexpr int BN = kPfWaves * NF * 16;  // columns per workgroup
-};
-constexpr int kPfBK = 128;                    // K chunk staged in LDS
-constexpr int kPfSlots = kPfBK / 8;           // 16-byte slots per LDS row
-constexpr int kPfGroupN = 4;                  // column tiles per group in the tile order
+//
+// Workgroup tile: BM rows (slots of one expert block) x BN = 4*NF*32 weight
+// rows; four waves (one per SIMD) split the weight rows (NF 32-column
+// fragments each) and every wave covers all BM rows, so each weight is
+// dequantised exactly once per workgroup.  MFMA is v_mfma_f32_32x32x16_bf16:
+// per instruction it does twice the work of the 16x16 shape for the same
+// operand registers, which leaves room to keep the next step's A fragments
+// and dequantised weights in flight without spilling.
+//
+// K is walked in 64-wide chunks through a 4-deep LDS ring holding, per chunk,
+// the A rows (bf16, gathered by slot) and the 4-bit weight codes, both copied
+// global -> LDS by the gfx950 LDS-DMA loads; the scales of the tile's rows
+// for the whole K sit in LDS from the start.  The DMA loads are issued from
+// inline assembly so the compiler never inserts waits for them; the pipeline
+// keeps its own count (every chunk issues the same number of DMA instructions
+// per wave and loads retire in order), so a chunk is waited for only when it
+// is needed and three more stay in flight.
+//
+// Lane mapping (lane l, c = l % 32, h = l / 32): in a 64-wide chunk the lane
+// owns k in [32h, 32h + 32); MFMA step s (0..3) takes k = 32h + 8s .. +8 of
+// it for both operands (a reduction's order is free).  The lane's A rows are
+// i*32 + c, its weight row is that of column c of each fragment, and its 32
+// codes of a chunk are one 16-byte LDS read.
 
 struct GemmArgs {
   const uint16_t* A;
-  int a_div;    // A row = sorted_id / a_div
-  int n_slots;  // sentinel
+  int a_div;       // A row = sorted_id / a_div
+  uint64_t a_mul;  // ceil(2^32 / a_div): sorted_id / a_div == (sorted_id * a_mul) >> 32 for ids < 2^24
+  int n_slots;     // sentinel
   int K, N, E;
   int n_mblocks, n_ntiles;
+  int group_m;     // prefill tile order: expert blocks per group
+  int block_m;     // rows per aligned block (expert_ids has one entry per block)
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
   const int32_t* num_post_pad;
@@ -316,29 +315,8 @@ struct GemmArgs {
 // land only in accumulator rows that the epilogue never stores (an MFMA row
 // depends on its own A row only), so no zero-fill or branch is needed.
 __device__ __forceinline__ const uint16_t* a_row(const GemmArgs& ga, int sid) {
-  return ga.A + (size_t)(sid < ga.n_slots ? sid / ga.a_div : 0) * ga.K;
-}
-
-// LDS rows hold 16 slots of 16 bytes; slot q of row r is stored at q ^ (r % 16),
-// so the 16 rows that one MFMA A fragment reads hit 16 different bank groups.
-__device__ __forceinline__ int swz(int r, int q) { return q ^ (r & 15); }
-
-// Logical tile of a workgroup: each XCD (workgroups are dealt to the 8 XCDs
-// round-robin) gets a contiguous run of logical tiles; logical tiles run over
-// groups of kPfGroupN column tiles, expert blocks ascending inside a group.
-__device__ __forceinline__ bool prefill_tile(const GemmArgs& a, int& mb, int& nt) {
-  const int total = a.n_mblocks * a.n_ntiles;
-  const int per_xcd = (total + 7) / 8;
-  const int pid = blockIdx.x;
-  const int lid = (pid & 7) * per_xcd + (pid >> 3);
-  if (lid >= total) return false;
-  const int group_tiles = a.n_mblocks * kPfGroupN;
-  const int grp = lid / group_tiles;
-  const int rem = lid - grp * group_tiles;
-  const int width = min(kPfGroupN, a.n_ntiles - grp * kPfGroupN);
-  mb = rem / width;
-  nt = grp * kPfGroupN + rem % width;
-  return true;
+  const int row = (int)(((uint64_t)(uint32_t)sid * ga.a_mul) >> 32);
+  return ga.A + (size_t)(sid < ga.n_slots ? row : 0) * ga.K;
 }
 
 // Weights of the wave's NF fragments for the chunk starting at k0 (lane range k0 + g*C/4).
@@ -351,158 +329,495 @@ __device__ __forceinline__ void load_frags(BChunk<FMT, C> (&b)[NF], const Weight
   for (int j = 0; j < NF; ++j) load_chunk<FMT, C>(b[j], W, e, nrow[j], N, K, k0 + g * (C / 4));
 }
 
-// MFMA steps of one C-wide chunk: A fragments from the swizzled LDS tile.
-template <int FMT, int C, int MI, int NF>
-__device__ __forceinline__ void pf_compute(f32x4 (&acc)[MI][NF], const uint4 (*As)[kPfSlots],
-                                           const BChunk<FMT, C> (&b)[NF], int c16, int g) {
-  // Software-pipelined: the weights of step s+1 are dequantised (VALU) while
-  // the MFMAs of step s run, so the matrix core and the vector ALU can work at
-  // the same time.
-  constexpr int S = C / 32;
-  bf16x8 bcur[NF];
+constexpr int kPfBK = 64;                  // K chunk
+constexpr int kPfStages = 4;               // LDS ring depth
+constexpr int kPfScaleBytes = 60 * 1024;   // LDS for the tile's scales over all of K
+
+template <int BM, int NF>
+struct Pf {
+  static constexpr int MI = BM / 32;
+  static constexpr int BN = 128 * NF;
+  static constexpr int kABytes = BM * kPfBK * 2;            // A rows of one chunk
+  static constexpr int kBBytes = BN * kPfBK / 2;            // weight codes of one chunk
+  static constexpr int kAIssue = kABytes / 1024 / 4;         // DMA instructions per wave per chunk
+  static constexpr int kBIssue = kBBytes / 1024 / 4;
+  static constexpr int kIssue = kAIssue + kBIssue;
+  static constexpr int kStage = kABytes + kBBytes;
+  static constexpr int kLds = kPfStages * kStage + kPfScaleBytes;
+  static_assert(kAIssue >= 1 && kBIssue >= 1, "tile too small for the DMA split");
+  static_assert(kLds <= 160 * 1024, "LDS");
+};
+
+// Bytes of LDS the scales of one BN-row tile take for the whole K.
+__host__ __device__ inline int pf_scale_bytes(int fmt, int K, int group, int bn) {
+  if (fmt == FMT_NVFP4) return bn * (K / 16);
+  if (fmt == FMT_MXFP4) return bn * (K / 32);
+  return (K / group) * (bn * 2 + bn / 2);  // fp16 scales + packed zero points
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+
+// One global -> LDS DMA instruction: lane l copies 16 bytes from g to
+// lds_base + 16*l (lds_base must be wave-uniform).  Issued as inline assembly
+// so the compiler does not track it; the kernel waits with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N): all but the N most recent vector-memory loads of this wave have landed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "I"(N) : "memory");
+}
+
+// Workgroup barrier that does not wait for the wave's outstanding loads
+// (__syncthreads waits for all of them, which would drain the ring).
+// The LDS reads issued before it are waited for first, so no DMA started
+// after the barrier can overwrite data a read has not yet taken.
+__device__ __forceinline__ void pf_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Tile of a workgroup.  Only the blocks moe_align actually filled are
+// scheduled: their number is read from num_post_pad, and the 8 XCDs (which
+// receive workgroups round-robin) each get a contiguous run of them.  Inside
+// a run, tiles go in groups of group_m expert blocks: the blocks of a group
+// cycle fastest, then the column tiles, so the workgroups that run at the
+// same time on one XCD share both their weight tiles (the blocks of one
+// expert) and their A blocks (across column tiles) in that XCD's L2.
+__device__ __forceinline__ bool prefill_tile(const GemmArgs& a, int bm, int& mb, int& nt) {
+  const int nmb = min(a.num_post_pad[0] / bm, a.n_mblocks);
+  const int total = nmb * a.n_ntiles;
+  const int per_xcd = (total + 7) / 8;
+  const int pid = blockIdx.x;
+  const int idx = pid >> 3;
+  const int lid = (pid & 7) * per_xcd + idx;
+  if (idx >= per_xcd || lid >= total) return false;
+  const int gsize = a.group_m * a.n_ntiles;
+  const int grp = lid / gsize;
+  const int rem = lid - grp * gsize;
+  const int h = min(a.group_m, nmb - grp * a.group_m);
+  nt = rem / h;
+  mb = grp * a.group_m + rem % h;
+  return true;
+}
+
+// Position (16-byte unit) of the codes of tile row r, half h inside its
+// 32-row block of a chunk's weight tile.  Gated tiles store even rows (the
+// gate halves of the pairs) before odd ones, so the 8 lanes that one LDS
+// cycle serves always hit 8 different bank groups.
+template <int EPI>
+__device__ __forceinline__ int pf_bpos(int r, int h) {
+  const int s = (EPI == EPI_SWIGLU) ? ((r & 31) >> 1) + 16 * (r & 1) : (r & 31);
+  return (r >> 5) * 64 + 32 * h + s;
+}
+// Tile row stored at position p (0..63) of 32-row block b (inverse of pf_bpos).
+template <int EPI>
+__device__ __forceinline__ int pf_brow(int b, int p) {
+  const int s = p & 31;
+  return 32 * b + ((EPI == EPI_SWIGLU) ? 2 * (s & 15) + (s >> 4) : s);
+}
+
+// Per-wave DMA of chunk kc into the ring stage at stage_lds.
+template <int FMT, int BM, int NF>
+__device__ __forceinline__ void pf_issue(uint32_t stage_lds, const uint16_t* const (&arow)[Pf<BM, NF>::kAIssue],
+                                         const uint8_t* const (&brow)[Pf<BM, NF>::kBIssue],
+                                         int kc, int wave_u, int N) {
+  using P = Pf<BM, NF>;
+  const int k0 = kc * kPfBK;
 #pragma unroll
-  for (int j = 0; j < NF; ++j) bcur[j] = deq_step<FMT, C>(b[j], 0);
+  for (int p = 0; p < P::kAIssue; ++p)  // instruction q = 4p + wave: A rows 8q .. 8q+7
+    dma16(arow[p] + k0, stage_lds + (uint32_t)(8 * (4 * p + wave_u)) * 128u);
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    bf16x8 bnext[NF];
-    if (s + 1 < S) {
+  for (int p = 0; p < P::kBIssue; ++p) {
+    const uint32_t dst = stage_lds + P::kABytes + (uint32_t)(4 * p + wave_u) * 1024u;
+    if (FMT == FMT_GPTQ)
+      dma16(brow[p] + (size_t)k0 / 8 * N * 4, dst);  // 256 words of the [8][BN] word tile
+    else
+      dma16(brow[p] + k0 / 2, dst);                  // one 32-row block
+  }
+}
+
+// Weight codes of one fragment for one chunk (one code word per MFMA step)
+// and its group scale(s): NVFP4 two e4m3 scales (k 0..15 and 16..31 of the
+// lane's range), MXFP4 one power of two, GPTQ scale and -zero*scale.
+struct PfB {
+  uint4 q;
+  float s0, s1;
+};
+
+template <int FMT>
+__device__ __forceinline__ bf16x8 pf_deq(uint32_t w, float s, float zs) {
+  uint4 r;
+  if (FMT == FMT_NVFP4) {
+    f32x2 p;
+    p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    r.x = pack_bf16x2(p[0] * s, p[1] * s);
+    p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    r.y = pack_bf16x2(p[0] * s, p[1] * s);
+    p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    r.z = pack_bf16x2(p[0] * s, p[1] * s);
+    p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    r.w = pack_bf16x2(p[0] * s, p[1] * s);
+  } else if (FMT == FMT_MXFP4) {
+    bf16x2 p;
+    p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+    __builtin_memcpy(&r.x, &p, 4);
+    p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+    __builtin_memcpy(&r.y, &p, 4);
+    p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+    __builtin_memcpy(&r.z, &p, 4);
+    p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+    __builtin_memcpy(&r.w, &p, 4);
+  } else {
+    float v[8];
 #pragma unroll
-      for (int j = 0; j < NF; ++j) bnext[j] = deq_step<FMT, C>(b[j], s + 1);
-    }
+    for (int i = 0; i < 8; ++i) v[i] = fmaf((float)((w >> (4 * i)) & 15u), s, zs);
+    r.x = pack_bf16x2(v[0], v[1]);
+    r.y = pack_bf16x2(v[2], v[3]);
+    r.z = pack_bf16x2(v[4], v[5]);
+    r.w = pack_bf16x2(v[6], v[7]);
+  }
+  bf16x8 o;
+  __builtin_memcpy(&o, &r, 16);
+  return o;
+}
+
+// Dequantised weights of MFMA step s from a fragment's raw chunk.
+template <int FMT>
+__device__ __forceinline__ bf16x8 pf_deq_step(const PfB& b, int s) {
+  const uint32_t w = s == 0 ? b.q.x : s == 1 ? b.q.y : s == 2 ? b.q.z : b.q.w;
+  if (FMT == FMT_NVFP4) return pf_deq<FMT>(w, s < 2 ? b.s0 : b.s1, 0.f);
+  return pf_deq<FMT>(w, b.s0, b.s1);
+}
+
+// LDS reads of the fragment weights of chunk kc (codes from the ring stage
+// at bstage, scales from the resident scale tile).  rl[j] is the lane's tile
+// row of fragment j.
+template <int FMT, int EPI, int NF>
+__device__ __forceinline__ void pf_read_b(PfB (&b)[NF], const uint8_t* bstage, const uint8_t* sc,
+                                          const int (&rl)[NF], int kc, int h, int K, int group,
+                                          int bn) {
+  const int k0 = kc * kPfBK;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const bf16x8 af = as_bf16x8(As[i * 16 + c16][(g * S + s) ^ c16]);
-#pragma unroll
-      for (int j = 0; j < NF; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bcur[j], acc[i][j], 0, 0, 0);
-    }
-    if (s + 1 < S) {
-#pragma unroll
-      for (int j = 0; j < NF; ++j) bcur[j] = bnext[j];
+  for (int j = 0; j < NF; ++j) {
+    const int r = rl[j];
+    if (FMT == FMT_GPTQ) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(bstage);
+      b[j].q.x = w[(4 * h + 0) * bn + r];
+      b[j].q.y = w[(4 * h + 1) * bn + r];
+      b[j].q.z = w[(4 * h + 2) * bn + r];
+      b[j].q.w = w[(4 * h + 3) * bn + r];
+      const int grp = (k0 + 32 * h) / group;
+      const float s = half_bits_to_f32(reinterpret_cast<const uint16_t*>(sc)[grp * bn + r]);
+      const uint32_t* zw = reinterpret_cast<const uint32_t*>(sc + (K / group) * bn * 2);
+      const float z = (float)((zw[grp * (bn / 8) + (r >> 3)] >> (4 * (r & 7))) & 15u);
+      b[j].s0 = s;
+      b[j].s1 = -z * s;
+    } else {
+      b[j].q = *reinterpret_cast<const uint4*>(bstage + 16 * pf_bpos<EPI>(r, h));
+      if (FMT == FMT_NVFP4) {
+        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sc + r * (K / 16) + k0 / 16 + 2 * h);
+        b[j].s0 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 0);
+        b[j].s1 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 1);
+      } else {
+        b[j].s0 = __uint_as_float((uint32_t)sc[r * (K / 32) + k0 / 32 + h] << 23);
+        b[j].s1 = 0.f;
+      }
     }
   }
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Stage one 128-wide A chunk straight from global memory into LDS (gfx950
-// global_load_lds_dwordx4: lane l of a wave writes 16 bytes at base + 16*l).
-// Pass p of wave w fills rows 16p + 4w .. 16p + 4w + 3; lane l writes physical
-// slot l%16 of row 16p + 4w + l/16, so it fetches that row's logical slot
-// (l%16) ^ (row%16) -- arow[p] already points there.
-template <int NP>
-__device__ __forceinline__ void pf_issue_a(uint4 (*As)[kPfSlots], const uint16_t* const (&arow)[NP],
-                                           int k0, int wave) {
+// A fragments of MFMA step s of a chunk: rows i*32 + c, k = 32h + 8s .. +8.
+// A rows are 128 bytes in LDS, 16-byte slot q of row r stored at q ^ (r % 8).
+template <int MI>
+__device__ __forceinline__ void pf_read_a(uint4 (&a)[MI], const uint8_t* astage, int c, int h, int s) {
 #pragma unroll
-  for (int p = 0; p < NP; ++p)
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(arow[p] + k0),
-                                     (lds_void*)(&As[16 * p + 4 * wave][0]), 16, 0, 0);
-}
-
-// Wait for every outstanding global load of this wave (the A chunk's LDS DMA
-// included), then for the whole workgroup.
-__device__ __forceinline__ void pf_sync() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-}
-
-// The K tail (K % 128, a multiple of 32) as one CW-wide chunk staged in As, unpipelined.
-template <int FMT, int CW, int BM, int NF>
-__device__ __forceinline__ void pf_tail(f32x4 (&acc)[BM / 16][NF], uint4 (*As)[kPfSlots],
-                                        const GemmArgs& ga, const WeightArgs& W, int e, int mb,
-                                        const int (&nrow)[NF], bool wave_on,
-                                        int k0, int tid, int c16, int g) {
-  constexpr int segs = CW / 8;
-  for (int idx = tid; idx < BM * segs; idx += 256) {
-    const int r = idx / segs, sg = idx % segs;
-    As[r][swz(r, sg)] = *reinterpret_cast<const uint4*>(a_row(ga, ga.sorted_ids[mb * BM + r]) + k0 + sg * 8);
+  for (int i = 0; i < MI; ++i) {
+    const int r = i * 32 + c;
+    a[i] = *reinterpret_cast<const uint4*>(astage + r * 128 + 16 * ((4 * h + s) ^ (r & 7)));
   }
-  BChunk<FMT, CW> bt[NF];
-  if (wave_on) load_frags<FMT, CW, NF>(bt, W, e, nrow, ga.N, ga.K, k0, g);
-  __syncthreads();
-  if (wave_on) pf_compute<FMT, CW, BM / 16, NF>(acc, As, bt, c16, g);
-  __syncthreads();
 }
 
-template <int FMT, int EPI, int BM>
-__global__ void __launch_bounds__(256, 2) gemm_prefill_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
-  constexpr int MI = BM / 16;
-  constexpr int NF = PfShape<BM, FMT>::NF;
-  constexpr int kPasses = BM / 16;  // 16 rows staged per pass (4 per wave)
-  // two separate LDS objects (not one [2][..] array), so the compiler can see
-  // that the LDS-DMA filling one buffer never aliases the reads of the other
-  // and need not wait for the DMA before every LDS read
-  __shared__ uint4 As0[BM][kPfSlots];
-  __shared__ uint4 As1[BM][kPfSlots];
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+template <int MI, int NF>
+__device__ __forceinline__ void pf_mfma(f32x16 (&acc)[MI][NF], const uint4 (&a)[MI], const bf16x8 (&b)[NF]) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const bf16x8 af = as_bf16x8(a[i]);
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// DMA of a region of `bytes` bytes into LDS at lds_base, described as rows of
+// row_bytes bytes (all sizes multiples of 16): LDS byte o comes from
+// src + (o / row_bytes) * ld + o % row_bytes, for the first valid_row_bytes
+// of each row only (the rest is left unfilled and never read).
+// Instructions are dealt to the four waves round-robin; lanes outside the
+// region are switched off.  Only the prologue uses it, before the ring starts.
+__device__ __forceinline__ void pf_dma_region(uint32_t lds_base, const uint8_t* src, size_t ld,
+                                              int row_bytes, int valid_row_bytes, int bytes,
+                                              int wave_u, int lane) {
+  const int nq = (bytes + 1023) / 1024;
+  for (int q = wave_u; q < nq; q += 4) {
+    const int o = q * 1024 + 16 * lane;
+    const int in_row = o % row_bytes;
+    if (o < bytes && in_row < valid_row_bytes)
+      dma16(src + (size_t)(o / row_bytes) * ld + in_row, lds_base + q * 1024);
+  }
+}
+
+// Weight row of fragment j (32 columns) for lane column c, and whether the
+// column exists (N % 16 == 0; gated N % 32 == 0, rows 2i / 2i+1 = gate / up
+// of output column i meet in one lane through fragments 2p / 2p+1).
+template <int EPI>
+__device__ __forceinline__ int frag32_row(int n0, int j, int c) {
+  return (EPI == EPI_SWIGLU) ? n0 + 64 * (j >> 1) + 2 * c + (j & 1) : n0 + 32 * j + c;
+}
+
+// Epilogue of the 32x32 accumulators: lane (c, h) holds column c of every
+// fragment and rows 8*(v/4) + 4h + v%4 (v = 0..15) of every 32-row fragment.
+template <int EPI, int FMT, int MI, int NF>
+__device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const EpiArgs& a,
+                                           const WeightArgs& W, int e, int n0, int lane) {
+  const int c = lane & 31, h = lane >> 5;
+  const float gsc = (FMT == FMT_NVFP4) ? W.global_scale[e] : 1.f;
+  float bias[NF];
+  bool on[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int n = frag32_row<EPI>(n0, j, c);
+    on[j] = n < a.N;
+    bias[j] = (W.bias != nullptr && on[j]) ? bf16_bits_to_f32(W.bias[(size_t)e * a.N + n]) : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    int sid[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sid[v] = a.sorted_ids[a.row0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3)];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      if (sid[v] >= a.n_slots) continue;
+      uint16_t* orow = a.out + (size_t)sid[v] * a.out_ld;
+      if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int p = 0; p < NF / 2; ++p) {
+          if (!on[2 * p]) continue;
+          float gate = acc[i][2 * p][v] * gsc + bias[2 * p];
+          float up = acc[i][2 * p + 1][v] * gsc + bias[2 * p + 1];
+          gate = fminf(gate, a.limit);
+          up = fminf(fmaxf(up, -a.limit), a.limit);
+          const float y = gate * sigmoid_fast(a.alpha * gate) * (up + a.beta);
+          orow[n0 / 2 + 32 * p + c] = f32_to_bf16_bits(y);
+        }
+      } else {
+        float tw = 1.f;
+        if (EPI == EPI_DOWN && a.mul_tw) tw = a.topk_w[sid[v]];
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          if (!on[j]) continue;
+          float y = acc[i][j][v] * gsc + bias[j];
+          if (EPI == EPI_RELU2) {
+            y = fmaxf(y, 0.f);
+            y = y * y;
+          } else if (EPI == EPI_DOWN) {
+            y = y * tw;
+          }
+          orow[n0 + 32 * j + c] = f32_to_bf16_bits(y);
+        }
+      }
+    }
+  }
+}
+
+// K tail (K % 64 == 32): two 16-wide MFMA steps with A and weights loaded
+// straight from global memory (lane k range k0 + 16h .. +16).
+template <int FMT, int EPI, int MI, int NF>
+__device__ __forceinline__ void pf_tail32(f32x16 (&acc)[MI][NF], const GemmArgs& ga, const WeightArgs& W,
+                                          int e, int mb, int n0, int c, int h, int k0) {
+  BChunk<FMT, 64> bt[NF];  // C = 64: the lane's 16 k in two 8-k steps
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int n = min(frag32_row<EPI>(n0, j, c), ga.N - 1);
+    load_chunk<FMT, 64>(bt[j], W, e, n, ga.N, ga.K, k0 + 16 * h);
+  }
+  uint4 a0[MI], a1[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const uint16_t* p = a_row(ga, ga.sorted_ids[mb * (32 * MI) + i * 32 + c]) + k0 + 16 * h;
+    a0[i] = *reinterpret_cast<const uint4*>(p);
+    a1[i] = *reinterpret_cast<const uint4*>(p + 8);
+  }
+  bf16x8 b0[NF], b1[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    b0[j] = deq_step<FMT, 64>(bt[j], 0);
+    b1[j] = deq_step<FMT, 64>(bt[j], 1);
+  }
+  pf_mfma<MI, NF>(acc, a0, b0);
+  pf_mfma<MI, NF>(acc, a1, b1);
+}
+
+template <int FMT, int EPI, int BM, int NF>
+__global__ void __launch_bounds__(256, 1) gemm_prefill_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
+  using P = Pf<BM, NF>;
+  constexpr int MI = P::MI;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[P::kLds];
+  uint8_t* const scale_lds = smem + kPfStages * P::kStage;
 
   int mb, nt;
-  if (!prefill_tile(ga, mb, nt)) return;
-  if (mb * BM >= ga.num_post_pad[0]) return;
+  if (!prefill_tile(ga, BM, mb, nt)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int c = lane & 31, h = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = ga.K, N = ga.N;
+
+  // slot ids of the A rows this lane copies, requested before anything waits:
+  // DMA instruction q = 4p + wave covers rows 8q .. 8q+7, lane l row 8q + l/8
+  int sid[P::kAIssue];
+#pragma unroll
+  for (int p = 0; p < P::kAIssue; ++p) sid[p] = ga.sorted_ids[mb * BM + 8 * (4 * p + wave_u) + (lane >> 3)];
   const int e = ga.expert_ids[mb];
   if (e < 0 || e >= ga.E) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c16 = lane & 15, g = lane >> 4;
-  const int n0 = nt * PfShape<BM, FMT>::BN + wave * NF * 16;
-  const bool wave_on = n0 < ga.N;
+  const int nt0 = nt * P::BN;             // first weight row of the tile
+  const int rows = min(P::BN, N - nt0);   // valid weight rows of the tile
+  const int n0 = nt0 + wave_u * NF * 32;  // first weight row of this wave
 
-  // A rows this lane stages (see pf_issue_a)
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const uint16_t* arow[kPasses];
+  // DMA sources.  A: lane l of instruction q fetches logical slot
+  // (l%8) ^ (row%8) of row 8q + l/8 (see pf_read_a).
+  const uint16_t* arow[P::kAIssue];
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int r = 16 * p + 4 * wave_u + (lane >> 4);
-    arow[p] = a_row(ga, ga.sorted_ids[mb * BM + r]) + 8 * ((lane & 15) ^ (r & 15));
+  for (int p = 0; p < P::kAIssue; ++p) {
+    const int r = 8 * (4 * p + wave_u) + (lane >> 3);
+    arow[p] = a_row(ga, sid[p]) + 8 * ((lane & 7) ^ (r & 7));
   }
-  int nrow[NF];
+  // Weight codes.  NVFP4/MXFP4: instruction q fills 32-row block q, lane l
+  // the half l/32 of tile row pf_brow(q, l) (rows past N re-read the last
+  // row).  GPTQ: instruction q covers words 256q .. 256q+255 of the chunk's
+  // [8 k-words][BN columns] tile, lane l four consecutive columns.
+  const uint8_t* brow[P::kBIssue];
 #pragma unroll
-  for (int j = 0; j < NF; ++j) nrow[j] = frag_on<EPI>(n0, j, ga.N) ? frag_row<EPI>(n0, j, c16) : 0;
+  for (int p = 0; p < P::kBIssue; ++p) {
+    const int q = 4 * p + wave_u;
+    if (FMT == FMT_GPTQ) {
+      const int w = q * 256 + 4 * lane;
+      const int col = min(nt0 + w % P::BN, N - 4);
+      brow[p] = W.qweight + (((size_t)e * (K / 8) + w / P::BN) * N + col) * 4;
+    } else {
+      const int n = min(nt0 + pf_brow<EPI>(q, lane), N - 1);
+      brow[p] = W.qweight + ((size_t)e * N + n) * (K / 2) + 16 * (lane >> 5);
+    }
+  }
 
-  f32x4 acc[MI][NF];
+  // the tile's scales for the whole K (resident in LDS), then ring stages
+  // 0..3 <- chunks 0..3 (chunks past the end re-read the last one)
+  const uint32_t ring = lds_addr(smem);
+  const uint32_t sc_lds = ring + kPfStages * P::kStage;
+  const int nchunks = K / kPfBK;  // (K < 64: only the 32-wide tail, no LDS)
+  if (nchunks == 0) {
+  } else if (FMT == FMT_NVFP4) {
+    const int nb = rows * (K / 16);
+    pf_dma_region(sc_lds, W.scales + ((size_t)e * N + nt0) * (K / 16), 0, nb, nb, nb, wave_u, lane);
+  } else if (FMT == FMT_MXFP4) {
+    const int nb = rows * (K / 32);
+    pf_dma_region(sc_lds, W.scales + ((size_t)e * N + nt0) * (K / 32), 0, nb, nb, nb, wave_u, lane);
+  } else {
+    // fp16 scales [groups][BN] and packed zero points [groups][BN/8]; columns
+    // past N are left unfilled (N % 32 == 0 keeps every piece 16-byte aligned)
+    const int ng = K / W.group;
+    pf_dma_region(sc_lds, W.scales + ((size_t)e * ng * N + nt0) * 2, (size_t)N * 2, P::BN * 2,
+                  rows * 2, ng * P::BN * 2, wave_u, lane);
+    pf_dma_region(sc_lds + ng * P::BN * 2,
+                  reinterpret_cast<const uint8_t*>(W.zeros) + ((size_t)e * ng * (N / 8) + nt0 / 8) * 4,
+                  (size_t)N / 2, P::BN / 2, rows / 2, ng * P::BN / 2, wave_u, lane);
+  }
+  if (nchunks > 0) {
+#pragma unroll
+    for (int s = 0; s < kPfStages; ++s)
+      pf_issue<FMT, BM, NF>(ring + s * P::kStage, arow, brow, min(s, nchunks - 1), wave_u, N);
+  }
+
+  // tile rows of this lane's fragments (columns past N read row 0)
+  int rl[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int n = frag32_row<EPI>(n0, j, c);
+    rl[j] = n < N ? n - nt0 : 0;
+  }
+
+  f32x16 acc[MI][NF];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nfull = ga.K / kPfBK;
-  BChunk<FMT, kPfBK> b0[NF], b1[NF];
+  if (nchunks > 0) {
+    // scales and chunk 0 have landed (chunks 1..3 may still be in flight)
+    wait_vmcnt<3 * P::kIssue>();
+    pf_barrier();
+    // chunk 0: weights, step-0 A fragments and dequant
+    PfB b[NF];
+    uint4 a0[MI], a1[MI];
+    bf16x8 q0[NF], q1[NF];
+    pf_read_b<FMT, EPI, NF>(b, smem + P::kABytes, scale_lds, rl, 0, h, K, W.group, P::BN);
+    pf_read_a<MI>(a0, smem, c, h, 0);
+#pragma unroll
+    for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
 
-  // two chunks per trip: even chunks use LDS buffer 0 and b0, odd ones buffer 1 and b1;
-  // each chunk's MFMAs overlap the loads of the next
-  if (nfull > 0) {
-    pf_issue_a<kPasses>(As0, arow, 0, wave_u);
-    if (wave_on) load_frags<FMT, kPfBK, NF>(b0, W, e, nrow, ga.N, ga.K, 0, g);
-  }
-  pf_sync();
-  for (int c = 0; c < nfull; c += 2) {
-    const bool m1 = c + 1 < nfull;
-    if (m1) {
-      pf_issue_a<kPasses>(As1, arow, (c + 1) * kPfBK, wave_u);
-      if (wave_on) load_frags<FMT, kPfBK, NF>(b1, W, e, nrow, ga.N, ga.K, (c + 1) * kPfBK, g);
+    for (int kc = 0; kc < nchunks; ++kc) {
+      const uint8_t* st = smem + (kc % kPfStages) * P::kStage;
+      // steps 0..2: each overlaps the next step's A reads and dequant
+      pf_read_a<MI>(a1, st, c, h, 1);
+#pragma unroll
+      for (int j = 0; j < NF; ++j) q1[j] = pf_deq_step<FMT>(b[j], 1);
+      pf_mfma<MI, NF>(acc, a0, q0);
+      pf_read_a<MI>(a0, st, c, h, 2);
+#pragma unroll
+      for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 2);
+      pf_mfma<MI, NF>(acc, a1, q1);
+      pf_read_a<MI>(a1, st, c, h, 3);
+#pragma unroll
+      for (int j = 0; j < NF; ++j) q1[j] = pf_deq_step<FMT>(b[j], 3);
+      pf_mfma<MI, NF>(acc, a0, q0);
+      // step 3 overlaps chunk kc+1's reads: chunk kc+1 has landed (all but the
+      // two newest chunks' DMA are done) and every wave is past its reads of
+      // chunk kc, whose stage is refilled with chunk kc+4
+      wait_vmcnt<2 * P::kIssue>();
+      pf_barrier();
+      pf_issue<FMT, BM, NF>(ring + (kc % kPfStages) * P::kStage, arow, brow,
+                            min(kc + kPfStages, nchunks - 1), wave_u, N);
+      const uint8_t* nx = smem + ((kc + 1) % kPfStages) * P::kStage;
+      pf_read_b<FMT, EPI, NF>(b, nx + P::kABytes, scale_lds, rl, min(kc + 1, nchunks - 1), h, K,
+                              W.group, P::BN);
+      pf_read_a<MI>(a0, nx, c, h, 0);
+      pf_mfma<MI, NF>(acc, a1, q1);
+#pragma unroll
+      for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
     }
-    if (wave_on) pf_compute<FMT, kPfBK, MI, NF>(acc, As0, b0, c16, g);
-    pf_sync();
-    if (!m1) break;
-    const bool m2 = c + 2 < nfull;
-    if (m2) {
-      pf_issue_a<kPasses>(As0, arow, (c + 2) * kPfBK, wave_u);
-      if (wave_on) load_frags<FMT, kPfBK, NF>(b0, W, e, nrow, ga.N, ga.K, (c + 2) * kPfBK, g);
-    }
-    if (wave_on) pf_compute<FMT, kPfBK, MI, NF>(acc, As1, b1, c16, g);
-    pf_sync();
   }
+  // no DMA may land in LDS after this workgroup is gone
+  wait_vmcnt<0>();
 
-  int k0 = nfull * kPfBK;
-  if (ga.K - k0 >= 64) {
-    pf_tail<FMT, 64, BM, NF>(acc, As0, ga, W, e, mb, nrow, wave_on, k0, tid, c16, g);
-    k0 += 64;
-  }
-  if (ga.K - k0 >= 32) pf_tail<FMT, 32, BM, NF>(acc, As0, ga, W, e, mb, nrow, wave_on, k0, tid, c16, g);
+  if (K % kPfBK) pf_tail32<FMT, EPI, MI, NF>(acc, ga, W, e, mb, n0, c, h, nchunks * kPfBK);
 
-  if (!wave_on) return;
+  if (n0 >= N) return;
   EpiArgs a = ea;
   a.row0 = mb * BM;
-  epilogue<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane);
+  epilogue32<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane);
 }
 
 // --------------------------------------------------------------------------
@@ -577,7 +892,7 @@ __global__ void __launch_bounds__(MAXT) gemm_decode_kernel(GemmArgs ga, WeightAr
 
   const int mb = blockIdx.x / ga.n_ntiles, nt = blockIdx.x % ga.n_ntiles;
   if (mb * BM >= ga.num_post_pad[0]) return;
-  const int e = ga.expert_ids[mb];
+  const int e = ga.expert_ids[mb * BM / ga.block_m];  // BM divides block_m
   if (e < 0 || e >= ga.E) return;
 
   const int nw = blockDim.x >> 6;
@@ -734,14 +1049,24 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
     else
       launch_decode<FMT, EPI, 2>(nf, ga, W, ea, st);
   } else {
-    const int bn = block_m == 64 ? PfShape<64, FMT>::BN : PfShape<128, FMT>::BN;
-    ga.n_ntiles = (ga.N + bn - 1) / bn;
-    const int total = ga.n_mblocks * ga.n_ntiles;
-    const dim3 grid((total + 7) / 8 * 8);
+    // widest tile whose scales fit the kernel's LDS; otherwise the split-K kernel
+    if (pf_scale_bytes(FMT, ga.K, W.group, Pf<128, 2>::BN) > kPfScaleBytes ||
+        (FMT == FMT_GPTQ && ga.N % 32 != 0)) {
+      // very long K (scales too large for LDS), or GPTQ zero-point rows that
+      // are not 16-byte multiples: the split-K kernel over 32-row sub-blocks
+      // of the aligned blocks
+      ga.n_mblocks = cap / 32;
+      ga.n_ntiles = (ga.N + 63) / 64;
+      launch_decode<FMT, EPI, 2>(4, ga, W, ea, st);
+      return hipGetLastError();
+    }
+    ga.n_ntiles = (ga.N + Pf<128, 2>::BN - 1) / Pf<128, 2>::BN;
+    ga.group_m = 4;  // measured flat between 1 and 16 at the gpt-oss-20b shape
+    const dim3 grid((ga.n_mblocks * ga.n_ntiles + 7) / 8 * 8);
     if (block_m == 64)
-      gemm_prefill_kernel<FMT, EPI, 64><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+      gemm_prefill_kernel<FMT, EPI, 64, 2><<<grid, dim3(256), 0, st>>>(ga, W, ea);
     else
-      gemm_prefill_kernel<FMT, EPI, 128><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+      gemm_prefill_kernel<FMT, EPI, 128, 2><<<grid, dim3(256), 0, st>>>(ga, W, ea);
   }
   return hipGetLastError();
 }
@@ -768,7 +1093,8 @@ extern "C" hipError_t moe_launch_gemm(int fmt, int epi, int block_m, int cap, co
                                       int mul, float alpha, float beta, float limit, uint16_t* out,
                                       int out_ld, hipStream_t st) {
   if (cap / block_m == 0) return hipSuccess;
-  moe::GemmArgs ga{A, a_div, n_slots, K, N, E, 0, 0, sid, eid, npp};
+  const uint64_t a_mul = ((1ull << 32) + (uint64_t)a_div - 1) / (uint64_t)a_div;
+  moe::GemmArgs ga{A, a_div, a_mul, n_slots, K, N, E, 0, 0, 1, block_m, sid, eid, npp};
   moe::EpiArgs ea{sid, 0, n_slots, N, tw, mul, alpha, beta, limit, out, out_ld};
   switch (fmt) {
     case moe::FMT_NVFP4: return moe::launch_fmt<moe::FMT_NVFP4>(epi, block_m, cap, ga, *W, ea, st);

@@ -34,7 +34,8 @@
  *   rows pair up).  K and N tails are handled exactly: no buffer is padded
  *   (hidden 2880 stays 2880; "gpt-oss-120b MXFP4 + --enable-expert-parallel
  *   crashes", root cause: the op's output is the unpadded width).
- * - Base pointers of qweight, x/a and outputs must be 16-byte aligned.
+ * - Base pointers of qweight, scales, zeros, x/a and outputs must be 16-byte
+ *   aligned (bias: 2-byte).
  */
 #ifndef MOE_W4A16_H
 #define MOE_W4A16_H

@@ -247,6 +247,12 @@ def _make_weights(ss, fmt, group, E, N, K, bias, threads=8):
                    zeros=zeros, global_scale=gscale, bias=b)
 
 
+def make_weights(fmt, *, E, N, K, group=None, bias=True, seed=0, threads=8) -> Weights:
+    """One family of synthetic 4-bit expert weights [E][N][K] (same recipe as make_layer)."""
+    return _make_weights(np.random.SeedSequence(seed), fmt, group or DEFAULT_GROUP[fmt], E, N, K,
+                         bias, threads)
+
+
 def make_layer(*, E, top_k, H, I, fmt, act="swigluoai", route="softmax", T,
                seed, group=None, bias=True, skew_std=0.0, router_bias_std=0.0,
                renormalize=True, mul_topk_weights=True, alpha=1.702, beta=1.0,

@@ -212,3 +212,26 @@ def test_gemm2_k_tails(K, B):
     dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
     y = M.moe_w4a16_gemm2(dev_bf16(a_bits), D["w2"], torch.from_numpy(tw).cuda(), True, dsi, dei, dnpp, B)
     assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 K={K} B{B}")
+
+
+@pytest.mark.parametrize("fmt,K,N,group,B", [
+    ("nvfp4", 12320, 96, None, 64),    # scales too long for LDS: split-K kernel on 32-row sub-blocks
+    ("gptq", 2560, 128, 32, 128),      # GPTQ group 32: narrow (128-column) prefill tiles
+    ("gptq", 256, 80, 64, 64),         # N % 32 != 0: split-K kernel on 32-row sub-blocks
+    ("mxfp4", 2880, 320, None, 128),   # MXFP4 at the gpt-oss K, ragged last column tile
+])
+def test_gemm2_tile_fallbacks(fmt, K, N, group, B):
+    """The prefill kernel's tile choices and fallbacks (scale tile size, zero-point alignment)."""
+    E, k, T = 3, 2, 40
+    w2 = S.make_weights(fmt, E=E, N=N, K=K, group=group, seed=K + N)
+    rng = np.random.default_rng(K + N)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    tw = rng.uniform(0.1, 1.0, size=T * k).astype(np.float32)
+    si, ei, npp = O.align(ids, E, B)
+    n = T * k
+    a_bits = S.f32_to_bf16_bits(rng.standard_normal((n, K)).astype(np.float32))
+    ref, cov = O.gemm2(a_bits, n, w2, tw, True, si, ei, npp, B)
+    dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
+    y = M.moe_w4a16_gemm2(dev_bf16(a_bits), upload_weights(w2), torch.from_numpy(tw).cuda(), True,
+                          dsi, dei, dnpp, B)
+    assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 {fmt} K={K} N={N} B{B}")
