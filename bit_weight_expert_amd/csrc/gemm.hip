@@ -131,6 +131,37 @@ __device__ __forceinline__ void load_chunk(BChunk<FMT, C>& b, const WeightArgs& 
   }
 }
 
+// The codes part of load_chunk only (the raw scale words are filled separately).
+template <int FMT, int C>
+__device__ __forceinline__ void load_codes(BChunk<FMT, C>& b, const WeightArgs& W, int e, int n,
+                                           int N, int K, int kl) {
+  constexpr int S = BChunk<FMT, C>::kSteps;
+  if (FMT == FMT_NVFP4 || FMT == FMT_MXFP4) {
+    const uint8_t* p = W.qweight + ((size_t)e * N + n) * (size_t)(K / 2) + kl / 2;
+    if (S >= 4) {
+#pragma unroll
+      for (int v = 0; v < S / 4; ++v) {
+        const uint4 t = *reinterpret_cast<const uint4*>(p + 16 * v);
+        b.q[4 * v] = t.x;
+        b.q[4 * v + 1] = t.y;
+        b.q[4 * v + 2] = t.z;
+        b.q[4 * v + 3] = t.w;
+      }
+    } else if (S == 2) {
+      const uint2 t = *reinterpret_cast<const uint2*>(p);
+      b.q[0] = t.x;
+      b.q[1] = t.y;
+    } else {
+      b.q[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+  } else {
+    const uint32_t* qw = reinterpret_cast<const uint32_t*>(W.qweight);
+    const size_t base = ((size_t)e * (K / 8) + kl / 8) * N + n;
+#pragma unroll
+    for (int i = 0; i < S; ++i) b.q[i] = qw[base + (size_t)i * N];
+  }
+}
+
 // 8 dequantised bf16 weights of MFMA step st.
 template <int FMT, int C>
 __device__ __forceinline__ bf16x8 deq_step(const BChunk<FMT, C>& b, int st) {
@@ -823,43 +854,136 @@ __global__ void __launch_bounds__(256, 1) gemm_prefill_kernel(GemmArgs ga, Weigh
 // --------------------------------------------------------------------------
 // decode kernel
 // --------------------------------------------------------------------------
+//
+// A few rows per expert: the weight stream is the whole cost.  Workgroup =
+// one row block (16*MI slots) x 32 weight rows (NF = 2 fragments), with
+// nw = 1, 2 or 4 waves that split K into contiguous runs of 128-wide chunks.
+// The tile's scales (contiguous in memory for NVFP4/MXFP4) are copied once
+// into LDS with full-width loads, so the per-chunk loads are only the 4-bit
+// codes and the A fragments.  Each wave walks its run with kDcDepth chunks of
+// those in flight in registers (a ring of slots, every load issued
+// unconditionally so the compiler can count exactly what is outstanding), so
+// the HBM stream never stops for a chunk's multiply; the waves' partial sums
+// are added through LDS in wave order (deterministic) and the epilogue is
+// spread over the waves.  The host picks nw so that the launch has enough
+// waves in flight when few experts are routed.
 
-constexpr int kDcBK = 256;
+constexpr int kDcBK = 128;    // K chunk
+constexpr int kDcDepth = 4;   // chunks in flight per wave
+constexpr int kDcRows = 32;   // weight rows per workgroup
 
-// One wave's share of a K chunk: weights of NF fragments plus its A fragments.
-template <int FMT, int C, int MI, int NF>
-struct DcChunk {
+// LDS scale tile of one workgroup: NVFP4 [32 rows][K/16] e4m3 bytes, MXFP4
+// [32 rows][K/32] e8m0 bytes, GPTQ [K/G][32 columns] fp16 scales followed by
+// [K/G][4] packed zero-point words.
+__host__ __device__ inline int dc_scale_bytes(int fmt, int K, int group) {
+  if (fmt == FMT_NVFP4) return kDcRows * (K / 16);
+  if (fmt == FMT_MXFP4) return kDcRows * (K / 32);
+  return (K / group) * (kDcRows * 2 + 16);
+}
+
+// Copy the tile's scales (weight rows n0 .. n0 + 31, those below N) into LDS.
+template <int FMT>
+__device__ __forceinline__ void dc_stage_scales(uint8_t* sc, const WeightArgs& W, int e, int n0,
+                                                int N, int K, int tid, int nthreads) {
+  const int rows = min(kDcRows, N - n0);  // a multiple of 16
+  if (FMT == FMT_NVFP4 || FMT == FMT_MXFP4) {
+    const int per_row = (FMT == FMT_NVFP4) ? K / 16 : K / 32;
+    const uint8_t* src = W.scales + ((size_t)e * N + n0) * per_row;
+    const int units = rows * per_row / 16;  // rows * per_row is a multiple of 16
+    for (int u = tid; u < units; u += nthreads)
+      reinterpret_cast<uint4*>(sc)[u] = reinterpret_cast<const uint4*>(src)[u];
+  } else {
+    const int ng = K / W.group;
+    const uint8_t* s16 = W.scales + ((size_t)e * ng * N + n0) * 2;
+    for (int u = tid; u < ng * (rows / 8); u += nthreads) {  // 16-byte pieces of fp16 scales
+      const int gr = u / (rows / 8), q = u % (rows / 8);
+      reinterpret_cast<uint4*>(sc + gr * kDcRows * 2)[q] =
+          *reinterpret_cast<const uint4*>(s16 + (size_t)gr * N * 2 + 16 * q);
+    }
+    const uint32_t* z = W.zeros + (size_t)e * ng * (N / 8) + n0 / 8;
+    uint32_t* zl = reinterpret_cast<uint32_t*>(sc + ng * kDcRows * 2);
+    for (int u = tid; u < ng * (rows / 8); u += nthreads) {  // one zero-point word per 8 columns
+      const int gr = u / (rows / 8), q = u % (rows / 8);
+      zl[gr * 4 + q] = z[(size_t)gr * (N / 8) + q];
+    }
+  }
+}
+
+// Raw scale words of one fragment for the lane's k range [kl, kl + C/4), from
+// the LDS tile (r = the fragment row's index inside the tile).
+template <int FMT, int C>
+__device__ __forceinline__ void dc_fill_scales(BChunk<FMT, C>& b, const uint8_t* sc, int r, int K,
+                                               int group, int kl) {
+  if (FMT == FMT_NVFP4) {
+    const uint8_t* sp = sc + r * (K / 16) + kl / 16;
+    if (C == 256) {
+      b.sr[0] = *reinterpret_cast<const uint16_t*>(sp);
+      b.sr[1] = *reinterpret_cast<const uint16_t*>(sp + 2);
+    } else if (C == 128) {
+      b.sr[0] = *reinterpret_cast<const uint16_t*>(sp);
+    } else {
+      b.sr[0] = *sp;
+    }
+  } else if (FMT == FMT_MXFP4) {
+    const uint8_t* sp = sc + r * (K / 32) + kl / 32;
+    b.sr[0] = sp[0];
+    if (C == 256) b.sr[1] = sp[1];
+  } else {
+    const int gr = kl / group;
+    b.sr[0] = reinterpret_cast<const uint16_t*>(sc)[gr * kDcRows + r];
+    b.sr[1] = reinterpret_cast<const uint32_t*>(sc + (K / group) * kDcRows * 2)[gr * 4 + (r >> 3)];
+    b.zsh = 4 * (r & 7);
+  }
+}
+
+// One wave's share of a K chunk: the weight codes of NF fragments, and
+// separately its A fragments (A comes from L2 and needs a shallower ring).
+template <int FMT, int C, int NF>
+struct DcB {
   BChunk<FMT, C> b[NF];
+};
+template <int C, int MI>
+struct DcA {
   uint4 a[MI][C / 32];
 };
 
-// A rows of padding slots are not read (their lanes keep stale values, which
-// only reach accumulator rows the epilogue skips).
-template <int FMT, int C, int MI, int NF>
-__device__ __forceinline__ void dc_load(DcChunk<FMT, C, MI, NF>& d, const WeightArgs& W,
-                                        const GemmArgs& ga, const uint16_t* const (&arow)[MI],
-                                        const bool (&aon)[MI], const int (&nrow)[NF], int e, int k0,
-                                        int g) {
-  load_frags<FMT, C, NF>(d.b, W, e, nrow, ga.N, ga.K, k0, g);
+template <int FMT, int C, int NF>
+__device__ __forceinline__ void dc_load_b(DcB<FMT, C, NF>& d, const WeightArgs& W, const GemmArgs& ga,
+                                          const int (&nrow)[NF], int e, int k0, int g) {
+#pragma unroll
+  for (int j = 0; j < NF; ++j) load_codes<FMT, C>(d.b[j], W, e, nrow[j], ga.N, ga.K, k0 + g * (C / 4));
+}
+
+// Padding slots read A row 0 (a_row), so every lane loads and no branch is
+// needed; their products only reach accumulator rows the epilogue skips.
+template <int C, int MI>
+__device__ __forceinline__ void dc_load_a(DcA<C, MI>& d, const uint16_t* const (&arow)[MI], int k0,
+                                          int g) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
-    if (aon[i]) {
 #pragma unroll
-      for (int s = 0; s < C / 32; ++s)
-        d.a[i][s] = *reinterpret_cast<const uint4*>(arow[i] + k0 + g * (C / 4) + 8 * s);
-    }
+    for (int s = 0; s < C / 32; ++s)
+      d.a[i][s] = *reinterpret_cast<const uint4*>(arow[i] + k0 + g * (C / 4) + 8 * s);
 }
 
 template <int FMT, int C, int MI, int NF>
-__device__ __forceinline__ void dc_compute(f32x4 (&acc)[MI][NF], const DcChunk<FMT, C, MI, NF>& d) {
+__device__ __forceinline__ void dc_compute(f32x4 (&acc)[MI][NF], const DcB<FMT, C, NF>& db,
+                                           const DcA<C, MI>& da, const uint8_t* sc,
+                                           const int (&rl)[NF], int K, int group, int g, int k0) {
+  BChunk<FMT, C> b[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    b[j] = db.b[j];
+    dc_fill_scales<FMT, C>(b[j], sc, rl[j], K, group, k0 + g * (C / 4));
+  }
 #pragma unroll
   for (int s = 0; s < C / 32; ++s) {
     bf16x8 bf[NF];
 #pragma unroll
-    for (int j = 0; j < NF; ++j) bf[j] = deq_step<FMT, C>(d.b[j], s);
+    for (int j = 0; j < NF; ++j) bf[j] = deq_step<FMT, C>(b[j], s);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const bf16x8 af = as_bf16x8(d.a[i][s]);
+      const bf16x8 af = as_bf16x8(da.a[i][s]);
 #pragma unroll
       for (int j = 0; j < NF; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
@@ -867,28 +991,24 @@ __device__ __forceinline__ void dc_compute(f32x4 (&acc)[MI][NF], const DcChunk<F
   }
 }
 
+// One unpipelined chunk of width C (the K tail).
 template <int FMT, int C, int MI, int NF>
 __device__ __forceinline__ void dc_chunk(f32x4 (&acc)[MI][NF], const WeightArgs& W,
                                          const GemmArgs& ga, const uint16_t* const (&arow)[MI],
-                                         const bool (&aon)[MI], const int (&nrow)[NF], int e,
-                                         int k0, int g) {
-  DcChunk<FMT, C, MI, NF> d;
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int s = 0; s < C / 32; ++s) d.a[i][s] = uint4{0u, 0u, 0u, 0u};
-  dc_load(d, W, ga, arow, aon, nrow, e, k0, g);
-  dc_compute(acc, d);
+                                         const int (&nrow)[NF], const int (&rl)[NF],
+                                         const uint8_t* sc, int e, int k0, int g) {
+  DcB<FMT, C, NF> db;
+  DcA<C, MI> da;
+  dc_load_b(db, W, ga, nrow, e, k0, g);
+  dc_load_a(da, arow, k0, g);
+  dc_compute(acc, db, da, sc, rl, ga.K, W.group, g, k0);
 }
 
-// Workgroup = 16*MI rows x 16*NF columns and one wave per 256-wide K chunk
-// (blockDim.x / 64 waves, at most MAXT / 64): every chunk of the tile is in
-// flight at once, which is what a weight-streaming GEMV needs.  The waves'
-// partial sums are added through LDS in wave order (deterministic).
-template <int FMT, int EPI, int MI, int NF, int MAXT>
-__global__ void __launch_bounds__(MAXT) gemm_decode_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
+template <int FMT, int EPI, int MI, int NF>
+__global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
+  static_assert(NF * 16 == kDcRows, "decode tile is 32 weight rows");
   constexpr int BM = 16 * MI;
-  extern __shared__ f32x4 red[];  // [nw][MI][NF][64]
+  extern __shared__ __attribute__((aligned(16))) uint8_t dc_smem[];  // scale tile, then [nw][MI][NF][64] partials
 
   const int mb = blockIdx.x / ga.n_ntiles, nt = blockIdx.x % ga.n_ntiles;
   if (mb * BM >= ga.num_post_pad[0]) return;
@@ -898,19 +1018,19 @@ __global__ void __launch_bounds__(MAXT) gemm_decode_kernel(GemmArgs ga, WeightAr
   const int nw = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int n0 = nt * NF * 16;
+  const int n0 = nt * kDcRows;
+  const int K = ga.K;
+  uint8_t* const sc = dc_smem;
 
   const uint16_t* arow[MI];
-  bool aon[MI];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int sid = ga.sorted_ids[mb * BM + i * 16 + c16];
-    aon[i] = sid < ga.n_slots;
-    arow[i] = a_row(ga, sid);
+  for (int i = 0; i < MI; ++i) arow[i] = a_row(ga, ga.sorted_ids[mb * BM + i * 16 + c16]);
+  int nrow[NF], rl[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    nrow[j] = frag_on<EPI>(n0, j, ga.N) ? frag_row<EPI>(n0, j, c16) : n0;
+    rl[j] = nrow[j] - n0;
   }
-  int nrow[NF];
-#pragma unroll
-  for (int j = 0; j < NF; ++j) nrow[j] = frag_on<EPI>(n0, j, ga.N) ? frag_row<EPI>(n0, j, c16) : 0;
 
   f32x4 acc[MI][NF];
 #pragma unroll
@@ -918,27 +1038,63 @@ __global__ void __launch_bounds__(MAXT) gemm_decode_kernel(GemmArgs ga, WeightAr
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nfull = ga.K / kDcBK;
-  for (int c = wave; c < nfull; c += nw)
-    dc_chunk<FMT, kDcBK, MI, NF>(acc, W, ga, arow, aon, nrow, e, c * kDcBK, g);
-  // tail (K % 256) in 128/64/32-wide pieces, one wave each, after the last chunk owner
-  int k0 = nfull * kDcBK;
-  int tw = nfull % nw;
-  if (ga.K - k0 >= 128) {
-    if (wave == tw) dc_chunk<FMT, 128, MI, NF>(acc, W, ga, arow, aon, nrow, e, k0, g);
-    k0 += 128;
-    tw = (tw + 1) % nw;
+  // this wave's run of full chunks [c0, c0 + n).  Weight codes run kDcDepth
+  // chunks ahead, A fragments two; the first ones are requested before the
+  // scale tile, whose copy then waits for them too.
+  const int nfull = K / kDcBK;
+  const int c0 = nfull * wave / nw, n = nfull * (wave + 1) / nw - c0;
+  const int last = max(c0 + n - 1, 0);
+  DcB<FMT, kDcBK, NF> b0, b1, b2, b3;
+  DcA<kDcBK, MI> a0, a1;
+  if (n > 0) {
+    dc_load_b(b0, W, ga, nrow, e, c0 * kDcBK, g);
+    dc_load_a(a0, arow, c0 * kDcBK, g);
+    dc_load_b(b1, W, ga, nrow, e, min(c0 + 1, last) * kDcBK, g);
+    dc_load_a(a1, arow, min(c0 + 1, last) * kDcBK, g);
+    dc_load_b(b2, W, ga, nrow, e, min(c0 + 2, last) * kDcBK, g);
+    dc_load_b(b3, W, ga, nrow, e, min(c0 + 3, last) * kDcBK, g);
   }
-  if (ga.K - k0 >= 64) {
-    if (wave == tw) dc_chunk<FMT, 64, MI, NF>(acc, W, ga, arow, aon, nrow, e, k0, g);
-    k0 += 64;
-    tw = (tw + 1) % nw;
+  dc_stage_scales<FMT>(sc, W, e, n0, ga.N, K, tid, 64 * nw);
+  __syncthreads();
+  const int group = W.group;
+  for (int i = 0; i < n; i += kDcDepth) {
+    // chunk c0 + i + d sits in b<d> and a<d % 2>; once multiplied its slots
+    // take chunk + 4 (codes) and chunk + 2 (A); past the run the last chunk
+    // is fetched again and never used
+#define MOE_DC_PHASE(D, BS, AS)                                                                    \
+    {                                                                                              \
+      const int kc = min(c0 + i + D, last);                                                        \
+      dc_compute(acc, BS, AS, sc, rl, K, group, g, kc * kDcBK);                                    \
+      dc_load_b(BS, W, ga, nrow, e, min(c0 + i + D + 4, last) * kDcBK, g);                         \
+      dc_load_a(AS, arow, min(c0 + i + D + 2, last) * kDcBK, g);                                   \
+    }
+    MOE_DC_PHASE(0, b0, a0)
+    if (i + 1 >= n) break;
+    MOE_DC_PHASE(1, b1, a1)
+    if (i + 2 >= n) break;
+    MOE_DC_PHASE(2, b2, a0)
+    if (i + 3 >= n) break;
+    MOE_DC_PHASE(3, b3, a1)
+#undef MOE_DC_PHASE
   }
-  if (ga.K - k0 >= 32) {
-    if (wave == tw) dc_chunk<FMT, 32, MI, NF>(acc, W, ga, arow, aon, nrow, e, k0, g);
+  // K tail (K % 128: a 64- and/or a 32-wide piece) on the last wave
+  if (wave == nw - 1) {
+    int k0 = nfull * kDcBK;
+    if (K - k0 >= 64) {
+      dc_chunk<FMT, 64, MI, NF>(acc, W, ga, arow, nrow, rl, sc, e, k0, g);
+      k0 += 64;
+    }
+    if (K - k0 >= 32) dc_chunk<FMT, 32, MI, NF>(acc, W, ga, arow, nrow, rl, sc, e, k0, g);
   }
 
-  // reduce the partial sums in wave order
+  EpiArgs a = ea;
+  a.row0 = mb * BM;
+  if (nw == 1) {
+    epilogue<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane);
+    return;
+  }
+  // add the waves' partial sums in wave order
+  f32x4* red = reinterpret_cast<f32x4*>(dc_smem + ((dc_scale_bytes(FMT, K, group) + 15) & ~15));
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -948,8 +1104,6 @@ __global__ void __launch_bounds__(MAXT) gemm_decode_kernel(GemmArgs ga, WeightAr
   // gate/up pair (gated) each
   constexpr int GF = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int kGroups = NF / GF;
-  EpiArgs a = ea;
-  a.row0 = mb * BM;
   for (int grp = wave; grp < kGroups; grp += nw) {
     f32x4 fin[MI][GF];
 #pragma unroll
@@ -957,15 +1111,15 @@ __global__ void __launch_bounds__(MAXT) gemm_decode_kernel(GemmArgs ga, WeightAr
 #pragma unroll
       for (int q = 0; q < GF; ++q) {
         const int j = grp * GF + q;
-        f32x4 s = red[(i * NF + j) * 64 + lane];
+        f32x4 sum = red[(i * NF + j) * 64 + lane];
         for (int w2 = 1; w2 < nw; ++w2) {
           const f32x4 t = red[((w2 * MI + i) * NF + j) * 64 + lane];
-          s[0] += t[0];
-          s[1] += t[1];
-          s[2] += t[2];
-          s[3] += t[3];
+          sum[0] += t[0];
+          sum[1] += t[1];
+          sum[2] += t[2];
+          sum[3] += t[3];
         }
-        fin[i][q] = s;
+        fin[i][q] = sum;
       }
     // the fragment group as its own "wave" starting at weight row n0 + 16*GF*grp
     epilogue<EPI, FMT, MI, GF>(fin, a, W, e, n0 + 16 * GF * grp, lane);
@@ -1009,24 +1163,19 @@ __global__ void __launch_bounds__(256) moe_sum_kernel(const uint16_t* __restrict
 // launch
 // --------------------------------------------------------------------------
 
-template <int FMT, int EPI, int MI, int NF, int MAXT>
-static void launch_decode_nw(const GemmArgs& ga, const WeightArgs& W, const EpiArgs& ea,
-                             hipStream_t st) {
-  const int chunks = ga.K / kDcBK + (ga.K % kDcBK ? 1 : 0);
-  const int nw = chunks < MAXT / 64 ? chunks : MAXT / 64;
-  const size_t lds = (size_t)nw * MI * NF * 64 * sizeof(f32x4);
-  gemm_decode_kernel<FMT, EPI, MI, NF, MAXT>
-      <<<dim3(ga.n_mblocks * ga.n_ntiles), dim3(64 * nw), lds, st>>>(ga, W, ea);
-}
-
+// Decode launch: 32-row weight tiles (NF = 2); K split over nw waves per
+// workgroup when few units would leave the chip short of waves.
 template <int FMT, int EPI, int MI>
-static void launch_decode(int nf, const GemmArgs& ga, const WeightArgs& W, const EpiArgs& ea,
+static void launch_decode(GemmArgs ga, const WeightArgs& W, const EpiArgs& ea, int blocks_est,
                           hipStream_t st) {
-  constexpr int kMaxT = MI == 1 ? 768 : 512;
-  if (nf == 2)
-    launch_decode_nw<FMT, EPI, MI, 2, kMaxT>(ga, W, ea, st);
-  else
-    launch_decode_nw<FMT, EPI, MI, 4, kMaxT>(ga, W, ea, st);
+  constexpr int NF = 2;
+  ga.n_ntiles = (ga.N + kDcRows - 1) / kDcRows;
+  const long units = (long)blocks_est * ga.n_ntiles;
+  const int nw = units >= 4096 ? 1 : units >= 2048 ? 2 : 4;
+  const size_t lds = (size_t)((dc_scale_bytes(FMT, ga.K, W.group) + 15) & ~15) +
+                     (nw > 1 ? (size_t)nw * MI * NF * 64 * sizeof(f32x4) : 0);
+  gemm_decode_kernel<FMT, EPI, MI, NF>
+      <<<dim3(ga.n_mblocks * ga.n_ntiles), dim3(64 * nw), lds, st>>>(ga, W, ea);
 }
 
 template <int FMT, int EPI>
@@ -1034,20 +1183,13 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
                              hipStream_t st) {
   ga.n_mblocks = cap / block_m;
   if (block_m <= 32) {
-    // few rows per expert: split K inside the workgroup.  Narrow (32-column)
-    // tiles when 64-column ones would leave fewer than two workgroups per CU
-    // (at most one block per routed expert is expected in this regime).
+    // at most one block per routed expert is expected in this regime: the
+    // number of routed experts bounds the blocks that hold slots
     const int blocks_est = ga.E < ga.n_slots ? ga.E : ga.n_slots;
-#ifdef MOE_DC_NF
-    const int nf = MOE_DC_NF;
-#else
-    const int nf = (long)blocks_est * ((ga.N + 63) / 64) < 512 ? 2 : 4;
-#endif
-    ga.n_ntiles = (ga.N + 16 * nf - 1) / (16 * nf);
     if (block_m == 16)
-      launch_decode<FMT, EPI, 1>(nf, ga, W, ea, st);
+      launch_decode<FMT, EPI, 1>(ga, W, ea, blocks_est, st);
     else
-      launch_decode<FMT, EPI, 2>(nf, ga, W, ea, st);
+      launch_decode<FMT, EPI, 2>(ga, W, ea, blocks_est, st);
   } else {
     // widest tile whose scales fit the kernel's LDS; otherwise the split-K kernel
     if (pf_scale_bytes(FMT, ga.K, W.group, Pf<128, 2>::BN) > kPfScaleBytes ||
@@ -1056,8 +1198,7 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
       // are not 16-byte multiples: the split-K kernel over 32-row sub-blocks
       // of the aligned blocks
       ga.n_mblocks = cap / 32;
-      ga.n_ntiles = (ga.N + 63) / 64;
-      launch_decode<FMT, EPI, 2>(4, ga, W, ea, st);
+      launch_decode<FMT, EPI, 2>(ga, W, ea, ga.n_mblocks, st);
       return hipGetLastError();
     }
     ga.n_ntiles = (ga.N + Pf<128, 2>::BN - 1) / Pf<128, 2>::BN;
