@@ -856,7 +856,7 @@ __global__ void __launch_bounds__(256, 1) gemm_prefill_kernel(GemmArgs ga, Weigh
 // --------------------------------------------------------------------------
 //
 // A few rows per expert: the weight stream is the whole cost.  Workgroup =
-// one row block (16*MI slots) x 32 weight rows (NF = 2 fragments), with
+// one row block (16*MI slots) x 16*NF weight rows (NF = 2 or 4), with
 // nw = 1, 2 or 4 waves that split K into contiguous runs of 128-wide chunks.
 // The tile's scales (contiguous in memory for NVFP4/MXFP4) are copied once
 // into LDS with full-width loads, so the per-chunk loads are only the 4-bit
@@ -870,22 +870,20 @@ __global__ void __launch_bounds__(256, 1) gemm_prefill_kernel(GemmArgs ga, Weigh
 
 constexpr int kDcBK = 128;    // K chunk
 constexpr int kDcDepth = 4;   // chunks in flight per wave
-constexpr int kDcRows = 32;   // weight rows per workgroup
-
-// LDS scale tile of one workgroup: NVFP4 [32 rows][K/16] e4m3 bytes, MXFP4
-// [32 rows][K/32] e8m0 bytes, GPTQ [K/G][32 columns] fp16 scales followed by
-// [K/G][4] packed zero-point words.
-__host__ __device__ inline int dc_scale_bytes(int fmt, int K, int group) {
-  if (fmt == FMT_NVFP4) return kDcRows * (K / 16);
-  if (fmt == FMT_MXFP4) return kDcRows * (K / 32);
-  return (K / group) * (kDcRows * 2 + 16);
+// LDS scale tile of one workgroup of R weight rows: NVFP4 [R rows][K/16]
+// e4m3 bytes, MXFP4 [R rows][K/32] e8m0 bytes, GPTQ [K/G][R columns] fp16
+// scales followed by [K/G][R/8] packed zero-point words.
+__host__ __device__ inline int dc_scale_bytes(int fmt, int K, int group, int R) {
+  if (fmt == FMT_NVFP4) return R * (K / 16);
+  if (fmt == FMT_MXFP4) return R * (K / 32);
+  return (K / group) * (R * 2 + R / 2);
 }
 
-// Copy the tile's scales (weight rows n0 .. n0 + 31, those below N) into LDS.
-template <int FMT>
+// Copy the tile's scales (weight rows n0 .. n0 + R - 1, those below N) into LDS.
+template <int FMT, int R>
 __device__ __forceinline__ void dc_stage_scales(uint8_t* sc, const WeightArgs& W, int e, int n0,
                                                 int N, int K, int tid, int nthreads) {
-  const int rows = min(kDcRows, N - n0);  // a multiple of 16
+  const int rows = min(R, N - n0);  // a multiple of 16
   if (FMT == FMT_NVFP4 || FMT == FMT_MXFP4) {
     const int per_row = (FMT == FMT_NVFP4) ? K / 16 : K / 32;
     const uint8_t* src = W.scales + ((size_t)e * N + n0) * per_row;
@@ -897,21 +895,21 @@ __device__ __forceinline__ void dc_stage_scales(uint8_t* sc, const WeightArgs& W
     const uint8_t* s16 = W.scales + ((size_t)e * ng * N + n0) * 2;
     for (int u = tid; u < ng * (rows / 8); u += nthreads) {  // 16-byte pieces of fp16 scales
       const int gr = u / (rows / 8), q = u % (rows / 8);
-      reinterpret_cast<uint4*>(sc + gr * kDcRows * 2)[q] =
+      reinterpret_cast<uint4*>(sc + gr * R * 2)[q] =
           *reinterpret_cast<const uint4*>(s16 + (size_t)gr * N * 2 + 16 * q);
     }
     const uint32_t* z = W.zeros + (size_t)e * ng * (N / 8) + n0 / 8;
-    uint32_t* zl = reinterpret_cast<uint32_t*>(sc + ng * kDcRows * 2);
+    uint32_t* zl = reinterpret_cast<uint32_t*>(sc + ng * R * 2);
     for (int u = tid; u < ng * (rows / 8); u += nthreads) {  // one zero-point word per 8 columns
       const int gr = u / (rows / 8), q = u % (rows / 8);
-      zl[gr * 4 + q] = z[(size_t)gr * (N / 8) + q];
+      zl[gr * (R / 8) + q] = z[(size_t)gr * (N / 8) + q];
     }
   }
 }
 
 // Raw scale words of one fragment for the lane's k range [kl, kl + C/4), from
 // the LDS tile (r = the fragment row's index inside the tile).
-template <int FMT, int C>
+template <int FMT, int C, int R>
 __device__ __forceinline__ void dc_fill_scales(BChunk<FMT, C>& b, const uint8_t* sc, int r, int K,
                                                int group, int kl) {
   if (FMT == FMT_NVFP4) {
@@ -930,8 +928,8 @@ __device__ __forceinline__ void dc_fill_scales(BChunk<FMT, C>& b, const uint8_t*
     if (C == 256) b.sr[1] = sp[1];
   } else {
     const int gr = kl / group;
-    b.sr[0] = reinterpret_cast<const uint16_t*>(sc)[gr * kDcRows + r];
-    b.sr[1] = reinterpret_cast<const uint32_t*>(sc + (K / group) * kDcRows * 2)[gr * 4 + (r >> 3)];
+    b.sr[0] = reinterpret_cast<const uint16_t*>(sc)[gr * R + r];
+    b.sr[1] = reinterpret_cast<const uint32_t*>(sc + (K / group) * R * 2)[gr * (R / 8) + (r >> 3)];
     b.zsh = 4 * (r & 7);
   }
 }
@@ -974,7 +972,7 @@ __device__ __forceinline__ void dc_compute(f32x4 (&acc)[MI][NF], const DcB<FMT, 
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     b[j] = db.b[j];
-    dc_fill_scales<FMT, C>(b[j], sc, rl[j], K, group, k0 + g * (C / 4));
+    dc_fill_scales<FMT, C, 16 * NF>(b[j], sc, rl[j], K, group, k0 + g * (C / 4));
   }
 #pragma unroll
   for (int s = 0; s < C / 32; ++s) {
@@ -1006,7 +1004,6 @@ __device__ __forceinline__ void dc_chunk(f32x4 (&acc)[MI][NF], const WeightArgs&
 
 template <int FMT, int EPI, int MI, int NF>
 __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
-  static_assert(NF * 16 == kDcRows, "decode tile is 32 weight rows");
   constexpr int BM = 16 * MI;
   extern __shared__ __attribute__((aligned(16))) uint8_t dc_smem[];  // scale tile, then [nw][MI][NF][64] partials
 
@@ -1018,7 +1015,7 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
   const int nw = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int n0 = nt * kDcRows;
+  const int n0 = nt * 16 * NF;
   const int K = ga.K;
   uint8_t* const sc = dc_smem;
 
@@ -1054,7 +1051,7 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
     dc_load_b(b2, W, ga, nrow, e, min(c0 + 2, last) * kDcBK, g);
     dc_load_b(b3, W, ga, nrow, e, min(c0 + 3, last) * kDcBK, g);
   }
-  dc_stage_scales<FMT>(sc, W, e, n0, ga.N, K, tid, 64 * nw);
+  dc_stage_scales<FMT, 16 * NF>(sc, W, e, n0, ga.N, K, tid, 64 * nw);
   __syncthreads();
   const int group = W.group;
   for (int i = 0; i < n; i += kDcDepth) {
@@ -1094,7 +1091,7 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
     return;
   }
   // add the waves' partial sums in wave order
-  f32x4* red = reinterpret_cast<f32x4*>(dc_smem + ((dc_scale_bytes(FMT, K, group) + 15) & ~15));
+  f32x4* red = reinterpret_cast<f32x4*>(dc_smem + ((dc_scale_bytes(FMT, K, group, 16 * NF) + 15) & ~15));
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -1163,19 +1160,24 @@ __global__ void __launch_bounds__(256) moe_sum_kernel(const uint16_t* __restrict
 // launch
 // --------------------------------------------------------------------------
 
-// Decode launch: 32-row weight tiles (NF = 2); K split over nw waves per
-// workgroup when few units would leave the chip short of waves.
-template <int FMT, int EPI, int MI>
-static void launch_decode(GemmArgs ga, const WeightArgs& W, const EpiArgs& ea, int blocks_est,
-                          hipStream_t st) {
-  constexpr int NF = 2;
-  ga.n_ntiles = (ga.N + kDcRows - 1) / kDcRows;
-  const long units = (long)blocks_est * ga.n_ntiles;
+// Decode launch: 32-row weight tiles (64-row ones measured no faster at
+// 64 tokens); K split over nw waves per workgroup when few units would leave
+// the chip short of waves.
+template <int FMT, int EPI, int MI, int NF>
+static void launch_decode_nf(GemmArgs ga, const WeightArgs& W, const EpiArgs& ea, long units,
+                             hipStream_t st) {
+  ga.n_ntiles = (ga.N + 16 * NF - 1) / (16 * NF);
   const int nw = units >= 4096 ? 1 : units >= 2048 ? 2 : 4;
-  const size_t lds = (size_t)((dc_scale_bytes(FMT, ga.K, W.group) + 15) & ~15) +
+  const size_t lds = (size_t)((dc_scale_bytes(FMT, ga.K, W.group, 16 * NF) + 15) & ~15) +
                      (nw > 1 ? (size_t)nw * MI * NF * 64 * sizeof(f32x4) : 0);
   gemm_decode_kernel<FMT, EPI, MI, NF>
       <<<dim3(ga.n_mblocks * ga.n_ntiles), dim3(64 * nw), lds, st>>>(ga, W, ea);
+}
+
+template <int FMT, int EPI, int MI>
+static void launch_decode(GemmArgs ga, const WeightArgs& W, const EpiArgs& ea, int blocks_est,
+                          hipStream_t st) {
+  launch_decode_nf<FMT, EPI, MI, 2>(ga, W, ea, (long)blocks_est * ((ga.N + 31) / 32), st);
 }
 
 template <int FMT, int EPI>
