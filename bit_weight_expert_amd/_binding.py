@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route.restype = i
         L.moe_align.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
         L.moe_align.restype = i
+        L.moe_route_align.argtypes = [vp, i, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp]
+        L.moe_route_align.restype = i
         L.moe_w4a16_gemm1.argtypes = [vp, i, i, i, i, i, wq, i, f, f, f, vp, vp, vp, i, vp, vp]
         L.moe_w4a16_gemm1.restype = i
         L.moe_w4a16_gemm2.argtypes = [vp, i, i, i, i, wq, vp, i, vp, vp, vp, i, vp, vp]
@@ -186,6 +188,28 @@ def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, sorted_ids=None, exp
     _check(lib().moe_align(_ptr(topk_ids), T, k, E, block_m, _ptr(sorted_ids), _ptr(expert_ids),
                            _ptr(num_post_pad), _stream()), "moe_align")
     return sorted_ids, expert_ids, num_post_pad
+
+
+def moe_route_align(logits: torch.Tensor, top_k: int, block_m: int, kind: str = "softmax",
+                    expert_bias=None, renormalize: bool = True):
+    """moe_route then moe_align in one call -> (topk_ids, topk_w, sorted_ids, expert_ids,
+    num_post_pad), shaped as those two functions return them."""
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    dev = logits.device
+    cap = moe_align_capacity(T, top_k, E, block_m)
+    topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    sorted_ids = torch.empty((cap,), dtype=torch.int32, device=dev)
+    expert_ids = torch.empty((cap // block_m if block_m else 0,), dtype=torch.int32, device=dev)
+    num_post_pad = torch.zeros((1,), dtype=torch.int32, device=dev)
+    if expert_bias is not None:
+        _dev(expert_bias, torch.float32, "expert_bias")
+    _check(lib().moe_route_align(_ptr(logits), T, E, top_k, ROUTE[kind], _ptr(expert_bias),
+                                 int(bool(renormalize)), block_m, _ptr(topk_ids), _ptr(topk_w),
+                                 _ptr(sorted_ids), _ptr(expert_ids), _ptr(num_post_pad),
+                                 _stream()), "moe_route_align")
+    return topk_ids, topk_w, sorted_ids, expert_ids, num_post_pad
 
 
 def moe_w4a16_gemm1(x: torch.Tensor, top_k: int, w13: QuantWeights, act: str, alpha: float,

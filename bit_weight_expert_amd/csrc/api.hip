@@ -12,6 +12,9 @@ extern "C" hipError_t moe_launch_route(const float*, int, int, int, int, const f
                                        int32_t*, float*, hipStream_t);
 extern "C" hipError_t moe_launch_align(const int32_t*, int, int, int, int, int32_t*, int32_t*,
                                        int32_t*, hipStream_t);
+extern "C" hipError_t moe_launch_route_align(const float*, int, int, int, int, const float*, int,
+                                             int32_t*, float*, int, int, int32_t*, int32_t*,
+                                             int32_t*, hipStream_t);
 extern "C" hipError_t moe_launch_gemm(int, int, int, int, const uint16_t*, int, int, int, int, int,
                                       const moe::WeightArgs*, const int32_t*, const int32_t*,
                                       const int32_t*, const float*, int, float, float, float,
@@ -155,6 +158,27 @@ moe_status_t moe_align(const int32_t* topk_ids, int T, int top_k, int E, int blo
                                      num_post_pad, static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_route_align(const float* logits, int T, int E, int top_k, moe_route_t kind,
+                             const float* expert_bias, int renormalize, int block_m,
+                             int32_t* topk_ids, float* topk_w, int32_t* sorted_ids,
+                             int32_t* expert_ids, int32_t* num_post_pad, moe_stream_t stream) {
+  if (T < 0 || E <= 0 || E > kMaxE || top_k < 1 || top_k > E || top_k > kMaxTopK ||
+      !valid_block_m(block_m))
+    return MOE_ERR_SHAPE;
+  if ((long long)T * top_k >= (1LL << 24)) return MOE_ERR_SHAPE;
+  if (kind != MOE_ROUTE_SOFTMAX && kind != MOE_ROUTE_SIGMOID_BIAS) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (logits == nullptr || topk_ids == nullptr || topk_w == nullptr || sorted_ids == nullptr ||
+      expert_ids == nullptr || num_post_pad == nullptr)
+    return MOE_ERR_NULL;
+  if (kind == MOE_ROUTE_SIGMOID_BIAS && expert_bias == nullptr) return MOE_ERR_NULL;
+  const int cap = (int)moe_align_capacity(T, top_k, E, block_m);
+  return hip_status(moe_launch_route_align(logits, T, E, top_k, (int)kind, expert_bias,
+                                           renormalize ? 1 : 0, topk_ids, topk_w, block_m, cap,
+                                           sorted_ids, expert_ids, num_post_pad,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 static moe_status_t gemm_common_checks(int size_m, int top_k, int E, int block_m) {
   if (size_m < 0 || top_k < 1 || E <= 0 || E > kMaxE || !valid_block_m(block_m))
     return MOE_ERR_SHAPE;
@@ -260,9 +284,9 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, i
   const int n = T * top_k;
   const int cap = (int)moe_align_capacity(T, top_k, E, block_m);
 
-  hipError_t e = moe_launch_route(logits, T, E, top_k, (int)kind, expert_bias, renormalize ? 1 : 0,
-                                  ids, tw, s);
-  if (e == hipSuccess) e = moe_launch_align(ids, n, E, block_m, cap, sorted, eids, npp, s);
+  hipError_t e = moe_launch_route_align(logits, T, E, top_k, (int)kind, expert_bias,
+                                        renormalize ? 1 : 0, ids, tw, block_m, cap, sorted, eids,
+                                        npp, s);
   if (e == hipSuccess)
     e = moe_launch_gemm((int)w13->fmt, epi, block_m, cap, x, top_k, n, hidden, n1, E, &W13, sorted, eids,
                         npp, nullptr, 0, alpha, beta, limit, actb, inter, s);

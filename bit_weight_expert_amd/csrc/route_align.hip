@@ -1,9 +1,7 @@
 // Top-k routing and the per-expert slot sort (moe_align) for gfx950.
 //
-// Routing: one wave64 per token.  Each lane holds up to 16 of the token's E
-// scores in registers; the k winners are found by k rounds of a wave-wide
-// argmax (descending score, ties to the lower expert id), so the selection is
-// a pure comparison of float32 scores, identical on every lane.
+// Routing: one wave64 per token, selection by pure comparison of float32
+// scores (descending, ties to the lower expert id), identical on every lane.
 //   softmax      topk(softmax(logits)) with optional renormalisation
 //                ("moe_wna16_marlin_gemm applies wrong per-row topk weights",
 //                repro, routing step).
@@ -11,6 +9,11 @@
 //                score = sigmoid + bias in float, weights = selected unbiased
 //                sigmoids renormalised; n_group = 1 makes the grouped top-k a
 //                plain top-k (Nemotron-3-Nano page, Analysis item 3).
+// For E <= 128 (one or two scores per lane) each score's rank is counted
+// directly against every other score, broadcast one lane at a time with
+// v_readlane: no cross-lane shuffles at all, and the rank is the output
+// position.  Larger E (up to 1024) keeps up to 16 scores per lane and finds
+// the k winners by k rounds of a wave-wide argmax.
 //
 // Align: one workgroup of 1024 threads.  Counts per expert with LDS atomics
 // (order-free), pads each count to block_m, and places every slot at
@@ -18,6 +21,9 @@
 // which makes the sort stable and the output unique.  The within-wave rank
 // comes from ballots over the bits of the expert id (lanes with an equal id
 // share every bit), the cross-wave part from a per-wave count table in LDS.
+//
+// For small batches moe_forward runs both in one workgroup (route_align_kernel):
+// the routed ids go through LDS straight into the sort, saving a launch.
 #include "common.h"
 
 namespace moe {
@@ -28,15 +34,100 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Score used for selection and the weight basis of expert e's logit l.
 template <int KIND>
-__global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits, int T, int E,
-                                                    int top_k, const float* __restrict__ ebias,
-                                                    int renorm, int32_t* __restrict__ ids,
-                                                    float* __restrict__ w) {
+__device__ __forceinline__ void route_score(float l, const float* ebias, int e, float& score,
+                                            float& base) {
+  if (KIND == 0) {
+    score = l;
+    base = l;
+  } else {
+    base = (float)(1.0 / (1.0 + exp(-(double)l)));
+    score = base + ebias[e];
+  }
+  if (score != score) score = -INFINITY;  // NaN never wins a comparison
+}
+
+// Route token t with the calling wave.  Writes ids/w[t*top_k + j] (and, if
+// lds_ids is not null, the ids to lds_ids[t*top_k + j]).
+template <int KIND>
+__device__ __forceinline__ void route_wave(const float* __restrict__ logits, int t, int E, int top_k,
+                                           const float* __restrict__ ebias, int renorm,
+                                           int32_t* __restrict__ ids, float* __restrict__ w,
+                                           int32_t* lds_ids) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // uniform per wave
   const float* row = logits + (size_t)t * E;
+  if (E <= 128) {
+    // up to two scores per lane: experts lane and lane + 64
+    float sc[2], bs[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int e = c * 64 + lane;
+      sc[c] = -INFINITY;
+      bs[c] = -INFINITY;
+      if (e < E) route_score<KIND>(row[e], ebias, e, sc[c], bs[c]);
+    }
+    // softmax denominator over all E in fp32 (fixed order: max, then the sum
+    // of exp over experts 0, 1, ..., E-1 accumulated lane by lane)
+    float denom = 1.f, lmax = -INFINITY;
+    if (KIND == 0) {
+      for (int o = 0; o < 64 && o < E; ++o) lmax = fmaxf(lmax, readlane_f(bs[0], o));
+      for (int o = 0; o + 64 < E; ++o) lmax = fmaxf(lmax, readlane_f(bs[1], o));
+      float ex0 = (lane < E) ? expf(bs[0] - lmax) : 0.f;
+      float ex1 = (64 + lane < E) ? expf(bs[1] - lmax) : 0.f;
+      float s = 0.f;
+      for (int o = 0; o < 64 && o < E; ++o) s += readlane_f(ex0, o);
+      for (int o = 0; o + 64 < E; ++o) s += readlane_f(ex1, o);
+      denom = s;
+    }
+    // rank of each of the lane's scores among all E
+    int rk[2] = {0, 0};
+    for (int o = 0; o < 64 && o < E; ++o) {
+      const float so = readlane_f(sc[0], o);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) rk[c] += better(so, o, sc[c], c * 64 + lane) ? 1 : 0;
+    }
+    for (int o = 0; o + 64 < E; ++o) {
+      const float so = readlane_f(sc[1], o);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) rk[c] += better(so, 64 + o, sc[c], c * 64 + lane) ? 1 : 0;
+    }
+    // weights of the selected experts, renormalised over the k of them
+    float p[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bool sel = (c * 64 + lane < E) && rk[c] < top_k;
+      p[c] = !sel ? 0.f : (KIND == 0) ? expf(bs[c] - lmax) / denom : bs[c];
+    }
+    float norm = 1.f;
+    if (renorm) {
+      // sum in output order (rank 0 .. k-1) so it does not depend on expert ids' lanes
+      float s = 0.f;
+      for (int r = 0; r < top_k; ++r) {
+        // the (unique) lane/slot holding rank r
+        const unsigned long long m0 = __ballot((lane < E) && rk[0] == r);
+        const unsigned long long m1 = __ballot((64 + lane < E) && rk[1] == r);
+        if (m0) s += readlane_f(p[0], __builtin_ctzll(m0));
+        else s += readlane_f(p[1], __builtin_ctzll(m1));
+      }
+      norm = s;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int e = c * 64 + lane;
+      if (e < E && rk[c] < top_k) {
+        const size_t f = (size_t)t * top_k + rk[c];
+        ids[f] = e;
+        w[f] = renorm ? p[c] / norm : p[c];
+        if (lds_ids != nullptr) lds_ids[f] = e;
+      }
+    }
+    return;
+  }
 
   float score[kRouteMaxPerLane];  // what selection compares
   float base[kRouteMaxPerLane];   // logit (softmax) or unbiased sigmoid
@@ -44,19 +135,12 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
 #pragma unroll
   for (int c = 0; c < kRouteMaxPerLane; ++c) {
     const int e = c * 64 + lane;
-    float v = -INFINITY, s = -INFINITY;
+    float s = -INFINITY, v = -INFINITY;
     if (e < E) {
-      const float l = row[e];
-      if (KIND == 0) {
-        v = l;
-        s = l;
-        lmax = fmaxf(lmax, l);
-      } else {
-        v = (float)(1.0 / (1.0 + exp(-(double)l)));
-        s = v + ebias[e];
-      }
+      route_score<KIND>(row[e], ebias, e, s, v);
+      if (KIND == 0) lmax = fmaxf(lmax, v);
     }
-    score[c] = (s != s) ? -INFINITY : s;  // NaN never wins a comparison
+    score[c] = s;
     base[c] = v;
   }
 
@@ -118,14 +202,36 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
     p = p / s;
   }
   if (lane < top_k) {
-    ids[(size_t)t * top_k + lane] = my_id;
-    w[(size_t)t * top_k + lane] = p;
+    const size_t f = (size_t)t * top_k + lane;
+    ids[f] = my_id;
+    w[f] = p;
+    if (lds_ids != nullptr) lds_ids[f] = my_id;
   }
+}
+
+template <int KIND>
+__global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits, int T, int E,
+                                                    int top_k, const float* __restrict__ ebias,
+                                                    int renorm, int32_t* __restrict__ ids,
+                                                    float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform per wave
+  route_wave<KIND>(logits, t, E, top_k, ebias, renorm, ids, w, nullptr);
 }
 
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / 64;
 constexpr int kAlignMaxE = 1024;
+
+// LDS of the sort.
+struct AlignLds {
+  int cnt[kAlignMaxE];
+  int off[kAlignMaxE];
+  int placed[kAlignMaxE];
+  int wave_cnt[kAlignWaves][kAlignMaxE];
+  int wave_tot[kAlignWaves];
+  int total;
+};
 
 // Exclusive prefix sum of one int per thread over the 1024-thread block.
 __device__ int block_exclusive_scan(int v, int* wave_tot) {
@@ -143,38 +249,34 @@ __device__ int block_exclusive_scan(int v, int* wave_tot) {
   return before + incl - v;
 }
 
-__global__ void __launch_bounds__(kAlignThreads) align_kernel(
-    const int32_t* __restrict__ topk_ids, int n_slots, int E, int block_m, int cap,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
-    int32_t* __restrict__ num_post_pad) {
-  __shared__ int cnt[kAlignMaxE];
-  __shared__ int off[kAlignMaxE];
-  __shared__ int placed[kAlignMaxE];
-  __shared__ int wave_cnt[kAlignWaves][kAlignMaxE];
-  __shared__ int wave_tot[kAlignWaves];
-  __shared__ int total_s;
+// The sort itself, for the whole 1024-thread workgroup; topk_ids may point to
+// global memory or to LDS.
+__device__ __forceinline__ void align_block(const int32_t* topk_ids, int n_slots, int E, int block_m,
+                                            int cap, int32_t* __restrict__ sorted_ids,
+                                            int32_t* __restrict__ expert_ids,
+                                            int32_t* __restrict__ num_post_pad, AlignLds& L) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
 
   for (int e = tid; e < E; e += kAlignThreads) {
-    cnt[e] = 0;
-    placed[e] = 0;
+    L.cnt[e] = 0;
+    L.placed[e] = 0;
   }
-  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) wave_cnt[i / E][i % E] = 0;
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) L.wave_cnt[i / E][i % E] = 0;
   __syncthreads();
   for (int f = tid; f < n_slots; f += kAlignThreads) {
     const int e = topk_ids[f];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    if (e >= 0 && e < E) atomicAdd(&L.cnt[e], 1);
   }
   __syncthreads();
 
   // padded segment offsets (E <= 1024: one expert per thread)
-  const int my_pad = (tid < E) ? (cnt[tid] + block_m - 1) / block_m * block_m : 0;
-  const int my_off = block_exclusive_scan(my_pad, wave_tot);
-  if (tid < E) off[tid] = my_off;
-  if (tid == E - 1) total_s = my_off + my_pad;
+  const int my_pad = (tid < E) ? (L.cnt[tid] + block_m - 1) / block_m * block_m : 0;
+  const int my_off = block_exclusive_scan(my_pad, L.wave_tot);
+  if (tid < E) L.off[tid] = my_off;
+  if (tid == E - 1) L.total = my_off + my_pad;
   __syncthreads();
-  const int total = total_s;
+  const int total = L.total;
   if (tid == 0) num_post_pad[0] = total;
 
   // expert of every block; -1 past the used length
@@ -185,7 +287,7 @@ __global__ void __launch_bounds__(kAlignThreads) align_kernel(
   for (int b = total / block_m + tid; b < nblocks; b += kAlignThreads) expert_ids[b] = -1;
   // sentinel in each expert's padding and past the used length
   if (tid < E) {
-    for (int i = my_off + cnt[tid]; i < my_off + my_pad; ++i) sorted_ids[i] = n_slots;
+    for (int i = my_off + L.cnt[tid]; i < my_off + my_pad; ++i) sorted_ids[i] = n_slots;
   }
   for (int i = total + tid; i < cap; i += kAlignThreads) sorted_ids[i] = n_slots;
 
@@ -203,20 +305,46 @@ __global__ void __launch_bounds__(kAlignThreads) align_kernel(
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int rank_in_wave = __popcll(same & lt);
     const bool leader = valid && ((same >> lane) >> 1) == 0ull;  // last lane of its group
-    if (leader) wave_cnt[wid][e] = __popcll(same);
+    if (leader) L.wave_cnt[wid][e] = __popcll(same);
     __syncthreads();
     if (valid) {
-      int before = placed[e];
-      for (int w2 = 0; w2 < wid; ++w2) before += wave_cnt[w2][e];
-      sorted_ids[off[e] + before + rank_in_wave] = f;
+      int before = L.placed[e];
+      for (int w2 = 0; w2 < wid; ++w2) before += L.wave_cnt[w2][e];
+      sorted_ids[L.off[e] + before + rank_in_wave] = f;
     }
     __syncthreads();
     if (leader) {
-      atomicAdd(&placed[e], __popcll(same));
-      wave_cnt[wid][e] = 0;
+      atomicAdd(&L.placed[e], __popcll(same));
+      L.wave_cnt[wid][e] = 0;
     }
     __syncthreads();
   }
+}
+
+__global__ void __launch_bounds__(kAlignThreads) align_kernel(
+    const int32_t* __restrict__ topk_ids, int n_slots, int E, int block_m, int cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ num_post_pad) {
+  __shared__ AlignLds L;
+  align_block(topk_ids, n_slots, E, block_m, cap, sorted_ids, expert_ids, num_post_pad, L);
+}
+
+// Routing and the sort in one workgroup (small batches): the 16 waves route
+// tokens wave, wave + 16, ...; the ids reach the sort through LDS.
+constexpr int kFusedMaxSlots = 4096;
+
+template <int KIND>
+__global__ void __launch_bounds__(kAlignThreads) route_align_kernel(
+    const float* __restrict__ logits, int T, int E, int top_k, const float* __restrict__ ebias,
+    int renorm, int32_t* __restrict__ ids, float* __restrict__ w, int block_m, int cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ num_post_pad) {
+  __shared__ AlignLds L;
+  __shared__ int32_t lds_ids[kFusedMaxSlots];
+  for (int t = threadIdx.x >> 6; t < T; t += kAlignWaves)
+    route_wave<KIND>(logits, t, E, top_k, ebias, renorm, ids, w, lds_ids);
+  __syncthreads();
+  align_block(lds_ids, T * top_k, E, block_m, cap, sorted_ids, expert_ids, num_post_pad, L);
 }
 
 }  // namespace moe
@@ -238,4 +366,26 @@ extern "C" hipError_t moe_launch_align(const int32_t* ids, int n_slots, int E, i
   moe::align_kernel<<<1, moe::kAlignThreads, 0, stream>>>(ids, n_slots, E, block_m, cap, sorted_ids,
                                                           expert_ids, npp);
   return hipGetLastError();
+}
+
+// Route + align in one launch when T*top_k fits the fused kernel and T is
+// small enough that one workgroup routes it quickly; otherwise the two
+// kernels.  Returns what the launches return.
+extern "C" hipError_t moe_launch_route_align(const float* logits, int T, int E, int top_k, int kind,
+                                             const float* ebias, int renorm, int32_t* ids, float* w,
+                                             int block_m, int cap, int32_t* sorted_ids,
+                                             int32_t* expert_ids, int32_t* npp,
+                                             hipStream_t stream) {
+  if (T <= 256 && T * top_k <= moe::kFusedMaxSlots) {
+    if (kind == 0)
+      moe::route_align_kernel<0><<<1, moe::kAlignThreads, 0, stream>>>(
+          logits, T, E, top_k, ebias, renorm, ids, w, block_m, cap, sorted_ids, expert_ids, npp);
+    else
+      moe::route_align_kernel<1><<<1, moe::kAlignThreads, 0, stream>>>(
+          logits, T, E, top_k, ebias, renorm, ids, w, block_m, cap, sorted_ids, expert_ids, npp);
+    return hipGetLastError();
+  }
+  hipError_t e = moe_launch_route(logits, T, E, top_k, kind, ebias, renorm, ids, w, stream);
+  if (e == hipSuccess) e = moe_launch_align(ids, T * top_k, E, block_m, cap, sorted_ids, expert_ids, npp, stream);
+  return e;
 }

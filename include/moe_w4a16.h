@@ -134,6 +134,15 @@ moe_status_t moe_align(const int32_t* topk_ids, int T, int top_k, int E, int blo
                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_post_pad,
                        moe_stream_t stream);
 
+/* moe_route followed by moe_align on its ids, with the same outputs as the
+ * two calls (all five written).  Small batches run both steps in one launch
+ * (the routed ids pass through on-chip memory); larger ones run the two
+ * kernels back to back.  Limits are those of moe_route and moe_align. */
+moe_status_t moe_route_align(const float* logits, int T, int E, int top_k, moe_route_t kind,
+                             const float* expert_bias, int renormalize, int block_m,
+                             int32_t* topk_ids, float* topk_w, int32_t* sorted_ids,
+                             int32_t* expert_ids, int32_t* num_post_pad, moe_stream_t stream);
+
 /* Grouped GEMM1 over aligned blocks.  For every real entry f of block b
  * (expert e = expert_ids[b]):
  *   h   = W13_e . x[f / top_k] (+ bias13_e)           fp32 accumulate

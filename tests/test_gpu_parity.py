@@ -55,6 +55,31 @@ def test_route_shapes(E, k, kind, renorm):
     np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=2e-6)
 
 
+@pytest.mark.parametrize("T,E,k,kind,B", [(1, 128, 8, "sigmoid_bias", 16), (8, 32, 4, "softmax", 16),
+                                           (64, 128, 6, "softmax", 32), (256, 64, 16, "sigmoid_bias", 64),
+                                           (37, 130, 5, "softmax", 16), (5, 1024, 16, "softmax", 16),
+                                           (300, 128, 4, "softmax", 64), (1, 3, 3, "softmax", 16)])
+def test_route_align_fused(T, E, k, kind, B):
+    """route + align in one call equals the oracle's route then align (one
+    launch up to 256 tokens, the two kernels above)."""
+    rng = np.random.default_rng(T * 7 + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[0, : min(E, 40)] = 0.5             # ties among the top scores
+    if T > 2 and kind == "sigmoid_bias":
+        logits[2, 1] = np.nan                 # a NaN score is never selected
+    bias = (rng.standard_normal(E) * 0.1).astype(np.float32) if kind == "sigmoid_bias" else None
+    ids_ref, w_ref = O.route(logits, k, kind, bias, True)
+    ref = O.align(ids_ref, E, B)
+    got = M.moe_route_align(torch.from_numpy(logits).cuda(), k, B, kind,
+                            None if bias is None else torch.from_numpy(bias).cuda(), True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got[0].cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(got[1].cpu().numpy(), w_ref, rtol=2e-6)
+    np.testing.assert_array_equal(got[2].cpu().numpy(), ref[0])
+    np.testing.assert_array_equal(got[3].cpu().numpy(), ref[1])
+    assert int(got[4].item()) == int(ref[2])
+
+
 # -------------------------------------------------------------------- align --
 
 @pytest.mark.parametrize("T,k,E,B", [(1, 4, 32, 16), (13, 2, 8, 16), (64, 4, 32, 64), (511, 6, 128, 32),
