@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_workspace_bytes.restype = sz
         L.moe_forward_block_m.argtypes = [i, i, i]
         L.moe_forward_block_m.restype = i
+        L.moe_set_decode_policy.argtypes = [i]
+        L.moe_set_decode_policy.restype = i
         L.moe_status_str.argtypes = [i]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_route.argtypes = [vp, i, i, i, i, vp, i, vp, vp, vp]
@@ -141,6 +143,13 @@ class QuantWeights:
     @property
     def E(self) -> int:
         return self.qweight.shape[0]
+
+
+def moe_set_decode_policy(policy: str) -> str:
+    """'auto', 'splitk' or 'wide' kernel for 16/32-row blocks; returns the previous policy."""
+    names = ["auto", "splitk", "wide"]
+    old = lib().moe_set_decode_policy(names.index(policy))
+    return names[old]
 
 
 def moe_align_capacity(T: int, top_k: int, E: int, block_m: int) -> int:

@@ -6,14 +6,19 @@
 // in the NVFP4 repro); its A rows are x[sorted_id / top_k] for GEMM1 and the
 // intermediate row of the slot itself for GEMM2 (the top_k = 1 view).
 //
-// Two kernels share the weight decoders and the routing-weight epilogue rule:
+// Three kernels share the weight decoders and the routing-weight epilogue rule:
 //   prefill  many rows per expert (blocks of 64/128 slots).  Workgroup = BM
 //            rows x 256 weight rows; four waves split the weight rows, so
 //            every weight is dequantised once per workgroup.  A rows and the
 //            4-bit codes stream through a 4-deep LDS ring filled by gfx950
 //            LDS-DMA, the tile's scales for the whole K sit in LDS, MFMA is
 //            v_mfma_f32_32x32x16_bf16 (details at the kernel).
-//   decode   a few rows per expert: the weight stream is the whole cost.
+//   wide     a few to a few dozen rows per expert (blocks of 16/32 slots)
+//            when (block, 128-column tile) pairs fill the chip: four waves
+//            of 32 columns over the whole K share each A chunk through LDS,
+//            the codes stream per wave through a register ring (details at
+//            the kernel).
+//   decode   a few rows per expert and too few tiles for the wide kernel:
 //            Workgroup = 16*MI rows x 16*NF columns with v_mfma_f32_16x16x32:
 //            lane l works on column l%16 of a 16-column fragment and on
 //            k-group g = l/16; each wave owns one or more 256-wide K chunks
@@ -907,6 +912,28 @@ __device__ __forceinline__ void dc_stage_scales(uint8_t* sc, const WeightArgs& W
   }
 }
 
+// NVFP4/MXFP4: the scale tile (contiguous in memory) copied by LDS-DMA, so
+// that its loads go out ahead of the weight stream and need no registers;
+// the kernel waits for them with wait_vmcnt, counting the loads it issued
+// after them.
+template <int FMT>
+__device__ __forceinline__ void dc_dma_scales(uint8_t* sc, const WeightArgs& W, int e, int n0,
+                                              int N, int K, int rows, int wave, int nw, int lane) {
+  const int per_row = (FMT == FMT_NVFP4) ? K / 16 : K / 32;
+  const uint8_t* src = W.scales + ((size_t)e * N + n0) * per_row;
+  const int bytes = rows * per_row;  // a multiple of 16
+  const uint32_t base = lds_addr(sc);
+  for (int q = __builtin_amdgcn_readfirstlane(wave); q * 1024 < bytes; q += nw) {
+    const int o = q * 1024 + 16 * lane;
+    if (o < bytes) dma16(src + o, base + q * 1024);
+  }
+}
+
+// LDS bytes before the partial-sum area (the scale tile, 16-byte aligned end).
+__host__ __device__ inline int dc_scale_region(int fmt, int K, int group, int R) {
+  return (dc_scale_bytes(fmt, K, group, R) + 15) & ~15;
+}
+
 // Raw scale words of one fragment for the lane's k range [kl, kl + C/4), from
 // the LDS tile (r = the fragment row's index inside the tile).
 template <int FMT, int C, int R>
@@ -951,6 +978,13 @@ __device__ __forceinline__ void dc_load_b(DcB<FMT, C, NF>& d, const WeightArgs& 
 #pragma unroll
   for (int j = 0; j < NF; ++j) load_codes<FMT, C>(d.b[j], W, e, nrow[j], ga.N, ga.K, k0 + g * (C / 4));
 }
+// The same with the lane's k offset given.
+template <int FMT, int C, int NF>
+__device__ __forceinline__ void dc_load_b(DcB<FMT, C, NF>& d, const WeightArgs& W, const GemmArgs& ga,
+                                          const int (&nrow)[NF], int e, int kl) {
+#pragma unroll
+  for (int j = 0; j < NF; ++j) load_codes<FMT, C>(d.b[j], W, e, nrow[j], ga.N, ga.K, kl);
+}
 
 // Padding slots read A row 0 (a_row), so every lane loads and no branch is
 // needed; their products only reach accumulator rows the epilogue skips.
@@ -964,7 +998,7 @@ __device__ __forceinline__ void dc_load_a(DcA<C, MI>& d, const uint16_t* const (
       d.a[i][s] = *reinterpret_cast<const uint4*>(arow[i] + k0 + g * (C / 4) + 8 * s);
 }
 
-template <int FMT, int C, int MI, int NF>
+template <int FMT, int C, int MI, int NF, int R = 16 * NF>
 __device__ __forceinline__ void dc_compute(f32x4 (&acc)[MI][NF], const DcB<FMT, C, NF>& db,
                                            const DcA<C, MI>& da, const uint8_t* sc,
                                            const int (&rl)[NF], int K, int group, int g, int k0) {
@@ -972,7 +1006,7 @@ __device__ __forceinline__ void dc_compute(f32x4 (&acc)[MI][NF], const DcB<FMT, 
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     b[j] = db.b[j];
-    dc_fill_scales<FMT, C, 16 * NF>(b[j], sc, rl[j], K, group, k0 + g * (C / 4));
+    dc_fill_scales<FMT, C, R>(b[j], sc, rl[j], K, group, k0 + g * (C / 4));
   }
 #pragma unroll
   for (int s = 0; s < C / 32; ++s) {
@@ -990,7 +1024,7 @@ __device__ __forceinline__ void dc_compute(f32x4 (&acc)[MI][NF], const DcB<FMT, 
 }
 
 // One unpipelined chunk of width C (the K tail).
-template <int FMT, int C, int MI, int NF>
+template <int FMT, int C, int MI, int NF, int R = 16 * NF>
 __device__ __forceinline__ void dc_chunk(f32x4 (&acc)[MI][NF], const WeightArgs& W,
                                          const GemmArgs& ga, const uint16_t* const (&arow)[MI],
                                          const int (&nrow)[NF], const int (&rl)[NF],
@@ -999,7 +1033,7 @@ __device__ __forceinline__ void dc_chunk(f32x4 (&acc)[MI][NF], const WeightArgs&
   DcA<C, MI> da;
   dc_load_b(db, W, ga, nrow, e, k0, g);
   dc_load_a(da, arow, k0, g);
-  dc_compute(acc, db, da, sc, rl, ga.K, W.group, g, k0);
+  dc_compute<FMT, C, MI, NF, R>(acc, db, da, sc, rl, ga.K, W.group, g, k0);
 }
 
 template <int FMT, int EPI, int MI, int NF>
@@ -1036,44 +1070,76 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
     for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // this wave's run of full chunks [c0, c0 + n).  Weight codes run kDcDepth
-  // chunks ahead, A fragments two; the first ones are requested before the
-  // scale tile, whose copy then waits for them too.
+  // chunks ahead; A fragments as far for one 16-row block (they are issued
+  // with the codes of the same chunk, so waiting for one chunk's A never
+  // waits for younger codes), two for two blocks (registers).  The scale
+  // tile's loads go out first (NVFP4/MXFP4).
+  constexpr int kADepth = (MI == 1) ? 4 : 2;
   const int nfull = K / kDcBK;
   const int c0 = nfull * wave / nw, n = nfull * (wave + 1) / nw - c0;
   const int last = max(c0 + n - 1, 0);
+  const int srows = min(16 * NF, ga.N - n0);
   DcB<FMT, kDcBK, NF> b0, b1, b2, b3;
-  DcA<kDcBK, MI> a0, a1;
-  if (n > 0) {
+  DcA<kDcBK, MI> a0, a1, a2, a3;
+  if (n > 0 && FMT != FMT_GPTQ) {
+    // (n is the same on all lanes of a wave, and every wave reaches exactly
+    // one of the two barriers)
+    dc_dma_scales<FMT>(sc, W, e, n0, ga.N, K, srows, wave, nw, lane);
     dc_load_b(b0, W, ga, nrow, e, c0 * kDcBK, g);
     dc_load_a(a0, arow, c0 * kDcBK, g);
     dc_load_b(b1, W, ga, nrow, e, min(c0 + 1, last) * kDcBK, g);
     dc_load_a(a1, arow, min(c0 + 1, last) * kDcBK, g);
     dc_load_b(b2, W, ga, nrow, e, min(c0 + 2, last) * kDcBK, g);
+    if (kADepth == 4) dc_load_a(a2, arow, min(c0 + 2, last) * kDcBK, g);
     dc_load_b(b3, W, ga, nrow, e, min(c0 + 3, last) * kDcBK, g);
+    if (kADepth == 4) dc_load_a(a3, arow, min(c0 + 3, last) * kDcBK, g);
+    // the scale DMAs are older than these prologue loads: wait for them only
+    constexpr int kPro = kDcDepth * NF * (kDcBK / 128) + kADepth * MI * (kDcBK / 32);
+    wait_vmcnt<kPro>();
+    pf_barrier();
+  } else if (n > 0) {
+    dc_load_b(b0, W, ga, nrow, e, c0 * kDcBK, g);
+    dc_load_a(a0, arow, c0 * kDcBK, g);
+    dc_load_b(b1, W, ga, nrow, e, min(c0 + 1, last) * kDcBK, g);
+    dc_load_a(a1, arow, min(c0 + 1, last) * kDcBK, g);
+    dc_load_b(b2, W, ga, nrow, e, min(c0 + 2, last) * kDcBK, g);
+    if (kADepth == 4) dc_load_a(a2, arow, min(c0 + 2, last) * kDcBK, g);
+    dc_load_b(b3, W, ga, nrow, e, min(c0 + 3, last) * kDcBK, g);
+    if (kADepth == 4) dc_load_a(a3, arow, min(c0 + 3, last) * kDcBK, g);
+    dc_stage_scales<FMT, 16 * NF>(sc, W, e, n0, ga.N, K, tid, 64 * nw);
+    __syncthreads();
+  } else {
+    dc_stage_scales<FMT, 16 * NF>(sc, W, e, n0, ga.N, K, tid, 64 * nw);
+    __syncthreads();
   }
-  dc_stage_scales<FMT, 16 * NF>(sc, W, e, n0, ga.N, K, tid, 64 * nw);
-  __syncthreads();
   const int group = W.group;
-  for (int i = 0; i < n; i += kDcDepth) {
-    // chunk c0 + i + d sits in b<d> and a<d % 2>; once multiplied its slots
-    // take chunk + 4 (codes) and chunk + 2 (A); past the run the last chunk
-    // is fetched again and never used
+  // groups of four chunks in straight-line code (no exit between the
+  // phases, so every prefetch is issued where it is written); chunk
+  // c0 + i + d sits in b<d> and a<d % kADepth>; once multiplied its slots
+  // take chunk + 4 (codes) and chunk + kADepth (A); past the run the last
+  // chunk is fetched again and never used
+  const int n4 = n & ~3;
+  for (int i = 0; i < n4; i += kDcDepth) {
 #define MOE_DC_PHASE(D, BS, AS)                                                                    \
     {                                                                                              \
-      const int kc = min(c0 + i + D, last);                                                        \
-      dc_compute(acc, BS, AS, sc, rl, K, group, g, kc * kDcBK);                                    \
+      dc_compute(acc, BS, AS, sc, rl, K, group, g, (c0 + i + D) * kDcBK);                          \
       dc_load_b(BS, W, ga, nrow, e, min(c0 + i + D + 4, last) * kDcBK, g);                         \
-      dc_load_a(AS, arow, min(c0 + i + D + 2, last) * kDcBK, g);                                   \
+      dc_load_a(AS, arow, min(c0 + i + D + kADepth, last) * kDcBK, g);                             \
     }
     MOE_DC_PHASE(0, b0, a0)
-    if (i + 1 >= n) break;
     MOE_DC_PHASE(1, b1, a1)
-    if (i + 2 >= n) break;
-    MOE_DC_PHASE(2, b2, a0)
-    if (i + 3 >= n) break;
-    MOE_DC_PHASE(3, b3, a1)
+    MOE_DC_PHASE(2, b2, (kADepth == 4 ? a2 : a0))
+    MOE_DC_PHASE(3, b3, (kADepth == 4 ? a3 : a1))
 #undef MOE_DC_PHASE
   }
+  // the run's last n % 4 chunks are already in the ring
+  const int rem = n - n4;
+  if (rem > 0) {
+    dc_compute(acc, b0, a0, sc, rl, K, group, g, (c0 + n4) * kDcBK);
+    if (kADepth == 2 && rem > 2) dc_load_a(a0, arow, (c0 + n4 + 2) * kDcBK, g);
+  }
+  if (rem > 1) dc_compute(acc, b1, a1, sc, rl, K, group, g, (c0 + n4 + 1) * kDcBK);
+  if (rem > 2) dc_compute(acc, b2, (kADepth == 4 ? a2 : a0), sc, rl, K, group, g, (c0 + n4 + 2) * kDcBK);
   // K tail (K % 128: a 64- and/or a 32-wide piece) on the last wave
   if (wave == nw - 1) {
     int k0 = nfull * kDcBK;
@@ -1091,7 +1157,7 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
     return;
   }
   // add the waves' partial sums in wave order
-  f32x4* red = reinterpret_cast<f32x4*>(dc_smem + ((dc_scale_bytes(FMT, K, group, 16 * NF) + 15) & ~15));
+  f32x4* red = reinterpret_cast<f32x4*>(dc_smem + dc_scale_region(FMT, K, group, 16 * NF));
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -1121,6 +1187,303 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
     // the fragment group as its own "wave" starting at weight row n0 + 16*GF*grp
     epilogue<EPI, FMT, MI, GF>(fin, a, W, e, n0 + 16 * GF * grp, lane);
   }
+}
+
+// --------------------------------------------------------------------------
+// wide decode kernel
+// --------------------------------------------------------------------------
+//
+// For a few to a few dozen rows per expert with enough (expert, column tile)
+// pairs to fill the chip.  Workgroup = 16*MI rows x 128 weight rows over the
+// whole K: four waves of 32 weight rows each, so every A chunk (16*MI rows x
+// 128 k, bf16) is fetched once per workgroup instead of once per 32 columns.
+// Each thread loads 16 bytes of it per 16 rows into a register ring as deep
+// as the codes ring, writes it to one of two LDS stages a chunk ahead of
+// use, and all four waves read their MFMA fragments from there (16-byte
+// slots of a row XOR-swizzled by the row, so a fragment read is free of bank
+// conflicts).  One barrier per chunk.  The codes stream per wave into a
+// 4-deep register ring; the tile's scales sit in LDS (NVFP4/MXFP4 copied by
+// LDS-DMA ahead of the stream).  The compiler counts every load but the
+// scale DMA, which the kernel waits for itself.
+
+constexpr int kWdCols = 128;  // weight rows per workgroup (4 waves x 32)
+constexpr int kWdBK = 128;    // K chunk
+constexpr int kWdDepth = 4;   // chunks in flight per wave
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Everything the epilogue reads besides the accumulators, loaded at the start
+// so that its latency hides behind the weight stream: the slot ids of the
+// lane's rows (i*16 + 4g + r), their routing weights (GEMM2), the lane's
+// bias values and the NVFP4 global scale.
+template <int MI, int NF>
+struct EpiPre {
+  int sid[MI][4];
+  float tw[MI][4];
+  float bias[NF];
+  float gsc;
+};
+
+// Every load is unconditional: a load inside a branch makes the compiler
+// wait for it at the branch's end.  Without a bias (or routing weights) the
+// load reads some other valid global word and the epilogue ignores it; rows
+// with the sentinel slot id read some valid routing weight, also unused.
+// (Both candidate bases are kernel-argument pointers, so the load stays a
+// global one: a flat load would make every later wait a full drain.)
+
+// Part 1: slot ids, bias, global scale.
+template <int EPI, int FMT, int MI, int NF>
+__device__ __forceinline__ void epi_prefetch_ids(EpiPre<MI, NF>& p, const EpiArgs& a,
+                                                 const WeightArgs& W, int e, int n0, int lane) {
+  const int c16 = lane & 15, g = lane >> 4;
+  p.gsc = (FMT == FMT_NVFP4) ? W.global_scale[e] : 1.f;
+  const bool has_bias = W.bias != nullptr;
+  const uint16_t* bbase = has_bias ? W.bias : reinterpret_cast<const uint16_t*>(W.qweight);
+  const int bmul = has_bias ? 1 : 0;
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int row = frag_on<EPI>(n0, j, a.N) ? frag_row<EPI>(n0, j, c16) : n0;
+    p.bias[j] = bf16_bits_to_f32(bbase[((size_t)e * a.N + row) * bmul]);
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p.sid[i][r] = a.sorted_ids[a.row0 + i * 16 + 4 * g + r];
+}
+
+// Part 2: routing weights (GEMM2), once the slot ids are in.
+template <int EPI, int MI, int NF>
+__device__ __forceinline__ void epi_prefetch_tw(EpiPre<MI, NF>& p, const EpiArgs& a) {
+  const bool use = EPI == EPI_DOWN && a.mul_tw;
+  const float* tbase = use ? a.topk_w : reinterpret_cast<const float*>(a.sorted_ids);
+  const int tmul = use ? 1 : 0;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      p.tw[i][r] = (EPI == EPI_DOWN) ? tbase[min(p.sid[i][r], a.n_slots - 1) * tmul] : 1.f;
+}
+
+// The epilogue of the 16x16 fragments with prefetched metadata (same
+// arithmetic as epilogue()).
+template <int EPI, int MI, int NF>
+__device__ __forceinline__ void epilogue_pre(const f32x4 (&acc)[MI][NF], const EpiPre<MI, NF>& p,
+                                             const EpiArgs& a, const WeightArgs& W, int n0,
+                                             int lane) {
+  const int c16 = lane & 15;
+  float bias[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) bias[j] = (W.bias != nullptr) ? p.bias[j] : 0.f;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int sid = p.sid[i][r];
+      if (sid >= a.n_slots) continue;
+      uint16_t* orow = a.out + (size_t)sid * a.out_ld;
+      if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int q = 0; q < NF / 2; ++q) {
+          if (!frag_on<EPI>(n0, 2 * q, a.N)) continue;
+          float gate = acc[i][2 * q][r] * p.gsc + bias[2 * q];
+          float up = acc[i][2 * q + 1][r] * p.gsc + bias[2 * q + 1];
+          gate = fminf(gate, a.limit);
+          up = fminf(fmaxf(up, -a.limit), a.limit);
+          const float v = gate * sigmoid_fast(a.alpha * gate) * (up + a.beta);
+          orow[n0 / 2 + 16 * q + c16] = f32_to_bf16_bits(v);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          if (!frag_on<EPI>(n0, j, a.N)) continue;
+          float v = acc[i][j][r] * p.gsc + bias[j];
+          if (EPI == EPI_RELU2) {
+            v = fmaxf(v, 0.f);
+            v = v * v;
+          } else if (EPI == EPI_DOWN && a.mul_tw) {
+            v = v * p.tw[i][r];
+          }
+          orow[n0 + 16 * j + c16] = f32_to_bf16_bits(v);
+        }
+      }
+    }
+  }
+}
+
+// A pieces of one chunk held by one thread: 16 bytes per 16 rows.  Piece q of
+// thread t is row 16q + t/16, 16-byte slot t%16 of the chunk.
+template <int MI>
+struct WdA {
+  u32x4 v[MI];  // native vectors (HIP's uint4 struct copies would keep the ring in memory)
+};
+
+// The last chunk may pass K (K % 128 != 0): its A pieces past K are stored as
+// zeros and read from a clamped address, so the weights the same lanes load
+// there (also from clamped addresses: real, finite values) add nothing.
+template <int MI>
+__device__ __forceinline__ void wd_load_a(WdA<MI>& r, const uint16_t* const (&prow)[MI], int k0,
+                                          int slot, int K) {
+#pragma unroll
+  for (int q = 0; q < MI; ++q)
+    r.v[q] = *reinterpret_cast<const u32x4*>(prow[q] + min(k0 + 8 * slot, K - 8));
+}
+
+// LDS stage: [16*MI rows][16 slots of 16 bytes], the slot XOR-swizzled by the
+// row so that the 16 rows of a fragment read hit distinct banks.
+template <int MI>
+__device__ __forceinline__ void wd_store_a(uint8_t* stage, const WdA<MI>& r, int tid, int k0, int K) {
+  // (k0 passes through an empty asm so that the select below, which needs
+  // the loaded value, cannot be hoisted ahead of the loads issued before)
+  asm volatile("" : "+v"(k0));
+  const bool live = k0 + 8 * (tid & 15) < K;
+#pragma unroll
+  for (int q = 0; q < MI; ++q) {
+    const int row = 16 * q + (tid >> 4), slot = tid & 15;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(stage + row * 256 + ((slot ^ (row & 15)) << 4)) = live ? r.v[q] : z;
+  }
+}
+
+// Multiply one chunk: the wave's codes of NF fragments (dequantised with the
+// scales of the LDS tile) by the A fragments read step by step from the stage
+// (row i*16 + c16, k = 32g + 8s .. +8).  kl = the lane's clamped k offset.
+template <int FMT, int MI, int NF>
+__device__ __forceinline__ void wd_compute(f32x4 (&acc)[MI][NF], const DcB<FMT, kWdBK, NF>& db,
+                                           const uint8_t* stage, const uint8_t* sc,
+                                           const int (&rl)[NF], int K, int group, int g, int c16,
+                                           int kl) {
+  BChunk<FMT, kWdBK> b[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    b[j] = db.b[j];
+    dc_fill_scales<FMT, kWdBK, kWdCols>(b[j], sc, rl[j], K, group, kl);
+  }
+#pragma unroll
+  for (int s = 0; s < kWdBK / 32; ++s) {
+    bf16x8 bf[NF];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) bf[j] = deq_step<FMT, kWdBK>(b[j], s);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int row = i * 16 + c16, slot = 4 * g + s;
+      const bf16x8 af =
+          as_bf16x8(*reinterpret_cast<const uint4*>(stage + row * 256 + ((slot ^ c16) << 4)));
+#pragma unroll
+      for (int j = 0; j < NF; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+template <int FMT, int EPI, int MI>
+__global__ void __launch_bounds__(256, (MI == 1 ? 4 : 3)) gemm_wide_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
+  constexpr int BM = 16 * MI, NF = 2, C = kWdBK, D = kWdDepth;
+  constexpr int kStage = BM * C * 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t wd_smem[];  // scale tile, 2 A stages
+
+  const int mb = blockIdx.x / ga.n_ntiles, nt = blockIdx.x % ga.n_ntiles;
+  const int npp = ga.num_post_pad[0];
+  const int e = ga.expert_ids[mb * BM / ga.block_m];  // BM divides block_m
+  if (mb * BM >= npp || e < 0 || e >= ga.E) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int n0 = nt * kWdCols, n0w = n0 + 32 * wave;
+  const int K = ga.K, group = W.group;
+  uint8_t* const sc = wd_smem;
+  uint8_t* const stages = wd_smem + dc_scale_region(FMT, K, group, kWdCols);
+
+  // chunks of 128 (the last may be partial); a lane's 32-wide k range is
+  // entirely inside K or entirely past it (K % 32 == 0); past it the lane
+  // loads codes and scales of its last valid range (clamped) and the A it
+  // meets there is zero
+  const int n = (K + C - 1) / C;
+  const int last = n - 1;
+  const int kmax = K - C / 4;  // largest lane offset
+  const int srows = min(kWdCols, ga.N - n0);
+
+  // prologue, in issue order: the scale DMA (it needs only the expert), the
+  // slot ids and the epilogue's metadata, the codes of chunks 0 .. D-1, then
+  // (once the slot ids are in -- which, loads retiring in order, also means
+  // the DMA has landed) the A pieces of chunks 0 .. D-1.
+  if (FMT != FMT_GPTQ) dc_dma_scales<FMT>(sc, W, e, n0, ga.N, K, srows, wave, 4, lane);
+  int psid[MI];  // slots of the A rows this thread copies
+#pragma unroll
+  for (int q = 0; q < MI; ++q) psid[q] = ga.sorted_ids[mb * BM + 16 * q + (tid >> 4)];
+  const int slot = tid & 15;
+  int nrow[NF], rl[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    nrow[j] = frag_on<EPI>(n0w, j, ga.N) ? frag_row<EPI>(n0w, j, c16) : n0;
+    rl[j] = nrow[j] - n0;
+  }
+  EpiArgs ep = ea;
+  ep.row0 = mb * BM;
+  EpiPre<MI, NF> pre;
+  epi_prefetch_ids<EPI, FMT, MI, NF>(pre, ep, W, e, n0w, lane);
+  f32x4 acc[MI][NF];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  DcB<FMT, C, NF> b[D];
+  WdA<MI> r[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    dc_load_b(b[d], W, ga, nrow, e, min(min(d, last) * C + g * (C / 4), kmax));
+  const uint16_t* prow[MI];
+#pragma unroll
+  for (int q = 0; q < MI; ++q) prow[q] = a_row(ga, psid[q]);
+  // the slot ids are waited for here, before any A load is issued
+#pragma unroll
+  for (int q = 0; q < MI; ++q) asm volatile("" : : "v"(prow[q]) : "memory");
+  epi_prefetch_tw<EPI, MI, NF>(pre, ep);
+#pragma unroll
+  for (int d = 0; d < D; ++d) wd_load_a(r[d], prow, min(d, last) * C, slot, K);
+  if (FMT == FMT_GPTQ) dc_stage_scales<FMT, kWdCols>(sc, W, e, n0, ga.N, K, tid, 256);
+  wd_store_a(stages, r[0], tid, 0, K);
+  pf_barrier();
+
+  // phase c (ring slot d = c % D): multiply chunk c (codes in b[d], A in
+  // stage c % 2); refill the slot with chunk c + D; then move chunk c + 1's
+  // A from its ring slot into the other stage (read by every wave in phase
+  // c - 1, which the previous barrier closed) and barrier.  Past the end the
+  // last chunk is fetched again and never used.  The first group of D
+  // phases is written out before the loop: the loads in flight when it
+  // starts differ from those at the loop's back edge, and a shared loop
+  // entry would make the compiler's waits drain the ring every iteration.
+#define MOE_WD_PHASE(c, d)                                                                         \
+  {                                                                                                \
+    wd_compute<FMT, MI, NF>(acc, b[d], stages + ((c) & 1) * kStage, sc, rl, K, group, g, c16,      \
+                            min((c) * C + g * (C / 4), kmax));                                     \
+    dc_load_b(b[d], W, ga, nrow, e, min(min((c) + D, last) * C + g * (C / 4), kmax));              \
+    wd_load_a(r[d], prow, min((c) + D, last) * C, slot, K);                                        \
+    asm volatile("" ::: "memory"); /* the loads above go out before the store waits */             \
+    wd_store_a(stages + (((c) + 1) & 1) * kStage, r[((d) + 1) % D], tid, ((c) + 1) * C, K);        \
+    pf_barrier();                                                                                  \
+  }
+  const int nd = n - n % D;
+  if (nd > 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) MOE_WD_PHASE(d, d)
+  }
+  for (int i = D; i < nd; i += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) MOE_WD_PHASE(i + d, d)
+  }
+#undef MOE_WD_PHASE
+  // the last n % D chunks are already in the rings
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) {
+    if (nd + d < n) {  // the same for the whole workgroup
+      const int c = nd + d;
+      wd_compute<FMT, MI, NF>(acc, b[d], stages + (c & 1) * kStage, sc, rl, K, group, g, c16,
+                              min(c * C + g * (C / 4), kmax));
+      wd_store_a(stages + ((c + 1) & 1) * kStage, r[(d + 1) % D], tid, (c + 1) * C, K);
+      pf_barrier();
+    }
+  }
+  epilogue_pre<EPI, MI, NF>(acc, pre, ep, W, n0w, lane);
 }
 
 // --------------------------------------------------------------------------
@@ -1168,15 +1531,35 @@ static void launch_decode_nf(GemmArgs ga, const WeightArgs& W, const EpiArgs& ea
                              hipStream_t st) {
   ga.n_ntiles = (ga.N + 16 * NF - 1) / (16 * NF);
   const int nw = units >= 4096 ? 1 : units >= 2048 ? 2 : 4;
-  const size_t lds = (size_t)((dc_scale_bytes(FMT, ga.K, W.group, 16 * NF) + 15) & ~15) +
+  const size_t lds = (size_t)dc_scale_region(FMT, ga.K, W.group, 16 * NF) +
                      (nw > 1 ? (size_t)nw * MI * NF * 64 * sizeof(f32x4) : 0);
   gemm_decode_kernel<FMT, EPI, MI, NF>
       <<<dim3(ga.n_mblocks * ga.n_ntiles), dim3(64 * nw), lds, st>>>(ga, W, ea);
 }
 
+// LDS of the wide kernel: the 128-row scale tile and two A stages.
+static inline size_t wide_lds(int fmt, int K, int group, int MI) {
+  return (size_t)dc_scale_region(fmt, K, group, kWdCols) + 2 * (size_t)(16 * MI) * kWdBK * 2;
+}
+constexpr size_t kWdMaxLds = 64 * 1024;
+// Wide kernel when the (expert block, 128-column tile) pairs alone give the
+// chip enough workgroups; otherwise the split-K kernel.  The process-wide
+// policy can force either (0 automatic, 1 split-K, 2 wide where its LDS fits).
+constexpr long kWdMinTiles = 640;
+static int g_decode_policy = 0;
+
 template <int FMT, int EPI, int MI>
 static void launch_decode(GemmArgs ga, const WeightArgs& W, const EpiArgs& ea, int blocks_est,
                           hipStream_t st) {
+  const long wide_tiles = (long)blocks_est * ((ga.N + kWdCols - 1) / kWdCols);
+  const size_t lds = wide_lds(FMT, ga.K, W.group, MI);
+  const bool want_wide = g_decode_policy == 2 || (g_decode_policy == 0 && wide_tiles >= kWdMinTiles);
+  if (want_wide && lds <= kWdMaxLds) {
+    ga.n_ntiles = (ga.N + kWdCols - 1) / kWdCols;
+    gemm_wide_kernel<FMT, EPI, MI>
+        <<<dim3(ga.n_mblocks * ga.n_ntiles), dim3(256), lds, st>>>(ga, W, ea);
+    return;
+  }
   launch_decode_nf<FMT, EPI, MI, 2>(ga, W, ea, (long)blocks_est * ((ga.N + 31) / 32), st);
 }
 
@@ -1244,6 +1627,13 @@ extern "C" hipError_t moe_launch_gemm(int fmt, int epi, int block_m, int cap, co
     case moe::FMT_MXFP4: return moe::launch_fmt<moe::FMT_MXFP4>(epi, block_m, cap, ga, *W, ea, st);
     default: return moe::launch_fmt<moe::FMT_GPTQ>(epi, block_m, cap, ga, *W, ea, st);
   }
+}
+
+extern "C" int moe_set_decode_policy(int policy) {
+  if (policy < 0 || policy > 2) return -1;
+  const int old = moe::g_decode_policy;
+  moe::g_decode_policy = policy;
+  return old;
 }
 
 extern "C" hipError_t moe_launch_sum(const uint16_t* y, const int32_t* ids, int T, int top_k, int H,

@@ -199,6 +199,16 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, i
                          int mul_topk_weights, void* workspace, size_t workspace_bytes,
                          uint16_t* out, moe_stream_t stream);
 
+/* Which kernel the grouped GEMMs use for blocks of 16 or 32 rows (few tokens
+ * per expert): 0 = automatic (the library's choice from the launch size),
+ * 1 = split-K kernel, 2 = wide kernel (128 weight rows per workgroup, A
+ * shared through LDS; falls back to split-K when its scale tile does not fit).
+ * Process-wide, for tuning and testing; results are the same to rounding of
+ * the fp32 accumulation order.  Returns the previous policy, or -1 for an
+ * invalid value (the policy is then unchanged).  Not synchronised with calls
+ * running on other threads. */
+int moe_set_decode_policy(int policy);
+
 /* Static description of a status code. */
 const char* moe_status_str(moe_status_t s);
 

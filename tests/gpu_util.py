@@ -1,4 +1,6 @@
 """Helpers for the GPU tests: upload synthetic layers and compare with the oracle."""
+import contextlib
+
 import numpy as np
 import torch
 
@@ -50,3 +52,13 @@ def assert_rows_close(got, ref, rows=None, tol=TOL, what=""):
     assert rel.size == 0 or rel.max() <= tol, (
         f"{what}: max per-row rel err {rel.max():.3e} at row {worst} (tol {tol})")
     return float(rel.max()) if rel.size else 0.0
+
+
+@contextlib.contextmanager
+def decode_policy(policy):
+    """Run the body with the library's kernel choice for 16/32-row blocks forced."""
+    old = M.moe_set_decode_policy(policy)
+    try:
+        yield
+    finally:
+        M.moe_set_decode_policy(old)

@@ -15,8 +15,12 @@ from oracle import moe as O
 pytestmark = pytest.mark.gpu
 
 M = pytest.importorskip("bit_weight_expert_amd")
-from gpu_util import (TOL, assert_rows_close, dev_bf16, gpu_forward, host_bf16,  # noqa: E402
-                      upload, upload_weights)
+from gpu_util import (TOL, assert_rows_close, decode_policy, dev_bf16, gpu_forward,  # noqa: E402
+                      host_bf16, upload, upload_weights)
+
+# "auto" takes the split-K kernel at these small sizes; "wide" forces the
+# 128-column kernel (both serve 16- and 32-row blocks).
+POLICIES = ["auto", "wide"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -119,22 +123,24 @@ def _small(fmt, act="swigluoai", E=4, k=2, H=320, I=192, T=13, seed=21, **kw):
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "gptq"])
 @pytest.mark.parametrize("act", ["none", "swigluoai", "relu2"])
-@pytest.mark.parametrize("B", [16, 64])
-def test_gemm1_parity(fmt, act, B):
+@pytest.mark.parametrize("B,policy", [(16, "auto"), (16, "wide"), (32, "wide"), (64, "auto")])
+def test_gemm1_parity(fmt, act, B, policy):
     L = _small(fmt, "relu2" if act == "relu2" else "swigluoai", x_std=12.0)
     D = upload(L)
     ids, w = O.route(L)
     si, ei, npp = O.align(ids, L.E, B)
     ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, act, L.alpha, L.beta, L.limit, si, ei, npp, B)
     dsi, dei, dnpp = (torch.from_numpy(a).cuda() for a in (si, ei, np.array([npp], np.int32)))
-    out = M.moe_w4a16_gemm1(D["x"], L.top_k, D["w13"], act, L.alpha, L.beta, L.limit, dsi, dei,
-                            dnpp, B)
-    assert_rows_close(host_bf16(out), ref, rows=cov, what=f"gemm1 {fmt} {act} B{B}")
+    with decode_policy(policy):
+        out = M.moe_w4a16_gemm1(D["x"], L.top_k, D["w13"], act, L.alpha, L.beta, L.limit, dsi,
+                                dei, dnpp, B)
+    assert_rows_close(host_bf16(out), ref, rows=cov, what=f"gemm1 {fmt} {act} B{B} {policy}")
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "gptq"])
-@pytest.mark.parametrize("B", [16, 32, 128])
-def test_gemm2_parity_and_mul_flag(fmt, B):
+@pytest.mark.parametrize("B,policy", [(16, "auto"), (32, "auto"), (16, "wide"), (32, "wide"),
+                                      (128, "auto")])
+def test_gemm2_parity_and_mul_flag(fmt, B, policy):
     L = _small(fmt, E=5, k=3, T=11)
     D = upload(L)
     ids, w = O.route(L)
@@ -147,9 +153,10 @@ def test_gemm2_parity_and_mul_flag(fmt, B):
     dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
     a = dev_bf16(a_bits)
     dtw = torch.from_numpy(tw).cuda()
-    y1 = M.moe_w4a16_gemm2(a, D["w2"], dtw, True, dsi, dei, dnpp, B)
-    y0 = M.moe_w4a16_gemm2(a, D["w2"], dtw, False, dsi, dei, dnpp, B)
-    assert_rows_close(host_bf16(y1), ref1, rows=cov, what=f"gemm2 {fmt} B{B}")
+    with decode_policy(policy):
+        y1 = M.moe_w4a16_gemm2(a, D["w2"], dtw, True, dsi, dei, dnpp, B)
+        y0 = M.moe_w4a16_gemm2(a, D["w2"], dtw, False, dsi, dei, dnpp, B)
+    assert_rows_close(host_bf16(y1), ref1, rows=cov, what=f"gemm2 {fmt} B{B} {policy}")
     # forensic check: the multiplier each row received is its own weight
     g1, g0 = host_bf16(y1), host_bf16(y0)
     ratio = (g1 * g0).sum(1) / np.maximum((g0 * g0).sum(1), 1e-30)
@@ -180,10 +187,12 @@ def test_gemm2_power_of_two_weights_bitwise(fmt):
 @pytest.mark.parametrize("fmt,act", [("nvfp4", "swigluoai"), ("mxfp4", "swigluoai"),
                                      ("gptq", "swigluoai"), ("nvfp4", "relu2")])
 @pytest.mark.parametrize("T", [1, 13, 100])
-def test_forward_parity_small(fmt, act, T):
+@pytest.mark.parametrize("policy", POLICIES)
+def test_forward_parity_small(fmt, act, T, policy):
     L = _small(fmt, act, E=6, k=3, T=T, skew_std=1.0)
     D = upload(L)
-    out = gpu_forward(L, D)
+    with decode_policy(policy):
+        out = gpu_forward(L, D)
     ref = O.forward(L)["out"]
     assert_rows_close(host_bf16(out), ref, what=f"forward {fmt} {act} T{T}")
 
@@ -221,8 +230,9 @@ def test_forward_top_k_equals_e():
 
 
 @pytest.mark.parametrize("K", [32, 96, 224, 256, 288, 480, 544, 4128])
-@pytest.mark.parametrize("B", [16, 32, 64, 128])
-def test_gemm2_k_tails(K, B):
+@pytest.mark.parametrize("B,policy", [(16, "auto"), (32, "auto"), (64, "auto"), (128, "auto"),
+                                      (16, "wide"), (32, "wide")])
+def test_gemm2_k_tails(K, B, policy):
     """Every K tail decomposition (256-chunks + 128/64/32 pieces) in both kernels."""
     fmt = "mxfp4" if K % 64 else "nvfp4"
     L = _small(fmt, E=3, k=2, H=96, I=K, T=40)
@@ -235,8 +245,10 @@ def test_gemm2_k_tails(K, B):
     tw = w.reshape(-1).astype(np.float32)
     ref, cov = O.gemm2(a_bits, n, L.w2, tw, True, si, ei, npp, B)
     dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
-    y = M.moe_w4a16_gemm2(dev_bf16(a_bits), D["w2"], torch.from_numpy(tw).cuda(), True, dsi, dei, dnpp, B)
-    assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 K={K} B{B}")
+    with decode_policy(policy):
+        y = M.moe_w4a16_gemm2(dev_bf16(a_bits), D["w2"], torch.from_numpy(tw).cuda(), True, dsi,
+                              dei, dnpp, B)
+    assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 K={K} B{B} {policy}")
 
 
 @pytest.mark.parametrize("fmt,K,N,group,B", [
@@ -245,7 +257,8 @@ def test_gemm2_k_tails(K, B):
     ("gptq", 256, 80, 64, 64),         # N % 32 != 0: split-K kernel on 32-row sub-blocks
     ("mxfp4", 2880, 320, None, 128),   # MXFP4 at the gpt-oss K, ragged last column tile
 ])
-def test_gemm2_tile_fallbacks(fmt, K, N, group, B):
+@pytest.mark.parametrize("policy", POLICIES)
+def test_gemm2_tile_fallbacks(fmt, K, N, group, B, policy):
     """The prefill kernel's tile choices and fallbacks (scale tile size, zero-point alignment)."""
     E, k, T = 3, 2, 40
     w2 = S.make_weights(fmt, E=E, N=N, K=K, group=group, seed=K + N)
@@ -257,6 +270,7 @@ def test_gemm2_tile_fallbacks(fmt, K, N, group, B):
     a_bits = S.f32_to_bf16_bits(rng.standard_normal((n, K)).astype(np.float32))
     ref, cov = O.gemm2(a_bits, n, w2, tw, True, si, ei, npp, B)
     dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
-    y = M.moe_w4a16_gemm2(dev_bf16(a_bits), upload_weights(w2), torch.from_numpy(tw).cuda(), True,
-                          dsi, dei, dnpp, B)
-    assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 {fmt} K={K} N={N} B{B}")
+    with decode_policy(policy):
+        y = M.moe_w4a16_gemm2(dev_bf16(a_bits), upload_weights(w2), torch.from_numpy(tw).cuda(),
+                              True, dsi, dei, dnpp, B)
+    assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 {fmt} K={K} N={N} B{B} {policy}")
