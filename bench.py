@@ -95,7 +95,7 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=4096)
     ap.add_argument("--sweep", default="1,8,64,512,4096")
     ap.add_argument("--copies", type=int, default=8)
-    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens the oracle is timed on")
+    ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay timings")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -121,7 +121,7 @@ def main() -> int:
     t0 = time.time()
     L = S.make_config(2)
     assert L.T >= t_max
-    log(f"generated config 2 inputs in {time.time() - t0:.1f}s")
+    log(f"generated the {S.CONFIGS[2]['name']} inputs in {time.time() - t0:.1f}s")
 
     dev = torch.device("cuda")
     x = torch.from_numpy(L.x.view(np.int16)).to(dev).view(torch.bfloat16)
