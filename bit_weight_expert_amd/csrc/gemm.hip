@@ -637,11 +637,31 @@ __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const Ep
     on[j] = n < a.N;
     bias[j] = (W.bias != nullptr && on[j]) ? bf16_bits_to_f32(W.bias[(size_t)e * a.N + n]) : 0.f;
   }
+  // routing weights: one unconditional load per row, all issued before any
+  // is used (a load inside the per-row branch would be waited for at once,
+  // one memory latency per row); sentinel rows read a valid unused weight
+  const bool use_tw = EPI == EPI_DOWN && a.mul_tw;
+  const float* tbase = use_tw ? a.topk_w : reinterpret_cast<const float*>(a.sorted_ids);
+  const int tmul = use_tw ? 1 : 0;
+  // slot ids one row group ahead of their use, so each group's loads overlap
+  // the previous group's stores
+  int sid_next[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) sid_next[v] = a.sorted_ids[a.row0 + 8 * (v >> 2) + 4 * h + (v & 3)];
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     int sid[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sid[v] = a.sorted_ids[a.row0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3)];
+    for (int v = 0; v < 16; ++v) sid[v] = sid_next[v];
+    float tws[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      tws[v] = (EPI == EPI_DOWN) ? tbase[min(sid[v], a.n_slots - 1) * tmul] : 1.f;
+    if (i + 1 < MI) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        sid_next[v] = a.sorted_ids[a.row0 + (i + 1) * 32 + 8 * (v >> 2) + 4 * h + (v & 3)];
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       if (sid[v] >= a.n_slots) continue;
@@ -658,8 +678,7 @@ __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const Ep
           orow[n0 / 2 + 32 * p + c] = f32_to_bf16_bits(y);
         }
       } else {
-        float tw = 1.f;
-        if (EPI == EPI_DOWN && a.mul_tw) tw = a.topk_w[sid[v]];
+        const float tw = use_tw ? tws[v] : 1.f;
 #pragma unroll
         for (int j = 0; j < NF; ++j) {
           if (!on[j]) continue;
