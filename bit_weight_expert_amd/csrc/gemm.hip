@@ -261,18 +261,38 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiAr
                                          const WeightArgs& W, int e, int n0, int lane) {
   const int c16 = lane & 15, g = lane >> 4;
   const float gsc = (FMT == FMT_NVFP4) ? W.global_scale[e] : 1.f;
+  // bias: unconditional loads (another valid word when there is none)
+  const bool has_bias = W.bias != nullptr;
+  const uint16_t* bbase = has_bias ? W.bias : reinterpret_cast<const uint16_t*>(W.qweight);
+  const int bmul = has_bias ? 1 : 0;
   float bias[NF];
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
-    bias[j] = 0.f;
-    if (W.bias != nullptr && frag_on<EPI>(n0, j, a.N))
-      bias[j] = bf16_bits_to_f32(W.bias[(size_t)e * a.N + frag_row<EPI>(n0, j, c16)]);
+    const int row = frag_on<EPI>(n0, j, a.N) ? frag_row<EPI>(n0, j, c16) : n0;
+    const float b = bf16_bits_to_f32(bbase[((size_t)e * a.N + row) * bmul]);
+    bias[j] = has_bias ? b : 0.f;
   }
+  // slot ids, then routing weights, each as one batch of unconditional loads
+  // (a load inside the per-row branch would be waited for at once)
+  int sids[MI][4];
+  float tws[MI][4];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sids[i][r] = a.sorted_ids[a.row0 + i * 16 + 4 * g + r];
+  const bool use_tw = EPI == EPI_DOWN && a.mul_tw;
+  const float* tbase = use_tw ? a.topk_w : reinterpret_cast<const float*>(a.sorted_ids);
+  const int tmul = use_tw ? 1 : 0;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      tws[i][r] = (EPI == EPI_DOWN) ? tbase[min(sids[i][r], a.n_slots - 1) * tmul] : 1.f;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int sid = a.sorted_ids[a.row0 + i * 16 + 4 * g + r];
+      const int sid = sids[i][r];
       if (sid >= a.n_slots) continue;
       uint16_t* orow = a.out + (size_t)sid * a.out_ld;
       if (EPI == EPI_SWIGLU) {
@@ -287,8 +307,7 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiAr
           orow[n0 / 2 + 16 * p + c16] = f32_to_bf16_bits(v);
         }
       } else {
-        float tw = 1.f;
-        if (EPI == EPI_DOWN && a.mul_tw) tw = a.topk_w[sid];
+        const float tw = use_tw ? tws[i][r] : 1.f;
 #pragma unroll
         for (int j = 0; j < NF; ++j) {
           if (!frag_on<EPI>(n0, j, a.N)) continue;
@@ -629,13 +648,18 @@ __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const Ep
                                            const WeightArgs& W, int e, int n0, int lane) {
   const int c = lane & 31, h = lane >> 5;
   const float gsc = (FMT == FMT_NVFP4) ? W.global_scale[e] : 1.f;
+  // bias: unconditional loads (another valid word when there is none)
+  const bool has_bias = W.bias != nullptr;
+  const uint16_t* bbase = has_bias ? W.bias : reinterpret_cast<const uint16_t*>(W.qweight);
+  const int bmul = has_bias ? 1 : 0;
   float bias[NF];
   bool on[NF];
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     const int n = frag32_row<EPI>(n0, j, c);
     on[j] = n < a.N;
-    bias[j] = (W.bias != nullptr && on[j]) ? bf16_bits_to_f32(W.bias[(size_t)e * a.N + n]) : 0.f;
+    const float b = bf16_bits_to_f32(bbase[((size_t)e * a.N + (on[j] ? n : n0)) * bmul]);
+    bias[j] = has_bias ? b : 0.f;
   }
   // routing weights: one unconditional load per row, all issued before any
   // is used (a load inside the per-row branch would be waited for at once,
