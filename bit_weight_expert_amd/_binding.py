@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
         L.moe_align.restype = i
         L.moe_route_align.argtypes = [vp, i, i, i, i, vp, i, i, vp, vp, vp, vp, vp, vp]
         L.moe_route_align.restype = i
-        L.moe_w4a16_gemm1.argtypes = [vp, i, i, i, i, i, wq, i, f, f, f, vp, vp, vp, i, vp, vp]
+        L.moe_w4a16_gemm1.argtypes = [vp, i, i, i, i, i, wq, i, f, f, f, vp, i, vp, vp, vp, i, vp, vp]
         L.moe_w4a16_gemm1.restype = i
         L.moe_w4a16_gemm2.argtypes = [vp, i, i, i, i, wq, vp, i, vp, vp, vp, i, vp, vp]
         L.moe_w4a16_gemm2.restype = i
@@ -223,17 +223,23 @@ def moe_route_align(logits: torch.Tensor, top_k: int, block_m: int, kind: str = 
 
 def moe_w4a16_gemm1(x: torch.Tensor, top_k: int, w13: QuantWeights, act: str, alpha: float,
                     beta: float, limit: float, sorted_ids, expert_ids, num_post_pad,
-                    block_m: int, out=None):
-    """x bf16 [size_m, K] -> out bf16 [size_m*top_k, N/2 (gated) or N]."""
+                    block_m: int, out=None, topk_w=None):
+    """x bf16 [size_m, K] -> out bf16 [size_m*top_k, N/2 (gated) or N].
+
+    topk_w (fp32 [size_m*top_k]) given: each input row is scaled by its slot's
+    routing weight (the weight applied on the input)."""
     _dev(x, torch.bfloat16, "x")
+    if topk_w is not None:
+        _dev(topk_w, torch.float32, "topk_w")
     size_m, K = x.shape
     n_out = w13.N // 2 if act == "swigluoai" else w13.N
     if out is None:
         out = torch.zeros((size_m * top_k, n_out), dtype=torch.bfloat16, device=x.device)
     s = w13.struct()
     _check(lib().moe_w4a16_gemm1(_ptr(x), size_m, top_k, K, w13.N, w13.E, ctypes.byref(s),
-                                 ACT[act], alpha, beta, limit, _ptr(sorted_ids), _ptr(expert_ids),
-                                 _ptr(num_post_pad), block_m, _ptr(out), _stream()),
+                                 ACT[act], alpha, beta, limit, _ptr(topk_w), int(topk_w is not None),
+                                 _ptr(sorted_ids), _ptr(expert_ids), _ptr(num_post_pad), block_m,
+                                 _ptr(out), _stream()),
            "moe_w4a16_gemm1")
     return out
 
@@ -257,8 +263,12 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, top_k: int, inter: int,
                 w13: QuantWeights, w2: QuantWeights, act: str = "swigluoai",
                 route: str = "softmax", expert_bias=None, renormalize: bool = True,
                 alpha: float = 1.702, beta: float = 1.0, limit: float = 7.0,
-                mul_topk_weights: bool = True, workspace=None, out=None):
-    """The whole layer: x bf16 [T, hidden], logits f32 [T, E] -> out bf16 [T, hidden]."""
+                mul_topk_weights: bool = True, workspace=None, out=None,
+                weight_on_input: bool = False):
+    """The whole layer: x bf16 [T, hidden], logits f32 [T, E] -> out bf16 [T, hidden].
+
+    weight_on_input: the routing weight scales GEMM1's input rows instead of
+    GEMM2's output rows (top_k must be 1)."""
     _dev(x, torch.bfloat16, "x")
     _dev(logits, torch.float32, "logits")
     T, hidden = x.shape
@@ -272,7 +282,7 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, top_k: int, inter: int,
     _check(lib().moe_forward(_ptr(x), _ptr(logits), T, E, top_k, hidden, inter, ROUTE[route],
                              _ptr(expert_bias), int(bool(renormalize)), ctypes.byref(s13),
                              ctypes.byref(s2), ACT[act], alpha, beta, limit,
-                             int(bool(mul_topk_weights)), _ptr(workspace),
+                             2 if weight_on_input else int(bool(mul_topk_weights)), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _ptr(out), _stream()),
            "moe_forward")
     return out

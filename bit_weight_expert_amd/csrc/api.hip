@@ -188,7 +188,8 @@ static moe_status_t gemm_common_checks(int size_m, int top_k, int E, int block_m
 
 moe_status_t moe_w4a16_gemm1(const uint16_t* x, int size_m, int top_k, int K, int N, int E,
                              const moe_wq_t* w13, moe_act_t act, float alpha, float beta,
-                             float limit, const int32_t* sorted_ids, const int32_t* expert_ids,
+                             float limit, const float* topk_w, int mul_topk_weights,
+                             const int32_t* sorted_ids, const int32_t* expert_ids,
                              const int32_t* num_post_pad, int block_m, uint16_t* out,
                              moe_stream_t stream) {
   moe_status_t st = gemm_common_checks(size_m, top_k, E, block_m);
@@ -203,12 +204,14 @@ moe_status_t moe_w4a16_gemm1(const uint16_t* x, int size_m, int top_k, int K, in
   if (x == nullptr || sorted_ids == nullptr || expert_ids == nullptr || num_post_pad == nullptr ||
       out == nullptr)
     return MOE_ERR_NULL;
+  if (mul_topk_weights && topk_w == nullptr) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(out)) return MOE_ERR_ALIGN;
   const int cap = (int)moe_align_capacity(size_m, top_k, E, block_m);
   const int out_ld = (epi == moe::EPI_SWIGLU) ? N / 2 : N;
   return hip_status(moe_launch_gemm((int)w13->fmt, epi, block_m, cap, x, top_k, size_m * top_k, K, N, E,
-                                    &W, sorted_ids, expert_ids, num_post_pad, nullptr, 0, alpha,
-                                    beta, limit, out, out_ld, static_cast<hipStream_t>(stream)));
+                                    &W, sorted_ids, expert_ids, num_post_pad, topk_w,
+                                    mul_topk_weights ? 1 : 0, alpha, beta, limit, out, out_ld,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_w4a16_gemm2(const uint16_t* a, int size_m, int K, int N, int E,
@@ -263,6 +266,8 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, i
   st = check_weights(w2, hidden, inter, &W2);
   if (st != MOE_OK) return st;
   if (epi == moe::EPI_SWIGLU && n1 % 32 != 0) return MOE_ERR_SHAPE;
+  if (mul_topk_weights < 0 || mul_topk_weights > 2) return MOE_ERR_UNSUPPORTED;
+  if (mul_topk_weights == 2 && top_k != 1) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (x == nullptr || logits == nullptr || out == nullptr || workspace == nullptr) return MOE_ERR_NULL;
   if (kind == MOE_ROUTE_SIGMOID_BIAS && expert_bias == nullptr) return MOE_ERR_NULL;
@@ -287,13 +292,14 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, i
   hipError_t e = moe_launch_route_align(logits, T, E, top_k, (int)kind, expert_bias,
                                         renormalize ? 1 : 0, ids, tw, block_m, cap, sorted, eids,
                                         npp, s);
+  // routing weight on GEMM2's output rows (mode 1) or GEMM1's input rows (mode 2)
   if (e == hipSuccess)
     e = moe_launch_gemm((int)w13->fmt, epi, block_m, cap, x, top_k, n, hidden, n1, E, &W13, sorted, eids,
-                        npp, nullptr, 0, alpha, beta, limit, actb, inter, s);
+                        npp, tw, mul_topk_weights == 2 ? 1 : 0, alpha, beta, limit, actb, inter, s);
   if (e == hipSuccess)
     e = moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, actb, 1, n, inter, hidden, E, &W2,
-                        sorted, eids, npp, tw, mul_topk_weights ? 1 : 0, 0.f, 0.f, 0.f, yb, hidden,
-                        s);
+                        sorted, eids, npp, tw, mul_topk_weights == 1 ? 1 : 0, 0.f, 0.f, 0.f, yb,
+                        hidden, s);
   if (e == hipSuccess) e = moe_launch_sum(yb, ids, T, top_k, hidden, E, out, s);
   return hip_status(e);
 }

@@ -280,14 +280,15 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiAr
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sids[i][r] = a.sorted_ids[a.row0 + i * 16 + 4 * g + r];
-  const bool use_tw = EPI == EPI_DOWN && a.mul_tw;
+  // (GEMM2: the output row is scaled; GEMM1: the accumulator, i.e. the
+  // input row -- the routing weight applied on the input)
+  const bool use_tw = a.mul_tw;
   const float* tbase = use_tw ? a.topk_w : reinterpret_cast<const float*>(a.sorted_ids);
   const int tmul = use_tw ? 1 : 0;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      tws[i][r] = (EPI == EPI_DOWN) ? tbase[min(sids[i][r], a.n_slots - 1) * tmul] : 1.f;
+    for (int r = 0; r < 4; ++r) tws[i][r] = tbase[min(sids[i][r], a.n_slots - 1) * tmul];
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -295,23 +296,24 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiAr
       const int sid = sids[i][r];
       if (sid >= a.n_slots) continue;
       uint16_t* orow = a.out + (size_t)sid * a.out_ld;
+      const float tw = use_tw ? tws[i][r] : 1.f;
+      const float gin = (EPI == EPI_DOWN) ? gsc : gsc * tw;
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
         for (int p = 0; p < NF / 2; ++p) {
           if (!frag_on<EPI>(n0, 2 * p, a.N)) continue;
-          float gate = acc[i][2 * p][r] * gsc + bias[2 * p];
-          float up = acc[i][2 * p + 1][r] * gsc + bias[2 * p + 1];
+          float gate = acc[i][2 * p][r] * gin + bias[2 * p];
+          float up = acc[i][2 * p + 1][r] * gin + bias[2 * p + 1];
           gate = fminf(gate, a.limit);
           up = fminf(fmaxf(up, -a.limit), a.limit);
           const float v = gate * sigmoid_fast(a.alpha * gate) * (up + a.beta);
           orow[n0 / 2 + 16 * p + c16] = f32_to_bf16_bits(v);
         }
       } else {
-        const float tw = use_tw ? tws[i][r] : 1.f;
 #pragma unroll
         for (int j = 0; j < NF; ++j) {
           if (!frag_on<EPI>(n0, j, a.N)) continue;
-          float v = acc[i][j][r] * gsc + bias[j];
+          float v = acc[i][j][r] * gin + bias[j];
           if (EPI == EPI_RELU2) {
             v = fmaxf(v, 0.f);
             v = v * v;
@@ -664,7 +666,9 @@ __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const Ep
   // routing weights: one unconditional load per row, all issued before any
   // is used (a load inside the per-row branch would be waited for at once,
   // one memory latency per row); sentinel rows read a valid unused weight
-  const bool use_tw = EPI == EPI_DOWN && a.mul_tw;
+  // (GEMM2: the output row is scaled; GEMM1: the accumulator, i.e. the
+  // input row -- the routing weight applied on the input)
+  const bool use_tw = a.mul_tw;
   const float* tbase = use_tw ? a.topk_w : reinterpret_cast<const float*>(a.sorted_ids);
   const int tmul = use_tw ? 1 : 0;
   // slot ids one row group ahead of their use, so each group's loads overlap
@@ -680,7 +684,7 @@ __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const Ep
     float tws[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v)
-      tws[v] = (EPI == EPI_DOWN) ? tbase[min(sid[v], a.n_slots - 1) * tmul] : 1.f;
+      tws[v] = tbase[min(sid[v], a.n_slots - 1) * tmul];
     if (i + 1 < MI) {
 #pragma unroll
       for (int v = 0; v < 16; ++v)
@@ -690,23 +694,24 @@ __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const Ep
     for (int v = 0; v < 16; ++v) {
       if (sid[v] >= a.n_slots) continue;
       uint16_t* orow = a.out + (size_t)sid[v] * a.out_ld;
+      const float tw = use_tw ? tws[v] : 1.f;
+      const float gin = (EPI == EPI_DOWN) ? gsc : gsc * tw;
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
         for (int p = 0; p < NF / 2; ++p) {
           if (!on[2 * p]) continue;
-          float gate = acc[i][2 * p][v] * gsc + bias[2 * p];
-          float up = acc[i][2 * p + 1][v] * gsc + bias[2 * p + 1];
+          float gate = acc[i][2 * p][v] * gin + bias[2 * p];
+          float up = acc[i][2 * p + 1][v] * gin + bias[2 * p + 1];
           gate = fminf(gate, a.limit);
           up = fminf(fmaxf(up, -a.limit), a.limit);
           const float y = gate * sigmoid_fast(a.alpha * gate) * (up + a.beta);
           orow[n0 / 2 + 32 * p + c] = f32_to_bf16_bits(y);
         }
       } else {
-        const float tw = use_tw ? tws[v] : 1.f;
 #pragma unroll
         for (int j = 0; j < NF; ++j) {
           if (!on[j]) continue;
-          float y = acc[i][j][v] * gsc + bias[j];
+          float y = acc[i][j][v] * gin + bias[j];
           if (EPI == EPI_RELU2) {
             y = fmaxf(y, 0.f);
             y = y * y;
@@ -1257,8 +1262,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Everything the epilogue reads besides the accumulators, loaded at the start
 // so that its latency hides behind the weight stream: the slot ids of the
-// lane's rows (i*16 + 4g + r), their routing weights (GEMM2), the lane's
-// bias values and the NVFP4 global scale.
+// lane's rows (i*16 + 4g + r), their routing weights, the lane's bias values
+// and the NVFP4 global scale.  The routing weight scales GEMM2's output row,
+// or GEMM1's accumulator when it is applied on the input instead.
 template <int MI, int NF>
 struct EpiPre {
   int sid[MI][4];
@@ -1297,14 +1303,13 @@ __device__ __forceinline__ void epi_prefetch_ids(EpiPre<MI, NF>& p, const EpiArg
 // Part 2: routing weights (GEMM2), once the slot ids are in.
 template <int EPI, int MI, int NF>
 __device__ __forceinline__ void epi_prefetch_tw(EpiPre<MI, NF>& p, const EpiArgs& a) {
-  const bool use = EPI == EPI_DOWN && a.mul_tw;
+  const bool use = a.mul_tw;
   const float* tbase = use ? a.topk_w : reinterpret_cast<const float*>(a.sorted_ids);
   const int tmul = use ? 1 : 0;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      p.tw[i][r] = (EPI == EPI_DOWN) ? tbase[min(p.sid[i][r], a.n_slots - 1) * tmul] : 1.f;
+    for (int r = 0; r < 4; ++r) p.tw[i][r] = tbase[min(p.sid[i][r], a.n_slots - 1) * tmul];
 }
 
 // The epilogue of the 16x16 fragments with prefetched metadata (same
@@ -1324,12 +1329,14 @@ __device__ __forceinline__ void epilogue_pre(const f32x4 (&acc)[MI][NF], const E
       const int sid = p.sid[i][r];
       if (sid >= a.n_slots) continue;
       uint16_t* orow = a.out + (size_t)sid * a.out_ld;
+      const float tw = a.mul_tw ? p.tw[i][r] : 1.f;
+      const float gin = (EPI == EPI_DOWN) ? p.gsc : p.gsc * tw;
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
         for (int q = 0; q < NF / 2; ++q) {
           if (!frag_on<EPI>(n0, 2 * q, a.N)) continue;
-          float gate = acc[i][2 * q][r] * p.gsc + bias[2 * q];
-          float up = acc[i][2 * q + 1][r] * p.gsc + bias[2 * q + 1];
+          float gate = acc[i][2 * q][r] * gin + bias[2 * q];
+          float up = acc[i][2 * q + 1][r] * gin + bias[2 * q + 1];
           gate = fminf(gate, a.limit);
           up = fminf(fmaxf(up, -a.limit), a.limit);
           const float v = gate * sigmoid_fast(a.alpha * gate) * (up + a.beta);
@@ -1339,12 +1346,12 @@ __device__ __forceinline__ void epilogue_pre(const f32x4 (&acc)[MI][NF], const E
 #pragma unroll
         for (int j = 0; j < NF; ++j) {
           if (!frag_on<EPI>(n0, j, a.N)) continue;
-          float v = acc[i][j][r] * p.gsc + bias[j];
+          float v = acc[i][j][r] * gin + bias[j];
           if (EPI == EPI_RELU2) {
             v = fmaxf(v, 0.f);
             v = v * v;
-          } else if (EPI == EPI_DOWN && a.mul_tw) {
-            v = v * p.tw[i][r];
+          } else if (EPI == EPI_DOWN) {
+            v = v * tw;
           }
           orow[n0 + 16 * j + c16] = f32_to_bf16_bits(v);
         }

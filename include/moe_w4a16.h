@@ -146,6 +146,10 @@ moe_status_t moe_route_align(const float* logits, int T, int E, int top_k, moe_r
 /* Grouped GEMM1 over aligned blocks.  For every real entry f of block b
  * (expert e = expert_ids[b]):
  *   h   = W13_e . x[f / top_k] (+ bias13_e)           fp32 accumulate
+ *         (with mul_topk_weights: W13_e . (topk_w[f] x[f / top_k]) + bias13_e,
+ *          the routing weight applied on the input, "apply_router_weight_on_input"
+ *          on the "moe_wna16_marlin_gemm applies wrong per-row topk weights" page;
+ *          topk_w fp32 [size_m*top_k], may be NULL when the flag is 0)
  *   out[f][:] = act(h)  bf16 (round to nearest even)
  *   x    bf16 [size_m][K]
  *   N    rows of W13 (2*intermediate when gated, intermediate for RELU2/NONE)
@@ -155,7 +159,8 @@ moe_status_t moe_route_align(const float* logits, int T, int E, int top_k, moe_r
  * block_m, size_m and top_k. */
 moe_status_t moe_w4a16_gemm1(const uint16_t* x, int size_m, int top_k, int K, int N, int E,
                              const moe_wq_t* w13, moe_act_t act, float alpha, float beta,
-                             float limit, const int32_t* sorted_ids, const int32_t* expert_ids,
+                             float limit, const float* topk_w, int mul_topk_weights,
+                             const int32_t* sorted_ids, const int32_t* expert_ids,
                              const int32_t* num_post_pad, int block_m, uint16_t* out,
                              moe_stream_t stream);
 
@@ -189,6 +194,10 @@ size_t moe_forward_workspace_bytes(int T, int E, int top_k, int hidden, int inte
  *   logits     fp32 [T][E]
  *   w13        N = 2*inter (SWIGLUOAI) or inter (RELU2), K = hidden
  *   w2         N = hidden, K = inter
+ *   mul_topk_weights  0: routing weights not applied; 1: each GEMM2 output row
+ *              times its own weight (mul_topk_weights=True on the pages); 2: each
+ *              GEMM1 input row times its weight instead (apply_router_weight_on_input;
+ *              top_k must be 1, else MOE_ERR_SHAPE)
  *   workspace  device scratch of at least moe_forward_workspace_bytes(), 256-byte aligned
  *   out        bf16 [T][hidden] (the unpadded width)
  * block_m is chosen by the library from T*top_k/E. */

@@ -58,17 +58,19 @@ def forward(layer, ids, tw):
     L = layer
     T = L.x.shape[0]
     out = [[0.0] * L.H for _ in range(T)]
+    on_input = getattr(L, "weight_on_input", False)   # routing weight scales the input row
     for t in range(T):
         xt = [_bf16(v) for v in L.x[t]]
         for j in range(L.top_k):
             e = int(ids[t][j])
             if not (0 <= e < L.E):
                 continue
+            xin = [v * float(tw[t][j]) for v in xt] if on_input else xt
             h = []
             for n in range(L.w13.N):
                 acc = 0.0
                 for k in range(L.H):
-                    acc += weight(L.w13, e, n, k) * xt[k]
+                    acc += weight(L.w13, e, n, k) * xin[k]
                 if L.w13.bias is not None:
                     acc += _bf16(L.w13.bias[e, n])
                 h.append(acc)
@@ -87,7 +89,7 @@ def forward(layer, ids, tw):
                     acc += weight(L.w2, e, n, k) * a[k]
                 if L.w2.bias is not None:
                     acc += _bf16(L.w2.bias[e, n])
-                if L.mul_topk_weights:
+                if L.mul_topk_weights and not on_input:
                     acc *= float(tw[t][j])
                 out[t][n] += acc
     return out

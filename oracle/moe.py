@@ -25,6 +25,9 @@ rounding):
   gemm2   y = (W2_e a + b2_e) * w_slot when mul_topk_weights, per row by the
           slot's own routing weight (repro fp32 reference
           "out[row] = (act[row] @ w[e].T + 0) * topk_w[row]").
+          The other mode the same page names, apply_router_weight_on_input
+          (top_k = 1): the routing weight scales GEMM1's input row instead,
+          h = W13_e (w_slot x_t) + b13_e, and GEMM2 multiplies nothing.
   sum     out_t = sum_j y_{t,j} at the true hidden width (the op's output is
           the unpadded 2880, "gpt-oss-120b MXFP4 ... crashes", root cause).
 
@@ -198,11 +201,13 @@ def _bias_f64(w, e):
 
 
 def gemm1(x_bits, size_m, top_k, w13, act, alpha, beta, limit,
-          sorted_ids, expert_ids, num_post_pad, block_m):
+          sorted_ids, expert_ids, num_post_pad, block_m, topk_w_flat=None):
     """Grouped GEMM1 over aligned blocks.
 
     Row f of the result (flat slot f = t*top_k + j) is
-    act(W13_e x_t + b13_e) with e the expert of f's block and t = f // top_k.
+    act(W13_e x_t + b13_e) with e the expert of f's block and t = f // top_k;
+    with topk_w_flat given (routing weight on the input), the input row is
+    w_f x_t instead.
     Returns (out float64 [size_m*top_k, N_out], covered bool [size_m*top_k]).
     """
     n_slots = size_m * top_k
@@ -210,10 +215,14 @@ def gemm1(x_bits, size_m, top_k, w13, act, alpha, beta, limit,
     re = slot_experts(sorted_ids, expert_ids, num_post_pad, block_m, n_slots)
     n_out = w13.N // 2 if act == "swigluoai" else w13.N
     out = np.zeros((n_slots, n_out), dtype=np.float64)
+    tw = None if topk_w_flat is None else np.asarray(topk_w_flat, dtype=np.float64).reshape(-1)
     for e in np.unique(re[re >= 0]):
         rows = np.nonzero(re == e)[0]
         W = decode_expert(w13, int(e))                       # [N1, K]
-        h = x[rows // top_k] @ W.T + _bias_f64(w13, int(e))
+        xr = x[rows // top_k]
+        if tw is not None:
+            xr = xr * tw[rows][:, None]
+        h = xr @ W.T + _bias_f64(w13, int(e))
         out[rows] = activation(h, act, alpha, beta, limit)
     return out, re >= 0
 
@@ -260,10 +269,12 @@ def forward(layer, block_m: int = 16, topk=None):
     L = layer
     T = L.x.shape[0]
     ids, w = route(L) if topk is None else topk
+    on_input = getattr(L, "weight_on_input", False)
     sorted_ids, expert_ids, npp = align(ids, L.E, block_m)
     act, _ = gemm1(L.x, T, L.top_k, L.w13, L.act, L.alpha, L.beta, L.limit,
-                   sorted_ids, expert_ids, npp, block_m)
-    y, _ = gemm2(act, T * L.top_k, L.w2, w.reshape(-1), L.mul_topk_weights,
+                   sorted_ids, expert_ids, npp, block_m,
+                   topk_w_flat=w.reshape(-1) if on_input else None)
+    y, _ = gemm2(act, T * L.top_k, L.w2, w.reshape(-1), L.mul_topk_weights and not on_input,
                  sorted_ids, expert_ids, npp, block_m)
     out = moe_sum(y, ids, L.E)
     return dict(topk_ids=ids, topk_w=w, sorted_ids=sorted_ids, expert_ids=expert_ids,
@@ -293,11 +304,13 @@ def forward_tokens(layer, tokens, topk=None):
     for e, items in sorted(by_expert.items()):
         W13 = decode_expert(L.w13, e)
         W2 = decode_expert(L.w2, e)
+        on_input = getattr(L, "weight_on_input", False)
         for i, t, j in items:
-            h = W13 @ x[t] + _bias_f64(L.w13, e)
+            xin = x[t] * float(w[t, j]) if on_input else x[t]
+            h = W13 @ xin + _bias_f64(L.w13, e)
             a = activation(h, L.act, L.alpha, L.beta, L.limit)
             yv = W2 @ a + _bias_f64(L.w2, e)
-            if L.mul_topk_weights:
+            if L.mul_topk_weights and not on_input:
                 yv = yv * float(w[t, j])
             y[i, j] = yv
         del W13, W2

@@ -191,6 +191,7 @@ class Layer:
     w13: Weights
     w2: Weights
     seed: int
+    weight_on_input: bool = False    # routing weight scales GEMM1's input (top_k = 1)
 
     @property
     def T(self) -> int:

@@ -38,7 +38,8 @@ def gpu_forward(L, D, **kw):
     return M.moe_forward(D["x"], D["logits"], L.top_k, L.I, D["w13"], D["w2"], act=L.act,
                          route=L.route, expert_bias=D["expert_bias"], renormalize=L.renormalize,
                          alpha=L.alpha, beta=L.beta, limit=L.limit,
-                         mul_topk_weights=L.mul_topk_weights, **kw)
+                         mul_topk_weights=L.mul_topk_weights,
+                         weight_on_input=getattr(L, "weight_on_input", False), **kw)
 
 
 def assert_rows_close(got, ref, rows=None, tol=TOL, what=""):

@@ -77,9 +77,9 @@ def test_align_rejects(L):
     assert L.moe_align(None, 0, 2, 8, 16, None, None, None, None) == OK
 
 
-def _g1(L, w, K=2880, N=5760, act=0, x=FAKE, out=FAKE, block_m=16):
+def _g1(L, w, K=2880, N=5760, act=0, x=FAKE, out=FAKE, block_m=16, tw=None, mul=0):
     return L.moe_w4a16_gemm1(x, 8, 4, K, N, 32, ctypes.byref(w), act, 1.702, 1.0, 7.0,
-                             FAKE, FAKE, FAKE, block_m, out, None)
+                             tw, mul, FAKE, FAKE, FAKE, block_m, out, None)
 
 
 def test_gemm1_rejects(L):
@@ -98,6 +98,7 @@ def test_gemm1_rejects(L):
     assert _g1(L, _wq(), x=FAKE + 2) == ALIGN
     assert _g1(L, _wq(), x=None) == NULL
     assert _g1(L, _wq(), block_m=8) == SHAPE
+    assert _g1(L, _wq(), mul=1) == NULL                  # weight on the input needs the weights
 
 
 def test_gemm2_rejects(L):
@@ -115,11 +116,14 @@ def test_forward_rejects(L):
     w13, w2 = _wq(), _wq()
     f = lambda **kw: L.moe_forward(FAKE, FAKE, kw.get("T", 8), 32, kw.get("k", 4), 2880, 2880,
                                    kw.get("kind", 0), None, 1, ctypes.byref(w13), ctypes.byref(w2),
-                                   kw.get("act", 0), 1.702, 1.0, 7.0, 1, kw.get("ws", FAKE * 16),
-                                   kw.get("wsb", 0), FAKE, None)
+                                   kw.get("act", 0), 1.702, 1.0, 7.0, kw.get("mul", 1),
+                                   kw.get("ws", FAKE * 16), kw.get("wsb", 0), FAKE, None)
     assert f() == WS                                     # workspace too small
     assert f(ws=FAKE + 16, wsb=1 << 40) == ALIGN         # workspace must be 256-byte aligned
     assert f(act=2) == UNSUP                             # forward needs a real activation
     assert f(k=33) == SHAPE
     assert f(kind=1) == NULL                             # sigmoid routing needs the bias
     assert f(T=0) == OK
+    assert f(mul=2) == SHAPE                             # weight on the input needs top_k = 1
+    assert f(mul=3) == UNSUP
+    assert f(mul=2, k=1) == WS                           # accepted with top_k = 1 (then sizes)

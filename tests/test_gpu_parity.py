@@ -5,6 +5,8 @@ bit-exact; float results within 5e-3 per-row relative error with no NaN/Inf.
 Shapes here are small enough for the oracle to finish in seconds but span
 several tiles and ragged K / N tails (K = 320 = 2*128 + 64).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -182,6 +184,24 @@ def test_gemm2_power_of_two_weights_bitwise(fmt):
     assert torch.equal(y1.view(torch.int16), ext.view(torch.int16))
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "gptq"])
+@pytest.mark.parametrize("B,policy", [(16, "auto"), (16, "wide"), (64, "auto")])
+def test_gemm1_weight_on_input(fmt, B, policy):
+    """GEMM1 with each input row scaled by its slot's routing weight, in all three kernels."""
+    L = _small(fmt, "swigluoai", x_std=12.0)
+    D = upload(L)
+    ids, _ = O.route(L)
+    tw = np.random.default_rng(7).uniform(0.05, 1.5, size=L.T * L.top_k).astype(np.float32)
+    si, ei, npp = O.align(ids, L.E, B)
+    ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, "swigluoai", L.alpha, L.beta, L.limit, si, ei,
+                       npp, B, topk_w_flat=tw)
+    dsi, dei, dnpp = (torch.from_numpy(a).cuda() for a in (si, ei, np.array([npp], np.int32)))
+    with decode_policy(policy):
+        out = M.moe_w4a16_gemm1(D["x"], L.top_k, D["w13"], "swigluoai", L.alpha, L.beta, L.limit,
+                                dsi, dei, dnpp, B, topk_w=torch.from_numpy(tw).cuda())
+    assert_rows_close(host_bf16(out), ref, rows=cov, what=f"gemm1 weight on input {fmt} B{B} {policy}")
+
+
 # ------------------------------------------------------------------ forward --
 
 @pytest.mark.parametrize("fmt,act", [("nvfp4", "swigluoai"), ("mxfp4", "swigluoai"),
@@ -195,6 +215,16 @@ def test_forward_parity_small(fmt, act, T, policy):
         out = gpu_forward(L, D)
     ref = O.forward(L)["out"]
     assert_rows_close(host_bf16(out), ref, what=f"forward {fmt} {act} T{T}")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("T", [1, 13, 100])
+def test_forward_weight_on_input(fmt, T):
+    """top_k = 1 with the routing weight on GEMM1's input (weights not renormalised)."""
+    L = dataclasses.replace(_small(fmt, E=6, k=1, T=T, renormalize=False), weight_on_input=True)
+    D = upload(L)
+    out = gpu_forward(L, D)
+    assert_rows_close(host_bf16(out), O.forward(L)["out"], what=f"forward weight on input {fmt} T{T}")
 
 
 def test_forward_config1_full():

@@ -1,4 +1,5 @@
 """Pins for the oracle's routing, align, GEMMs, activation and sum (CPU only)."""
+import dataclasses
 import os
 
 import numpy as np
@@ -202,6 +203,25 @@ def test_mul_topk_weights_equals_external_multiply_and_forensic_ratio():
         if row:
             applied, own = float(row[1]), float(row[2])
             assert abs(applied / own - 1) > 0.01       # the check flags every buggy row
+
+
+def test_weight_on_input_is_linear_in_the_weight_and_matches_brute_force():
+    """Routing weight applied on GEMM1's input: with the activation left out,
+    h_w - b = w (h - b) row by row; the whole layer (top_k = 1, weights not
+    renormalised, so they differ from 1) equals the pure-Python brute force."""
+    L = _tiny_layer("nvfp4", E=4, k=1, H=64, I=32, T=9, renormalize=False)
+    ids, w = O.route(L)
+    assert np.all(w < 1.0)
+    si, ei, npp = O.align(ids, L.E, 16)
+    h1, _ = O.gemm1(L.x, L.T, 1, L.w13, "none", 0, 0, 0, si, ei, npp, 16, topk_w_flat=w.reshape(-1))
+    h0, _ = O.gemm1(L.x, L.T, 1, L.w13, "none", 0, 0, 0, si, ei, npp, 16)
+    b = np.stack([F.bf16_to_f64(L.w13.bias[e]) for e in ids.reshape(-1)])
+    np.testing.assert_allclose(h1 - b, (h0 - b) * w.reshape(-1, 1), rtol=1e-12, atol=1e-12)
+    Lw = dataclasses.replace(L, weight_on_input=True)
+    ref = O.forward(Lw, block_m=16)
+    out = np.array(brute.forward(Lw, ref["topk_ids"], ref["topk_w"]))
+    np.testing.assert_allclose(ref["out"], out, rtol=1e-10, atol=1e-12)
+    assert not np.allclose(ref["out"], O.forward(L, block_m=16)["out"], rtol=1e-3)
 
 
 def test_tail_scale_group_is_applied_at_true_k():
