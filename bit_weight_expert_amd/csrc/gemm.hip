@@ -387,6 +387,12 @@ __device__ __forceinline__ void load_frags(BChunk<FMT, C> (&b)[NF], const Weight
 }
 
 constexpr int kPfBK = 64;                  // K chunk
+// Waves per SIMD of the prefill kernel (row split): two for MXFP4, whose
+// dequant is one convert per two weights (measured 3-4% faster at the
+// gpt-oss-120b shape), one otherwise (the doubled dequant of NVFP4 / GPTQ
+// costs more than the overlap gains: GPTQ measured 13% slower).
+template <int FMT>
+constexpr int pf_rs() { return FMT == FMT_MXFP4 ? 2 : 1; }
 constexpr int kPfStages = 4;               // LDS ring depth
 constexpr int kPfScaleBytes = 60 * 1024;   // LDS for the tile's scales over all of K
 
@@ -729,7 +735,7 @@ __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const Ep
 // straight from global memory (lane k range k0 + 16h .. +16).
 template <int FMT, int EPI, int MI, int NF>
 __device__ __forceinline__ void pf_tail32(f32x16 (&acc)[MI][NF], const GemmArgs& ga, const WeightArgs& W,
-                                          int e, int mb, int n0, int c, int h, int k0) {
+                                          int e, int row0, int n0, int c, int h, int k0) {
   BChunk<FMT, 64> bt[NF];  // C = 64: the lane's 16 k in two 8-k steps
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
@@ -739,7 +745,7 @@ __device__ __forceinline__ void pf_tail32(f32x16 (&acc)[MI][NF], const GemmArgs&
   uint4 a0[MI], a1[MI];
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    const uint16_t* p = a_row(ga, ga.sorted_ids[mb * (32 * MI) + i * 32 + c]) + k0 + 16 * h;
+    const uint16_t* p = a_row(ga, ga.sorted_ids[row0 + i * 32 + c]) + k0 + 16 * h;
     a0[i] = *reinterpret_cast<const uint4*>(p);
     a1[i] = *reinterpret_cast<const uint4*>(p + 8);
   }
@@ -753,10 +759,14 @@ __device__ __forceinline__ void pf_tail32(f32x16 (&acc)[MI][NF], const GemmArgs&
   pf_mfma<MI, NF>(acc, a1, b1);
 }
 
-template <int FMT, int EPI, int BM, int NF>
-__global__ void __launch_bounds__(256, 1) gemm_prefill_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
+template <int FMT, int EPI, int BM, int NF, int RS>
+__global__ void __launch_bounds__(256 * RS, 1) gemm_prefill_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
   using P = Pf<BM, NF>;
-  constexpr int MI = P::MI;
+  // RS = 2: eight waves, two per SIMD; waves w and w + 4 take the same
+  // columns and one half of the rows each (both dequantise the same codes),
+  // so one wave's dequant and LDS reads overlap the other's MFMAs.  Only the
+  // first four waves issue the DMA.
+  constexpr int MI = P::MI / RS;
   __shared__ __attribute__((aligned(16))) uint8_t smem[P::kLds];
   uint8_t* const scale_lds = smem + kPfStages * P::kStage;
 
@@ -764,7 +774,11 @@ __global__ void __launch_bounds__(256, 1) gemm_prefill_kernel(GemmArgs ga, Weigh
   if (!prefill_tile(ga, BM, mb, nt)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int c = lane & 31, h = lane >> 5;
-  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_u = wave_all & 3;            // column group, and DMA share
+  const int rpart = wave_all >> 2;            // row part (RS = 2)
+  const bool dma_wave = rpart == 0;
+  const int aoff = rpart * MI * 32 * 128;     // this wave's rows in an A stage
   const int K = ga.K, N = ga.N;
 
   // slot ids of the A rows this lane copies, requested before anything waits:
@@ -810,7 +824,7 @@ __global__ void __launch_bounds__(256, 1) gemm_prefill_kernel(GemmArgs ga, Weigh
   const uint32_t ring = lds_addr(smem);
   const uint32_t sc_lds = ring + kPfStages * P::kStage;
   const int nchunks = K / kPfBK;  // (K < 64: only the 32-wide tail, no LDS)
-  if (nchunks == 0) {
+  if (nchunks == 0 || !dma_wave) {
   } else if (FMT == FMT_NVFP4) {
     const int nb = rows * (K / 16);
     pf_dma_region(sc_lds, W.scales + ((size_t)e * N + nt0) * (K / 16), 0, nb, nb, nb, wave_u, lane);
@@ -827,7 +841,7 @@ __global__ void __launch_bounds__(256, 1) gemm_prefill_kernel(GemmArgs ga, Weigh
                   reinterpret_cast<const uint8_t*>(W.zeros) + ((size_t)e * ng * (N / 8) + nt0 / 8) * 4,
                   (size_t)N / 2, P::BN / 2, rows / 2, ng * P::BN / 2, wave_u, lane);
   }
-  if (nchunks > 0) {
+  if (nchunks > 0 && dma_wave) {
 #pragma unroll
     for (int s = 0; s < kPfStages; ++s)
       pf_issue<FMT, BM, NF>(ring + s * P::kStage, arow, brow, min(s, nchunks - 1), wave_u, N);
@@ -858,12 +872,12 @@ __global__ void __launch_bounds__(256, 1) gemm_prefill_kernel(GemmArgs ga, Weigh
     uint4 a0[MI], a1[MI];
     bf16x8 q0[NF], q1[NF];
     pf_read_b<FMT, EPI, NF>(b, smem + P::kABytes, scale_lds, rl, 0, h, K, W.group, P::BN);
-    pf_read_a<MI>(a0, smem, c, h, 0);
+    pf_read_a<MI>(a0, smem + aoff, c, h, 0);
 #pragma unroll
     for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
 
     for (int kc = 0; kc < nchunks; ++kc) {
-      const uint8_t* st = smem + (kc % kPfStages) * P::kStage;
+      const uint8_t* st = smem + (kc % kPfStages) * P::kStage + aoff;
       // steps 0..2: each overlaps the next step's A reads and dequant
       pf_read_a<MI>(a1, st, c, h, 1);
 #pragma unroll
@@ -882,12 +896,13 @@ __global__ void __launch_bounds__(256, 1) gemm_prefill_kernel(GemmArgs ga, Weigh
       // chunk kc, whose stage is refilled with chunk kc+4
       wait_vmcnt<2 * P::kIssue>();
       pf_barrier();
-      pf_issue<FMT, BM, NF>(ring + (kc % kPfStages) * P::kStage, arow, brow,
-                            min(kc + kPfStages, nchunks - 1), wave_u, N);
+      if (dma_wave)
+        pf_issue<FMT, BM, NF>(ring + (kc % kPfStages) * P::kStage, arow, brow,
+                              min(kc + kPfStages, nchunks - 1), wave_u, N);
       const uint8_t* nx = smem + ((kc + 1) % kPfStages) * P::kStage;
       pf_read_b<FMT, EPI, NF>(b, nx + P::kABytes, scale_lds, rl, min(kc + 1, nchunks - 1), h, K,
                               W.group, P::BN);
-      pf_read_a<MI>(a0, nx, c, h, 0);
+      pf_read_a<MI>(a0, nx + aoff, c, h, 0);
       pf_mfma<MI, NF>(acc, a1, q1);
 #pragma unroll
       for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
@@ -896,11 +911,12 @@ __global__ void __launch_bounds__(256, 1) gemm_prefill_kernel(GemmArgs ga, Weigh
   // no DMA may land in LDS after this workgroup is gone
   wait_vmcnt<0>();
 
-  if (K % kPfBK) pf_tail32<FMT, EPI, MI, NF>(acc, ga, W, e, mb, n0, c, h, nchunks * kPfBK);
+  const int row0 = mb * BM + rpart * MI * 32;
+  if (K % kPfBK) pf_tail32<FMT, EPI, MI, NF>(acc, ga, W, e, row0, n0, c, h, nchunks * kPfBK);
 
   if (n0 >= N) return;
   EpiArgs a = ea;
-  a.row0 = mb * BM;
+  a.row0 = row0;
   epilogue32<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane);
 }
 
@@ -1640,9 +1656,9 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
     ga.group_m = 4;  // measured flat between 1 and 16 at the gpt-oss-20b shape
     const dim3 grid((ga.n_mblocks * ga.n_ntiles + 7) / 8 * 8);
     if (block_m == 64)
-      gemm_prefill_kernel<FMT, EPI, 64, 2><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+      gemm_prefill_kernel<FMT, EPI, 64, 2, pf_rs<FMT>()><<<grid, dim3(256 * pf_rs<FMT>()), 0, st>>>(ga, W, ea);
     else
-      gemm_prefill_kernel<FMT, EPI, 128, 2><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+      gemm_prefill_kernel<FMT, EPI, 128, 2, pf_rs<FMT>()><<<grid, dim3(256 * pf_rs<FMT>()), 0, st>>>(ga, W, ea);
   }
   return hipGetLastError();
 }
