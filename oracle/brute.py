@@ -47,7 +47,8 @@ def weight(w, e: int, n: int, k: int, _cache={}) -> float:
     # gptq: storage is [K/8][N] words, zeros [K/G][N/8] words, scales [K/G][N]
     word = int(w.qweight[e, k // 8, n]) & 0xFFFFFFFF
     q = (word >> (4 * (k % 8))) & 0xF
-    g = k // w.group
+    g_idx = getattr(w, "g_idx", None)      # act-order: the row's own group
+    g = k // w.group if g_idx is None else int(g_idx[e, k])
     zword = int(w.zeros[e, g, n // 8]) & 0xFFFFFFFF
     z = (zword >> (4 * (n % 8))) & 0xF
     return (q - z) * float(w.scales[e, g, n])

@@ -22,13 +22,17 @@ Sources
   (mixed_gptq)", sections "Why GPT-OSS needs special handling" and
   "1. Quantize with 4-bit MoE experts").  Packing: 8 nibbles per int32,
   low nibble first; zeros packed along N; w = (q - z) * s with no +1
-  zero offset; identity g_idx.
+  zero offset.  g_idx gives the group of each row: k // G when absent
+  (identity), any map for weights quantised in activation order (the page
+  lists g_idx beside qweight, qzeros and scales; its meaning is GPTQ's).
 
 Pinned by tests/test_oracle_formats.py: the table equals the page's printed
 table and the closed form of e2m1; e4m3fn against torch's float8 decode for
 all 256 bytes; e8m0 against ldexp; GPTQ against hand-built words; group
 counts 2880/64 = 45 and 2688/16 = 168 (the "168 real + 8 padded scale
-groups" of the Nemotron page) via distinctive per-group scales.
+groups" of the Nemotron page) via distinctive per-group scales; act-order
+decode against the float weights it was quantised from (error within half a
+step of the row's own group) and against the group-sorted form.
 """
 from __future__ import annotations
 
@@ -128,6 +132,38 @@ def decode_gptq(qweight_e: np.ndarray, zeros_e: np.ndarray, scales_e: np.ndarray
     return np.ascontiguousarray(wt.T)
 
 
+def act_order_sort(qweight_e: np.ndarray, g_idx_e: np.ndarray, group: int):
+    """One act-order GPTQ expert with its rows in group order.
+
+    Returns (qweight_sorted int32 [K/8, N], perm int32 [K], ok).  perm is the
+    stable sort of the rows by g_idx (ascending k inside a group) and row j
+    of qweight_sorted is row perm[j] of qweight; the groups then sit in runs
+    of `group` rows, so the sorted weight decodes with the identity g_idx,
+    its column k of W multiplying input channel perm[k].  ok is False when
+    g_idx is not an act-order map (a value outside [0, K/G), or a group
+    without exactly `group` rows); perm is then the identity and qweight is
+    returned unchanged.
+    """
+    kq, n = qweight_e.shape
+    k = 8 * kq
+    g = np.asarray(g_idx_e, dtype=np.int64)
+    ngroups = k // group
+    ok = bool(g.shape == (k,) and g.min() >= 0 and g.max() < ngroups and
+              np.all(np.bincount(g, minlength=ngroups) == group))
+    if not ok:
+        return qweight_e.copy(), np.arange(k, dtype=np.int32), False
+    perm = np.argsort(g, kind="stable")
+    qw = qweight_e.view(np.uint32).astype(np.int64)
+    q = np.empty((k, n), dtype=np.int64)
+    for i in range(8):
+        q[i::8, :] = (qw >> (4 * i)) & 0xF
+    qs = q[perm, :]
+    out = np.zeros((kq, n), dtype=np.int64)
+    for i in range(8):
+        out |= qs[i::8, :] << (4 * i)
+    return out.astype(np.uint32).view(np.int32), perm.astype(np.int32), True
+
+
 def decode_expert(w, e: int) -> np.ndarray:
     """Decode expert e of a weight family (synthetic.Weights-like object)."""
     if w.fmt == "nvfp4":
@@ -135,5 +171,7 @@ def decode_expert(w, e: int) -> np.ndarray:
     if w.fmt == "mxfp4":
         return decode_mxfp4(w.qweight[e], w.scales[e], w.group)
     if w.fmt == "gptq":
-        return decode_gptq(w.qweight[e], w.zeros[e], w.scales[e], w.group)
+        g_idx = getattr(w, "g_idx", None)
+        return decode_gptq(w.qweight[e], w.zeros[e], w.scales[e], w.group,
+                           None if g_idx is None else g_idx[e])
     raise ValueError(w.fmt)

@@ -150,6 +150,34 @@ def quantize_gptq(w: np.ndarray, group: int = 64):
     return (qw.astype(np.uint32).view(np.int32), zz.astype(np.uint32).view(np.int32), s16)
 
 
+def quantize_gptq_act_order(w: np.ndarray, perm: np.ndarray, group: int = 64):
+    """INT4 GPTQ bytes quantised in activation order, for one expert.
+
+    perm is the order in which the input channels (columns of w [N, K]) are
+    quantised; channel perm[j] joins group j // G.  The columns are grouped in
+    that order, quantised as quantize_gptq does, and the rows of qweight are
+    put back in channel order.  Returns (qweight int32 [K/8, N], zeros int32
+    [K/G, N/8], scales fp16 [K/G, N], g_idx int32 [K]) with
+    g_idx[perm[j]] = j // G.
+    """
+    n, k = w.shape
+    perm = np.asarray(perm, dtype=np.int64)
+    qw_p, zz, s16 = quantize_gptq(np.ascontiguousarray(w[:, perm]), group)
+    # unpack the permuted rows, put row j back at channel perm[j], repack
+    qp = qw_p.view(np.uint32).astype(np.int64)
+    q_perm = np.empty((k, n), dtype=np.int64)
+    for i in range(8):
+        q_perm[i::8, :] = (qp >> (4 * i)) & 0xF
+    q = np.empty_like(q_perm)
+    q[perm, :] = q_perm
+    qw = np.zeros((k // 8, n), dtype=np.int64)
+    for i in range(8):
+        qw |= q[i::8, :] << (4 * i)
+    g_idx = np.empty((k,), dtype=np.int32)
+    g_idx[perm] = (np.arange(k) // group).astype(np.int32)
+    return qw.astype(np.uint32).view(np.int32), zz, s16, g_idx
+
+
 # --------------------------------------------------------------------------
 # Layer description
 # --------------------------------------------------------------------------
@@ -170,6 +198,7 @@ class Weights:
     zeros: np.ndarray | None
     global_scale: np.ndarray | None
     bias: np.ndarray | None          # bf16 bits [E, N] or None
+    g_idx: np.ndarray | None = None  # GPTQ act-order: int32 [E, K] group of each row, or None
 
 
 @dataclasses.dataclass
@@ -206,13 +235,16 @@ class Layer:
         return dataclasses.replace(self, logits=self.logits[:T], x=self.x[:T])
 
 
-def _make_weights(ss, fmt, group, E, N, K, bias, threads=8):
+def _make_weights(ss, fmt, group, E, N, K, bias, threads=8, act_order=False):
     """Draw E experts of W[N, K] ~ N(0, 0.02), quantise each, then the bias.
 
     Expert e draws from its own child stream ss.spawn(E+1)[e] (the last child
     draws the bias), so experts can be generated in parallel and the bytes do
-    not depend on the thread count.
+    not depend on the thread count.  act_order (GPTQ only): after W, the
+    expert's stream draws a uniform random channel order and the expert is
+    quantised in that order (quantize_gptq_act_order); W itself is unchanged.
     """
+    assert not act_order or fmt == "gptq"
     kids = ss.spawn(E + 1)
     if fmt in ("nvfp4", "mxfp4"):
         qweight = np.empty((E, N, K // 2), dtype=np.uint8)
@@ -223,11 +255,16 @@ def _make_weights(ss, fmt, group, E, N, K, bias, threads=8):
         scales = np.empty((E, K // group, N), dtype=np.float16)
         zeros = np.empty((E, K // group, N // 8), dtype=np.int32)
     gscale = np.empty((E,), dtype=np.float32) if fmt == "nvfp4" else None
+    g_idx = np.empty((E, K), dtype=np.int32) if act_order else None
 
     def one(e):
-        w = np.random.Generator(np.random.PCG64(kids[e])).standard_normal((N, K), dtype=np.float32)
+        rng = np.random.Generator(np.random.PCG64(kids[e]))
+        w = rng.standard_normal((N, K), dtype=np.float32)
         w *= np.float32(0.02)
-        if fmt == "nvfp4":
+        if act_order:
+            qweight[e], zeros[e], scales[e], g_idx[e] = quantize_gptq_act_order(
+                w, rng.permutation(K), group)
+        elif fmt == "nvfp4":
             qweight[e], scales[e], gscale[e] = quantize_nvfp4(w, group)
         elif fmt == "mxfp4":
             qweight[e], scales[e] = quantize_mxfp4(w, group)
@@ -245,19 +282,20 @@ def _make_weights(ss, fmt, group, E, N, K, bias, threads=8):
         rb = np.random.Generator(np.random.PCG64(kids[E]))
         b = f32_to_bf16_bits(rb.standard_normal((E, N), dtype=np.float32) * np.float32(0.02))
     return Weights(fmt=fmt, group=group, N=N, K=K, qweight=qweight, scales=scales,
-                   zeros=zeros, global_scale=gscale, bias=b)
+                   zeros=zeros, global_scale=gscale, bias=b, g_idx=g_idx)
 
 
-def make_weights(fmt, *, E, N, K, group=None, bias=True, seed=0, threads=8) -> Weights:
+def make_weights(fmt, *, E, N, K, group=None, bias=True, seed=0, threads=8,
+                 act_order=False) -> Weights:
     """One family of synthetic 4-bit expert weights [E][N][K] (same recipe as make_layer)."""
     return _make_weights(np.random.SeedSequence(seed), fmt, group or DEFAULT_GROUP[fmt], E, N, K,
-                         bias, threads)
+                         bias, threads, act_order)
 
 
 def make_layer(*, E, top_k, H, I, fmt, act="swigluoai", route="softmax", T,
                seed, group=None, bias=True, skew_std=0.0, router_bias_std=0.0,
                renormalize=True, mul_topk_weights=True, alpha=1.702, beta=1.0,
-               limit=7.0, x_std=1.0, threads=8) -> Layer:
+               limit=7.0, x_std=1.0, threads=8, act_order=False) -> Layer:
     """Draw one synthetic MoE layer (see the module docstring for the recipe)."""
     group = group or DEFAULT_GROUP[fmt]
     ss_router, ss_x, ss_w13, ss_w2 = np.random.SeedSequence(seed).spawn(4)
@@ -272,8 +310,8 @@ def make_layer(*, E, top_k, H, I, fmt, act="swigluoai", route="softmax", T,
     rx = np.random.Generator(np.random.PCG64(ss_x))
     x = f32_to_bf16_bits(rx.standard_normal((T, H), dtype=np.float32) * np.float32(x_std))
     n1 = 2 * I if act == "swigluoai" else I
-    w13 = _make_weights(ss_w13, fmt, group, E, n1, H, bias, threads)
-    w2 = _make_weights(ss_w2, fmt, group, E, H, I, bias, threads)
+    w13 = _make_weights(ss_w13, fmt, group, E, n1, H, bias, threads, act_order)
+    w2 = _make_weights(ss_w2, fmt, group, E, H, I, bias, threads, act_order)
     return Layer(E=E, top_k=top_k, H=H, I=I, act=act, route=route,
                  renormalize=renormalize, mul_topk_weights=mul_topk_weights,
                  alpha=alpha, beta=beta, limit=limit, logits=logits,

@@ -134,3 +134,74 @@ def test_group_counts_from_pages(row):
         W = F.decode_gptq(qw, zw, s, G)
         for g in range(ngroups):
             assert np.all(W[:, g * G:(g + 1) * G] == 2.0 ** (g % 5))
+
+
+# ------------------------------------------------------------- act-order --
+
+def _act_order_expert(N=24, K=256, G=32, seed=3):
+    import synthetic as S
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    perm = rng.permutation(K)
+    qw, zz, s16, g_idx = S.quantize_gptq_act_order(w, perm, G)
+    return w, perm, qw, zz, s16, g_idx
+
+
+def test_gptq_act_order_decode_equals_group_ordered_quantisation():
+    """Quantising in activation order is quantising the column-permuted matrix.
+
+    Channel perm[j] belongs to group j // G, so column j of the decode of
+    quantize_gptq(W[:, perm]) (identity groups, pinned above by hand-built
+    words) must equal column perm[j] of the act-order decode, exactly.  A
+    decode that used k // G instead of g_idx[k] fails this."""
+    import synthetic as S
+    G = 32
+    w, perm, qw, zz, s16, g_idx = _act_order_expert(G=G)
+    W_act = F.decode_gptq(qw, zz, s16, G, g_idx)
+    qw_p, zz_p, s_p = S.quantize_gptq(np.ascontiguousarray(w[:, perm]), G)
+    W_grp = F.decode_gptq(qw_p, zz_p, s_p, G)
+    np.testing.assert_array_equal(W_act[:, perm], W_grp)
+    assert not np.array_equal(F.decode_gptq(qw, zz, s16, G), W_act)   # g_idx matters here
+
+
+def test_gptq_act_order_decode_is_within_one_step_of_the_float_weight():
+    """Round-to-nearest quantisation keeps each decoded weight within one step
+    (the scale of the element's own group, with the clip at 15 allowed for)
+    of the float weight it came from; decoding with the identity groups does
+    not."""
+    G = 32
+    w, perm, qw, zz, s16, g_idx = _act_order_expert(G=G)
+    s_own = s16.astype(np.float64)[g_idx, :].T          # [N, K]: scale of (n, k)'s group
+    err = np.abs(F.decode_gptq(qw, zz, s16, G, g_idx) - w)
+    assert np.all(err <= s_own * 1.01)
+    err_id = np.abs(F.decode_gptq(qw, zz, s16, G) - w)
+    assert np.any(err_id > s_own * 1.01)
+
+
+def test_act_order_sort_decodes_to_the_permuted_weight():
+    """Rows in group order decode (identity groups) to the act-order weight's
+    columns taken in perm order; perm is the stable sort of g_idx."""
+    G = 32
+    w, perm0, qw, zz, s16, g_idx = _act_order_expert(G=G, seed=8)
+    qs, perm, ok = F.act_order_sort(qw, g_idx, G)
+    assert ok
+    assert np.all(np.diff(g_idx[perm]) >= 0)                       # groups ascending
+    for g in range(256 // G):                                     # ascending k inside a group
+        run = perm[g * G:(g + 1) * G]
+        assert np.all(np.diff(run) > 0) and np.all(g_idx[run] == g)
+    np.testing.assert_array_equal(F.decode_gptq(qs, zz, s16, G),
+                                  F.decode_gptq(qw, zz, s16, G, g_idx)[:, perm])
+
+
+def test_act_order_sort_rejects_maps_that_are_not_act_order():
+    G = 32
+    _, _, qw, zz, s16, g_idx = _act_order_expert(G=G)
+    uneven = g_idx.copy()
+    uneven[np.flatnonzero(uneven == 0)[0]] = 1                    # group 0 short, group 1 long
+    out_of_range = g_idx.copy()
+    out_of_range[5] = 256 // G
+    for bad in (uneven, out_of_range):
+        qs, perm, ok = F.act_order_sort(qw, bad, G)
+        assert not ok
+        np.testing.assert_array_equal(perm, np.arange(256))
+        np.testing.assert_array_equal(qs, qw)

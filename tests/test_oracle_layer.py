@@ -249,3 +249,17 @@ def test_forward_tokens_matches_forward():
     full = O.forward(L)["out"]
     rows = [0, 3, 8]
     np.testing.assert_allclose(O.forward_tokens(L, rows), full[rows], rtol=1e-12, atol=1e-15)
+
+
+def test_act_order_layer_matches_brute_force():
+    """GPTQ weights quantised in activation order (random channel order per
+    expert, both families): the vectorised layer equals the pure-Python
+    brute force, which reads each element's group from g_idx by hand."""
+    L = _tiny_layer("gptq", E=3, k=2, H=128, I=64, T=4, group=32, act_order=True, x_std=2.0)
+    assert L.w13.g_idx is not None and L.w2.g_idx is not None
+    assert not np.array_equal(L.w13.g_idx[0], np.arange(128) // 32)
+    ref = O.forward(L, block_m=16)
+    out = np.array(brute.forward(L, ref["topk_ids"], ref["topk_w"]))
+    np.testing.assert_allclose(ref["out"], out, rtol=1e-10, atol=1e-12)
+    plain = dataclasses.replace(L, w13=dataclasses.replace(L.w13, g_idx=None))
+    assert not np.allclose(O.forward(plain, block_m=16)["out"], ref["out"], rtol=1e-3)
