@@ -33,6 +33,7 @@ class _Wq(ctypes.Structure):
         ("global_scale", ctypes.c_void_p),
         ("g_idx", ctypes.c_void_p),
         ("bias", ctypes.c_void_p),
+        ("k_perm", ctypes.c_void_p),
     ]
 
 
@@ -76,6 +77,10 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.argtypes = [vp, vp, i, i, i, i, i, i, vp, i, wq, wq, i, f, f, f, i, vp, sz,
                                   vp, vp]
         L.moe_forward.restype = i
+        L.moe_gptq_act_order_sort.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, vp]
+        L.moe_gptq_act_order_sort.restype = i
+        L.moe_permute_slots.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
+        L.moe_permute_slots.restype = i
         _lib = L
     return _lib
 
@@ -121,6 +126,7 @@ class QuantWeights:
     zeros: torch.Tensor | None = None
     global_scale: torch.Tensor | None = None
     bias: torch.Tensor | None = None
+    k_perm: torch.Tensor | None = None     # GPTQ act-order, from moe_gptq_act_order_sort
 
     @classmethod
     def from_arrays(cls, fmt, group, N, K, qweight, scales, zeros=None, global_scale=None,
@@ -138,7 +144,8 @@ class QuantWeights:
 
     def struct(self) -> _Wq:
         return _Wq(FMT[self.fmt], self.group, _ptr(self.qweight), _ptr(self.scales),
-                   _ptr(self.zeros), _ptr(self.global_scale), None, _ptr(self.bias))
+                   _ptr(self.zeros), _ptr(self.global_scale), None, _ptr(self.bias),
+                   _ptr(self.k_perm))
 
     @property
     def E(self) -> int:
@@ -256,6 +263,45 @@ def moe_w4a16_gemm2(a: torch.Tensor, w2: QuantWeights, topk_w, mul_topk_weights:
                                  _ptr(topk_w), int(bool(mul_topk_weights)), _ptr(sorted_ids),
                                  _ptr(expert_ids), _ptr(num_post_pad), block_m, _ptr(out),
                                  _stream()), "moe_w4a16_gemm2")
+    return out
+
+
+def moe_gptq_act_order_sort(qweight: torch.Tensor, g_idx: torch.Tensor, group: int):
+    """Put act-order GPTQ rows in group order.
+
+    qweight int32 [E, K/8, N], g_idx int32 [E, K] -> (qweight_sorted int32
+    [E, K/8, N], k_perm int32 [E, K], status int32 [E]); status[e] != 0 marks
+    an expert whose g_idx is not an act-order map."""
+    _dev(qweight, torch.int32, "qweight")
+    _dev(g_idx, torch.int32, "g_idx")
+    E, kq, N = qweight.shape
+    K = 8 * kq
+    if tuple(g_idx.shape) != (E, K):
+        raise ValueError(f"g_idx shape {tuple(g_idx.shape)} != {(E, K)}")
+    out = torch.empty_like(qweight)
+    k_perm = torch.empty((E, K), dtype=torch.int32, device=qweight.device)
+    status = torch.empty((E,), dtype=torch.int32, device=qweight.device)
+    _check(lib().moe_gptq_act_order_sort(_ptr(qweight), _ptr(g_idx), E, K, N, group, _ptr(out),
+                                         _ptr(k_perm), _ptr(status), _stream()),
+           "moe_gptq_act_order_sort")
+    return out, k_perm, status
+
+
+def moe_permute_slots(src: torch.Tensor, top_k: int, k_perm: torch.Tensor,
+                      topk_ids: torch.Tensor, out=None):
+    """dst[f] = src[f // top_k][k_perm[topk_ids[f]]] for every flat slot f.
+
+    src bf16 [size_m, K]; topk_ids int32 [size_m*top_k]; out bf16
+    [size_m*top_k, K] (may be src itself when top_k is 1)."""
+    _dev(src, torch.bfloat16, "src")
+    _dev(k_perm, torch.int32, "k_perm")
+    _dev(topk_ids, torch.int32, "topk_ids")
+    size_m, K = src.shape
+    E = k_perm.shape[0]
+    if out is None:
+        out = torch.zeros((size_m * top_k, K), dtype=torch.bfloat16, device=src.device)
+    _check(lib().moe_permute_slots(_ptr(src), size_m, top_k, K, E, _ptr(k_perm), _ptr(topk_ids),
+                                   _ptr(out), _stream()), "moe_permute_slots")
     return out
 
 

@@ -21,11 +21,16 @@ extern "C" hipError_t moe_launch_gemm(int, int, int, int, const uint16_t*, int, 
                                       uint16_t*, int, hipStream_t);
 extern "C" hipError_t moe_launch_sum(const uint16_t*, const int32_t*, int, int, int, int,
                                      uint16_t*, hipStream_t);
+extern "C" hipError_t moe_launch_gptq_sort(const int32_t*, const int32_t*, int, int, int, int,
+                                           int32_t*, int32_t*, int32_t*, hipStream_t);
+extern "C" hipError_t moe_launch_permute_slots(const uint16_t*, int, int, int, int, const int32_t*,
+                                               const int32_t*, uint16_t*, hipStream_t);
 
 namespace {
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxTopK = 16;
+constexpr int kMaxPermK = 8192;  // act-order: K of a permuted family (LDS staging)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -36,7 +41,9 @@ size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Validate one weight family for logical [N][K] and build the kernel view.
-moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out) {
+// allow_perm: the caller gathers the GEMM input through w->k_perm itself.
+moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out,
+                           bool allow_perm = false) {
   if (w == nullptr || w->qweight == nullptr || w->scales == nullptr) return MOE_ERR_NULL;
   if (K <= 0 || N <= 0 || K % 32 != 0 || N % 16 != 0) return MOE_ERR_SHAPE;
   switch (w->fmt) {
@@ -53,10 +60,16 @@ moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out
       if (K % w->group_size != 0) return MOE_ERR_SHAPE;
       if (w->zeros == nullptr) return MOE_ERR_NULL;
       if (w->g_idx != nullptr) return MOE_ERR_UNSUPPORTED;
+      if (w->k_perm != nullptr) {
+        if (!allow_perm) return MOE_ERR_UNSUPPORTED;
+        if (K > kMaxPermK) return MOE_ERR_SHAPE;
+        if (!aligned16(w->k_perm)) return MOE_ERR_ALIGN;
+      }
       break;
     default:
       return MOE_ERR_UNSUPPORTED;
   }
+  if (w->fmt != MOE_W_INT4_GPTQ && w->k_perm != nullptr) return MOE_ERR_UNSUPPORTED;
   if (!aligned16(w->qweight) || !aligned16(w->scales)) return MOE_ERR_ALIGN;
   if (w->fmt == MOE_W_INT4_GPTQ && !aligned16(w->zeros)) return MOE_ERR_ALIGN;
   if (w->bias != nullptr && (reinterpret_cast<uintptr_t>(w->bias) & 1u)) return MOE_ERR_ALIGN;
@@ -237,6 +250,35 @@ moe_status_t moe_w4a16_gemm2(const uint16_t* a, int size_m, int K, int N, int E,
                                     static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_gptq_act_order_sort(const int32_t* qweight, const int32_t* g_idx, int E, int K,
+                                     int N, int group_size, int32_t* qweight_sorted,
+                                     int32_t* k_perm, int32_t* status, moe_stream_t stream) {
+  if (E <= 0 || E > kMaxE || K <= 0 || N <= 0 || K > kMaxPermK) return MOE_ERR_SHAPE;
+  if (group_size != 32 && group_size != 64 && group_size != 128) return MOE_ERR_UNSUPPORTED;
+  if (K % group_size != 0) return MOE_ERR_SHAPE;
+  if (qweight == nullptr || g_idx == nullptr || qweight_sorted == nullptr || k_perm == nullptr ||
+      status == nullptr)
+    return MOE_ERR_NULL;
+  if (qweight_sorted == qweight) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe_launch_gptq_sort(qweight, g_idx, E, K, N, group_size, qweight_sorted,
+                                         k_perm, status, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_permute_slots(const uint16_t* src, int size_m, int top_k, int K, int E,
+                               const int32_t* k_perm, const int32_t* topk_ids, uint16_t* dst,
+                               moe_stream_t stream) {
+  if (size_m < 0 || top_k < 1 || E <= 0 || E > kMaxE || K <= 0 || K % 8 != 0 || K > kMaxPermK)
+    return MOE_ERR_SHAPE;
+  if ((long long)size_m * top_k >= (1LL << 24)) return MOE_ERR_SHAPE;
+  if (size_m == 0) return MOE_OK;
+  if (src == nullptr || k_perm == nullptr || topk_ids == nullptr || dst == nullptr)
+    return MOE_ERR_NULL;
+  if (dst == src && top_k != 1) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(src) || !aligned16(dst) || !aligned16(k_perm)) return MOE_ERR_ALIGN;
+  return hip_status(moe_launch_permute_slots(src, size_m * top_k, top_k, K, E, k_perm, topk_ids,
+                                             dst, static_cast<hipStream_t>(stream)));
+}
+
 int moe_forward_block_m(int T, int top_k, int E) {
   if (T <= 0 || top_k <= 0 || E <= 0) return 16;
   return pick_block_m(T, top_k, E);
@@ -261,9 +303,9 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, i
   if (epi != moe::EPI_SWIGLU && epi != moe::EPI_RELU2) return MOE_ERR_UNSUPPORTED;
   const int n1 = (epi == moe::EPI_SWIGLU) ? 2 * inter : inter;
   moe::WeightArgs W13, W2;
-  moe_status_t st = check_weights(w13, n1, hidden, &W13);
+  moe_status_t st = check_weights(w13, n1, hidden, &W13, true);
   if (st != MOE_OK) return st;
-  st = check_weights(w2, hidden, inter, &W2);
+  st = check_weights(w2, hidden, inter, &W2, true);
   if (st != MOE_OK) return st;
   if (epi == moe::EPI_SWIGLU && n1 % 32 != 0) return MOE_ERR_SHAPE;
   if (mul_topk_weights < 0 || mul_topk_weights > 2) return MOE_ERR_UNSUPPORTED;
@@ -292,10 +334,23 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, i
   hipError_t e = moe_launch_route_align(logits, T, E, top_k, (int)kind, expert_bias,
                                         renormalize ? 1 : 0, ids, tw, block_m, cap, sorted, eids,
                                         npp, s);
+  // Act-order families: GEMM1 reads one gathered input row per slot from the
+  // y buffer (free until GEMM2), in the top_k = 1 view; GEMM2's input rows are
+  // permuted in place.
+  const uint16_t* g1_in = x;
+  int g1_topk = top_k;
+  if (e == hipSuccess && w13->k_perm != nullptr) {
+    e = moe_launch_permute_slots(x, n, top_k, hidden, E, w13->k_perm, ids, yb, s);
+    g1_in = yb;
+    g1_topk = 1;
+  }
   // routing weight on GEMM2's output rows (mode 1) or GEMM1's input rows (mode 2)
   if (e == hipSuccess)
-    e = moe_launch_gemm((int)w13->fmt, epi, block_m, cap, x, top_k, n, hidden, n1, E, &W13, sorted, eids,
-                        npp, tw, mul_topk_weights == 2 ? 1 : 0, alpha, beta, limit, actb, inter, s);
+    e = moe_launch_gemm((int)w13->fmt, epi, block_m, cap, g1_in, g1_topk, n, hidden, n1, E, &W13,
+                        sorted, eids, npp, tw, mul_topk_weights == 2 ? 1 : 0, alpha, beta, limit,
+                        actb, inter, s);
+  if (e == hipSuccess && w2->k_perm != nullptr)
+    e = moe_launch_permute_slots(actb, n, 1, inter, E, w2->k_perm, ids, actb, s);
   if (e == hipSuccess)
     e = moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, actb, 1, n, inter, hidden, E, &W2,
                         sorted, eids, npp, tw, mul_topk_weights == 1 ? 1 : 0, 0.f, 0.f, 0.f, yb,

@@ -101,8 +101,16 @@ typedef struct {
                                  GPTQ: fp16 [E][K/G][N] */
   const void* zeros;          /* GPTQ: int32 [E][K/G][N/8], nibble i holds n%8 == i. Else NULL */
   const float* global_scale;  /* NVFP4: fp32 [E]. Else NULL */
-  const int32_t* g_idx;       /* GPTQ act-order map; must be NULL (identity) */
+  const int32_t* g_idx;       /* GPTQ group of each row, int32 [E][K]; the GEMMs take only NULL
+                                 (group = k / group_size): act-order weights are first put
+                                 in group order by moe_gptq_act_order_sort */
   const uint16_t* bias;       /* bf16 [E][N], or NULL for no bias */
+  const int32_t* k_perm;      /* GPTQ act-order: NULL, or int32 [E][K] from moe_gptq_act_order_sort
+                                 (row k of the stored weight multiplies input channel
+                                 k_perm[e][k]; 16-byte aligned, K <= 8192).  Only moe_forward
+                                 accepts it (it gathers the GEMM inputs through it); the
+                                 single GEMM calls return MOE_ERR_UNSUPPORTED: gather with
+                                 moe_permute_slots and call them in the top_k = 1 view. */
 } moe_wq_t;
 
 /* Length of sorted_ids for T tokens: T*top_k + min(E, T*top_k)*(block_m-1),
@@ -179,6 +187,43 @@ moe_status_t moe_w4a16_gemm2(const uint16_t* a, int size_m, int K, int N, int E,
                              const int32_t* num_post_pad, int block_m, uint16_t* y,
                              moe_stream_t stream);
 
+/* GPTQ act-order preparation, run once when the weights are loaded.  A GPTQ
+ * checkpoint quantised in activation order stores its rows in input-channel
+ * order with the group of each row in g_idx (the per-expert qweight / qzeros /
+ * scales / g_idx tensors of the OneCompression "GPT-OSS (mixed_gptq)" page,
+ * section 1); the dequantised weight is w[k][n] = (q[k][n] - z[g_idx[k]][n]) *
+ * s[g_idx[k]][n].  Per expert e this computes
+ *   k_perm[e]          the rows sorted by group, ascending k within a group
+ *   qweight_sorted[e]  row j = row k_perm[e][j] of qweight[e] (same packing)
+ *   status[e]          0, or 1 when g_idx[e] is not an act-order map (a value
+ *                      outside [0, K/G) or a group without exactly G rows);
+ *                      k_perm[e] is then the identity and the expert must not
+ *                      be used with k_perm.
+ * With status 0 everywhere, {qweight_sorted, the same scales and zeros,
+ * g_idx = NULL, k_perm} describes the same weights as {qweight, g_idx}.
+ *   qweight         int32 [E][K/8][N] (the moe_wq_t GPTQ packing)
+ *   g_idx           int32 [E][K]
+ *   qweight_sorted  out int32 [E][K/8][N]; must not overlap qweight
+ *   k_perm          out int32 [E][K];  status  out int32 [E]
+ * group_size in {32, 64, 128}, K a multiple of it, K <= 8192, E <= 1024.
+ * The statuses are written on the device: read them after the stream. */
+moe_status_t moe_gptq_act_order_sort(const int32_t* qweight, const int32_t* g_idx, int E, int K,
+                                     int N, int group_size, int32_t* qweight_sorted,
+                                     int32_t* k_perm, int32_t* status, moe_stream_t stream);
+
+/* Gather of GEMM input rows through an act-order permutation, one row per
+ * flat slot f < size_m*top_k, permuted by the slot's own expert:
+ *   dst[f][k] = src[f / top_k][k_perm[e][k]],  e = topk_ids[f]
+ * Rows of slots whose expert is outside [0, E) are left untouched (moe_align
+ * gives them no block).  k_perm values outside [0, K) read channel K-1.
+ *   src  bf16 [size_m][K];  dst  bf16 [size_m*top_k][K]
+ * dst may equal src when top_k is 1 (each row is read whole before it is
+ * written); other overlaps are not allowed.  K a multiple of 8, K <= 8192;
+ * src, dst and k_perm 16-byte aligned. */
+moe_status_t moe_permute_slots(const uint16_t* src, int size_m, int top_k, int K, int E,
+                               const int32_t* k_perm, const int32_t* topk_ids, uint16_t* dst,
+                               moe_stream_t stream);
+
 /* The block_m moe_forward uses for T tokens (the smallest of 16/32/64/128
  * that covers the average number of slots per expert, T*top_k/E); callers
  * that run the steps one by one can use it to get the same tiling. */
@@ -194,6 +239,9 @@ size_t moe_forward_workspace_bytes(int T, int E, int top_k, int hidden, int inte
  *   logits     fp32 [T][E]
  *   w13        N = 2*inter (SWIGLUOAI) or inter (RELU2), K = hidden
  *   w2         N = hidden, K = inter
+ *   w13/w2 k_perm (act-order, optional): GEMM1 then reads one gathered
+ *              copy of x per slot (placed in the workspace's y region) and
+ *              GEMM2's input rows are permuted in place before it runs
  *   mul_topk_weights  0: routing weights not applied; 1: each GEMM2 output row
  *              times its own weight (mul_topk_weights=True on the pages); 2: each
  *              GEMM1 input row times its weight instead (apply_router_weight_on_input;

@@ -55,8 +55,9 @@ def test_capacity_and_workspace(L):
 FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 
-def _wq(fmt=0, group=16, qweight=FAKE, scales=FAKE, zeros=None, gs=FAKE, g_idx=None, bias=None):
-    return _Wq(fmt, group, qweight, scales, zeros, gs, g_idx, bias)
+def _wq(fmt=0, group=16, qweight=FAKE, scales=FAKE, zeros=None, gs=FAKE, g_idx=None, bias=None,
+        k_perm=None):
+    return _Wq(fmt, group, qweight, scales, zeros, gs, g_idx, bias, k_perm)
 
 
 def test_route_rejects(L):
@@ -90,6 +91,8 @@ def test_gemm1_rejects(L):
     assert _g1(L, _wq(fmt=1, group=16)) == UNSUP         # MXFP4 is group 32
     assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE), K=2880 + 32) == SHAPE   # K % group
     assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, g_idx=FAKE)) == UNSUP    # act-order
+    assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, k_perm=FAKE)) == UNSUP   # gather first
+    assert _g1(L, _wq(k_perm=FAKE)) == UNSUP             # act-order is a GPTQ form
     assert _g1(L, _wq(fmt=2, group=64)) == NULL          # zeros missing
     assert _g1(L, _wq(gs=None)) == NULL                  # NVFP4 global scale missing
     assert _g1(L, _wq(fmt=9)) == UNSUP
@@ -127,3 +130,28 @@ def test_forward_rejects(L):
     assert f(mul=2) == SHAPE                             # weight on the input needs top_k = 1
     assert f(mul=3) == UNSUP
     assert f(mul=2, k=1) == WS                           # accepted with top_k = 1 (then sizes)
+    g = dict(fmt=2, group=64, zeros=FAKE)
+    w13, w2 = _wq(k_perm=FAKE, **g), _wq(k_perm=FAKE, **g)
+    assert f() == WS                                     # act-order families are accepted
+    w13 = _wq(k_perm=FAKE + 4, **g)
+    assert f(ws=FAKE * 16, wsb=1 << 40) == ALIGN         # k_perm must be 16-byte aligned
+
+
+def test_act_order_entry_points_reject(L):
+    s = lambda **kw: L.moe_gptq_act_order_sort(kw.get("q", FAKE), kw.get("g", FAKE), kw.get("E", 4),
+                                               kw.get("K", 2880), 256, kw.get("G", 64),
+                                               kw.get("o", FAKE * 2), FAKE, FAKE, None)
+    assert s(G=16) == UNSUP
+    assert s(K=2880 + 32) == SHAPE                       # K % group
+    assert s(K=8192 + 128, G=128) == SHAPE               # K above the staging limit
+    assert s(E=0) == SHAPE
+    assert s(g=None) == NULL
+    assert s(o=FAKE) == UNSUP                            # in place is not allowed
+    p = lambda **kw: L.moe_permute_slots(kw.get("src", FAKE), kw.get("m", 8), kw.get("k", 4),
+                                         kw.get("K", 2880), 32, kw.get("perm", FAKE), FAKE,
+                                         kw.get("dst", FAKE * 2), None)
+    assert p(K=2884) == SHAPE
+    assert p(dst=FAKE) == UNSUP                          # in place needs top_k = 1
+    assert p(perm=FAKE + 4) == ALIGN
+    assert p(src=None) == NULL
+    assert p(m=0, src=None) == OK
