@@ -13,6 +13,11 @@ Weight copies are rotated between calls so that no call finds its weights in
 the 256 MB last-level cache left behind by the previous one.
 
 Prints ONE JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+
+--act-order adds a leg on the INT4-GPTQ g64 layer of the same shape: the layer
+with plain (group-ordered) weights against the same layer quantised in
+activation order (both families sorted at load time, inputs gathered per slot
+at run time), and the gather kernel alone; reported under "act_order".
 """
 from __future__ import annotations
 
@@ -87,6 +92,71 @@ def profiled_traffic():
         return None
 
 
+def act_order_leg(args, time_calls):
+    """GPTQ g64 layer (E=32, top-4, 2880/2880): plain vs act-order weights."""
+    import torch
+    import synthetic as S
+    import bit_weight_expert_amd as M
+
+    c = dict(S.CONFIGS[3])
+    c.pop("name")
+    c.pop("T")
+    ts = [int(t) for t in args.act_order_tokens.split(",") if t]
+    t0 = time.time()
+    Lp = S.make_layer(T=max(ts), seed=S.config_seed(3) + 1, **c)
+    La = S.make_layer(T=max(ts), seed=S.config_seed(3) + 1, act_order=True, **c)
+    log(f"act-order leg: generated the plain and act-order GPTQ layers in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda")
+
+    def up(w):
+        return M.QuantWeights.from_arrays(w.fmt, w.group, w.N, w.K, w.qweight, w.scales, w.zeros,
+                                          w.global_scale, w.bias)
+
+    def prep(w):
+        d = up(w)
+        qs, kp, st = M.moe_gptq_act_order_sort(d.qweight, torch.from_numpy(w.g_idx).to(dev),
+                                               w.group)
+        torch.cuda.synchronize()
+        assert not st.any().item()
+        d.qweight, d.k_perm = qs, kp
+        return d
+
+    fams = {"plain": (up(Lp.w13), up(Lp.w2)), "act_order": (prep(La.w13), prep(La.w2))}
+    x = torch.from_numpy(Lp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    logits = torch.from_numpy(Lp.logits).to(dev)
+    ws = torch.empty((M.moe_forward_workspace_bytes(max(ts), Lp.E, Lp.top_k, Lp.H, Lp.I),),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((max(ts), Lp.H), dtype=torch.bfloat16, device=dev)
+    rows = []
+    for T in ts:
+        r = {"T": T}
+        for name, (w13, w2) in fams.items():
+            def f(i, w13=w13, w2=w2):
+                M.moe_forward(x[:T], logits[:T], Lp.top_k, Lp.I, w13, w2, act=Lp.act,
+                              route=Lp.route, renormalize=Lp.renormalize, alpha=Lp.alpha,
+                              beta=Lp.beta, limit=Lp.limit, mul_topk_weights=Lp.mul_topk_weights,
+                              workspace=ws, out=out[:T])
+            r[f"{name}_us"] = time_calls(f, max(args.steps, 20), args.warmup) * 1e3
+        # the gather of GEMM1's input alone: x rows -> one permuted row per slot
+        ids = M.moe_route(logits[:T], Lp.top_k, Lp.route, None, Lp.renormalize)[0].reshape(-1)
+        kp = fams["act_order"][0].k_perm
+        xp = torch.empty((T * Lp.top_k, Lp.H), dtype=torch.bfloat16, device=dev)
+        g_ms = time_calls(lambda i: M.moe_permute_slots(x[:T], Lp.top_k, kp, ids, out=xp),
+                          max(args.steps, 20), args.warmup)
+        touched = len(set(ids.cpu().numpy().tolist()))
+        nb = T * Lp.H * 2 + T * Lp.top_k * Lp.H * 2 + touched * Lp.H * 4
+        r.update(gather_us=g_ms * 1e3, gather_alg_bytes=nb,
+                 gather_GBps=nb / (g_ms * 1e-3) / 1e9,
+                 gather_hbm_frac=nb / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 overhead_frac=r["act_order_us"] / r["plain_us"] - 1.0)
+        log(f"act-order T={T}: plain {r['plain_us']:.1f} us, act-order {r['act_order_us']:.1f} us "
+            f"(+{r['overhead_frac'] * 100:.1f}%), gather alone {r['gather_us']:.1f} us "
+            f"{r['gather_GBps']:.0f} GB/s")
+        rows.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+    return {"workload": "gpt-oss-20b-shaped MoE layer, INT4-GPTQ g64 (E=32, top_k=4, 2880/2880), "
+                        "plain vs activation-order weights", "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +168,9 @@ def main() -> int:
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay timings")
+    ap.add_argument("--act-order", action="store_true",
+                    help="also time the GPTQ layer with act-order weights (and its gather)")
+    ap.add_argument("--act-order-tokens", default="1,64,2048")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -240,6 +313,8 @@ def main() -> int:
                          f"dequant of every touched expert, both GEMMs, sum); {dt:.1f}s wall"}
         log(f"oracle: {n} tokens in {dt:.1f}s")
 
+    act_order = act_order_leg(args, time_calls) if args.act_order else None
+
     line = {
         "metric": "fused W4A16 MoE layer tokens/s + % HBM/MFMA roofline, E32 top4 h2880",
         "value": head["tokens_per_s"],
@@ -263,6 +338,7 @@ def main() -> int:
         "layer_roofline": {"bound": head["bound"], "frac": head["roofline_frac"],
                            "GBps": head["GBps"], "TFLOPs": head["TFLOPs"]},
         "cpu_baseline": cpu,
+        "act_order": act_order,
         "sweep": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in results[t].items()}
                   for t in sweep],
     }
