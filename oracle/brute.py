@@ -54,14 +54,63 @@ def weight(w, e: int, n: int, k: int, _cache={}) -> float:
     return (q - z) * float(w.scales[e, g, n])
 
 
+_E4M3_POS = None
+
+
+def _e4m3_nearest(v: float) -> float:
+    """Nearest finite e4m3 value by search over all codes (ties to the even
+    code), saturating at 448."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        _E4M3_POS = [(_e4m3(c), c) for c in range(0x7F)]      # 0 .. 448, codes 0x00 .. 0x7E
+    a = abs(v)
+    if a >= 448.0:
+        r = 448.0
+    else:
+        best = min(_E4M3_POS, key=lambda vc: (abs(a - vc[0]), vc[1] & 1))
+        r = best[0]
+    return -r if v < 0 else r
+
+
+def _bf16_nearest(v: float) -> float:
+    """Nearest bf16 value (8 significant bits, ties to even) of a normal float."""
+    if v == 0.0:
+        return 0.0
+    m, e = math.frexp(v)            # v = m * 2**e, 0.5 <= |m| < 1
+    s = abs(m) * 256.0
+    lo = math.floor(s)
+    d = s - lo
+    q = lo + 1 if (d > 0.5 or (d == 0.5 and lo % 2 == 1)) else lo
+    return math.copysign(q * 2.0 ** (e - 8), v)
+
+
+def _mxfp8(vals):
+    """MXFP8 value of a row, block by block of 32 (shared exponent
+    floor(log2 amax) - 8, elements rounded to e4m3)."""
+    out = []
+    for b0 in range(0, len(vals), 32):
+        blk = vals[b0:b0 + 32]
+        amax = max(abs(v) for v in blk)
+        if amax == 0.0:
+            out.extend([0.0] * len(blk))
+            continue
+        ex = math.frexp(amax)[1] - 1 - 8
+        ex = max(ex, -127)
+        out.extend(_e4m3_nearest(v / 2.0 ** ex) * 2.0 ** ex for v in blk)
+    return out
+
+
 def forward(layer, ids, tw):
     """out[t][h] for every token, given routing (ids[t][j], tw[t][j])."""
     L = layer
     T = L.x.shape[0]
     out = [[0.0] * L.H for _ in range(T)]
     on_input = getattr(L, "weight_on_input", False)   # routing weight scales the input row
+    mx = getattr(L, "act_fmt", "bf16") == "mxfp8"      # GEMM inputs at their MXFP8 values
     for t in range(T):
         xt = [_bf16(v) for v in L.x[t]]
+        if mx:
+            xt = _mxfp8(xt)
         for j in range(L.top_k):
             e = int(ids[t][j])
             if not (0 <= e < L.E):
@@ -84,6 +133,8 @@ def forward(layer, ids, tw):
                     a.append(g / (1.0 + math.exp(-L.alpha * g)) * (u + L.beta))
             else:
                 a = [max(v, 0.0) ** 2 for v in h]
+            if mx:
+                a = _mxfp8([_bf16_nearest(v) for v in a])
             for n in range(L.H):
                 acc = 0.0
                 for k in range(L.I):

@@ -164,6 +164,84 @@ def act_order_sort(qweight_e: np.ndarray, g_idx_e: np.ndarray, group: int):
     return out.astype(np.uint32).view(np.int32), perm.astype(np.int32), True
 
 
+# ---------------------------------------------------------------------------
+# MXFP8 activations (e4m3 elements, one e8m0 shared exponent per 32 along K)
+# ---------------------------------------------------------------------------
+#
+# The MXFP4 x MXFP8 variant of the layer ("gpt-oss-120b MXFP4 +
+# --enable-expert-parallel crashes", sections "Actual behavior" and "Why the
+# mxfp8 workaround is not a fix": the activation option switches the MoE to
+# MXFP8 activations).  The page names the format only; the encoding is the OCP
+# microscaling one: per block of 32 the shared exponent is
+# floor(log2(amax)) - 8 (8 = the exponent of e4m3's largest normal, 448 =
+# 1.75 * 2**8), the elements are value / 2**exponent rounded to the nearest
+# e4m3 value (ties to even), and magnitudes past 448 saturate to 448.
+# Readings: an all-zero block takes the smallest exponent (byte 0); the
+# exponent is clamped to the e8m0 range [-127, 127]; a block holding a NaN or
+# an infinity gets the NaN exponent 0xFF and NaN elements.
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """float64 -> e4m3fn byte: round to nearest, ties to even, saturating at
+    +-448; NaN -> 0x7F (sign kept)."""
+    v = np.asarray(v, dtype=np.float64)
+    sign = np.signbit(v).astype(np.uint8) << 7
+    a = np.abs(v)
+    fin = np.isfinite(a)
+    a0 = np.where(fin, a, 0.0)
+    # normal range: a = q * 2**(E-3) with q in [8, 16) after rounding
+    _, ex = np.frexp(np.where(a0 > 0, a0, 1.0))
+    E = np.maximum(ex.astype(np.int64) - 1, -6)          # below 2**-6: the subnormal step 2**-9
+    q = np.rint(np.ldexp(a0, -(E - 3))).astype(np.int64)  # exact scaling, then ties-to-even
+    up = q == 16
+    E = np.where(up, E + 1, E)
+    q = np.where(up, 8, q)
+    sub = q < 8                                           # only when E == -6: subnormal code q
+    mag = np.where(sub, q, ((E + 7) << 3) | (q - 8))
+    mag = np.minimum(mag, 0x7E)                           # 448 is the largest finite value
+    mag = np.where(np.isnan(a), 0x7F, np.where(np.isinf(a), 0x7E, mag))
+    return (mag.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def quantize_mxfp8(v: np.ndarray, block: int = 32):
+    """float64 [..., K] -> (codes uint8 [..., K], scales uint8 e8m0 [..., K/block])."""
+    v = np.asarray(v, dtype=np.float64)
+    k = v.shape[-1]
+    assert k % block == 0, k
+    blk = v.reshape(v.shape[:-1] + (k // block, block))
+    amax = np.max(np.abs(blk), axis=-1)
+    bad = ~np.isfinite(amax)
+    _, ex = np.frexp(np.where((amax > 0) & ~bad, amax, 1.0))
+    e = np.where((amax > 0) & ~bad, ex.astype(np.int64) - 1 - 8, -127)
+    e = np.clip(e, -127, 127)
+    codes = e4m3_encode(np.ldexp(blk, -e[..., None]))
+    codes = np.where(bad[..., None], np.uint8(0x7F), codes).astype(np.uint8)
+    scales = np.where(bad, 255, e + 127).astype(np.uint8)
+    return codes.reshape(v.shape), scales
+
+
+def dequantize_mxfp8(codes: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """(codes [..., K], e8m0 scales [..., K/block]) -> float64 [..., K], exactly."""
+    return E4M3FN_TABLE[codes] * np.repeat(E8M0_TABLE[scales], block, axis=-1)
+
+
+def mxfp8_round_trip(v: np.ndarray, block: int = 32) -> np.ndarray:
+    """The values an MXFP8 operand holds for float64 input v."""
+    return dequantize_mxfp8(*quantize_mxfp8(v, block), block)
+
+
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    """float64 -> the nearest bf16 value (ties to even), as float64, in one
+    rounding: 8 significant bits, exponent >= -126 (below that the subnormal
+    step 2**-133), past the largest finite bf16 -> infinity."""
+    v = np.asarray(v, dtype=np.float64)
+    _, ex = np.frexp(np.where(np.isfinite(v) & (v != 0), v, 1.0))
+    step = np.maximum(ex.astype(np.int64) - 8, -133)      # |v| in [2**(ex-1), 2**ex)
+    r = np.ldexp(np.rint(np.ldexp(v, -step)), step)
+    r = np.where(np.abs(r) > 3.3895313892515355e38, np.copysign(np.inf, v), r)
+    return np.where(np.isfinite(v), r, v)
+
+
 def decode_expert(w, e: int) -> np.ndarray:
     """Decode expert e of a weight family (synthetic.Weights-like object)."""
     if w.fmt == "nvfp4":

@@ -30,6 +30,9 @@ rounding):
           h = W13_e (w_slot x_t) + b13_e, and GEMM2 multiplies nothing.
   sum     out_t = sum_j y_{t,j} at the true hidden width (the op's output is
           the unpadded 2880, "gpt-oss-120b MXFP4 ... crashes", root cause).
+  mxfp8   (act_fmt = "mxfp8", the MXFP8-activation variant the same page
+          names) each GEMM takes its input at its MXFP8 value: x as given,
+          the activation after its bf16 rounding (formats.quantize_mxfp8).
 
 Readings where the pages are silent (each listed in the design notes):
   * swigluoai: g' = min(g, limit), u' = clamp(u, -limit, limit),
@@ -51,7 +54,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import bf16_to_f64, decode_expert
+from .formats import bf16_round, bf16_to_f64, decode_expert, mxfp8_round_trip
 
 # ---------------------------------------------------------------------------
 # routing
@@ -201,17 +204,19 @@ def _bias_f64(w, e):
 
 
 def gemm1(x_bits, size_m, top_k, w13, act, alpha, beta, limit,
-          sorted_ids, expert_ids, num_post_pad, block_m, topk_w_flat=None):
+          sorted_ids, expert_ids, num_post_pad, block_m, topk_w_flat=None, act_fmt="bf16"):
     """Grouped GEMM1 over aligned blocks.
 
     Row f of the result (flat slot f = t*top_k + j) is
     act(W13_e x_t + b13_e) with e the expert of f's block and t = f // top_k;
     with topk_w_flat given (routing weight on the input), the input row is
-    w_f x_t instead.
+    w_f x_t instead.  act_fmt "mxfp8": x_t is taken at its MXFP8 value.
     Returns (out float64 [size_m*top_k, N_out], covered bool [size_m*top_k]).
     """
     n_slots = size_m * top_k
     x = bf16_to_f64(x_bits)
+    if act_fmt == "mxfp8":
+        x = mxfp8_round_trip(x)
     re = slot_experts(sorted_ids, expert_ids, num_post_pad, block_m, n_slots)
     n_out = w13.N // 2 if act == "swigluoai" else w13.N
     out = np.zeros((n_slots, n_out), dtype=np.float64)
@@ -228,14 +233,18 @@ def gemm1(x_bits, size_m, top_k, w13, act, alpha, beta, limit,
 
 
 def gemm2(a_bits_or_f64, size_m, w2, topk_w_flat, mul_topk_weights,
-          sorted_ids, expert_ids, num_post_pad, block_m):
+          sorted_ids, expert_ids, num_post_pad, block_m, act_fmt="bf16"):
     """Grouped GEMM2 in the top_k = 1 view: row f = (W2_e a_f + b2_e) [* w_f].
 
-    a is bf16 bits (uint16) or float64 rows indexed by flat slot.
+    a is bf16 bits (uint16) or float64 rows indexed by flat slot.  act_fmt
+    "mxfp8": a_f is taken at the MXFP8 value of its bf16 rounding (the
+    activation is held in bf16 between the GEMMs).
     Returns (y float64 [size_m, N], covered bool [size_m]).
     """
     a = a_bits_or_f64
     a = bf16_to_f64(a) if a.dtype == np.uint16 else np.asarray(a, dtype=np.float64)
+    if act_fmt == "mxfp8":
+        a = mxfp8_round_trip(bf16_round(a))
     re = slot_experts(sorted_ids, expert_ids, num_post_pad, block_m, size_m)
     y = np.zeros((size_m, w2.N), dtype=np.float64)
     tw = np.asarray(topk_w_flat, dtype=np.float64).reshape(-1)
@@ -270,12 +279,13 @@ def forward(layer, block_m: int = 16, topk=None):
     T = L.x.shape[0]
     ids, w = route(L) if topk is None else topk
     on_input = getattr(L, "weight_on_input", False)
+    act_fmt = getattr(L, "act_fmt", "bf16")
     sorted_ids, expert_ids, npp = align(ids, L.E, block_m)
     act, _ = gemm1(L.x, T, L.top_k, L.w13, L.act, L.alpha, L.beta, L.limit,
                    sorted_ids, expert_ids, npp, block_m,
-                   topk_w_flat=w.reshape(-1) if on_input else None)
+                   topk_w_flat=w.reshape(-1) if on_input else None, act_fmt=act_fmt)
     y, _ = gemm2(act, T * L.top_k, L.w2, w.reshape(-1), L.mul_topk_weights and not on_input,
-                 sorted_ids, expert_ids, npp, block_m)
+                 sorted_ids, expert_ids, npp, block_m, act_fmt=act_fmt)
     out = moe_sum(y, ids, L.E)
     return dict(topk_ids=ids, topk_w=w, sorted_ids=sorted_ids, expert_ids=expert_ids,
                 num_post_pad=npp, act=act, y=y, out=out)
@@ -294,6 +304,7 @@ def forward_tokens(layer, tokens, topk=None):
     ids, w = route(L) if topk is None else topk
     tokens = list(tokens)
     x = bf16_to_f64(L.x)
+    mx = getattr(L, "act_fmt", "bf16") == "mxfp8"
     y = np.zeros((len(tokens), L.top_k, L.H), dtype=np.float64)
     by_expert = {}
     for i, t in enumerate(tokens):
@@ -307,8 +318,12 @@ def forward_tokens(layer, tokens, topk=None):
         on_input = getattr(L, "weight_on_input", False)
         for i, t, j in items:
             xin = x[t] * float(w[t, j]) if on_input else x[t]
+            if mx:
+                xin = mxfp8_round_trip(xin)
             h = W13 @ xin + _bias_f64(L.w13, e)
             a = activation(h, L.act, L.alpha, L.beta, L.limit)
+            if mx:
+                a = mxfp8_round_trip(bf16_round(a))
             yv = W2 @ a + _bias_f64(L.w2, e)
             if L.mul_topk_weights and not on_input:
                 yv = yv * float(w[t, j])

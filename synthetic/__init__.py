@@ -221,6 +221,7 @@ class Layer:
     w2: Weights
     seed: int
     weight_on_input: bool = False    # routing weight scales GEMM1's input (top_k = 1)
+    act_fmt: str = "bf16"            # "mxfp8": each GEMM takes its input at its MXFP8 value
 
     @property
     def T(self) -> int:

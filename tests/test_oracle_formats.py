@@ -205,3 +205,81 @@ def test_act_order_sort_rejects_maps_that_are_not_act_order():
         assert not ok
         np.testing.assert_array_equal(perm, np.arange(256))
         np.testing.assert_array_equal(qs, qw)
+
+
+# ------------------------------------------------------------------ MXFP8 --
+
+def test_e4m3_encode_matches_torch_in_range():
+    """Every finite e4m3 value, every midpoint between neighbours (ties go to
+    the even code) and random float32 values in [-448, 448] encode as torch's
+    float8_e4m3fn cast of the same float32 values does."""
+    vals = F.E4M3FN_TABLE[np.isfinite(F.E4M3FN_TABLE)]
+    pos = np.unique(vals[vals >= 0])
+    mids = (pos[1:] + pos[:-1]) / 2
+    rnd = np.random.default_rng(4).uniform(-448, 448, 20000)
+    x = np.concatenate([pos, -pos, mids, -mids, rnd, rnd * 1e-3]).astype(np.float32)
+    got = F.e4m3_encode(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, ref)
+    # the tie cases really are ties: each midpoint lands on an even code
+    assert np.all(F.e4m3_encode(mids) % 2 == 0)
+
+
+def test_e4m3_encode_saturates_and_keeps_nan():
+    big = np.array([448.0, 460.0, 464.0, 500.0, 511.9, 1e6, np.inf])
+    assert np.all(F.e4m3_encode(big) == 0x7E)
+    assert np.all(F.e4m3_encode(-big) == 0xFE)
+    assert F.e4m3_encode(np.array([np.nan]))[0] & 0x7F == 0x7F
+
+
+def test_mxfp8_block_rules():
+    """Shared exponent floor(log2 amax) - 8 puts each block's largest element
+    in e4m3's top binade [256, 512); every element is within half an e4m3 step
+    of its value (saturated ones: within 64 units); zero blocks are zero;
+    quantising the dequantised values gives the same bytes back."""
+    rng = np.random.default_rng(9)
+    v = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-20, 20, (64, 1)))
+    v[3, 32:64] = 0.0
+    codes, scales = F.quantize_mxfp8(v)
+    blk = v.reshape(64, 8, 32)
+    amax = np.abs(blk).max(-1)
+    unit = F.E8M0_TABLE[scales]
+    nz = amax > 0
+    assert np.all((amax[nz] / unit[nz] >= 256) & (amax[nz] / unit[nz] < 512))
+    assert scales[3, 1] == 0 and not codes[3, 32:64].any()
+    deq = F.dequantize_mxfp8(codes, scales)
+    s = np.abs(v) / np.repeat(unit, 32, axis=1)                  # element in units of the scale
+    _, ex = np.frexp(np.where(s > 0, s, 1.0))
+    half_step = np.ldexp(1.0, np.maximum(ex - 1, -6) - 4)       # half of 2**(E-3)
+    err = np.abs(deq - v) / np.repeat(unit, 32, axis=1)
+    assert np.all(np.where(s < 448, err <= half_step, err <= 64))
+    c2, s2 = F.quantize_mxfp8(deq)
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(s2, scales)
+
+
+def test_mxfp8_hand_examples():
+    one = np.zeros(32); one[0] = 1.0                # amax 1 -> exponent -8, 1 = 256 * 2**-8
+    c, s = F.quantize_mxfp8(one)
+    assert s[0] == 127 - 8 and c[0] == 0x78 and not c[1:].any()
+    top = np.zeros(32); top[5] = -448.0; top[6] = 3.0   # amax 448 -> exponent 0, values kept
+    c, s = F.quantize_mxfp8(top)
+    assert s[0] == 127 and c[5] == 0xFE and F.E4M3FN_TABLE[c[6]] == 3.0
+    tiny = np.full(32, 2.0 ** -134)                  # exponent clamped at -127: e4m3 subnormal 2**-7
+    c, s = F.quantize_mxfp8(tiny)
+    assert s[0] == 0 and np.all(c == 0x04)
+    c, s = F.quantize_mxfp8(np.full(32, 2.0 ** -140))  # below half the smallest subnormal: zero
+    assert s[0] == 0 and not c.any()
+
+
+def test_bf16_round_is_one_rounding():
+    """Nearest bf16 in one step: agrees with torch's cast on float32 inputs
+    (no double rounding possible), and picks the nearer neighbour where a
+    float64 value sits just below a bf16 midpoint."""
+    x = (np.random.default_rng(5).standard_normal(50000) * 10.0).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(F.bf16_round(x.astype(np.float64)), ref)
+    mid = 1.0 + 2.0 ** -8                            # midpoint of 1 and 1 + 2**-7
+    assert F.bf16_round(np.array([mid - 2.0 ** -40]))[0] == 1.0
+    assert F.bf16_round(np.array([mid]))[0] == 1.0   # tie -> even
+    assert F.bf16_round(np.array([mid + 2.0 ** -40]))[0] == 1.0 + 2.0 ** -7

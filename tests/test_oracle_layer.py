@@ -263,3 +263,19 @@ def test_act_order_layer_matches_brute_force():
     np.testing.assert_allclose(ref["out"], out, rtol=1e-10, atol=1e-12)
     plain = dataclasses.replace(L, w13=dataclasses.replace(L.w13, g_idx=None))
     assert not np.allclose(O.forward(plain, block_m=16)["out"], ref["out"], rtol=1e-3)
+
+
+def test_mxfp8_layer_matches_brute_force_and_differs_from_bf16():
+    """MXFP8 activations: the vectorised layer equals the pure-Python brute
+    force (its e4m3 rounding a search over all codes); the result is close to
+    the bf16-activation layer (e4m3 keeps 4 significant bits) but not equal."""
+    L = dataclasses.replace(_tiny_layer("mxfp4", E=3, k=2, H=64, I=64, T=4, x_std=2.0),
+                            act_fmt="mxfp8")
+    ref = O.forward(L, block_m=16)
+    out = np.array(brute.forward(L, ref["topk_ids"], ref["topk_w"]))
+    np.testing.assert_allclose(ref["out"], out, rtol=1e-10, atol=1e-12)
+    b16 = O.forward(dataclasses.replace(L, act_fmt="bf16"), block_m=16)["out"]
+    rel = O.row_rel_err(ref["out"], b16)
+    assert np.all(rel < 0.1) and np.all(rel > 1e-4)
+    tok = O.forward_tokens(L, [0, 3])
+    np.testing.assert_allclose(tok, ref["out"][[0, 3]], rtol=1e-12, atol=1e-12)
