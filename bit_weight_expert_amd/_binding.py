@@ -81,6 +81,17 @@ def lib() -> ctypes.CDLL:
         L.moe_gptq_act_order_sort.restype = i
         L.moe_permute_slots.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
         L.moe_permute_slots.restype = i
+        L.moe_mxfp8_quantize.argtypes = [vp, i, i, vp, vp, vp, vp]
+        L.moe_mxfp8_quantize.restype = i
+        L.moe_mx_gemm1.argtypes = [vp, vp, i, i, i, i, i, wq, i, f, f, f, vp, vp, vp, i, vp, vp]
+        L.moe_mx_gemm1.restype = i
+        L.moe_mx_gemm2.argtypes = [vp, vp, i, i, i, i, wq, vp, i, vp, vp, vp, i, vp, vp]
+        L.moe_mx_gemm2.restype = i
+        L.moe_forward_mxfp8_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.moe_forward_mxfp8_workspace_bytes.restype = sz
+        L.moe_forward_mxfp8.argtypes = [vp, vp, i, i, i, i, i, i, vp, i, wq, wq, i, f, f, f, i, vp,
+                                        sz, vp, vp]
+        L.moe_forward_mxfp8.restype = i
         _lib = L
     return _lib
 
@@ -302,6 +313,92 @@ def moe_permute_slots(src: torch.Tensor, top_k: int, k_perm: torch.Tensor,
         out = torch.zeros((size_m * top_k, K), dtype=torch.bfloat16, device=src.device)
     _check(lib().moe_permute_slots(_ptr(src), size_m, top_k, K, E, _ptr(k_perm), _ptr(topk_ids),
                                    _ptr(out), _stream()), "moe_permute_slots")
+    return out
+
+
+def mxfp8_lda(K: int) -> int:
+    """Row stride of MXFP8 codes: K rounded up to 128."""
+    return (K + 127) // 128 * 128
+
+
+def mxfp8_lds(K: int) -> int:
+    """Row stride of MXFP8 scales: K/32 rounded up to 16."""
+    return (K // 32 + 15) // 16 * 16
+
+
+def moe_mxfp8_quantize(x: torch.Tensor, codes=True, dequant=False):
+    """x bf16 [rows, K] -> (codes uint8 [rows, lda], scales uint8 [rows, lds]) and/or the
+    dequantised bf16 [rows, K]; returns (codes, scales, dequant) with None for what was
+    not asked for."""
+    _dev(x, torch.bfloat16, "x")
+    rows, K = x.shape
+    c = s = d = None
+    if codes:
+        c = torch.empty((rows, mxfp8_lda(K)), dtype=torch.uint8, device=x.device)
+        s = torch.empty((rows, mxfp8_lds(K)), dtype=torch.uint8, device=x.device)
+    if dequant:
+        d = torch.empty_like(x)
+    _check(lib().moe_mxfp8_quantize(_ptr(x), rows, K, _ptr(c), _ptr(s), _ptr(d), _stream()),
+           "moe_mxfp8_quantize")
+    return c, s, d
+
+
+def moe_mx_gemm1(codes, scales, top_k: int, K: int, w13: QuantWeights, act: str, alpha: float,
+                 beta: float, limit: float, sorted_ids, expert_ids, num_post_pad, block_m: int,
+                 out=None):
+    """MXFP8 rows (codes [size_m, lda], scales [size_m, lds]) x MXFP4 w13 -> bf16 act."""
+    size_m = codes.shape[0]
+    n_out = w13.N // 2 if act == "swigluoai" else w13.N
+    if out is None:
+        out = torch.zeros((size_m * top_k, n_out), dtype=torch.bfloat16, device=codes.device)
+    s = w13.struct()
+    _check(lib().moe_mx_gemm1(_ptr(codes), _ptr(scales), size_m, top_k, K, w13.N, w13.E,
+                              ctypes.byref(s), ACT[act], alpha, beta, limit, _ptr(sorted_ids),
+                              _ptr(expert_ids), _ptr(num_post_pad), block_m, _ptr(out), _stream()),
+           "moe_mx_gemm1")
+    return out
+
+
+def moe_mx_gemm2(codes, scales, K: int, w2: QuantWeights, topk_w, mul_topk_weights: bool,
+                 sorted_ids, expert_ids, num_post_pad, block_m: int, out=None):
+    """MXFP8 rows (one per flat slot) x MXFP4 w2 -> bf16 y [size_m, N]."""
+    size_m = codes.shape[0]
+    if out is None:
+        out = torch.zeros((size_m, w2.N), dtype=torch.bfloat16, device=codes.device)
+    s = w2.struct()
+    _check(lib().moe_mx_gemm2(_ptr(codes), _ptr(scales), size_m, K, w2.N, w2.E, ctypes.byref(s),
+                              _ptr(topk_w), int(bool(mul_topk_weights)), _ptr(sorted_ids),
+                              _ptr(expert_ids), _ptr(num_post_pad), block_m, _ptr(out), _stream()),
+           "moe_mx_gemm2")
+    return out
+
+
+def moe_forward_mxfp8_workspace_bytes(T: int, E: int, top_k: int, hidden: int, inter: int) -> int:
+    return lib().moe_forward_mxfp8_workspace_bytes(T, E, top_k, hidden, inter)
+
+
+def moe_forward_mxfp8(x: torch.Tensor, logits: torch.Tensor, top_k: int, inter: int,
+                      w13: QuantWeights, w2: QuantWeights, act: str = "swigluoai",
+                      route: str = "softmax", expert_bias=None, renormalize: bool = True,
+                      alpha: float = 1.702, beta: float = 1.0, limit: float = 7.0,
+                      mul_topk_weights: bool = True, workspace=None, out=None):
+    """The layer with MXFP8 activations (MXFP4 weights): x bf16 [T, hidden] -> out bf16."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(logits, torch.float32, "logits")
+    T, hidden = x.shape
+    E = logits.shape[1]
+    need = moe_forward_mxfp8_workspace_bytes(T, E, top_k, hidden, inter)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
+    s13, s2 = w13.struct(), w2.struct()
+    _check(lib().moe_forward_mxfp8(_ptr(x), _ptr(logits), T, E, top_k, hidden, inter, ROUTE[route],
+                                   _ptr(expert_bias), int(bool(renormalize)), ctypes.byref(s13),
+                                   ctypes.byref(s2), ACT[act], alpha, beta, limit,
+                                   int(bool(mul_topk_weights)), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _ptr(out),
+                                   _stream()), "moe_forward_mxfp8")
     return out
 
 

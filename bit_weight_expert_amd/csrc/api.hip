@@ -23,6 +23,12 @@ extern "C" hipError_t moe_launch_sum(const uint16_t*, const int32_t*, int, int, 
                                      uint16_t*, hipStream_t);
 extern "C" hipError_t moe_launch_gptq_sort(const int32_t*, const int32_t*, int, int, int, int,
                                            int32_t*, int32_t*, int32_t*, hipStream_t);
+extern "C" hipError_t moe_launch_mxfp8_quant(const uint16_t*, int, int, int, int, uint8_t*, uint8_t*,
+                                             uint16_t*, hipStream_t);
+extern "C" hipError_t moe_launch_gemm_mx(int, int, int, const uint8_t*, const uint8_t*, int, int, int,
+                                         int, int, int, int, const moe::WeightArgs*, const int32_t*,
+                                         const int32_t*, const int32_t*, const float*, int, float,
+                                         float, float, uint16_t*, int, hipStream_t);
 extern "C" hipError_t moe_launch_permute_slots(const uint16_t*, int, int, int, int, const int32_t*,
                                                const int32_t*, uint16_t*, hipStream_t);
 
@@ -116,6 +122,37 @@ WsLayout ws_layout(int T, int E, int top_k, int hidden, int inter, int block_m) 
   L.npp = o; o = round_up(o + 4, 256);
   L.act = o; o = round_up(o + n * (size_t)inter * 2, 256);
   L.y = o; o = round_up(o + n * (size_t)hidden * 2, 256);
+  L.total = o;
+  return L;
+}
+
+// MXFP8 operand layout: codes row stride K rounded up to 128, scales row
+// stride K/32 rounded up to 16 (zero padded by the quantiser).
+int mx_lda(int K) { return (K + 127) / 128 * 128; }
+int mx_lds(int K) { return (K / 32 + 15) / 16 * 16; }
+
+// Scale tiles of the MX GEMM kernel must fit its LDS (56 KB), and the A
+// scale tile its 4 x 6 DMA instructions of 64 16-byte pieces.
+bool mx_fits(int K, int block_m) {
+  const int b = (256 * (K / 32) + 1023) / 1024 * 1024;
+  return b + (block_m * mx_lds(K) + 1023) / 1024 * 1024 <= 56 * 1024 &&
+         block_m * (mx_lds(K) / 16) <= 4 * 6 * 64;
+}
+
+struct MxWsLayout {
+  WsLayout base;
+  size_t xq, xs, aq, as, total;
+};
+
+MxWsLayout mx_ws_layout(int T, int E, int top_k, int hidden, int inter, int block_m) {
+  MxWsLayout L;
+  L.base = ws_layout(T, E, top_k, hidden, inter, block_m);
+  const size_t n = (size_t)T * top_k;
+  size_t o = L.base.total;
+  L.xq = o; o = round_up(o + (size_t)T * mx_lda(hidden), 256);
+  L.xs = o; o = round_up(o + (size_t)T * mx_lds(hidden), 256);
+  L.aq = o; o = round_up(o + n * mx_lda(inter), 256);
+  L.as = o; o = round_up(o + n * mx_lds(inter), 256);
   L.total = o;
   return L;
 }
@@ -277,6 +314,166 @@ moe_status_t moe_permute_slots(const uint16_t* src, int size_m, int top_k, int K
   if (!aligned16(src) || !aligned16(dst) || !aligned16(k_perm)) return MOE_ERR_ALIGN;
   return hip_status(moe_launch_permute_slots(src, size_m * top_k, top_k, K, E, k_perm, topk_ids,
                                              dst, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_mxfp8_quantize(const uint16_t* x, int rows, int K, uint8_t* codes, uint8_t* scales,
+                                uint16_t* dequant, moe_stream_t stream) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_ERR_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (x == nullptr || (codes == nullptr && scales == nullptr && dequant == nullptr))
+    return MOE_ERR_NULL;
+  if (!aligned16(x) || (codes && !aligned16(codes)) || (dequant && !aligned16(dequant)))
+    return MOE_ERR_ALIGN;
+  return hip_status(moe_launch_mxfp8_quant(x, rows, K, mx_lda(K), mx_lds(K), codes, scales,
+                                           dequant, static_cast<hipStream_t>(stream)));
+}
+
+static moe_status_t mx_gemm_checks(const moe_wq_t* w, int N, int K, int block_m,
+                                   moe::WeightArgs* W) {
+  moe_status_t st = check_weights(w, N, K, W);
+  if (st != MOE_OK) return st;
+  if (w->fmt != MOE_W_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (block_m != 64 && block_m != 128) return MOE_ERR_UNSUPPORTED;
+  if (!mx_fits(K, block_m)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t moe_mx_gemm1(const uint8_t* x_codes, const uint8_t* x_scales, int size_m, int top_k,
+                          int K, int N, int E, const moe_wq_t* w13, moe_act_t act, float alpha,
+                          float beta, float limit, const int32_t* sorted_ids,
+                          const int32_t* expert_ids, const int32_t* num_post_pad, int block_m,
+                          uint16_t* out, moe_stream_t stream) {
+  moe_status_t st = gemm_common_checks(size_m, top_k, E, block_m);
+  if (st != MOE_OK) return st;
+  const int epi = epi_of(act);
+  if (epi < 0) return MOE_ERR_UNSUPPORTED;
+  moe::WeightArgs W;
+  st = mx_gemm_checks(w13, N, K, block_m, &W);
+  if (st != MOE_OK) return st;
+  if (epi == moe::EPI_SWIGLU && N % 32 != 0) return MOE_ERR_SHAPE;
+  if (size_m == 0) return MOE_OK;
+  if (x_codes == nullptr || x_scales == nullptr || sorted_ids == nullptr || expert_ids == nullptr ||
+      num_post_pad == nullptr || out == nullptr)
+    return MOE_ERR_NULL;
+  if (!aligned16(x_codes) || !aligned16(x_scales) || !aligned16(out)) return MOE_ERR_ALIGN;
+  const int cap = (int)moe_align_capacity(size_m, top_k, E, block_m);
+  const int out_ld = (epi == moe::EPI_SWIGLU) ? N / 2 : N;
+  return hip_status(moe_launch_gemm_mx(epi, block_m, cap, x_codes, x_scales, mx_lda(K), mx_lds(K),
+                                       top_k, size_m * top_k, K, N, E, &W, sorted_ids, expert_ids,
+                                       num_post_pad, nullptr, 0, alpha, beta, limit, out, out_ld,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_mx_gemm2(const uint8_t* a_codes, const uint8_t* a_scales, int size_m, int K, int N,
+                          int E, const moe_wq_t* w2, const float* topk_w, int mul_topk_weights,
+                          const int32_t* sorted_ids, const int32_t* expert_ids,
+                          const int32_t* num_post_pad, int block_m, uint16_t* y,
+                          moe_stream_t stream) {
+  moe_status_t st = gemm_common_checks(size_m, 1, E, block_m);
+  if (st != MOE_OK) return st;
+  moe::WeightArgs W;
+  st = mx_gemm_checks(w2, N, K, block_m, &W);
+  if (st != MOE_OK) return st;
+  if (size_m == 0) return MOE_OK;
+  if (a_codes == nullptr || a_scales == nullptr || sorted_ids == nullptr || expert_ids == nullptr ||
+      num_post_pad == nullptr || y == nullptr)
+    return MOE_ERR_NULL;
+  if (mul_topk_weights && topk_w == nullptr) return MOE_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(y)) return MOE_ERR_ALIGN;
+  const int cap = (int)moe_align_capacity(size_m, 1, E, block_m);
+  return hip_status(moe_launch_gemm_mx(moe::EPI_DOWN, block_m, cap, a_codes, a_scales, mx_lda(K),
+                                       mx_lds(K), 1, size_m, K, N, E, &W, sorted_ids, expert_ids,
+                                       num_post_pad, topk_w, mul_topk_weights ? 1 : 0, 0.f, 0.f,
+                                       0.f, y, N, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_forward_mxfp8_workspace_bytes(int T, int E, int top_k, int hidden, int inter) {
+  if (T <= 0 || E <= 0 || top_k <= 0 || hidden <= 0 || inter <= 0) return 0;
+  return mx_ws_layout(T, E, top_k, hidden, inter, pick_block_m(T, top_k, E)).total;
+}
+
+moe_status_t moe_forward_mxfp8(const uint16_t* x, const float* logits, int T, int E, int top_k,
+                               int hidden, int inter, moe_route_t kind, const float* expert_bias,
+                               int renormalize, const moe_wq_t* w13, const moe_wq_t* w2,
+                               moe_act_t act, float alpha, float beta, float limit,
+                               int mul_topk_weights, void* workspace, size_t workspace_bytes,
+                               uint16_t* out, moe_stream_t stream) {
+  if (T < 0 || E <= 0 || E > kMaxE || top_k < 1 || top_k > E || top_k > kMaxTopK)
+    return MOE_ERR_SHAPE;
+  if ((long long)T * top_k >= (1LL << 24)) return MOE_ERR_SHAPE;
+  if (kind != MOE_ROUTE_SOFTMAX && kind != MOE_ROUTE_SIGMOID_BIAS) return MOE_ERR_UNSUPPORTED;
+  const int epi = epi_of(act);
+  if (epi != moe::EPI_SWIGLU && epi != moe::EPI_RELU2) return MOE_ERR_UNSUPPORTED;
+  const int n1 = (epi == moe::EPI_SWIGLU) ? 2 * inter : inter;
+  moe::WeightArgs W13, W2;
+  moe_status_t st = check_weights(w13, n1, hidden, &W13);
+  if (st != MOE_OK) return st;
+  st = check_weights(w2, hidden, inter, &W2);
+  if (st != MOE_OK) return st;
+  if (w13->fmt != MOE_W_MXFP4 || w2->fmt != MOE_W_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (epi == moe::EPI_SWIGLU && n1 % 32 != 0) return MOE_ERR_SHAPE;
+  if (mul_topk_weights < 0 || mul_topk_weights > 1) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || logits == nullptr || out == nullptr || workspace == nullptr) return MOE_ERR_NULL;
+  if (kind == MOE_ROUTE_SIGMOID_BIAS && expert_bias == nullptr) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return MOE_ERR_ALIGN;
+  const int block_m = pick_block_m(T, top_k, E);
+  const MxWsLayout L = mx_ws_layout(T, E, top_k, hidden, inter, block_m);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.base.ids);
+  float* tw = reinterpret_cast<float*>(ws + L.base.w);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.base.sorted);
+  int32_t* eids = reinterpret_cast<int32_t*>(ws + L.base.eids);
+  int32_t* npp = reinterpret_cast<int32_t*>(ws + L.base.npp);
+  uint16_t* actb = reinterpret_cast<uint16_t*>(ws + L.base.act);
+  uint16_t* yb = reinterpret_cast<uint16_t*>(ws + L.base.y);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(ws + L.xs);
+  uint8_t* aq = reinterpret_cast<uint8_t*>(ws + L.aq);
+  uint8_t* as = reinterpret_cast<uint8_t*>(ws + L.as);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n = T * top_k;
+  const int cap = (int)moe_align_capacity(T, top_k, E, block_m);
+  const int mul = mul_topk_weights;
+
+  hipError_t e = moe_launch_route_align(logits, T, E, top_k, (int)kind, expert_bias,
+                                        renormalize ? 1 : 0, ids, tw, block_m, cap, sorted, eids,
+                                        npp, s);
+  if (block_m >= 64 && mx_fits(hidden, block_m) && mx_fits(inter, block_m)) {
+    // MX-scaled MFMA: both GEMMs read e4m3 codes and e8m0 scales
+    if (e == hipSuccess)
+      e = moe_launch_mxfp8_quant(x, T, hidden, mx_lda(hidden), mx_lds(hidden), xq, xs, nullptr, s);
+    if (e == hipSuccess)
+      e = moe_launch_gemm_mx(epi, block_m, cap, xq, xs, mx_lda(hidden), mx_lds(hidden), top_k, n,
+                             hidden, n1, E, &W13, sorted, eids, npp, tw, 0, alpha, beta, limit,
+                             actb, inter, s);
+    if (e == hipSuccess)
+      e = moe_launch_mxfp8_quant(actb, n, inter, mx_lda(inter), mx_lds(inter), aq, as, nullptr, s);
+    if (e == hipSuccess)
+      e = moe_launch_gemm_mx(moe::EPI_DOWN, block_m, cap, aq, as, mx_lda(inter), mx_lds(inter), 1,
+                             n, inter, hidden, E, &W2, sorted, eids, npp, tw, mul, 0.f, 0.f, 0.f,
+                             yb, hidden, s);
+  } else {
+    // few rows per expert: the operands are taken at their MXFP8 values
+    // (quantised and dequantised to bf16, exactly) by the bf16 kernels
+    if (e == hipSuccess)
+      e = moe_launch_mxfp8_quant(x, T, hidden, mx_lda(hidden), mx_lds(hidden), nullptr, nullptr,
+                                 yb, s);
+    if (e == hipSuccess)
+      e = moe_launch_gemm((int)w13->fmt, epi, block_m, cap, yb, top_k, n, hidden, n1, E, &W13,
+                          sorted, eids, npp, tw, 0, alpha, beta, limit, actb, inter, s);
+    if (e == hipSuccess)
+      e = moe_launch_mxfp8_quant(actb, n, inter, mx_lda(inter), mx_lds(inter), nullptr, nullptr,
+                                 actb, s);
+    if (e == hipSuccess)
+      e = moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, actb, 1, n, inter, hidden, E,
+                          &W2, sorted, eids, npp, tw, mul, 0.f, 0.f, 0.f, yb, hidden, s);
+  }
+  if (e == hipSuccess) e = moe_launch_sum(yb, ids, T, top_k, hidden, E, out, s);
+  return hip_status(e);
 }
 
 int moe_forward_block_m(int T, int top_k, int E) {

@@ -1663,6 +1663,254 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
   return hipGetLastError();
 }
 
+// --------------------------------------------------------------------------
+// MXFP8 activations x MXFP4 weights: MX-scaled MFMA kernel (blocks of 64/128)
+// --------------------------------------------------------------------------
+//
+// The A operand is MXFP8 as the quantiser writes it: e4m3 codes [rows][lda]
+// (lda = K rounded up to 128, zero past K) and e8m0 scales [rows][lds]
+// (lds = K/32 rounded up to 16, zero past K/32).  The weights are the MXFP4
+// layout as is.  v_mfma_scale_f32_32x32x64_f8f6f4 multiplies e4m3 by e2m1 and
+// applies both e8m0 scales per 32-deep block, so nothing is dequantised.
+//
+// Operand layout of one 64-deep step (measured on gfx950 with one-hot
+// operands): lane (c, g), c = lane % 32, g = lane / 32, supplies
+//   A  row c: k = 16g .. 16g+15 in bytes 0..15 and 32+16g .. 32+16g+15 in
+//      bytes 16..31, and the scale of row c's 32-block g;
+//   B  weight row c: k = 32g .. 32g+31 (16 bytes of codes), and the scale of
+//      that row's block g.
+// The accumulators have the layout of the bf16 32x32 MFMA (epilogue32).
+//
+// Tile: BM rows x 256 weight rows, four waves side by side over the weight
+// rows (two 32-row fragments each), all BM rows per wave.  K moves in chunks
+// of 128 through a 3-deep LDS ring filled by LDS-DMA (A: 128 bytes per row,
+// 16-byte slot q of row r at q ^ (r % 8); weights: 64 bytes per row at the
+// row's position, slot q at q ^ ((position / 4) % 4)); both scale tiles stay
+// in LDS for the whole K.
+
+struct MxA {
+  const uint8_t* codes;   // e4m3 [rows][lda]
+  const uint8_t* scales;  // e8m0 [rows][lds]
+  int lda, lds;
+};
+
+constexpr int kMxBK = 128;
+constexpr int kMxStages = 3;
+constexpr int kMxScaleBytes = 56 * 1024;
+constexpr int kMxScaleIssue = 6;  // A-scale DMA instructions per wave (BM * lds <= 1536 pieces)
+
+template <int BM>
+struct Mx {
+  static constexpr int MI = BM / 32;
+  static constexpr int NF = 2;
+  static constexpr int BN = 4 * NF * 32;
+  static constexpr int kABytes = BM * kMxBK;
+  static constexpr int kBBytes = BN * kMxBK / 2;
+  static constexpr int kAIssue = kABytes / 1024 / 4;  // DMA instructions per wave per chunk
+  static constexpr int kBIssue = kBBytes / 1024 / 4;
+  static constexpr int kIssue = kAIssue + kBIssue;
+  static constexpr int kStage = kABytes + kBBytes;
+  static constexpr int kLds = kMxStages * kStage + kMxScaleBytes;
+  static_assert(kAIssue >= 1 && kBIssue >= 1, "tile too small for the DMA split");
+  static_assert(kLds <= 160 * 1024, "LDS");
+};
+
+// LDS bytes of both scale tiles (weights: BN rows of K/32; A: BM rows of lds,
+// rounded up to whole DMA instructions).
+__host__ __device__ inline int mx_scale_bytes(int K, int bm, int lds) {
+  const int b = (256 * (K / 32) + 1023) / 1024 * 1024;
+  return b + (bm * lds + 1023) / 1024 * 1024;
+}
+
+// Position (0..255) of tile row r in the weight stage: 32-row blocks, gated
+// tiles with the gate rows (even) before the up rows, so the eight lanes that
+// one LDS cycle serves read eight consecutive positions.
+template <int EPI>
+__device__ __forceinline__ int mx_bpos(int r) {
+  const int s = r & 31;
+  return (r & ~31) + ((EPI == EPI_SWIGLU) ? (s >> 1) + 16 * (s & 1) : s);
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16e __attribute__((ext_vector_type(16)));
+
+template <int OPSEL>
+__device__ __forceinline__ void mx_mfma(f32x16& acc, const i32x8& a, const i32x8& b, int sa, int sb) {
+  f32x16e c;
+  __builtin_memcpy(&c, &acc, sizeof(c));
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, OPSEL, sa, OPSEL, sb);
+  __builtin_memcpy(&acc, &c, sizeof(c));
+}
+
+// One 64-deep step st (0 or 1) of chunk stage `stg`: A reads, weight reads, MFMAs.
+template <int EPI, int MI, int NF, int ST>
+__device__ __forceinline__ void mx_step(f32x16 (&acc)[MI][NF], const uint8_t* stg, int abytes,
+                                        const int (&bpos)[NF], int c, int g, const int (&sa)[MI],
+                                        const int (&sb)[NF]) {
+  i32x8 b[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int p = bpos[j];
+    const uint4 v = *reinterpret_cast<const uint4*>(stg + abytes + p * 64 +
+                                                    16 * ((2 * ST + g) ^ ((p >> 2) & 3)));
+    b[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int r = 32 * i + c;
+    const uint8_t* row = stg + r * 128;
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * ((4 * ST + g) ^ (r & 7)));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * ((4 * ST + 2 + g) ^ (r & 7)));
+    const i32x8 a{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+    for (int j = 0; j < NF; ++j) mx_mfma<2 * ST>(acc[i][j], a, b[j], sa[i], sb[j]);
+  }
+}
+
+template <int EPI, int BM>
+__global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, WeightArgs W, EpiArgs ea) {
+  using P = Mx<BM>;
+  constexpr int MI = P::MI, NF = P::NF;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[P::kLds];
+
+  int mb, nt;
+  if (!prefill_tile(ga, BM, mb, nt)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int c = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = ga.K, N = ga.N, kb = K / 32;
+
+  // slot ids of the A rows this lane copies (instruction q = 4p + wave covers
+  // rows 8q .. 8q+7) and of the A scale rows (instruction q = 4i + wave covers
+  // 16-byte pieces 64q .. 64q+63 of the [BM][lds] tile), all requested before
+  // anything waits
+  const int parts = ma.lds / 16;
+  const int na = BM * parts;
+  int sid[P::kAIssue], ssid[kMxScaleIssue];
+#pragma unroll
+  for (int p = 0; p < P::kAIssue; ++p) sid[p] = ga.sorted_ids[mb * BM + 8 * (4 * p + wave) + (lane >> 3)];
+#pragma unroll
+  for (int i = 0; i < kMxScaleIssue; ++i) {
+    const int pc = min((4 * i + wave) * 64 + lane, na - 1);  // lanes past the end repeat the last piece
+    ssid[i] = ga.sorted_ids[mb * BM + pc / parts];
+  }
+  const int e = ga.expert_ids[mb];
+  if (e < 0 || e >= ga.E) return;
+
+  const int nt0 = nt * P::BN;
+  const int rows = min(P::BN, N - nt0);
+  const int n0 = nt0 + wave * NF * 32;
+
+  // DMA sources.  A: lane l fetches logical slot (l%8) ^ (row%8) of row 8q + l/8.
+  const uint8_t* arow[P::kAIssue];
+#pragma unroll
+  for (int p = 0; p < P::kAIssue; ++p) {
+    const int r = 8 * (4 * p + wave) + (lane >> 3);
+    const int s = sid[p];
+    const int row = s < ga.n_slots ? (int)(((uint64_t)(uint32_t)s * ga.a_mul) >> 32) : 0;
+    arow[p] = ma.codes + (size_t)row * ma.lda + 16 * ((lane & 7) ^ (r & 7));
+  }
+  // Weights: instruction q fills positions 16q .. 16q+15, lane l the physical
+  // slot l%4 of position 16q + l/4 (rows past N re-read the last row; offsets
+  // past the row's K/2 bytes re-read its last 16, multiplied by zero A codes).
+  const uint8_t* brow[P::kBIssue];
+  int bls[P::kBIssue];
+#pragma unroll
+  for (int p = 0; p < P::kBIssue; ++p) {
+    const int pos = 16 * (4 * p + wave) + (lane >> 2);
+    const int n = min(nt0 + pf_brow<EPI>(pos >> 5, pos & 31), N - 1);
+    brow[p] = W.qweight + ((size_t)e * N + n) * (K / 2);
+    bls[p] = 16 * ((lane & 3) ^ ((pos >> 2) & 3));
+  }
+
+  const uint32_t ring = lds_addr(smem);
+  const uint32_t scb_lds = ring + kMxStages * P::kStage;                  // weight scales
+  const int scb_bytes = (256 * kb + 1023) / 1024 * 1024;
+  const uint32_t sca_lds = scb_lds + scb_bytes;                           // A scales
+  const uint8_t* scb = smem + kMxStages * P::kStage;
+  const uint8_t* sca = scb + scb_bytes;
+  const int nchunks = (K + kMxBK - 1) / kMxBK;
+
+  // weight scales of the tile rows (contiguous), then the A scale rows
+  {
+    const int nb = rows * kb;
+    pf_dma_region(scb_lds, W.scales + ((size_t)e * N + nt0) * kb, 0, nb, nb, nb, wave, lane);
+#pragma unroll
+    for (int i = 0; i < kMxScaleIssue; ++i) {
+      const int q = 4 * i + wave;
+      if (q * 64 >= na) break;
+      const int pc = min(q * 64 + lane, na - 1);
+      const int s = ssid[i];
+      const int row = s < ga.n_slots ? (int)(((uint64_t)(uint32_t)s * ga.a_mul) >> 32) : 0;
+      dma16(ma.scales + (size_t)row * ma.lds + 16 * (pc % parts), sca_lds + q * 1024);
+    }
+  }
+  auto issue = [&](uint32_t stage, int kc) {
+#pragma unroll
+    for (int p = 0; p < P::kAIssue; ++p)
+      dma16(arow[p] + kc * kMxBK, stage + (uint32_t)(4 * p + wave) * 1024u);
+#pragma unroll
+    for (int p = 0; p < P::kBIssue; ++p)
+      dma16(brow[p] + min(kc * (kMxBK / 2) + bls[p], K / 2 - 16),
+            stage + P::kABytes + (uint32_t)(4 * p + wave) * 1024u);
+  };
+#pragma unroll
+  for (int s = 0; s < kMxStages; ++s) issue(ring + s * P::kStage, min(s, nchunks - 1));
+
+  // this lane's weight positions and scale rows
+  int bpos[NF], rl[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int n = frag32_row<EPI>(n0, j, c);
+    rl[j] = n < N ? n - nt0 : 0;
+    bpos[j] = mx_bpos<EPI>(rl[j]);
+  }
+
+  f32x16 acc[MI][NF];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // scales and chunk 0 have landed
+  wait_vmcnt<(kMxStages - 1) * P::kIssue>();
+  pf_barrier();
+  for (int kc = 0; kc < nchunks; ++kc) {
+    const uint8_t* stg = smem + (kc % kMxStages) * P::kStage;
+    // scales of the chunk: A dword of blocks 4kc..4kc+3 shifted so byte 0 /
+    // byte 2 are this lane's blocks of steps 0 / 1; weight bytes likewise
+    // (blocks past K/32 read as 2^0: their A codes are zero)
+    int sa[MI], sb[NF];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sca + (32 * i + c) * ma.lds + 4 * kc) >> (8 * g));
+    const int b0 = 4 * kc + g, b1 = 4 * kc + 2 + g;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const uint8_t* sr = scb + rl[j] * kb;
+      const int s0 = b0 < kb ? sr[b0] : 127;
+      const int s1 = b1 < kb ? sr[b1] : 127;
+      sb[j] = s0 | (s1 << 16);
+    }
+    mx_step<EPI, MI, NF, 0>(acc, stg, P::kABytes, bpos, c, g, sa, sb);
+    if (kc * kMxBK + 64 < K) mx_step<EPI, MI, NF, 1>(acc, stg, P::kABytes, bpos, c, g, sa, sb);
+    // chunk kc+1 has landed (only chunk kc+2 may be in flight) and every wave
+    // is past its reads of chunk kc, whose stage takes chunk kc+3
+    wait_vmcnt<P::kIssue>();
+    pf_barrier();
+    issue(ring + (kc % kMxStages) * P::kStage, min(kc + kMxStages, nchunks - 1));
+  }
+  // no DMA may land in LDS after this workgroup is gone
+  wait_vmcnt<0>();
+
+  if (n0 >= N) return;
+  EpiArgs a = ea;
+  a.row0 = mb * BM;
+  epilogue32<EPI, FMT_MXFP4, MI, NF>(acc, a, W, e, n0, lane);
+}
+
 template <int FMT>
 static hipError_t launch_fmt(int epi, int block_m, int cap, const GemmArgs& ga, const WeightArgs& W,
                              const EpiArgs& ea, hipStream_t st) {
@@ -1693,6 +1941,41 @@ extern "C" hipError_t moe_launch_gemm(int fmt, int epi, int block_m, int cap, co
     case moe::FMT_MXFP4: return moe::launch_fmt<moe::FMT_MXFP4>(epi, block_m, cap, ga, *W, ea, st);
     default: return moe::launch_fmt<moe::FMT_GPTQ>(epi, block_m, cap, ga, *W, ea, st);
   }
+}
+
+// Grouped GEMM with MXFP8 activations and MXFP4 weights, blocks of 64 or 128
+// rows.  Returns hipErrorInvalidValue when the scale tiles do not fit.
+extern "C" hipError_t moe_launch_gemm_mx(int epi, int block_m, int cap, const uint8_t* a_codes,
+                                         const uint8_t* a_scales, int lda, int lds, int a_div,
+                                         int n_slots, int K, int N, int E, const moe::WeightArgs* W,
+                                         const int32_t* sid, const int32_t* eid, const int32_t* npp,
+                                         const float* tw, int mul, float alpha, float beta,
+                                         float limit, uint16_t* out, int out_ld, hipStream_t st) {
+  if (cap / block_m == 0) return hipSuccess;
+  if (moe::mx_scale_bytes(K, block_m, lds) > moe::kMxScaleBytes ||
+      block_m * (lds / 16) > 4 * moe::kMxScaleIssue * 64)
+    return hipErrorInvalidValue;
+  const uint64_t a_mul = ((1ull << 32) + (uint64_t)a_div - 1) / (uint64_t)a_div;
+  moe::GemmArgs ga{nullptr, a_div, a_mul, n_slots, K, N, E, cap / block_m, 0, 4, block_m, sid, eid, npp};
+  ga.n_ntiles = (N + moe::Mx<128>::BN - 1) / moe::Mx<128>::BN;
+  moe::MxA ma{a_codes, a_scales, lda, lds};
+  moe::EpiArgs ea{sid, 0, n_slots, N, tw, mul, alpha, beta, limit, out, out_ld};
+  const dim3 grid((ga.n_mblocks * ga.n_ntiles + 7) / 8 * 8);
+#define MOE_MX_LAUNCH(EPI)                                                                  \
+  do {                                                                                      \
+    if (block_m == 64)                                                                      \
+      moe::gemm_mx_kernel<EPI, 64><<<grid, dim3(256), 0, st>>>(ga, ma, *W, ea);             \
+    else                                                                                    \
+      moe::gemm_mx_kernel<EPI, 128><<<grid, dim3(256), 0, st>>>(ga, ma, *W, ea);            \
+  } while (0)
+  switch (epi) {
+    case moe::EPI_SWIGLU: MOE_MX_LAUNCH(moe::EPI_SWIGLU); break;
+    case moe::EPI_RELU2: MOE_MX_LAUNCH(moe::EPI_RELU2); break;
+    case moe::EPI_NONE: MOE_MX_LAUNCH(moe::EPI_NONE); break;
+    default: MOE_MX_LAUNCH(moe::EPI_DOWN); break;
+  }
+#undef MOE_MX_LAUNCH
+  return hipGetLastError();
 }
 
 extern "C" int moe_set_decode_policy(int policy) {

@@ -256,6 +256,62 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, i
                          int mul_topk_weights, void* workspace, size_t workspace_bytes,
                          uint16_t* out, moe_stream_t stream);
 
+/* ---- MXFP8 activations (MXFP4 weights x MXFP8 activations) ----
+ * The variant of the layer with MXFP8 activations ("gpt-oss-120b MXFP4 +
+ * --enable-expert-parallel crashes", sections "Actual behavior" and "Why the
+ * mxfp8 workaround is not a fix": the activation option switches the MoE to
+ * MXFP8 activations).  Encoding (OCP microscaling): per block of 32
+ * consecutive values of a row, shared e8m0 exponent floor(log2(amax)) - 8,
+ * elements value / 2^exponent rounded to the nearest e4m3fn value (ties to
+ * even, saturating at 448); an all-zero block has exponent byte 0; a block
+ * with a NaN or an infinity has exponent byte 0xFF and NaN elements.
+ * Operand layout: codes uint8 [rows][lda], lda = K rounded up to 128, zero
+ * past K; scales uint8 [rows][lds], lds = K/32 rounded up to 16, zero past
+ * K/32. */
+
+/* Quantise bf16 rows [rows][K] (K % 32 == 0).  Any of codes, scales and
+ * dequant may be NULL (not all three): dequant receives the MXFP8 values as
+ * bf16 [rows][K] (exact except below 2^-133) and may be x itself. */
+moe_status_t moe_mxfp8_quantize(const uint16_t* x, int rows, int K, uint8_t* codes, uint8_t* scales,
+                                uint16_t* dequant, moe_stream_t stream);
+
+/* moe_w4a16_gemm1 with the input rows in MXFP8 ([size_m] rows in the layout
+ * above) and MXFP4 weights, on the MX-scaled matrix cores (e4m3 x e2m1 with
+ * both e8m0 scales applied per 32-deep block, fp32 accumulate).  block_m must
+ * be 64 or 128, and both scale tiles must fit the kernel's 56 KB of LDS
+ * (256*K/32 + block_m*lds bytes, each rounded up to 1 KB; K <= ~4600), else
+ * MOE_ERR_UNSUPPORTED.  No routing weight on the input. */
+moe_status_t moe_mx_gemm1(const uint8_t* x_codes, const uint8_t* x_scales, int size_m, int top_k,
+                          int K, int N, int E, const moe_wq_t* w13, moe_act_t act, float alpha,
+                          float beta, float limit, const int32_t* sorted_ids,
+                          const int32_t* expert_ids, const int32_t* num_post_pad, int block_m,
+                          uint16_t* out, moe_stream_t stream);
+
+/* moe_w4a16_gemm2 with MXFP8 input rows (one per flat slot); limits as
+ * moe_mx_gemm1. */
+moe_status_t moe_mx_gemm2(const uint8_t* a_codes, const uint8_t* a_scales, int size_m, int K, int N,
+                          int E, const moe_wq_t* w2, const float* topk_w, int mul_topk_weights,
+                          const int32_t* sorted_ids, const int32_t* expert_ids,
+                          const int32_t* num_post_pad, int block_m, uint16_t* y,
+                          moe_stream_t stream);
+
+/* Workspace of moe_forward_mxfp8: that of moe_forward plus the MXFP8 copies
+ * of x and of the activation. */
+size_t moe_forward_mxfp8_workspace_bytes(int T, int E, int top_k, int hidden, int inter);
+
+/* moe_forward with MXFP8 activations: x is quantised to MXFP8 before GEMM1,
+ * GEMM1's bf16 output before GEMM2; both weight families must be MXFP4
+ * (else MOE_ERR_UNSUPPORTED); mul_topk_weights 0 or 1; no k_perm.  Blocks of
+ * 64/128 rows run the MX-scaled kernels; smaller blocks (few tokens per
+ * expert) feed the MXFP8 values, dequantised to bf16 exactly, to the bf16
+ * kernels -- the same products, summed in fp32. */
+moe_status_t moe_forward_mxfp8(const uint16_t* x, const float* logits, int T, int E, int top_k,
+                               int hidden, int inter, moe_route_t kind, const float* expert_bias,
+                               int renormalize, const moe_wq_t* w13, const moe_wq_t* w2,
+                               moe_act_t act, float alpha, float beta, float limit,
+                               int mul_topk_weights, void* workspace, size_t workspace_bytes,
+                               uint16_t* out, moe_stream_t stream);
+
 /* Which kernel the grouped GEMMs use for blocks of 16 or 32 rows (few tokens
  * per expert): 0 = automatic (the library's choice from the launch size),
  * 1 = split-K kernel, 2 = wide kernel (128 weight rows per workgroup, A

@@ -155,3 +155,28 @@ def test_act_order_entry_points_reject(L):
     assert p(perm=FAKE + 4) == ALIGN
     assert p(src=None) == NULL
     assert p(m=0, src=None) == OK
+
+
+def test_mxfp8_entry_points_reject(L):
+    q = lambda **kw: L.moe_mxfp8_quantize(kw.get("x", FAKE), kw.get("rows", 4), kw.get("K", 2880),
+                                          kw.get("c", FAKE), kw.get("s", FAKE), kw.get("d", None), None)
+    assert q(K=2880 + 16) == SHAPE
+    assert q(c=None, s=None, d=None) == NULL
+    assert q(x=FAKE + 2) == ALIGN
+    assert q(rows=0, x=None) == OK
+    mx = dict(fmt=1, group=32)
+    g1 = lambda w, bm=128, K=2880, act=0: L.moe_mx_gemm1(FAKE, FAKE, 64, 4, K, 5760, 32, ctypes.byref(w),
+                                                         act, 1.702, 1.0, 7.0, FAKE, FAKE, FAKE, bm,
+                                                         FAKE, None)
+    assert g1(_wq()) == UNSUP                            # NVFP4 weights: not an MX operand
+    assert g1(_wq(**mx), bm=32) == UNSUP                 # MX kernel tiles are 64 or 128 rows
+    assert g1(_wq(**mx), K=8192) == UNSUP                # scale tiles past the kernel's LDS
+    assert g1(_wq(**mx), act=7) == UNSUP
+    f = lambda w13, w2, mul=1: L.moe_forward_mxfp8(FAKE, FAKE, 8, 32, 4, 2880, 2880, 0, None, 1,
+                                                   ctypes.byref(w13), ctypes.byref(w2), 0, 1.702, 1.0,
+                                                   7.0, mul, FAKE * 16, 0, FAKE, None)
+    assert f(_wq(), _wq()) == UNSUP                      # MXFP4 weights only
+    assert f(_wq(**mx), _wq(**mx), mul=2) == UNSUP       # no routing weight on the input
+    assert f(_wq(**mx), _wq(**mx)) == WS
+    assert L.moe_forward_mxfp8_workspace_bytes(64, 32, 4, 2880, 2880) > \
+        L.moe_forward_workspace_bytes(64, 32, 4, 2880, 2880)
