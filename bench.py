@@ -18,6 +18,11 @@ Prints ONE JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 with plain (group-ordered) weights against the same layer quantised in
 activation order (both families sorted at load time, inputs gathered per slot
 at run time), and the gather kernel alone; reported under "act_order".
+
+--mxfp8 adds a leg on the gpt-oss-120b-shaped MXFP4 layer (E=128, top-4,
+2880/2880): bf16 activations against MXFP8 activations (moe_forward_mxfp8),
+and GEMM1 alone on the MX-scaled matrix cores against its fp8 peak; reported
+under "mxfp8".
 """
 from __future__ import annotations
 
@@ -157,6 +162,64 @@ def act_order_leg(args, time_calls):
                         "plain vs activation-order weights", "rows": rows}
 
 
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, TFLOP/s (e4m3 x e2m1 runs at the fp8 rate)
+
+
+def mxfp8_leg(args, time_calls):
+    """gpt-oss-120b-shaped MXFP4 layer: bf16 vs MXFP8 activations, and GEMM1 alone."""
+    import torch
+    import synthetic as S
+    import bit_weight_expert_amd as M
+
+    ts = [int(t) for t in args.mxfp8_tokens.split(",") if t]
+    t0 = time.time()
+    L = S.make_config(4)
+    log(f"mxfp8 leg: generated the {S.CONFIGS[4]['name']} inputs in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda")
+    copies = []
+    for _ in range(max(1, min(args.copies, 3))):   # 3 x 2.4 GB: each call misses the 256 MB cache
+        copies.append(tuple(M.QuantWeights.from_arrays(w.fmt, w.group, w.N, w.K, w.qweight, w.scales,
+                                                       None, None, w.bias) for w in (L.w13, L.w2)))
+    x = torch.from_numpy(L.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    logits = torch.from_numpy(L.logits).to(dev)
+    tmax = max(ts)
+    ws = torch.empty((max(M.moe_forward_mxfp8_workspace_bytes(tmax, L.E, L.top_k, L.H, L.I),
+                          M.moe_forward_workspace_bytes(tmax, L.E, L.top_k, L.H, L.I)),),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((tmax, L.H), dtype=torch.bfloat16, device=dev)
+    rows = []
+    for T in ts:
+        r = {"T": T, "block_m": M.moe_forward_block_m(T, L.top_k, L.E)}
+        for name, fn in (("bf16", M.moe_forward), ("mxfp8", M.moe_forward_mxfp8)):
+            def f(i, fn=fn):
+                w13, w2 = copies[i % len(copies)]
+                fn(x[:T], logits[:T], L.top_k, L.I, w13, w2, act=L.act, route=L.route,
+                   renormalize=L.renormalize, alpha=L.alpha, beta=L.beta, limit=L.limit,
+                   mul_topk_weights=L.mul_topk_weights, workspace=ws, out=out[:T])
+            r[f"{name}_us"] = time_calls(f, max(args.steps, 20), args.warmup) * 1e3
+        r["speedup"] = r["bf16_us"] / r["mxfp8_us"]
+        if r["block_m"] >= 64:
+            # GEMM1 alone on the MX-scaled matrix cores
+            bm = r["block_m"]
+            ids, tw, si, ei, npp = M.moe_route_align(logits[:T], L.top_k, bm, L.route, None,
+                                                     L.renormalize)
+            xc, xs, _ = M.moe_mxfp8_quantize(x[:T])
+            act = torch.empty((T * L.top_k, L.I), dtype=torch.bfloat16, device=dev)
+            g_ms = time_calls(lambda i: M.moe_mx_gemm1(xc, xs, L.top_k, L.H, copies[i % len(copies)][0],
+                                                       L.act, L.alpha, L.beta, L.limit, si, ei, npp,
+                                                       bm, out=act), max(args.steps, 20), args.warmup)
+            fl = 2.0 * T * L.top_k * L.H * L.w13.N
+            r.update(gemm1_us=g_ms * 1e3, gemm1_TFLOPs=fl / (g_ms * 1e-3) / 1e12,
+                     gemm1_fp8_frac=fl / (g_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS)
+        log(f"mxfp8 T={T}: bf16 {r['bf16_us']:.1f} us, mxfp8 {r['mxfp8_us']:.1f} us "
+            f"(x{r['speedup']:.2f})" + (f", MX GEMM1 {r['gemm1_us']:.1f} us = {r['gemm1_TFLOPs']:.0f} "
+                                        f"TFLOP/s ({r['gemm1_fp8_frac'] * 100:.1f}% of fp8)"
+                                        if "gemm1_us" in r else ""))
+        rows.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+    return {"workload": "gpt-oss-120b-shaped MoE layer, MXFP4 weights (E=128, top_k=4, 2880/2880, "
+                        "skewed routing), bf16 vs MXFP8 activations", "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +234,9 @@ def main() -> int:
     ap.add_argument("--act-order", action="store_true",
                     help="also time the GPTQ layer with act-order weights (and its gather)")
     ap.add_argument("--act-order-tokens", default="1,64,2048")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="also time the MXFP4 layer with MXFP8 activations")
+    ap.add_argument("--mxfp8-tokens", default="1,128,1024,8192")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -314,6 +380,7 @@ def main() -> int:
         log(f"oracle: {n} tokens in {dt:.1f}s")
 
     act_order = act_order_leg(args, time_calls) if args.act_order else None
+    mxfp8 = mxfp8_leg(args, time_calls) if args.mxfp8 else None
 
     line = {
         "metric": "fused W4A16 MoE layer tokens/s + % HBM/MFMA roofline, E32 top4 h2880",
@@ -339,6 +406,7 @@ def main() -> int:
                            "GBps": head["GBps"], "TFLOPs": head["TFLOPs"]},
         "cpu_baseline": cpu,
         "act_order": act_order,
+        "mxfp8": mxfp8,
         "sweep": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in results[t].items()}
                   for t in sweep],
     }

@@ -1734,26 +1734,24 @@ __device__ __forceinline__ int mx_bpos(int r) {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16e __attribute__((ext_vector_type(16)));
 
-template <int OPSEL>
-__device__ __forceinline__ void mx_mfma(f32x16& acc, const i32x8& a, const i32x8& b, int sa, int sb) {
-  f32x16e c;
-  __builtin_memcpy(&c, &acc, sizeof(c));
-  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, OPSEL, sa, OPSEL, sb);
-  __builtin_memcpy(&acc, &c, sizeof(c));
-}
-
-// One 64-deep step st (0 or 1) of chunk stage `stg`: A reads, weight reads, MFMAs.
-template <int EPI, int MI, int NF, int ST>
-__device__ __forceinline__ void mx_step(f32x16 (&acc)[MI][NF], const uint8_t* stg, int abytes,
-                                        const int (&bpos)[NF], int c, int g, const int (&sa)[MI],
-                                        const int (&sb)[NF]) {
+// Operands of one 64-deep step: A fragments of the MI row tiles, weight
+// fragments of the NF column fragments.
+template <int MI, int NF>
+struct MxOps {
+  i32x8 a[MI];
   i32x8 b[NF];
+};
+
+// LDS reads of step ST (0 or 1) of the chunk in stage `stg`.
+template <int MI, int NF, int ST>
+__device__ __forceinline__ void mx_read(MxOps<MI, NF>& o, const uint8_t* stg, int abytes,
+                                        const int (&bpos)[NF], int c, int g) {
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     const int p = bpos[j];
     const uint4 v = *reinterpret_cast<const uint4*>(stg + abytes + p * 64 +
                                                     16 * ((2 * ST + g) ^ ((p >> 2) & 3)));
-    b[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    o.b[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
   }
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
@@ -1761,9 +1759,39 @@ __device__ __forceinline__ void mx_step(f32x16 (&acc)[MI][NF], const uint8_t* st
     const uint8_t* row = stg + r * 128;
     const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * ((4 * ST + g) ^ (r & 7)));
     const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * ((4 * ST + 2 + g) ^ (r & 7)));
-    const i32x8 a{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    o.a[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+}
+
+// The MI x NF MFMAs of one step; byte 2*ST of each scale word is the lane's block.
+template <int MI, int NF, int ST>
+__device__ __forceinline__ void mx_mfma(f32x16e (&acc)[MI][NF], const MxOps<MI, NF>& o,
+                                        const int (&sa)[MI], const int (&sb)[NF]) {
 #pragma unroll
-    for (int j = 0; j < NF; ++j) mx_mfma<2 * ST>(acc[i][j], a, b[j], sa[i], sb[j]);
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[i], o.b[j], acc[i][j], 0, 4,
+                                                                   2 * ST, sa[i], 2 * ST, sb[j]);
+}
+
+// Scale words of chunk kc: A dword of blocks 4kc..4kc+3 shifted so bytes 0 / 2
+// are this lane's blocks of steps 0 / 1; weight bytes likewise (blocks past
+// K/32 read as 2^0: their A codes are zero).
+template <int MI, int NF>
+__device__ __forceinline__ void mx_scales(int (&sa)[MI], int (&sb)[NF], const uint8_t* sca, int lds,
+                                          const uint8_t* scb, int kb, const int (&rl)[NF], int c,
+                                          int g, int kc) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+    sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sca + (32 * i + c) * lds + 4 * kc) >> (8 * g));
+  const int b0 = 4 * kc + g, b1 = 4 * kc + 2 + g;
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const uint8_t* sr = scb + rl[j] * kb;
+    const int s0 = sr[min(b0, kb - 1)];
+    const int s1 = sr[min(b1, kb - 1)];
+    sb[j] = (b0 < kb ? s0 : 127) | ((b1 < kb ? s1 : 127) << 16);
   }
 }
 
@@ -1866,7 +1894,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, We
     bpos[j] = mx_bpos<EPI>(rl[j]);
   }
 
-  f32x16 acc[MI][NF];
+  f32x16e acc[MI][NF];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -1874,33 +1902,33 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, We
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // scales and chunk 0 have landed
+  // scales and chunk 0 have landed.  Both 64-deep steps of every chunk run
+  // (past K the A codes are zero), so the loop has no branch; each step's
+  // LDS reads are issued while the other step's MFMAs run.
   wait_vmcnt<(kMxStages - 1) * P::kIssue>();
   pf_barrier();
+  MxOps<MI, NF> o0, o1;
+  int sa[MI], sb[NF];
+  mx_scales<MI, NF>(sa, sb, sca, ma.lds, scb, kb, rl, c, g, 0);
+  mx_read<MI, NF, 0>(o0, smem, P::kABytes, bpos, c, g);
   for (int kc = 0; kc < nchunks; ++kc) {
     const uint8_t* stg = smem + (kc % kMxStages) * P::kStage;
-    // scales of the chunk: A dword of blocks 4kc..4kc+3 shifted so byte 0 /
-    // byte 2 are this lane's blocks of steps 0 / 1; weight bytes likewise
-    // (blocks past K/32 read as 2^0: their A codes are zero)
-    int sa[MI], sb[NF];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-      sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sca + (32 * i + c) * ma.lds + 4 * kc) >> (8 * g));
-    const int b0 = 4 * kc + g, b1 = 4 * kc + 2 + g;
-#pragma unroll
-    for (int j = 0; j < NF; ++j) {
-      const uint8_t* sr = scb + rl[j] * kb;
-      const int s0 = b0 < kb ? sr[b0] : 127;
-      const int s1 = b1 < kb ? sr[b1] : 127;
-      sb[j] = s0 | (s1 << 16);
-    }
-    mx_step<EPI, MI, NF, 0>(acc, stg, P::kABytes, bpos, c, g, sa, sb);
-    if (kc * kMxBK + 64 < K) mx_step<EPI, MI, NF, 1>(acc, stg, P::kABytes, bpos, c, g, sa, sb);
+    mx_read<MI, NF, 1>(o1, stg, P::kABytes, bpos, c, g);
+    mx_mfma<MI, NF, 0>(acc, o0, sa, sb);
     // chunk kc+1 has landed (only chunk kc+2 may be in flight) and every wave
     // is past its reads of chunk kc, whose stage takes chunk kc+3
     wait_vmcnt<P::kIssue>();
     pf_barrier();
     issue(ring + (kc % kMxStages) * P::kStage, min(kc + kMxStages, nchunks - 1));
+    int na_[MI], nb_[NF];
+    const int kn = min(kc + 1, nchunks - 1);
+    mx_scales<MI, NF>(na_, nb_, sca, ma.lds, scb, kb, rl, c, g, kn);
+    mx_read<MI, NF, 0>(o0, smem + (kn % kMxStages) * P::kStage, P::kABytes, bpos, c, g);
+    mx_mfma<MI, NF, 1>(acc, o1, sa, sb);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) sa[i] = na_[i];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) sb[j] = nb_[j];
   }
   // no DMA may land in LDS after this workgroup is gone
   wait_vmcnt<0>();
@@ -1908,7 +1936,14 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, We
   if (n0 >= N) return;
   EpiArgs a = ea;
   a.row0 = mb * BM;
-  epilogue32<EPI, FMT_MXFP4, MI, NF>(acc, a, W, e, n0, lane);
+  f32x16 accv[MI][NF];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) accv[i][j][v] = acc[i][j][v];
+  epilogue32<EPI, FMT_MXFP4, MI, NF>(accv, a, W, e, n0, lane);
 }
 
 template <int FMT>
