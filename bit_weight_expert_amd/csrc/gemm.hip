@@ -1699,15 +1699,20 @@ constexpr int kMxStages = 3;
 constexpr int kMxScaleBytes = 56 * 1024;
 constexpr int kMxScaleIssue = 6;  // A-scale DMA instructions per wave (BM * lds <= 1536 pieces)
 
-template <int BM>
+// RS = 2: eight waves, waves w and w + 4 take the same weight rows and one
+// half of the A rows each, so one wave's LDS reads and waits overlap the
+// other's MFMAs on the same SIMD.
+template <int BM, int RS = 1>
 struct Mx {
-  static constexpr int MI = BM / 32;
+  static constexpr int NW = 4 * RS;                   // waves
+  static constexpr int MI = BM / 32 / RS;             // 32-row tiles per wave
   static constexpr int NF = 2;
   static constexpr int BN = 4 * NF * 32;
   static constexpr int kABytes = BM * kMxBK;
   static constexpr int kBBytes = BN * kMxBK / 2;
-  static constexpr int kAIssue = kABytes / 1024 / 4;  // DMA instructions per wave per chunk
-  static constexpr int kBIssue = kBBytes / 1024 / 4;
+  static constexpr int kAIssue = kABytes / 1024 / NW;  // DMA instructions per wave per chunk
+  static constexpr int kBIssue = kBBytes / 1024 / NW;
+  static constexpr int kSIssue = (4 * kMxScaleIssue + NW - 1) / NW;  // A-scale DMA per wave
   static constexpr int kIssue = kAIssue + kBIssue;
   static constexpr int kStage = kABytes + kBBytes;
   static constexpr int kLds = kMxStages * kStage + kMxScaleBytes;
@@ -1742,10 +1747,10 @@ struct MxOps {
   i32x8 b[NF];
 };
 
-// LDS reads of step ST (0 or 1) of the chunk in stage `stg`.
+// LDS reads of step ST (0 or 1) of the chunk in stage `stg` (A rows from r0).
 template <int MI, int NF, int ST>
 __device__ __forceinline__ void mx_read(MxOps<MI, NF>& o, const uint8_t* stg, int abytes,
-                                        const int (&bpos)[NF], int c, int g) {
+                                        const int (&bpos)[NF], int c, int g, int r0) {
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     const int p = bpos[j];
@@ -1755,7 +1760,7 @@ __device__ __forceinline__ void mx_read(MxOps<MI, NF>& o, const uint8_t* stg, in
   }
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    const int r = 32 * i + c;
+    const int r = r0 + 32 * i + c;
     const uint8_t* row = stg + r * 128;
     const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * ((4 * ST + g) ^ (r & 7)));
     const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * ((4 * ST + 2 + g) ^ (r & 7)));
@@ -1781,10 +1786,10 @@ __device__ __forceinline__ void mx_mfma(f32x16e (&acc)[MI][NF], const MxOps<MI, 
 template <int MI, int NF>
 __device__ __forceinline__ void mx_scales(int (&sa)[MI], int (&sb)[NF], const uint8_t* sca, int lds,
                                           const uint8_t* scb, int kb, const int (&rl)[NF], int c,
-                                          int g, int kc) {
+                                          int g, int kc, int r0) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
-    sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sca + (32 * i + c) * lds + 4 * kc) >> (8 * g));
+    sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sca + (r0 + 32 * i + c) * lds + 4 * kc) >> (8 * g));
   const int b0 = 4 * kc + g, b1 = 4 * kc + 2 + g;
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
@@ -1795,31 +1800,33 @@ __device__ __forceinline__ void mx_scales(int (&sa)[MI], int (&sb)[NF], const ui
   }
 }
 
-template <int EPI, int BM>
-__global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, WeightArgs W, EpiArgs ea) {
-  using P = Mx<BM>;
-  constexpr int MI = P::MI, NF = P::NF;
+template <int EPI, int BM, int RS>
+__global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, WeightArgs W, EpiArgs ea) {
+  using P = Mx<BM, RS>;
+  constexpr int MI = P::MI, NF = P::NF, NW = P::NW;
   __shared__ __attribute__((aligned(16))) uint8_t smem[P::kLds];
 
   int mb, nt;
   if (!prefill_tile(ga, BM, mb, nt)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int c = lane & 31, g = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // DMA share (0 .. NW-1)
+  const int wave_u = wave & 3;                                 // weight-row group
+  const int r0 = (wave >> 2) * MI * 32;                        // this wave's first A row
   const int K = ga.K, N = ga.N, kb = K / 32;
 
-  // slot ids of the A rows this lane copies (instruction q = 4p + wave covers
-  // rows 8q .. 8q+7) and of the A scale rows (instruction q = 4i + wave covers
-  // 16-byte pieces 64q .. 64q+63 of the [BM][lds] tile), all requested before
-  // anything waits
+  // slot ids of the A rows this lane copies (instruction q = NW*p + wave covers
+  // rows 8q .. 8q+7) and of the A scale rows (instruction q = NW*i + wave
+  // covers 16-byte pieces 64q .. 64q+63 of the [BM][lds] tile), all requested
+  // before anything waits
   const int parts = ma.lds / 16;
   const int na = BM * parts;
-  int sid[P::kAIssue], ssid[kMxScaleIssue];
+  int sid[P::kAIssue], ssid[P::kSIssue];
 #pragma unroll
-  for (int p = 0; p < P::kAIssue; ++p) sid[p] = ga.sorted_ids[mb * BM + 8 * (4 * p + wave) + (lane >> 3)];
+  for (int p = 0; p < P::kAIssue; ++p) sid[p] = ga.sorted_ids[mb * BM + 8 * (NW * p + wave) + (lane >> 3)];
 #pragma unroll
-  for (int i = 0; i < kMxScaleIssue; ++i) {
-    const int pc = min((4 * i + wave) * 64 + lane, na - 1);  // lanes past the end repeat the last piece
+  for (int i = 0; i < P::kSIssue; ++i) {
+    const int pc = min((NW * i + wave) * 64 + lane, na - 1);  // lanes past the end repeat the last piece
     ssid[i] = ga.sorted_ids[mb * BM + pc / parts];
   }
   const int e = ga.expert_ids[mb];
@@ -1827,13 +1834,13 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, We
 
   const int nt0 = nt * P::BN;
   const int rows = min(P::BN, N - nt0);
-  const int n0 = nt0 + wave * NF * 32;
+  const int n0 = nt0 + wave_u * NF * 32;
 
   // DMA sources.  A: lane l fetches logical slot (l%8) ^ (row%8) of row 8q + l/8.
   const uint8_t* arow[P::kAIssue];
 #pragma unroll
   for (int p = 0; p < P::kAIssue; ++p) {
-    const int r = 8 * (4 * p + wave) + (lane >> 3);
+    const int r = 8 * (NW * p + wave) + (lane >> 3);
     const int s = sid[p];
     const int row = s < ga.n_slots ? (int)(((uint64_t)(uint32_t)s * ga.a_mul) >> 32) : 0;
     arow[p] = ma.codes + (size_t)row * ma.lda + 16 * ((lane & 7) ^ (r & 7));
@@ -1845,7 +1852,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, We
   int bls[P::kBIssue];
 #pragma unroll
   for (int p = 0; p < P::kBIssue; ++p) {
-    const int pos = 16 * (4 * p + wave) + (lane >> 2);
+    const int pos = 16 * (NW * p + wave) + (lane >> 2);
     const int n = min(nt0 + pf_brow<EPI>(pos >> 5, pos & 31), N - 1);
     brow[p] = W.qweight + ((size_t)e * N + n) * (K / 2);
     bls[p] = 16 * ((lane & 3) ^ ((pos >> 2) & 3));
@@ -1861,11 +1868,13 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, We
 
   // weight scales of the tile rows (contiguous), then the A scale rows
   {
-    const int nb = rows * kb;
-    pf_dma_region(scb_lds, W.scales + ((size_t)e * N + nt0) * kb, 0, nb, nb, nb, wave, lane);
+    const int nb = rows * kb;   // a multiple of 16 (N % 16 == 0)
+    const uint8_t* src = W.scales + ((size_t)e * N + nt0) * kb;
+    for (int q = wave; q * 1024 < nb; q += NW)
+      if (q * 1024 + 16 * lane < nb) dma16(src + q * 1024 + 16 * lane, scb_lds + q * 1024);
 #pragma unroll
-    for (int i = 0; i < kMxScaleIssue; ++i) {
-      const int q = 4 * i + wave;
+    for (int i = 0; i < P::kSIssue; ++i) {
+      const int q = NW * i + wave;
       if (q * 64 >= na) break;
       const int pc = min(q * 64 + lane, na - 1);
       const int s = ssid[i];
@@ -1876,11 +1885,11 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, We
   auto issue = [&](uint32_t stage, int kc) {
 #pragma unroll
     for (int p = 0; p < P::kAIssue; ++p)
-      dma16(arow[p] + kc * kMxBK, stage + (uint32_t)(4 * p + wave) * 1024u);
+      dma16(arow[p] + kc * kMxBK, stage + (uint32_t)(NW * p + wave) * 1024u);
 #pragma unroll
     for (int p = 0; p < P::kBIssue; ++p)
       dma16(brow[p] + min(kc * (kMxBK / 2) + bls[p], K / 2 - 16),
-            stage + P::kABytes + (uint32_t)(4 * p + wave) * 1024u);
+            stage + P::kABytes + (uint32_t)(NW * p + wave) * 1024u);
   };
 #pragma unroll
   for (int s = 0; s < kMxStages; ++s) issue(ring + s * P::kStage, min(s, nchunks - 1));
@@ -1909,11 +1918,11 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, We
   pf_barrier();
   MxOps<MI, NF> o0, o1;
   int sa[MI], sb[NF];
-  mx_scales<MI, NF>(sa, sb, sca, ma.lds, scb, kb, rl, c, g, 0);
-  mx_read<MI, NF, 0>(o0, smem, P::kABytes, bpos, c, g);
+  mx_scales<MI, NF>(sa, sb, sca, ma.lds, scb, kb, rl, c, g, 0, r0);
+  mx_read<MI, NF, 0>(o0, smem, P::kABytes, bpos, c, g, r0);
   for (int kc = 0; kc < nchunks; ++kc) {
     const uint8_t* stg = smem + (kc % kMxStages) * P::kStage;
-    mx_read<MI, NF, 1>(o1, stg, P::kABytes, bpos, c, g);
+    mx_read<MI, NF, 1>(o1, stg, P::kABytes, bpos, c, g, r0);
     mx_mfma<MI, NF, 0>(acc, o0, sa, sb);
     // chunk kc+1 has landed (only chunk kc+2 may be in flight) and every wave
     // is past its reads of chunk kc, whose stage takes chunk kc+3
@@ -1922,8 +1931,8 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, We
     issue(ring + (kc % kMxStages) * P::kStage, min(kc + kMxStages, nchunks - 1));
     int na_[MI], nb_[NF];
     const int kn = min(kc + 1, nchunks - 1);
-    mx_scales<MI, NF>(na_, nb_, sca, ma.lds, scb, kb, rl, c, g, kn);
-    mx_read<MI, NF, 0>(o0, smem + (kn % kMxStages) * P::kStage, P::kABytes, bpos, c, g);
+    mx_scales<MI, NF>(na_, nb_, sca, ma.lds, scb, kb, rl, c, g, kn, r0);
+    mx_read<MI, NF, 0>(o0, smem + (kn % kMxStages) * P::kStage, P::kABytes, bpos, c, g, r0);
     mx_mfma<MI, NF, 1>(acc, o1, sa, sb);
 #pragma unroll
     for (int i = 0; i < MI; ++i) sa[i] = na_[i];
@@ -1935,7 +1944,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, We
 
   if (n0 >= N) return;
   EpiArgs a = ea;
-  a.row0 = mb * BM;
+  a.row0 = mb * BM + r0;
   f32x16 accv[MI][NF];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -1996,12 +2005,13 @@ extern "C" hipError_t moe_launch_gemm_mx(int epi, int block_m, int cap, const ui
   moe::MxA ma{a_codes, a_scales, lda, lds};
   moe::EpiArgs ea{sid, 0, n_slots, N, tw, mul, alpha, beta, limit, out, out_ld};
   const dim3 grid((ga.n_mblocks * ga.n_ntiles + 7) / 8 * 8);
+  constexpr int kMxRS = 2;
 #define MOE_MX_LAUNCH(EPI)                                                                  \
   do {                                                                                      \
     if (block_m == 64)                                                                      \
-      moe::gemm_mx_kernel<EPI, 64><<<grid, dim3(256), 0, st>>>(ga, ma, *W, ea);             \
+      moe::gemm_mx_kernel<EPI, 64, kMxRS><<<grid, dim3(256 * kMxRS), 0, st>>>(ga, ma, *W, ea); \
     else                                                                                    \
-      moe::gemm_mx_kernel<EPI, 128><<<grid, dim3(256), 0, st>>>(ga, ma, *W, ea);            \
+      moe::gemm_mx_kernel<EPI, 128, kMxRS><<<grid, dim3(256 * kMxRS), 0, st>>>(ga, ma, *W, ea); \
   } while (0)
   switch (epi) {
     case moe::EPI_SWIGLU: MOE_MX_LAUNCH(moe::EPI_SWIGLU); break;
