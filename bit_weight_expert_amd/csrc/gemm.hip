@@ -393,6 +393,11 @@ constexpr int kPfBK = 64;                  // K chunk
 // costs more than the overlap gains: GPTQ measured 13% slower).
 template <int FMT>
 constexpr int pf_rs() { return FMT == FMT_MXFP4 ? 2 : 1; }
+// K split (KS = 2): eight waves, waves w and w + 4 take the same rows and
+// columns and alternate MFMA steps (two of the four of each chunk), so no
+// dequant or LDS read is done twice; their sums meet through LDS at the end.
+template <int FMT>
+constexpr int pf_ks() { return FMT == FMT_MXFP4 ? 1 : 2; }
 constexpr int kPfStages = 4;               // LDS ring depth
 constexpr int kPfScaleBytes = 60 * 1024;   // LDS for the tile's scales over all of K
 
@@ -759,8 +764,8 @@ __device__ __forceinline__ void pf_tail32(f32x16 (&acc)[MI][NF], const GemmArgs&
   pf_mfma<MI, NF>(acc, a1, b1);
 }
 
-template <int FMT, int EPI, int BM, int NF, int RS>
-__global__ void __launch_bounds__(256 * RS, 1) gemm_prefill_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
+template <int FMT, int EPI, int BM, int NF, int RS, int KS>
+__global__ void __launch_bounds__(256 * RS * KS, 1) gemm_prefill_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
   using P = Pf<BM, NF>;
   // RS = 2: eight waves, two per SIMD; waves w and w + 4 take the same
   // columns and one half of the rows each (both dequantise the same codes),
@@ -776,8 +781,9 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_prefill_kernel(GemmArgs ga, 
   const int c = lane & 31, h = lane >> 5;
   const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_u = wave_all & 3;            // column group, and DMA share
-  const int rpart = wave_all >> 2;            // row part (RS = 2)
-  const bool dma_wave = rpart == 0;
+  const int rpart = RS == 2 ? wave_all >> 2 : 0;  // row part (RS = 2)
+  const int kp = KS == 2 ? wave_all >> 2 : 0;     // K part (KS = 2): MFMA steps 2kp, 2kp+1
+  const bool dma_wave = (wave_all >> 2) == 0;
   const int aoff = rpart * MI * 32 * 128;     // this wave's rows in an A stage
   const int K = ga.K, N = ga.N;
 
@@ -863,7 +869,38 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_prefill_kernel(GemmArgs ga, 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  if (nchunks > 0) {
+  if (KS == 2 && nchunks > 0) {
+    wait_vmcnt<3 * P::kIssue>();
+    pf_barrier();
+    const int s0 = 2 * kp, s1 = 2 * kp + 1;
+    PfB b[NF];
+    uint4 a0[MI], a1[MI];
+    bf16x8 q0[NF], q1[NF];
+    pf_read_b<FMT, EPI, NF>(b, smem + P::kABytes, scale_lds, rl, 0, h, K, W.group, P::BN);
+    pf_read_a<MI>(a0, smem + aoff, c, h, s0);
+#pragma unroll
+    for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], s0);
+    for (int kc = 0; kc < nchunks; ++kc) {
+      const uint8_t* st = smem + (kc % kPfStages) * P::kStage + aoff;
+      pf_read_a<MI>(a1, st, c, h, s1);
+#pragma unroll
+      for (int j = 0; j < NF; ++j) q1[j] = pf_deq_step<FMT>(b[j], s1);
+      pf_mfma<MI, NF>(acc, a0, q0);
+      // chunk kc+1 has landed and every wave is past its reads of chunk kc
+      wait_vmcnt<2 * P::kIssue>();
+      pf_barrier();
+      if (dma_wave)
+        pf_issue<FMT, BM, NF>(ring + (kc % kPfStages) * P::kStage, arow, brow,
+                              min(kc + kPfStages, nchunks - 1), wave_u, N);
+      const uint8_t* nx = smem + ((kc + 1) % kPfStages) * P::kStage;
+      pf_read_b<FMT, EPI, NF>(b, nx + P::kABytes, scale_lds, rl, min(kc + 1, nchunks - 1), h, K,
+                              W.group, P::BN);
+      pf_read_a<MI>(a0, nx + aoff, c, h, s0);
+      pf_mfma<MI, NF>(acc, a1, q1);
+#pragma unroll
+      for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], s0);
+    }
+  } else if (nchunks > 0) {
     // scales and chunk 0 have landed (chunks 1..3 may still be in flight)
     wait_vmcnt<3 * P::kIssue>();
     pf_barrier();
@@ -912,7 +949,58 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_prefill_kernel(GemmArgs ga, 
   wait_vmcnt<0>();
 
   const int row0 = mb * BM + rpart * MI * 32;
-  if (K % kPfBK) pf_tail32<FMT, EPI, MI, NF>(acc, ga, W, e, row0, n0, c, h, nchunks * kPfBK);
+  if (K % kPfBK && kp == 0) pf_tail32<FMT, EPI, MI, NF>(acc, ga, W, e, row0, n0, c, h, nchunks * kPfBK);
+
+  if constexpr (KS == 2) {
+    // the two K parts meet: each wave hands over the half of the rows the
+    // other finalises (lane-major in LDS, the ring is free now), then adds
+    // the other's half of its own rows and runs the epilogue on them
+    constexpr int HM = MI / 2;
+    constexpr int kRed = HM * NF * 16 * 64;  // floats per wave
+    float* red = reinterpret_cast<float*>(smem);
+    pf_barrier();
+    float* mine = red + (size_t)(wave_u * 2 + kp) * kRed;
+    const float* theirs = red + (size_t)(wave_u * 2 + (1 - kp)) * kRed;
+    f32x16 acch[HM][NF];
+    if (kp == 0) {
+#pragma unroll
+      for (int i = 0; i < HM; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mine[((i * NF + j) * 16 + v) * 64 + lane] = acc[HM + i][j][v];
+    } else {
+#pragma unroll
+      for (int i = 0; i < HM; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mine[((i * NF + j) * 16 + v) * 64 + lane] = acc[i][j][v];
+    }
+    pf_barrier();
+    if (kp == 0) {
+#pragma unroll
+      for (int i = 0; i < HM; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            acch[i][j][v] = acc[i][j][v] + theirs[((i * NF + j) * 16 + v) * 64 + lane];
+    } else {
+#pragma unroll
+      for (int i = 0; i < HM; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            acch[i][j][v] = theirs[((i * NF + j) * 16 + v) * 64 + lane] + acc[HM + i][j][v];
+    }
+    if (n0 >= N) return;
+    EpiArgs a = ea;
+    a.row0 = row0 + kp * HM * 32;
+    epilogue32<EPI, FMT, HM, NF>(acch, a, W, e, n0, lane);
+    return;
+  }
 
   if (n0 >= N) return;
   EpiArgs a = ea;
@@ -1656,9 +1744,11 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
     ga.group_m = 4;  // measured flat between 1 and 16 at the gpt-oss-20b shape
     const dim3 grid((ga.n_mblocks * ga.n_ntiles + 7) / 8 * 8);
     if (block_m == 64)
-      gemm_prefill_kernel<FMT, EPI, 64, 2, pf_rs<FMT>()><<<grid, dim3(256 * pf_rs<FMT>()), 0, st>>>(ga, W, ea);
+      gemm_prefill_kernel<FMT, EPI, 64, 2, pf_rs<FMT>(), pf_ks<FMT>()>
+          <<<grid, dim3(256 * pf_rs<FMT>() * pf_ks<FMT>()), 0, st>>>(ga, W, ea);
     else
-      gemm_prefill_kernel<FMT, EPI, 128, 2, pf_rs<FMT>()><<<grid, dim3(256 * pf_rs<FMT>()), 0, st>>>(ga, W, ea);
+      gemm_prefill_kernel<FMT, EPI, 128, 2, pf_rs<FMT>(), pf_ks<FMT>()>
+          <<<grid, dim3(256 * pf_rs<FMT>() * pf_ks<FMT>()), 0, st>>>(ga, W, ea);
   }
   return hipGetLastError();
 }
