@@ -147,3 +147,11 @@ def test_forward_act_order_full_size(T):
     got = host_bf16(out)
     assert np.isfinite(got).all()
     assert_rows_close(got[toks], ref, what=f"act-order full size T{T}")
+
+
+def test_forward_act_order_empty_batch():
+    L = _layer(T=4)
+    D = upload(L)
+    D["w13"], D["w2"] = prepare(L.w13, D["w13"]), prepare(L.w2, D["w2"])
+    out = M.moe_forward(D["x"][:0], D["logits"][:0], L.top_k, L.I, D["w13"], D["w2"])
+    assert out.shape == (0, L.H)

@@ -236,3 +236,27 @@ def test_forward_mxfp8_full_size(T):
     assert np.isfinite(got).all()
     bits = act_gpu.view(torch.int16).cpu().numpy().view(np.uint16)
     _check_layer(L, D, got, bits, toks)
+
+
+def test_mx_gemm1_longest_k_that_fits():
+    """K = 4608: both scale tiles just fit the kernel's LDS and the A scale
+    tile takes 18 of its 24 DMA instructions."""
+    L = _layer("swigluoai", E=3, H=4608, I=64, T=100)
+    D = upload(L)
+    ids, w = O.route(L)
+    si, ei, npp = O.align(ids, L.E, 64)
+    xc, xs = F.quantize_mxfp8(F.bf16_to_f64(L.x))
+    dc, ds = _up_mx(xc, xs, L.H)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out = M.moe_mx_gemm1(dc, ds, L.top_k, L.H, D["w13"], "swigluoai", L.alpha, L.beta, L.limit,
+                         t(si), t(ei), t(np.array([npp], np.int32)), 64)
+    ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, "swigluoai", L.alpha, L.beta, L.limit, si, ei,
+                       npp, 64, act_fmt="mxfp8")
+    assert_rows_close(host_bf16(out), ref, rows=cov, what="mx gemm1 K=4608")
+
+
+def test_forward_mxfp8_empty_batch():
+    L = _layer(T=4)
+    D = upload(L)
+    out = M.moe_forward_mxfp8(D["x"][:0], D["logits"][:0], L.top_k, L.I, D["w13"], D["w2"])
+    assert out.shape == (0, L.H)
