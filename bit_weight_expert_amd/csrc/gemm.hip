@@ -656,9 +656,12 @@ __device__ __forceinline__ int frag32_row(int n0, int j, int c) {
 
 // Epilogue of the 32x32 accumulators: lane (c, h) holds column c of every
 // fragment and rows 8*(v/4) + 4h + v%4 (v = 0..15) of every 32-row fragment.
+// rows: null, or the block's (slot id, routing weight bits) pairs in LDS,
+// indexed by the row within the block; rloc0 is this wave's first such row.
 template <int EPI, int FMT, int MI, int NF>
 __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const EpiArgs& a,
-                                           const WeightArgs& W, int e, int n0, int lane) {
+                                           const WeightArgs& W, int e, int n0, int lane,
+                                           const int2* rows = nullptr, int rloc0 = 0) {
   const int c = lane & 31, h = lane >> 5;
   const float gsc = (FMT == FMT_NVFP4) ? W.global_scale[e] : 1.f;
   // bias: unconditional loads (another valid word when there is none)
@@ -685,21 +688,32 @@ __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const Ep
   // slot ids one row group ahead of their use, so each group's loads overlap
   // the previous group's stores
   int sid_next[16];
+  if (rows == nullptr) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) sid_next[v] = a.sorted_ids[a.row0 + 8 * (v >> 2) + 4 * h + (v & 3)];
+    for (int v = 0; v < 16; ++v) sid_next[v] = a.sorted_ids[a.row0 + 8 * (v >> 2) + 4 * h + (v & 3)];
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     int sid[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sid[v] = sid_next[v];
     float tws[16];
+    if (rows != nullptr) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      tws[v] = tbase[min(sid[v], a.n_slots - 1) * tmul];
-    if (i + 1 < MI) {
+      for (int v = 0; v < 16; ++v) {
+        const int2 r = rows[rloc0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3)];
+        sid[v] = r.x;
+        tws[v] = __int_as_float(r.y);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sid[v] = sid_next[v];
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        sid_next[v] = a.sorted_ids[a.row0 + (i + 1) * 32 + 8 * (v >> 2) + 4 * h + (v & 3)];
+        tws[v] = tbase[min(sid[v], a.n_slots - 1) * tmul];
+      if (i + 1 < MI) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          sid_next[v] = a.sorted_ids[a.row0 + (i + 1) * 32 + 8 * (v >> 2) + 4 * h + (v & 3)];
+      }
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -794,6 +808,9 @@ __global__ void __launch_bounds__(256 * RS * KS, 1) gemm_prefill_kernel(GemmArgs
   for (int p = 0; p < P::kAIssue; ++p) sid[p] = ga.sorted_ids[mb * BM + 8 * (4 * p + wave_u) + (lane >> 3)];
   const int e = ga.expert_ids[mb];
   if (e < 0 || e >= ga.E) return;
+  // slot id of block row tid, for the epilogue: requested now, first used
+  // after the K loop, so its latency hides behind the loop
+  const int row_sid = ga.sorted_ids[mb * BM + min(tid, BM - 1)];
 
   const int nt0 = nt * P::BN;             // first weight row of the tile
   const int rows = min(P::BN, N - nt0);   // valid weight rows of the tile
@@ -951,6 +968,16 @@ __global__ void __launch_bounds__(256 * RS * KS, 1) gemm_prefill_kernel(GemmArgs
   const int row0 = mb * BM + rpart * MI * 32;
   if (K % kPfBK && kp == 0) pf_tail32<FMT, EPI, MI, NF>(acc, ga, W, e, row0, n0, c, h, nchunks * kPfBK);
 
+  // (slot id, routing weight) of every block row, in the last KB of LDS
+  // (beyond what the K-split exchange uses); one load of the weights per tile
+  int2* rowtab = reinterpret_cast<int2*>(smem + P::kLds - 1024);
+  {
+    const bool use_tw = ea.mul_tw;
+    const float tw = use_tw ? ea.topk_w[min(row_sid, ea.n_slots - 1)] : 1.f;
+    pf_barrier();  // every wave is past its reads of the ring and the scale tile
+    if (tid < BM) rowtab[tid] = int2{row_sid, __float_as_int(tw)};
+  }
+
   if constexpr (KS == 2) {
     // the two K parts meet: each wave hands over the half of the rows the
     // other finalises (lane-major in LDS, the ring is free now), then adds
@@ -958,7 +985,6 @@ __global__ void __launch_bounds__(256 * RS * KS, 1) gemm_prefill_kernel(GemmArgs
     constexpr int HM = MI / 2;
     constexpr int kRed = HM * NF * 16 * 64;  // floats per wave
     float* red = reinterpret_cast<float*>(smem);
-    pf_barrier();
     float* mine = red + (size_t)(wave_u * 2 + kp) * kRed;
     const float* theirs = red + (size_t)(wave_u * 2 + (1 - kp)) * kRed;
     f32x16 acch[HM][NF];
@@ -998,14 +1024,15 @@ __global__ void __launch_bounds__(256 * RS * KS, 1) gemm_prefill_kernel(GemmArgs
     if (n0 >= N) return;
     EpiArgs a = ea;
     a.row0 = row0 + kp * HM * 32;
-    epilogue32<EPI, FMT, HM, NF>(acch, a, W, e, n0, lane);
+    epilogue32<EPI, FMT, HM, NF>(acch, a, W, e, n0, lane, rowtab, a.row0 - mb * BM);
     return;
   }
 
+  pf_barrier();  // the row table is complete
   if (n0 >= N) return;
   EpiArgs a = ea;
   a.row0 = row0;
-  epilogue32<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane);
+  epilogue32<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane, rowtab, row0 - mb * BM);
 }
 
 // --------------------------------------------------------------------------
