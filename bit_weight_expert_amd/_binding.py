@@ -34,6 +34,7 @@ class _Wq(ctypes.Structure):
         ("g_idx", ctypes.c_void_p),
         ("bias", ctypes.c_void_p),
         ("k_perm", ctypes.c_void_p),
+        ("scales_kc", ctypes.c_void_p),
     ]
 
 
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.moe_gptq_act_order_sort.restype = i
         L.moe_permute_slots.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
         L.moe_permute_slots.restype = i
+        L.moe_nvfp4_scales_by_chunk.argtypes = [vp, i, i, i, vp, vp]
+        L.moe_nvfp4_scales_by_chunk.restype = i
         L.moe_mxfp8_quantize.argtypes = [vp, i, i, vp, vp, vp, vp]
         L.moe_mxfp8_quantize.restype = i
         L.moe_mx_gemm1.argtypes = [vp, vp, i, i, i, i, i, wq, i, f, f, f, vp, vp, vp, i, vp, vp]
@@ -138,6 +141,7 @@ class QuantWeights:
     global_scale: torch.Tensor | None = None
     bias: torch.Tensor | None = None
     k_perm: torch.Tensor | None = None     # GPTQ act-order, from moe_gptq_act_order_sort
+    scales_kc: torch.Tensor | None = None  # NVFP4 scales by K chunk, from moe_nvfp4_scales_by_chunk
 
     @classmethod
     def from_arrays(cls, fmt, group, N, K, qweight, scales, zeros=None, global_scale=None,
@@ -156,7 +160,7 @@ class QuantWeights:
     def struct(self) -> _Wq:
         return _Wq(FMT[self.fmt], self.group, _ptr(self.qweight), _ptr(self.scales),
                    _ptr(self.zeros), _ptr(self.global_scale), None, _ptr(self.bias),
-                   _ptr(self.k_perm))
+                   _ptr(self.k_perm), _ptr(self.scales_kc))
 
     @property
     def E(self) -> int:
@@ -296,6 +300,19 @@ def moe_gptq_act_order_sort(qweight: torch.Tensor, g_idx: torch.Tensor, group: i
                                          _ptr(k_perm), _ptr(status), _stream()),
            "moe_gptq_act_order_sort")
     return out, k_perm, status
+
+
+def moe_nvfp4_scales_by_chunk(w: "QuantWeights") -> torch.Tensor:
+    """NVFP4 e4m3 scales [E, N, K/16] re-laid by 64-deep K chunk -> uint8 [E, K/64, N, 4]
+    (set it as w.scales_kc to let the 64/128-row GEMM kernel stream the scales)."""
+    if w.fmt != "nvfp4":
+        raise ValueError("scales by chunk are an NVFP4 layout")
+    _dev(w.scales, torch.uint8, "scales")
+    E = w.scales.shape[0]
+    out = torch.empty((E, w.K // 64, w.N, 4), dtype=torch.uint8, device=w.scales.device)
+    _check(lib().moe_nvfp4_scales_by_chunk(_ptr(w.scales), E, w.N, w.K, _ptr(out), _stream()),
+           "moe_nvfp4_scales_by_chunk")
+    return out
 
 
 def moe_permute_slots(src: torch.Tensor, top_k: int, k_perm: torch.Tensor,

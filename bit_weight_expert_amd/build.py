@@ -12,7 +12,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_w4a16.so")
-SOURCES = ["api.hip", "route_align.hip", "gemm.hip", "act_order.hip", "mxfp8.hip"]
+SOURCES = ["api.hip", "route_align.hip", "gemm.hip", "act_order.hip", "mxfp8.hip", "nvfp4_chunk.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

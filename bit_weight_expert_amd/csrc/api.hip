@@ -29,6 +29,8 @@ extern "C" hipError_t moe_launch_gemm_mx(int, int, int, const uint8_t*, const ui
                                          int, int, int, int, const moe::WeightArgs*, const int32_t*,
                                          const int32_t*, const int32_t*, const float*, int, float,
                                          float, float, uint16_t*, int, hipStream_t);
+extern "C" hipError_t moe_launch_nvfp4_scales_by_chunk(const uint8_t*, int, int, int, uint8_t*,
+                                                       hipStream_t);
 extern "C" hipError_t moe_launch_permute_slots(const uint16_t*, int, int, int, int, const int32_t*,
                                                const int32_t*, uint16_t*, hipStream_t);
 
@@ -76,6 +78,11 @@ moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out
       return MOE_ERR_UNSUPPORTED;
   }
   if (w->fmt != MOE_W_INT4_GPTQ && w->k_perm != nullptr) return MOE_ERR_UNSUPPORTED;
+  if (w->scales_kc != nullptr) {
+    if (w->fmt != MOE_W_NVFP4) return MOE_ERR_UNSUPPORTED;
+    if (K % 64 != 0) return MOE_ERR_SHAPE;
+    if (!aligned16(w->scales_kc)) return MOE_ERR_ALIGN;
+  }
   if (!aligned16(w->qweight) || !aligned16(w->scales)) return MOE_ERR_ALIGN;
   if (w->fmt == MOE_W_INT4_GPTQ && !aligned16(w->zeros)) return MOE_ERR_ALIGN;
   if (w->bias != nullptr && (reinterpret_cast<uintptr_t>(w->bias) & 1u)) return MOE_ERR_ALIGN;
@@ -84,6 +91,7 @@ moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out
   out->zeros = static_cast<const uint32_t*>(w->zeros);
   out->global_scale = w->global_scale;
   out->bias = w->bias;
+  out->scales_kc = w->scales_kc;
   out->group = w->group_size;
   return MOE_OK;
 }
@@ -299,6 +307,16 @@ moe_status_t moe_gptq_act_order_sort(const int32_t* qweight, const int32_t* g_id
   if (qweight_sorted == qweight) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe_launch_gptq_sort(qweight, g_idx, E, K, N, group_size, qweight_sorted,
                                          k_perm, status, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_nvfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int K, uint8_t* out,
+                                       moe_stream_t stream) {
+  if (E <= 0 || E > kMaxE || N <= 0 || K <= 0 || K % 64 != 0) return MOE_ERR_SHAPE;
+  if (scales == nullptr || out == nullptr) return MOE_ERR_NULL;
+  if (!aligned16(scales) || !aligned16(out)) return MOE_ERR_ALIGN;
+  if (out == scales) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe_launch_nvfp4_scales_by_chunk(scales, E, N, K, out,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_permute_slots(const uint16_t* src, int size_m, int top_k, int K, int E,

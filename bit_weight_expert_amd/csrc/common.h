@@ -44,6 +44,7 @@ struct WeightArgs {
   const float* global_scale;   // NVFP4 [E]
   const uint16_t* bias;        // bf16 [E][N] or null
   int group;
+  const uint8_t* scales_kc;    // NVFP4 e4m3 scales by 64-deep K chunk [E][K/64][N][4], or null
 };
 
 }  // namespace moe

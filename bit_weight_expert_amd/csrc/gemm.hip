@@ -398,22 +398,33 @@ constexpr int pf_rs() { return FMT == FMT_MXFP4 ? 2 : 1; }
 // dequant or LDS read is done twice; their sums meet through LDS at the end.
 template <int FMT>
 constexpr int pf_ks() { return FMT == FMT_MXFP4 ? 1 : 2; }
-constexpr int kPfStages = 4;               // LDS ring depth
 constexpr int kPfScaleBytes = 60 * 1024;   // LDS for the tile's scales over all of K
 
-template <int BM, int NF>
+// SK = 1 (NVFP4 with scales laid out by K chunk, [E][K/64][N][4]): each
+// chunk's scales (4 bytes per weight row, contiguous over the tile's rows)
+// travel through the ring with its codes, so no scale tile stays resident;
+// with 3 stages the workgroup needs 76 KB of LDS and two share a CU, one's
+// prologue and epilogue overlapping the other's K loop.
+template <int BM, int NF, int SK = 0>
 struct Pf {
   static constexpr int MI = BM / 32;
   static constexpr int BN = 128 * NF;
   static constexpr int kABytes = BM * kPfBK * 2;            // A rows of one chunk
   static constexpr int kBBytes = BN * kPfBK / 2;            // weight codes of one chunk
+  static constexpr int kSBytes = SK ? BN * 4 : 0;           // streamed scales of one chunk
   static constexpr int kAIssue = kABytes / 1024 / 4;         // DMA instructions per wave per chunk
   static constexpr int kBIssue = kBBytes / 1024 / 4;
-  static constexpr int kIssue = kAIssue + kBIssue;
-  static constexpr int kStage = kABytes + kBBytes;
-  static constexpr int kLds = kPfStages * kStage + kPfScaleBytes;
+  static constexpr int kSIssue = SK ? 1 : 0;                 // 64 lanes x 4 bytes per wave
+  static constexpr int kIssue = kAIssue + kBIssue + kSIssue;
+  static constexpr int kStage = kABytes + kBBytes + kSBytes;
+  static constexpr int kStages = SK ? 3 : 4;                 // LDS ring depth
+  // the last KB holds the row table of the epilogue (inside the scale area
+  // when the scales are resident: it is written after their last read)
+  static constexpr int kLds = kStages * kStage + (SK ? 1024 : kPfScaleBytes);
   static_assert(kAIssue >= 1 && kBIssue >= 1, "tile too small for the DMA split");
+  static_assert(!SK || kSBytes == 4 * 256, "one 256-byte scale run per wave");
   static_assert(kLds <= 160 * 1024, "LDS");
+  static_assert((kStages - 1) * kIssue < 64, "vmcnt range");
 };
 
 // Bytes of LDS the scales of one BN-row tile take for the whole K.
@@ -434,6 +445,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // so the compiler does not track it; the kernel waits with wait_vmcnt.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory");
+}
+
+// Same with 4 bytes per lane: lane l copies g[0..3] to lds_base + 4*l.
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                :
                : "v"(g), "s"(lds_base)
                : "memory");
@@ -494,12 +513,13 @@ __device__ __forceinline__ int pf_brow(int b, int p) {
   return 32 * b + ((EPI == EPI_SWIGLU) ? 2 * (s & 15) + (s >> 4) : s);
 }
 
-// Per-wave DMA of chunk kc into the ring stage at stage_lds.
-template <int FMT, int BM, int NF>
-__device__ __forceinline__ void pf_issue(uint32_t stage_lds, const uint16_t* const (&arow)[Pf<BM, NF>::kAIssue],
-                                         const uint8_t* const (&brow)[Pf<BM, NF>::kBIssue],
-                                         int kc, int wave_u, int N) {
-  using P = Pf<BM, NF>;
+// Per-wave DMA of chunk kc into the ring stage at stage_lds (SK: plus the
+// chunk's 4-byte scale runs of tile rows 64*wave .. 64*wave+63, from skc).
+template <int FMT, int BM, int NF, int SK>
+__device__ __forceinline__ void pf_issue(uint32_t stage_lds, const uint16_t* const (&arow)[Pf<BM, NF, SK>::kAIssue],
+                                         const uint8_t* const (&brow)[Pf<BM, NF, SK>::kBIssue],
+                                         const uint8_t* skc, int kc, int wave_u, int N) {
+  using P = Pf<BM, NF, SK>;
   const int k0 = kc * kPfBK;
 #pragma unroll
   for (int p = 0; p < P::kAIssue; ++p)  // instruction q = 4p + wave: A rows 8q .. 8q+7
@@ -512,6 +532,7 @@ __device__ __forceinline__ void pf_issue(uint32_t stage_lds, const uint16_t* con
     else
       dma16(brow[p] + k0 / 2, dst);                  // one 32-row block
   }
+  if (SK) dma4(skc + (size_t)kc * N * 4, stage_lds + P::kABytes + P::kBBytes + (uint32_t)wave_u * 256u);
 }
 
 // Weight codes of one fragment for one chunk (one code word per MFMA step)
@@ -570,7 +591,7 @@ __device__ __forceinline__ bf16x8 pf_deq_step(const PfB& b, int s) {
 // LDS reads of the fragment weights of chunk kc (codes from the ring stage
 // at bstage, scales from the resident scale tile).  rl[j] is the lane's tile
 // row of fragment j.
-template <int FMT, int EPI, int NF>
+template <int FMT, int EPI, int NF, int SK = 0>
 __device__ __forceinline__ void pf_read_b(PfB (&b)[NF], const uint8_t* bstage, const uint8_t* sc,
                                           const int (&rl)[NF], int kc, int h, int K, int group,
                                           int bn) {
@@ -593,7 +614,9 @@ __device__ __forceinline__ void pf_read_b(PfB (&b)[NF], const uint8_t* bstage, c
     } else {
       b[j].q = *reinterpret_cast<const uint4*>(bstage + 16 * pf_bpos<EPI>(r, h));
       if (FMT == FMT_NVFP4) {
-        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sc + r * (K / 16) + k0 / 16 + 2 * h);
+        // SK: sc is the stage's [BN][4] scale run of this chunk
+        const uint32_t s2 = SK ? *reinterpret_cast<const uint16_t*>(sc + r * 4 + 2 * h)
+                               : *reinterpret_cast<const uint16_t*>(sc + r * (K / 16) + k0 / 16 + 2 * h);
         b[j].s0 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 0);
         b[j].s1 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 1);
       } else {
@@ -778,16 +801,18 @@ __device__ __forceinline__ void pf_tail32(f32x16 (&acc)[MI][NF], const GemmArgs&
   pf_mfma<MI, NF>(acc, a1, b1);
 }
 
-template <int FMT, int EPI, int BM, int NF, int RS, int KS>
-__global__ void __launch_bounds__(256 * RS * KS, 1) gemm_prefill_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
-  using P = Pf<BM, NF>;
+template <int FMT, int EPI, int BM, int NF, int RS, int KS, int SK>
+__global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
+  using P = Pf<BM, NF, SK>;
+  constexpr int kStages = P::kStages;
+  static_assert(!SK || (RS == 1 && KS == 1 && FMT == FMT_NVFP4), "streamed scales: one wave per SIMD per workgroup, NVFP4");
   // RS = 2: eight waves, two per SIMD; waves w and w + 4 take the same
   // columns and one half of the rows each (both dequantise the same codes),
   // so one wave's dequant and LDS reads overlap the other's MFMAs.  Only the
   // first four waves issue the DMA.
   constexpr int MI = P::MI / RS;
   __shared__ __attribute__((aligned(16))) uint8_t smem[P::kLds];
-  uint8_t* const scale_lds = smem + kPfStages * P::kStage;
+  uint8_t* const scale_lds = smem + kStages * P::kStage;  // resident scales (SK = 0)
 
   int mb, nt;
   if (!prefill_tile(ga, BM, mb, nt)) return;
@@ -845,9 +870,12 @@ __global__ void __launch_bounds__(256 * RS * KS, 1) gemm_prefill_kernel(GemmArgs
   // the tile's scales for the whole K (resident in LDS), then ring stages
   // 0..3 <- chunks 0..3 (chunks past the end re-read the last one)
   const uint32_t ring = lds_addr(smem);
-  const uint32_t sc_lds = ring + kPfStages * P::kStage;
+  const uint32_t sc_lds = ring + kStages * P::kStage;
+  // SK: this lane's scale-run source, tile row 64*wave + lane of chunk 0
+  const uint8_t* skc = SK ? W.scales_kc + ((size_t)e * (K / 64) * N + min(nt0 + 64 * wave_u + lane, N - 1)) * 4
+                          : nullptr;
   const int nchunks = K / kPfBK;  // (K < 64: only the 32-wide tail, no LDS)
-  if (nchunks == 0 || !dma_wave) {
+  if (nchunks == 0 || !dma_wave || SK) {
   } else if (FMT == FMT_NVFP4) {
     const int nb = rows * (K / 16);
     pf_dma_region(sc_lds, W.scales + ((size_t)e * N + nt0) * (K / 16), 0, nb, nb, nb, wave_u, lane);
@@ -866,8 +894,8 @@ __global__ void __launch_bounds__(256 * RS * KS, 1) gemm_prefill_kernel(GemmArgs
   }
   if (nchunks > 0 && dma_wave) {
 #pragma unroll
-    for (int s = 0; s < kPfStages; ++s)
-      pf_issue<FMT, BM, NF>(ring + s * P::kStage, arow, brow, min(s, nchunks - 1), wave_u, N);
+    for (int s = 0; s < kStages; ++s)
+      pf_issue<FMT, BM, NF, SK>(ring + s * P::kStage, arow, brow, skc, min(s, nchunks - 1), wave_u, N);
   }
 
   // tile rows of this lane's fragments (columns past N read row 0)
@@ -887,30 +915,32 @@ __global__ void __launch_bounds__(256 * RS * KS, 1) gemm_prefill_kernel(GemmArgs
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   if (KS == 2 && nchunks > 0) {
-    wait_vmcnt<3 * P::kIssue>();
+    wait_vmcnt<(kStages - 1) * P::kIssue>();
     pf_barrier();
     const int s0 = 2 * kp, s1 = 2 * kp + 1;
     PfB b[NF];
     uint4 a0[MI], a1[MI];
     bf16x8 q0[NF], q1[NF];
-    pf_read_b<FMT, EPI, NF>(b, smem + P::kABytes, scale_lds, rl, 0, h, K, W.group, P::BN);
+    pf_read_b<FMT, EPI, NF, SK>(b, smem + P::kABytes, SK ? smem + P::kABytes + P::kBBytes : scale_lds, rl,
+                                0, h, K, W.group, P::BN);
     pf_read_a<MI>(a0, smem + aoff, c, h, s0);
 #pragma unroll
     for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], s0);
     for (int kc = 0; kc < nchunks; ++kc) {
-      const uint8_t* st = smem + (kc % kPfStages) * P::kStage + aoff;
+      const uint8_t* st = smem + (kc % kStages) * P::kStage + aoff;
       pf_read_a<MI>(a1, st, c, h, s1);
 #pragma unroll
       for (int j = 0; j < NF; ++j) q1[j] = pf_deq_step<FMT>(b[j], s1);
       pf_mfma<MI, NF>(acc, a0, q0);
       // chunk kc+1 has landed and every wave is past its reads of chunk kc
-      wait_vmcnt<2 * P::kIssue>();
+      wait_vmcnt<(kStages - 2) * P::kIssue>();
       pf_barrier();
       if (dma_wave)
-        pf_issue<FMT, BM, NF>(ring + (kc % kPfStages) * P::kStage, arow, brow,
-                              min(kc + kPfStages, nchunks - 1), wave_u, N);
-      const uint8_t* nx = smem + ((kc + 1) % kPfStages) * P::kStage;
-      pf_read_b<FMT, EPI, NF>(b, nx + P::kABytes, scale_lds, rl, min(kc + 1, nchunks - 1), h, K,
+        pf_issue<FMT, BM, NF, SK>(ring + (kc % kStages) * P::kStage, arow, brow, skc,
+                                  min(kc + kStages, nchunks - 1), wave_u, N);
+      const uint8_t* nx = smem + ((kc + 1) % kStages) * P::kStage;
+      pf_read_b<FMT, EPI, NF, SK>(b, nx + P::kABytes, SK ? nx + P::kABytes + P::kBBytes : scale_lds, rl,
+                                  min(kc + 1, nchunks - 1), h, K,
                               W.group, P::BN);
       pf_read_a<MI>(a0, nx + aoff, c, h, s0);
       pf_mfma<MI, NF>(acc, a1, q1);
@@ -919,19 +949,20 @@ __global__ void __launch_bounds__(256 * RS * KS, 1) gemm_prefill_kernel(GemmArgs
     }
   } else if (nchunks > 0) {
     // scales and chunk 0 have landed (chunks 1..3 may still be in flight)
-    wait_vmcnt<3 * P::kIssue>();
+    wait_vmcnt<(kStages - 1) * P::kIssue>();
     pf_barrier();
     // chunk 0: weights, step-0 A fragments and dequant
     PfB b[NF];
     uint4 a0[MI], a1[MI];
     bf16x8 q0[NF], q1[NF];
-    pf_read_b<FMT, EPI, NF>(b, smem + P::kABytes, scale_lds, rl, 0, h, K, W.group, P::BN);
+    pf_read_b<FMT, EPI, NF, SK>(b, smem + P::kABytes, SK ? smem + P::kABytes + P::kBBytes : scale_lds, rl,
+                                0, h, K, W.group, P::BN);
     pf_read_a<MI>(a0, smem + aoff, c, h, 0);
 #pragma unroll
     for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
 
     for (int kc = 0; kc < nchunks; ++kc) {
-      const uint8_t* st = smem + (kc % kPfStages) * P::kStage + aoff;
+      const uint8_t* st = smem + (kc % kStages) * P::kStage + aoff;
       // steps 0..2: each overlaps the next step's A reads and dequant
       pf_read_a<MI>(a1, st, c, h, 1);
 #pragma unroll
@@ -948,13 +979,14 @@ __global__ void __launch_bounds__(256 * RS * KS, 1) gemm_prefill_kernel(GemmArgs
       // step 3 overlaps chunk kc+1's reads: chunk kc+1 has landed (all but the
       // two newest chunks' DMA are done) and every wave is past its reads of
       // chunk kc, whose stage is refilled with chunk kc+4
-      wait_vmcnt<2 * P::kIssue>();
+      wait_vmcnt<(kStages - 2) * P::kIssue>();
       pf_barrier();
       if (dma_wave)
-        pf_issue<FMT, BM, NF>(ring + (kc % kPfStages) * P::kStage, arow, brow,
-                              min(kc + kPfStages, nchunks - 1), wave_u, N);
-      const uint8_t* nx = smem + ((kc + 1) % kPfStages) * P::kStage;
-      pf_read_b<FMT, EPI, NF>(b, nx + P::kABytes, scale_lds, rl, min(kc + 1, nchunks - 1), h, K,
+        pf_issue<FMT, BM, NF, SK>(ring + (kc % kStages) * P::kStage, arow, brow, skc,
+                                  min(kc + kStages, nchunks - 1), wave_u, N);
+      const uint8_t* nx = smem + ((kc + 1) % kStages) * P::kStage;
+      pf_read_b<FMT, EPI, NF, SK>(b, nx + P::kABytes, SK ? nx + P::kABytes + P::kBBytes : scale_lds, rl,
+                                  min(kc + 1, nchunks - 1), h, K,
                               W.group, P::BN);
       pf_read_a<MI>(a0, nx + aoff, c, h, 0);
       pf_mfma<MI, NF>(acc, a1, q1);
@@ -1770,12 +1802,24 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
     ga.n_ntiles = (ga.N + Pf<128, 2>::BN - 1) / Pf<128, 2>::BN;
     ga.group_m = 4;  // measured flat between 1 and 16 at the gpt-oss-20b shape
     const dim3 grid((ga.n_mblocks * ga.n_ntiles + 7) / 8 * 8);
-    if (block_m == 64)
-      gemm_prefill_kernel<FMT, EPI, 64, 2, pf_rs<FMT>(), pf_ks<FMT>()>
-          <<<grid, dim3(256 * pf_rs<FMT>() * pf_ks<FMT>()), 0, st>>>(ga, W, ea);
-    else
-      gemm_prefill_kernel<FMT, EPI, 128, 2, pf_rs<FMT>(), pf_ks<FMT>()>
-          <<<grid, dim3(256 * pf_rs<FMT>() * pf_ks<FMT>()), 0, st>>>(ga, W, ea);
+    constexpr int kThreads = 256 * pf_rs<FMT>() * pf_ks<FMT>();
+    if constexpr (FMT == FMT_NVFP4) {
+      if (W.scales_kc != nullptr) {
+        // scales by K chunk: two 256-thread workgroups per CU
+        if (block_m == 64)
+          gemm_prefill_kernel<FMT, EPI, 64, 2, 1, 1, 1><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+        else
+          gemm_prefill_kernel<FMT, EPI, 128, 2, 1, 1, 1><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+        return hipGetLastError();
+      }
+    }
+    if (block_m == 64) {
+      gemm_prefill_kernel<FMT, EPI, 64, 2, pf_rs<FMT>(), pf_ks<FMT>(), 0>
+          <<<grid, dim3(kThreads), 0, st>>>(ga, W, ea);
+    } else {
+      gemm_prefill_kernel<FMT, EPI, 128, 2, pf_rs<FMT>(), pf_ks<FMT>(), 0>
+          <<<grid, dim3(kThreads), 0, st>>>(ga, W, ea);
+    }
   }
   return hipGetLastError();
 }

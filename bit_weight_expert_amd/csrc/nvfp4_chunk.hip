@@ -1,0 +1,35 @@
+// NVFP4 scales re-laid by 64-deep K chunk, once, when the weights are loaded.
+//
+// The checkpoint layout keeps each weight row's e4m3 group scales (one per 16
+// along K) together: [E][N][K/16].  The 64/128-row GEMM kernel reads, for each
+// 64-deep chunk, the four scales of that chunk for 256 consecutive rows; in
+// the checkpoint layout those are 4 bytes every K/16 bytes, one memory request
+// per row.  Laid out as [E][K/64][N][4] they are one contiguous kilobyte that
+// the kernel copies into on-chip memory with the chunk's codes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+// One thread per (expert, chunk, row): one aligned 4-byte word moved.
+__global__ __launch_bounds__(256) void nvfp4_scales_by_chunk_kernel(const uint32_t* __restrict__ in,
+                                                                    int N, int KC,
+                                                                    uint32_t* __restrict__ out) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.y;
+  const int e = blockIdx.z;
+  if (n >= N) return;
+  // in: row (e, n) holds KC words (4 scales each); out: [e][c][n]
+  out[((size_t)e * KC + c) * N + n] = in[((size_t)e * N + n) * KC + c];
+}
+
+}  // namespace
+
+extern "C" hipError_t moe_launch_nvfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int K,
+                                                       uint8_t* out, hipStream_t st) {
+  const int kc = K / 64;
+  hipLaunchKernelGGL(nvfp4_scales_by_chunk_kernel, dim3((N + 255) / 256, kc, E), dim3(256), 0, st,
+                     reinterpret_cast<const uint32_t*>(scales), N, kc,
+                     reinterpret_cast<uint32_t*>(out));
+  return hipGetLastError();
+}

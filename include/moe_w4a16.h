@@ -111,6 +111,12 @@ typedef struct {
                                  accepts it (it gathers the GEMM inputs through it); the
                                  single GEMM calls return MOE_ERR_UNSUPPORTED: gather with
                                  moe_permute_slots and call them in the top_k = 1 view. */
+  const uint8_t* scales_kc;   /* NVFP4 only, optional: the same e4m3 scales laid out by 64-deep K
+                                 chunk, uint8 [E][K/64][N][4] (moe_nvfp4_scales_by_chunk), K a
+                                 multiple of 64, 16-byte aligned.  `scales` stays required; with
+                                 scales_kc the 64/128-row GEMM kernel streams each chunk's scales
+                                 with its codes instead of holding the tile's scales for the whole
+                                 K in on-chip memory, which lets two workgroups share a CU. */
 } moe_wq_t;
 
 /* Length of sorted_ids for T tokens: T*top_k + min(E, T*top_k)*(block_m-1),
@@ -210,6 +216,14 @@ moe_status_t moe_w4a16_gemm2(const uint16_t* a, int size_m, int K, int N, int E,
 moe_status_t moe_gptq_act_order_sort(const int32_t* qweight, const int32_t* g_idx, int E, int K,
                                      int N, int group_size, int32_t* qweight_sorted,
                                      int32_t* k_perm, int32_t* status, moe_stream_t stream);
+
+/* NVFP4 scales re-laid by K chunk, run once when the weights are loaded:
+ *   out[e][c][n][j] = scales[e][n][4c + j]   (c < K/64, j < 4)
+ * i.e. the four e4m3 group scales of each 64-deep chunk of each weight row,
+ * rows of one chunk contiguous.  scales uint8 [E][N][K/16] (the moe_wq_t NVFP4
+ * layout); out uint8 [E][K/64][N][4]; K % 64 == 0; both 16-byte aligned. */
+moe_status_t moe_nvfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int K, uint8_t* out,
+                                       moe_stream_t stream);
 
 /* Gather of GEMM input rows through an act-order permutation, one row per
  * flat slot f < size_m*top_k, permuted by the slot's own expert:
