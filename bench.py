@@ -10,7 +10,10 @@ tokens with everything already resident in HBM.  The headline line is at
 T = 4096; the same JSON line carries the other token counts of the sweep.
 
 Weight copies are rotated between calls so that no call finds its weights in
-the 256 MB last-level cache left behind by the previous one.
+the 256 MB last-level cache left behind by the previous one.  The weights are
+loaded as a user of the library loads them: the checkpoint bytes plus the
+NVFP4 scales re-laid by K chunk (moe_nvfp4_scales_by_chunk, done once at load
+time; --checkpoint-scales runs without that copy).
 
 Prints ONE JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 
@@ -231,6 +234,8 @@ def main() -> int:
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay timings")
+    ap.add_argument("--checkpoint-scales", action="store_true",
+                    help="run on the checkpoint scale layout only (no scales by K chunk)")
     ap.add_argument("--act-order", action="store_true",
                     help="also time the GPTQ layer with act-order weights (and its gather)")
     ap.add_argument("--act-order-tokens", default="1,64,2048")
@@ -271,6 +276,11 @@ def main() -> int:
                                          L.w13.scales, None, L.w13.global_scale, L.w13.bias)
         w2 = M.QuantWeights.from_arrays(L.w2.fmt, L.w2.group, L.w2.N, L.w2.K, L.w2.qweight,
                                         L.w2.scales, None, L.w2.global_scale, L.w2.bias)
+        if not args.checkpoint_scales:
+            # the load-time layout of the NVFP4 scales by K chunk (a copy of the
+            # same bytes), which the 64/128-row GEMM kernel streams with the codes
+            w13.scales_kc = M.moe_nvfp4_scales_by_chunk(w13)
+            w2.scales_kc = M.moe_nvfp4_scales_by_chunk(w2)
         copies.append((w13, w2))
     ws = torch.empty((M.moe_forward_workspace_bytes(t_max, L.E, L.top_k, L.H, L.I),),
                      dtype=torch.uint8, device=dev)
@@ -398,7 +408,8 @@ def main() -> int:
         "config": {"workload": "gpt-oss-20b-shaped MoE layer: E=32, top_k=4, hidden=2880, "
                                "intermediate=2880, NVFP4 g16 weights + bias, swigluoai, "
                                f"T={args.tokens} tokens",
-                   "tokens": args.tokens, "block_m": bm, "weight_copies_rotated": args.copies},
+                   "tokens": args.tokens, "block_m": bm, "weight_copies_rotated": args.copies,
+                   "nvfp4_scales_by_chunk": not args.checkpoint_scales},
         "roofline": {"kernel": "grouped_gemm (GEMM1, w13 + swigluoai)", "bound": g_bound,
                      "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
                      "traffic": profiled_traffic(), "kernel_us": g1_ms * 1e3},
