@@ -12,8 +12,10 @@ T = 4096; the same JSON line carries the other token counts of the sweep.
 Weight copies are rotated between calls so that no call finds its weights in
 the 256 MB last-level cache left behind by the previous one.  The weights are
 loaded as a user of the library loads them: the checkpoint bytes plus the
-NVFP4 scales re-laid by K chunk (moe_nvfp4_scales_by_chunk, done once at load
-time; --checkpoint-scales runs without that copy).
+NVFP4 scales and codes re-laid by K chunk (moe_nvfp4_scales_by_chunk and
+moe_nvfp4_codes_by_chunk, done once at load time; the token counts up to 64
+read the checkpoint codes).  --checkpoint-codes runs without the codes copy,
+--checkpoint-scales without either.
 
 Prints ONE JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 
@@ -235,7 +237,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay timings")
     ap.add_argument("--checkpoint-scales", action="store_true",
-                    help="run on the checkpoint scale layout only (no scales by K chunk)")
+                    help="run on the checkpoint layout only (no scales or codes by K chunk)")
+    ap.add_argument("--checkpoint-codes", action="store_true",
+                    help="scales by K chunk, codes in the checkpoint layout only")
     ap.add_argument("--act-order", action="store_true",
                     help="also time the GPTQ layer with act-order weights (and its gather)")
     ap.add_argument("--act-order-tokens", default="1,64,2048")
@@ -281,6 +285,10 @@ def main() -> int:
             # same bytes), which the 64/128-row GEMM kernel streams with the codes
             w13.scales_kc = M.moe_nvfp4_scales_by_chunk(w13)
             w2.scales_kc = M.moe_nvfp4_scales_by_chunk(w2)
+            if not args.checkpoint_codes:
+                # and the codes: a second copy, read by the same kernel
+                w13.qweight_kc = M.moe_nvfp4_codes_by_chunk(w13)
+                w2.qweight_kc = M.moe_nvfp4_codes_by_chunk(w2)
         copies.append((w13, w2))
     ws = torch.empty((M.moe_forward_workspace_bytes(t_max, L.E, L.top_k, L.H, L.I),),
                      dtype=torch.uint8, device=dev)
@@ -409,7 +417,8 @@ def main() -> int:
                                "intermediate=2880, NVFP4 g16 weights + bias, swigluoai, "
                                f"T={args.tokens} tokens",
                    "tokens": args.tokens, "block_m": bm, "weight_copies_rotated": args.copies,
-                   "nvfp4_scales_by_chunk": not args.checkpoint_scales},
+                   "nvfp4_scales_by_chunk": not args.checkpoint_scales,
+                   "nvfp4_codes_by_chunk": not (args.checkpoint_scales or args.checkpoint_codes)},
         "roofline": {"kernel": "grouped_gemm (GEMM1, w13 + swigluoai)", "bound": g_bound,
                      "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
                      "traffic": profiled_traffic(), "kernel_us": g1_ms * 1e3},

@@ -35,6 +35,7 @@ class _Wq(ctypes.Structure):
         ("bias", ctypes.c_void_p),
         ("k_perm", ctypes.c_void_p),
         ("scales_kc", ctypes.c_void_p),
+        ("qweight_kc", ctypes.c_void_p),
     ]
 
 
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.moe_permute_slots.restype = i
         L.moe_nvfp4_scales_by_chunk.argtypes = [vp, i, i, i, vp, vp]
         L.moe_nvfp4_scales_by_chunk.restype = i
+        L.moe_nvfp4_codes_by_chunk.argtypes = [vp, i, i, i, vp, vp]
+        L.moe_nvfp4_codes_by_chunk.restype = i
         L.moe_mxfp8_quantize.argtypes = [vp, i, i, vp, vp, vp, vp]
         L.moe_mxfp8_quantize.restype = i
         L.moe_mx_gemm1.argtypes = [vp, vp, i, i, i, i, i, wq, i, f, f, f, vp, vp, vp, i, vp, vp]
@@ -142,6 +145,7 @@ class QuantWeights:
     bias: torch.Tensor | None = None
     k_perm: torch.Tensor | None = None     # GPTQ act-order, from moe_gptq_act_order_sort
     scales_kc: torch.Tensor | None = None  # NVFP4 scales by K chunk, from moe_nvfp4_scales_by_chunk
+    qweight_kc: torch.Tensor | None = None  # NVFP4 codes by K chunk (with scales_kc), moe_nvfp4_codes_by_chunk
 
     @classmethod
     def from_arrays(cls, fmt, group, N, K, qweight, scales, zeros=None, global_scale=None,
@@ -160,7 +164,7 @@ class QuantWeights:
     def struct(self) -> _Wq:
         return _Wq(FMT[self.fmt], self.group, _ptr(self.qweight), _ptr(self.scales),
                    _ptr(self.zeros), _ptr(self.global_scale), None, _ptr(self.bias),
-                   _ptr(self.k_perm), _ptr(self.scales_kc))
+                   _ptr(self.k_perm), _ptr(self.scales_kc), _ptr(self.qweight_kc))
 
     @property
     def E(self) -> int:
@@ -312,6 +316,20 @@ def moe_nvfp4_scales_by_chunk(w: "QuantWeights") -> torch.Tensor:
     out = torch.empty((E, w.K // 64, w.N, 4), dtype=torch.uint8, device=w.scales.device)
     _check(lib().moe_nvfp4_scales_by_chunk(_ptr(w.scales), E, w.N, w.K, _ptr(out), _stream()),
            "moe_nvfp4_scales_by_chunk")
+    return out
+
+
+def moe_nvfp4_codes_by_chunk(w: "QuantWeights") -> torch.Tensor:
+    """NVFP4 codes [E, N, K/2] re-laid by 64-deep K chunk -> uint8 [E, K/64, N, 32]
+    (set it as w.qweight_kc, together with w.scales_kc, for the 64/128-row GEMM kernel;
+    it is a second copy of the codes: the 1..64-token kernels keep reading w.qweight)."""
+    if w.fmt != "nvfp4":
+        raise ValueError("codes by chunk are an NVFP4 layout")
+    _dev(w.qweight, torch.uint8, "qweight")
+    E = w.qweight.shape[0]
+    out = torch.empty((E, w.K // 64, w.N, 32), dtype=torch.uint8, device=w.qweight.device)
+    _check(lib().moe_nvfp4_codes_by_chunk(_ptr(w.qweight), E, w.N, w.K, _ptr(out), _stream()),
+           "moe_nvfp4_codes_by_chunk")
     return out
 
 

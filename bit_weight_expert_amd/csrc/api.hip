@@ -31,6 +31,8 @@ extern "C" hipError_t moe_launch_gemm_mx(int, int, int, const uint8_t*, const ui
                                          float, float, uint16_t*, int, hipStream_t);
 extern "C" hipError_t moe_launch_nvfp4_scales_by_chunk(const uint8_t*, int, int, int, uint8_t*,
                                                        hipStream_t);
+extern "C" hipError_t moe_launch_nvfp4_codes_by_chunk(const uint8_t*, int, int, int, uint8_t*,
+                                                       hipStream_t);
 extern "C" hipError_t moe_launch_permute_slots(const uint16_t*, int, int, int, int, const int32_t*,
                                                const int32_t*, uint16_t*, hipStream_t);
 
@@ -83,6 +85,10 @@ moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out
     if (K % 64 != 0) return MOE_ERR_SHAPE;
     if (!aligned16(w->scales_kc)) return MOE_ERR_ALIGN;
   }
+  if (w->qweight_kc != nullptr) {
+    if (w->scales_kc == nullptr) return MOE_ERR_UNSUPPORTED;  // NVFP4 and K % 64 checked above
+    if (!aligned16(w->qweight_kc)) return MOE_ERR_ALIGN;
+  }
   if (!aligned16(w->qweight) || !aligned16(w->scales)) return MOE_ERR_ALIGN;
   if (w->fmt == MOE_W_INT4_GPTQ && !aligned16(w->zeros)) return MOE_ERR_ALIGN;
   if (w->bias != nullptr && (reinterpret_cast<uintptr_t>(w->bias) & 1u)) return MOE_ERR_ALIGN;
@@ -92,6 +98,7 @@ moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out
   out->global_scale = w->global_scale;
   out->bias = w->bias;
   out->scales_kc = w->scales_kc;
+  out->qweight_kc = w->qweight_kc;
   out->group = w->group_size;
   return MOE_OK;
 }
@@ -317,6 +324,16 @@ moe_status_t moe_nvfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int 
   if (out == scales) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe_launch_nvfp4_scales_by_chunk(scales, E, N, K, out,
                                                      static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_nvfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int K, uint8_t* out,
+                                      moe_stream_t stream) {
+  if (E <= 0 || E > kMaxE || N <= 0 || K <= 0 || K % 64 != 0) return MOE_ERR_SHAPE;
+  if (qweight == nullptr || out == nullptr) return MOE_ERR_NULL;
+  if (!aligned16(qweight) || !aligned16(out)) return MOE_ERR_ALIGN;
+  if (out == qweight) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe_launch_nvfp4_codes_by_chunk(qweight, E, N, K, out,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_permute_slots(const uint16_t* src, int size_m, int top_k, int K, int E,

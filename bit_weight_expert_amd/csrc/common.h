@@ -45,6 +45,7 @@ struct WeightArgs {
   const uint16_t* bias;        // bf16 [E][N] or null
   int group;
   const uint8_t* scales_kc;    // NVFP4 e4m3 scales by 64-deep K chunk [E][K/64][N][4], or null
+  const uint8_t* qweight_kc;   // NVFP4 codes by 64-deep K chunk [E][K/64][N][32], or null (needs scales_kc)
 };
 
 }  // namespace moe

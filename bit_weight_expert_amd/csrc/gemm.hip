@@ -404,7 +404,9 @@ constexpr int kPfScaleBytes = 60 * 1024;   // LDS for the tile's scales over all
 // chunk's scales (4 bytes per weight row, contiguous over the tile's rows)
 // travel through the ring with its codes, so no scale tile stays resident;
 // with 3 stages the workgroup needs 76 KB of LDS and two share a CU, one's
-// prologue and epilogue overlapping the other's K loop.
+// prologue and epilogue overlapping the other's K loop.  SK = 2: the
+// codes are laid out by K chunk too ([E][K/64][N][32]), so the copy of one
+// 32-row block of a chunk reads one contiguous kilobyte.
 template <int BM, int NF, int SK = 0>
 struct Pf {
   static constexpr int MI = BM / 32;
@@ -454,6 +456,26 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                :
+               : "v"(g), "s"(lds_base)
+               : "memory");
+}
+
+// The same two DMA instructions, pinned between MFMAs: `after` and `before`
+// are read-write register operands the instruction leaves untouched, so the
+// compiler keeps it after the last reader of `after` and before the first
+// reader of `before` (an asm statement with only a memory clobber may drift
+// past MFMAs, which touch no memory).
+__device__ __forceinline__ void dma16_pinned(const void* g, uint32_t lds_base, uint32_t& after,
+                                             uint32_t& before) {
+  asm volatile("s_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %2, off"
+               : "+v"(after), "+v"(before)
+               : "v"(g), "s"(lds_base)
+               : "memory");
+}
+__device__ __forceinline__ void dma4_pinned(const void* g, uint32_t lds_base, uint32_t& after,
+                                            uint32_t& before) {
+  asm volatile("s_mov_b32 m0, %3\n\tglobal_load_lds_dword %2, off"
+               : "+v"(after), "+v"(before)
                : "v"(g), "s"(lds_base)
                : "memory");
 }
@@ -513,26 +535,55 @@ __device__ __forceinline__ int pf_brow(int b, int p) {
   return 32 * b + ((EPI == EPI_SWIGLU) ? 2 * (s & 15) + (s >> 4) : s);
 }
 
-// Per-wave DMA of chunk kc into the ring stage at stage_lds (SK: plus the
-// chunk's 4-byte scale runs of tile rows 64*wave .. 64*wave+63, from skc).
+// DMA instruction d (0 <= d < kIssue) of one wave's share of chunk kc, into
+// the ring stage at stage_lds: first the A rows, then the weight codes, then
+// (SK) the chunk's 4-byte scale runs of tile rows 64*wave .. 64*wave+63.
+// PIN places it between MFMAs (dma16_pinned).
+template <int FMT, int BM, int NF, int SK, bool PIN>
+__device__ __forceinline__ void pf_issue_one(int d, uint32_t stage_lds,
+                                             const uint16_t* const (&arow)[Pf<BM, NF, SK>::kAIssue],
+                                             const uint8_t* const (&brow)[Pf<BM, NF, SK>::kBIssue],
+                                             const uint8_t* skc, int kc, int wave_u, int N,
+                                             uint32_t& after, uint32_t& before) {
+  using P = Pf<BM, NF, SK>;
+  const int k0 = kc * kPfBK;
+  const void* src;
+  uint32_t dst;
+  if (d < P::kAIssue) {  // instruction q = 4d + wave: A rows 8q .. 8q+7
+    src = arow[d] + k0;
+    dst = stage_lds + (uint32_t)(8 * (4 * d + wave_u)) * 128u;
+  } else if (d < P::kAIssue + P::kBIssue) {
+    const int p = d - P::kAIssue;
+    dst = stage_lds + P::kABytes + (uint32_t)(4 * p + wave_u) * 1024u;
+    if (FMT == FMT_GPTQ)
+      src = brow[p] + (size_t)k0 / 8 * N * 4;  // 256 words of the [8][BN] word tile
+    else if (SK == 2)
+      src = brow[p] + (size_t)kc * N * 32;     // one 32-row block, codes by chunk
+    else
+      src = brow[p] + k0 / 2;                  // one 32-row block
+  } else {
+    src = skc + (size_t)kc * N * 4;
+    dst = stage_lds + P::kABytes + P::kBBytes + (uint32_t)wave_u * 256u;
+  }
+  const bool word = SK && d == P::kIssue - 1;
+  if (PIN) {
+    if (word) dma4_pinned(src, dst, after, before);
+    else dma16_pinned(src, dst, after, before);
+  } else {
+    if (word) dma4(src, dst);
+    else dma16(src, dst);
+  }
+}
+
+// All of one wave's DMA of chunk kc into the ring stage at stage_lds.
 template <int FMT, int BM, int NF, int SK>
 __device__ __forceinline__ void pf_issue(uint32_t stage_lds, const uint16_t* const (&arow)[Pf<BM, NF, SK>::kAIssue],
                                          const uint8_t* const (&brow)[Pf<BM, NF, SK>::kBIssue],
                                          const uint8_t* skc, int kc, int wave_u, int N) {
-  using P = Pf<BM, NF, SK>;
-  const int k0 = kc * kPfBK;
+  uint32_t unused = 0;
 #pragma unroll
-  for (int p = 0; p < P::kAIssue; ++p)  // instruction q = 4p + wave: A rows 8q .. 8q+7
-    dma16(arow[p] + k0, stage_lds + (uint32_t)(8 * (4 * p + wave_u)) * 128u);
-#pragma unroll
-  for (int p = 0; p < P::kBIssue; ++p) {
-    const uint32_t dst = stage_lds + P::kABytes + (uint32_t)(4 * p + wave_u) * 1024u;
-    if (FMT == FMT_GPTQ)
-      dma16(brow[p] + (size_t)k0 / 8 * N * 4, dst);  // 256 words of the [8][BN] word tile
-    else
-      dma16(brow[p] + k0 / 2, dst);                  // one 32-row block
-  }
-  if (SK) dma4(skc + (size_t)kc * N * 4, stage_lds + P::kABytes + P::kBBytes + (uint32_t)wave_u * 256u);
+  for (int d = 0; d < Pf<BM, NF, SK>::kIssue; ++d)
+    pf_issue_one<FMT, BM, NF, SK, false>(d, stage_lds, arow, brow, skc, kc, wave_u, N, unused, unused);
 }
 
 // Weight codes of one fragment for one chunk (one code word per MFMA step)
@@ -648,6 +699,33 @@ __device__ __forceinline__ void pf_mfma(f32x16 (&acc)[MI][NF], const uint4 (&a)[
 #pragma unroll
     for (int j = 0; j < NF; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// One MFMA step (as pf_mfma) with one wave's DMA of chunk kc dealt between
+// its rows: issued back to back, a wave's 5..7 DMA instructions wait on the
+// CU's memory pipeline and hold up the MFMAs behind them; between rows the
+// pipeline drains while the matrix core works.  The A fragments serve as the
+// pins, so `a` reads as modified afterwards (callers reload it).
+template <int FMT, int BM, int NF, int SK, int MI>
+__device__ __forceinline__ void pf_mfma_issue(f32x16 (&acc)[MI][NF], uint4 (&a)[MI], const bf16x8 (&b)[NF],
+                                              uint32_t stage_lds,
+                                              const uint16_t* const (&arow)[Pf<BM, NF, SK>::kAIssue],
+                                              const uint8_t* const (&brow)[Pf<BM, NF, SK>::kBIssue],
+                                              const uint8_t* skc, int kc, int wave_u, int N) {
+  using P = Pf<BM, NF, SK>;
+  constexpr int kPer = (P::kIssue + MI - 1) / MI;  // DMA instructions after each row
+  uint32_t last = 0;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const bf16x8 af = as_bf16x8(a[i]);
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int d = kPer * i; d < kPer * (i + 1) && d < P::kIssue; ++d)
+      pf_issue_one<FMT, BM, NF, SK, true>(d, stage_lds, arow, brow, skc, kc, wave_u, N, a[i].x,
+                                          i + 1 < MI ? a[i + 1 < MI ? i + 1 : i].x : last);
   }
 }
 
@@ -863,7 +941,8 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
       brow[p] = W.qweight + (((size_t)e * (K / 8) + w / P::BN) * N + col) * 4;
     } else {
       const int n = min(nt0 + pf_brow<EPI>(q, lane), N - 1);
-      brow[p] = W.qweight + ((size_t)e * N + n) * (K / 2) + 16 * (lane >> 5);
+      brow[p] = SK == 2 ? W.qweight_kc + ((size_t)e * (K / 64) * N + n) * 32 + 16 * (lane >> 5)
+                        : W.qweight + ((size_t)e * N + n) * (K / 2) + 16 * (lane >> 5);
     }
   }
 
@@ -981,15 +1060,23 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
       // chunk kc, whose stage is refilled with chunk kc+4
       wait_vmcnt<(kStages - 2) * P::kIssue>();
       pf_barrier();
-      if (dma_wave)
-        pf_issue<FMT, BM, NF, SK>(ring + (kc % kStages) * P::kStage, arow, brow, skc,
-                                  min(kc + kStages, nchunks - 1), wave_u, N);
       const uint8_t* nx = smem + ((kc + 1) % kStages) * P::kStage;
-      pf_read_b<FMT, EPI, NF, SK>(b, nx + P::kABytes, SK ? nx + P::kABytes + P::kBBytes : scale_lds, rl,
-                                  min(kc + 1, nchunks - 1), h, K,
-                              W.group, P::BN);
-      pf_read_a<MI>(a0, nx + aoff, c, h, 0);
-      pf_mfma<MI, NF>(acc, a1, q1);
+      if constexpr (SK != 0) {
+        // every wave copies (one per SIMD): its DMA goes between step 3's rows
+        pf_read_b<FMT, EPI, NF, SK>(b, nx + P::kABytes, nx + P::kABytes + P::kBBytes, rl,
+                                    min(kc + 1, nchunks - 1), h, K, W.group, P::BN);
+        pf_read_a<MI>(a0, nx + aoff, c, h, 0);
+        pf_mfma_issue<FMT, BM, NF, SK, MI>(acc, a1, q1, ring + (kc % kStages) * P::kStage, arow, brow,
+                                           skc, min(kc + kStages, nchunks - 1), wave_u, N);
+      } else {
+        if (dma_wave)
+          pf_issue<FMT, BM, NF, SK>(ring + (kc % kStages) * P::kStage, arow, brow, skc,
+                                    min(kc + kStages, nchunks - 1), wave_u, N);
+        pf_read_b<FMT, EPI, NF, SK>(b, nx + P::kABytes, scale_lds, rl, min(kc + 1, nchunks - 1), h, K,
+                                    W.group, P::BN);
+        pf_read_a<MI>(a0, nx + aoff, c, h, 0);
+        pf_mfma<MI, NF>(acc, a1, q1);
+      }
 #pragma unroll
       for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
     }
@@ -1805,11 +1892,17 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
     constexpr int kThreads = 256 * pf_rs<FMT>() * pf_ks<FMT>();
     if constexpr (FMT == FMT_NVFP4) {
       if (W.scales_kc != nullptr) {
-        // scales by K chunk: two 256-thread workgroups per CU
-        if (block_m == 64)
+        // scales (and codes) by K chunk: two 256-thread workgroups per CU
+        if (W.qweight_kc != nullptr) {
+          if (block_m == 64)
+            gemm_prefill_kernel<FMT, EPI, 64, 2, 1, 1, 2><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+          else
+            gemm_prefill_kernel<FMT, EPI, 128, 2, 1, 1, 2><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+        } else if (block_m == 64) {
           gemm_prefill_kernel<FMT, EPI, 64, 2, 1, 1, 1><<<grid, dim3(256), 0, st>>>(ga, W, ea);
-        else
+        } else {
           gemm_prefill_kernel<FMT, EPI, 128, 2, 1, 1, 1><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+        }
         return hipGetLastError();
       }
     }

@@ -1,4 +1,5 @@
-// NVFP4 scales re-laid by 64-deep K chunk, once, when the weights are loaded.
+// NVFP4 scales and codes re-laid by 64-deep K chunk, once, when the weights
+// are loaded.
 //
 // The checkpoint layout keeps each weight row's e4m3 group scales (one per 16
 // along K) together: [E][N][K/16].  The 64/128-row GEMM kernel reads, for each
@@ -6,6 +7,12 @@
 // the checkpoint layout those are 4 bytes every K/16 bytes, one memory request
 // per row.  Laid out as [E][K/64][N][4] they are one contiguous kilobyte that
 // the kernel copies into on-chip memory with the chunk's codes.
+//
+// The codes ([E][N][K/2], 32 bytes per row per chunk) have the same problem
+// at a larger grain: one chunk of a 32-row block is 32 pieces of 32 bytes, a
+// quarter of a cache line each, and the other three quarters are evicted
+// before the next chunks use them.  Laid out as [E][K/64][N][32] a block's
+// chunk is one contiguous kilobyte.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -23,6 +30,22 @@ __global__ __launch_bounds__(256) void nvfp4_scales_by_chunk_kernel(const uint32
   out[((size_t)e * KC + c) * N + n] = in[((size_t)e * N + n) * KC + c];
 }
 
+
+// One thread per (expert, chunk, row): 32 aligned bytes moved.
+__global__ __launch_bounds__(256) void nvfp4_codes_by_chunk_kernel(const uint4* __restrict__ in,
+                                                                   int N, int KC,
+                                                                   uint4* __restrict__ out) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.y;
+  const int e = blockIdx.z;
+  if (n >= N) return;
+  // in: row (e, n) holds 2*KC 16-byte units; out: [e][c][n] two units
+  const uint4* src = in + (((size_t)e * N + n) * KC + c) * 2;
+  uint4* dst = out + (((size_t)e * KC + c) * N + n) * 2;
+  dst[0] = src[0];
+  dst[1] = src[1];
+}
+
 }  // namespace
 
 extern "C" hipError_t moe_launch_nvfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int K,
@@ -31,5 +54,13 @@ extern "C" hipError_t moe_launch_nvfp4_scales_by_chunk(const uint8_t* scales, in
   hipLaunchKernelGGL(nvfp4_scales_by_chunk_kernel, dim3((N + 255) / 256, kc, E), dim3(256), 0, st,
                      reinterpret_cast<const uint32_t*>(scales), N, kc,
                      reinterpret_cast<uint32_t*>(out));
+  return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_nvfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int K,
+                                                      uint8_t* out, hipStream_t st) {
+  const int kc = K / 64;
+  hipLaunchKernelGGL(nvfp4_codes_by_chunk_kernel, dim3((N + 255) / 256, kc, E), dim3(256), 0, st,
+                     reinterpret_cast<const uint4*>(qweight), N, kc, reinterpret_cast<uint4*>(out));
   return hipGetLastError();
 }

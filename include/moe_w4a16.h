@@ -117,6 +117,12 @@ typedef struct {
                                  scales_kc the 64/128-row GEMM kernel streams each chunk's scales
                                  with its codes instead of holding the tile's scales for the whole
                                  K in on-chip memory, which lets two workgroups share a CU. */
+  const uint8_t* qweight_kc;  /* NVFP4 only, optional, and only together with scales_kc: the same
+                                 codes laid out by 64-deep K chunk, uint8 [E][K/64][N][32]
+                                 (moe_nvfp4_codes_by_chunk), 16-byte aligned.  `qweight` stays
+                                 required (the 1..64-token kernels read it); with qweight_kc the
+                                 64/128-row kernel copies each chunk's codes for 32 rows as one
+                                 contiguous kilobyte instead of 32-byte pieces of 32 rows. */
 } moe_wq_t;
 
 /* Length of sorted_ids for T tokens: T*top_k + min(E, T*top_k)*(block_m-1),
@@ -224,6 +230,16 @@ moe_status_t moe_gptq_act_order_sort(const int32_t* qweight, const int32_t* g_id
  * layout); out uint8 [E][K/64][N][4]; K % 64 == 0; both 16-byte aligned. */
 moe_status_t moe_nvfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int K, uint8_t* out,
                                        moe_stream_t stream);
+
+/* NVFP4 codes re-laid by K chunk, run once when the weights are loaded:
+ *   out[e][c][n][j] = qweight[e][n][32c + j]   (c < K/64, j < 32)
+ * i.e. the 32 code bytes (64 packed values) of each 64-deep chunk of each
+ * weight row, rows of one chunk contiguous.  qweight uint8 [E][N][K/2] (the
+ * moe_wq_t NVFP4 layout); out uint8 [E][K/64][N][32], a separate buffer;
+ * K % 64 == 0; both 16-byte aligned.  Costs a second copy of the codes: the
+ * 1..64-token kernels keep reading qweight. */
+moe_status_t moe_nvfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int K, uint8_t* out,
+                                      moe_stream_t stream);
 
 /* Gather of GEMM input rows through an act-order permutation, one row per
  * flat slot f < size_m*top_k, permuted by the slot's own expert:

@@ -56,8 +56,8 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 
 def _wq(fmt=0, group=16, qweight=FAKE, scales=FAKE, zeros=None, gs=FAKE, g_idx=None, bias=None,
-        k_perm=None, scales_kc=None):
-    return _Wq(fmt, group, qweight, scales, zeros, gs, g_idx, bias, k_perm, scales_kc)
+        k_perm=None, scales_kc=None, qweight_kc=None):
+    return _Wq(fmt, group, qweight, scales, zeros, gs, g_idx, bias, k_perm, scales_kc, qweight_kc)
 
 
 def test_route_rejects(L):
@@ -96,6 +96,10 @@ def test_gemm1_rejects(L):
     assert _g1(L, _wq(fmt=1, group=32, scales_kc=FAKE)) == UNSUP   # scales by chunk: NVFP4 only
     assert _g1(L, _wq(scales_kc=FAKE), K=2880 + 32) == SHAPE       # needs K % 64 == 0
     assert _g1(L, _wq(scales_kc=FAKE + 4)) == ALIGN
+    assert _g1(L, _wq(qweight_kc=FAKE)) == UNSUP         # codes by chunk need scales by chunk
+    assert _g1(L, _wq(fmt=1, group=32, qweight_kc=FAKE)) == UNSUP
+    assert _g1(L, _wq(scales_kc=FAKE, qweight_kc=FAKE), K=2880 + 32) == SHAPE
+    assert _g1(L, _wq(scales_kc=FAKE, qweight_kc=FAKE + 4)) == ALIGN
     assert _g1(L, _wq(fmt=2, group=64)) == NULL          # zeros missing
     assert _g1(L, _wq(gs=None)) == NULL                  # NVFP4 global scale missing
     assert _g1(L, _wq(fmt=9)) == UNSUP
@@ -183,6 +187,16 @@ def test_mxfp8_entry_points_reject(L):
     assert f(_wq(**mx), _wq(**mx)) == WS
     assert L.moe_forward_mxfp8_workspace_bytes(64, 32, 4, 2880, 2880) > \
         L.moe_forward_workspace_bytes(64, 32, 4, 2880, 2880)
+
+
+def test_codes_by_chunk_rejects(L):
+    f = lambda **kw: L.moe_nvfp4_codes_by_chunk(kw.get("q", FAKE), kw.get("E", 4), 256,
+                                                kw.get("K", 2880), kw.get("o", FAKE * 2), None)
+    assert f(K=2880 + 32) == SHAPE
+    assert f(E=0) == SHAPE
+    assert f(q=None) == NULL
+    assert f(o=FAKE) == UNSUP                            # not in place
+    assert f(o=FAKE * 2 + 4) == ALIGN
 
 
 def test_scales_by_chunk_rejects(L):

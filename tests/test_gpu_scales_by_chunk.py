@@ -1,8 +1,9 @@
-"""GPU parity of the NVFP4 weights with their scales laid out by K chunk.
+"""GPU parity of the NVFP4 weights with their scales (and codes) laid out by K chunk.
 
-The re-layout moves bytes only and is compared bit-exact with NumPy; the
-64/128-row GEMM kernel that streams the chunk scales is compared with the
-float64 oracle (which reads the checkpoint layout) like the other GEMM paths.
+The re-layouts move bytes only and are compared bit-exact with NumPy; the
+64/128-row GEMM kernel that streams the chunk scales (scales only, or scales
+and codes by chunk) is compared with the float64 oracle (which reads the
+checkpoint layout) like the other GEMM paths.
 """
 import dataclasses
 
@@ -26,8 +27,12 @@ def _need_gpu():
     M.lib()
 
 
-def with_kc(Dw):
-    return dataclasses.replace(Dw, scales_kc=M.moe_nvfp4_scales_by_chunk(Dw))
+def with_kc(Dw, codes=False):
+    return dataclasses.replace(Dw, scales_kc=M.moe_nvfp4_scales_by_chunk(Dw),
+                               qweight_kc=M.moe_nvfp4_codes_by_chunk(Dw) if codes else None)
+
+
+CODES = pytest.mark.parametrize("codes", [False, True], ids=["scales", "scales+codes"])
 
 
 @pytest.mark.parametrize("E,N,K", [(3, 384, 320), (2, 2880, 2880), (5, 16, 64)])
@@ -41,42 +46,55 @@ def test_scales_by_chunk_bitexact(E, N, K):
     assert Dw.scales.shape == (E, N, K // 16)
 
 
+@pytest.mark.parametrize("E,N,K", [(3, 384, 320), (2, 2880, 2880), (5, 16, 64)])
+def test_codes_by_chunk_bitexact(E, N, K):
+    w = S.make_weights("nvfp4", E=E, N=N, K=K, bias=False, seed=N + K + 1)
+    Dw = M.QuantWeights.from_arrays(w.fmt, w.group, w.N, w.K, w.qweight, w.scales, None,
+                                    w.global_scale, None)
+    got = M.moe_nvfp4_codes_by_chunk(Dw).cpu().numpy()
+    ref = w.qweight.reshape(E, N, K // 64, 32).transpose(0, 2, 1, 3)
+    np.testing.assert_array_equal(got, ref)
+    assert got.shape == (E, K // 64, N, 32)
+
+
 def _small(act="swigluoai", E=4, k=2, H=320, I=192, T=300, seed=51, **kw):
     route = "sigmoid_bias" if act == "relu2" else "softmax"
     return S.make_layer(E=E, top_k=k, H=H, I=I, fmt="nvfp4", act=act, route=route, T=T, seed=seed,
                         router_bias_std=0.1 if route == "sigmoid_bias" else 0.0, **kw)
 
 
+@CODES
 @pytest.mark.parametrize("act", ["none", "swigluoai", "relu2"])
 @pytest.mark.parametrize("B", [64, 128])
 @pytest.mark.parametrize("H", [320, 2880])
-def test_gemm1_scales_by_chunk(act, B, H):
+def test_gemm1_scales_by_chunk(act, B, H, codes):
     L = _small("relu2" if act == "relu2" else "swigluoai", H=H, T=300 if H < 2880 else 150,
                x_std=12.0)
     D = upload(L)
-    w13 = with_kc(D["w13"])
+    w13 = with_kc(D["w13"], codes)
     ids, w = O.route(L)
     si, ei, npp = O.align(ids, L.E, B)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    print(f"gemm1 scales by chunk act={act} B={B} H={H}", flush=True)
+    print(f"gemm1 by chunk act={act} B={B} H={H} codes={codes}", flush=True)
     out = M.moe_w4a16_gemm1(D["x"], L.top_k, w13, act, L.alpha, L.beta, L.limit, t(si), t(ei),
                             t(np.array([npp], np.int32)), B)
     ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, act, L.alpha, L.beta, L.limit, si, ei, npp, B)
     assert_rows_close(host_bf16(out), ref, rows=cov, what=f"gemm1 scales by chunk {act} B{B} H{H}")
 
 
+@CODES
 @pytest.mark.parametrize("B", [64, 128])
 @pytest.mark.parametrize("I", [192, 2880])
-def test_gemm2_scales_by_chunk(B, I):
+def test_gemm2_scales_by_chunk(B, I, codes):
     L = _small(I=I, T=300 if I < 2880 else 150)
     D = upload(L)
-    w2 = with_kc(D["w2"])
+    w2 = with_kc(D["w2"], codes)
     ids, w = O.route(L)
     si, ei, npp = O.align(ids, L.E, B)
     n = L.T * L.top_k
     a_bits = S.f32_to_bf16_bits(np.random.default_rng(I + B).standard_normal((n, I)).astype(np.float32))
     t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).cuda()
-    print(f"gemm2 scales by chunk B={B} I={I}", flush=True)
+    print(f"gemm2 by chunk B={B} I={I} codes={codes}", flush=True)
     y = M.moe_w4a16_gemm2(t(a_bits.view(np.int16)).view(torch.bfloat16), w2,
                           t(w.reshape(-1).astype(np.float32)), True, t(si), t(ei),
                           t(np.array([npp], np.int32)), B)
@@ -84,24 +102,27 @@ def test_gemm2_scales_by_chunk(B, I):
     assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 scales by chunk B{B} I{I}")
 
 
+@CODES
 @pytest.mark.parametrize("T", [13, 200, 600])
-def test_forward_scales_by_chunk(T):
-    """T = 13: 16-row blocks (the decode kernels ignore the re-laid copy);
+def test_forward_scales_by_chunk(T, codes):
+    """T = 13: 16-row blocks (the decode kernels ignore the re-laid copies);
     T = 200, 600: 128-row blocks on the streaming kernel."""
     L = _small(T=T, E=6)
     D = upload(L)
-    D["w13"], D["w2"] = with_kc(D["w13"]), with_kc(D["w2"])
-    print(f"forward scales by chunk T={T}", flush=True)
+    D["w13"], D["w2"] = with_kc(D["w13"], codes), with_kc(D["w2"], codes)
+    print(f"forward by chunk T={T} codes={codes}", flush=True)
     out = gpu_forward(L, D)
     assert_rows_close(host_bf16(out), O.forward(L)["out"], what=f"forward scales by chunk T{T}")
 
 
-def test_forward_scales_by_chunk_full_size():
+@CODES
+def test_forward_scales_by_chunk_full_size(codes):
     """The gpt-oss-20b NVFP4 layer at T = 4096 (the benchmark's headline
     configuration); sampled tokens against the oracle, bitwise repeatable."""
     L = S.make_config(2, 4096)
     D = upload(L)
-    D["w13"], D["w2"] = with_kc(D["w13"]), with_kc(D["w2"])
+    D["w13"], D["w2"] = with_kc(D["w13"], codes), with_kc(D["w2"], codes)
+    print(f"forward by chunk full size codes={codes}", flush=True)
     out = gpu_forward(L, D)
     out2 = gpu_forward(L, D)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
