@@ -15,12 +15,14 @@
 // position.  Larger E (up to 1024) keeps up to 16 scores per lane and finds
 // the k winners by k rounds of a wave-wide argmax.
 //
-// Align: one workgroup of 1024 threads.  Counts per expert with LDS atomics
-// (order-free), pads each count to block_m, and places every slot at
+// Align: one workgroup of 1024 threads.  Pads each expert's count to block_m
+// and places every slot at
 //   offset[e] + (number of earlier slots with the same expert),
-// which makes the sort stable and the output unique.  The within-wave rank
-// comes from ballots over the bits of the expert id (lanes with an equal id
-// share every bit), the cross-wave part from a per-wave count table in LDS.
+// which makes the sort stable and the output unique.  Each wave owns one
+// contiguous run of slots and makes two passes over it (count, then place),
+// with one block-wide step between them; the within-wave rank comes from
+// ballots over the bits of the expert id (lanes with an equal id share every
+// bit), the cross-wave part from a per-wave count table in LDS.
 //
 // For small batches moe_forward runs both in one workgroup (route_align_kernel):
 // the routed ids go through LDS straight into the sort, saving a launch.
@@ -225,10 +227,7 @@ constexpr int kAlignMaxE = 1024;
 
 // LDS of the sort.
 struct AlignLds {
-  int cnt[kAlignMaxE];
-  int off[kAlignMaxE];
-  int placed[kAlignMaxE];
-  int wave_cnt[kAlignWaves][kAlignMaxE];
+  int wave_cnt[kAlignWaves][kAlignMaxE];  // per-wave counts, then per-wave cursors
   int wave_tot[kAlignWaves];
   int total;
 };
@@ -249,32 +248,78 @@ __device__ int block_exclusive_scan(int v, int* wave_tot) {
   return before + incl - v;
 }
 
+constexpr int kIdBatch = 8;  // 64-slot groups whose ids are loaded together
+
+// Lanes of this wave holding the same expert id as this lane (ballots over
+// the id's nbits bits), among the lanes where `valid` holds.
+__device__ __forceinline__ unsigned long long match_expert(int e, bool valid, int nbits) {
+  unsigned long long same = __ballot(valid);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const unsigned long long m = __ballot((e >> bit) & 1);
+    same &= ((e >> bit) & 1) ? m : ~m;
+  }
+  return same;
+}
+
 // The sort itself, for the whole 1024-thread workgroup; topk_ids may point to
-// global memory or to LDS.
+// global memory or to LDS.  Each of the 16 waves owns one contiguous run of
+// slots.  Pass 1: the wave counts its run per expert (per 64-slot group one
+// lane per expert adds the group's count to the wave's own LDS row, so no
+// atomics).  Then per expert: the total, the padded segment offsets (a block
+// scan) and, in wave order, where each wave's share of the segment starts.
+// Pass 2: the wave walks its run again and places each slot at its expert's
+// cursor plus its rank among the group's lanes of that expert.  Runs are in
+// wave order and groups in slot order, so equal experts keep slot order.
 __device__ __forceinline__ void align_block(const int32_t* topk_ids, int n_slots, int E, int block_m,
                                             int cap, int32_t* __restrict__ sorted_ids,
                                             int32_t* __restrict__ expert_ids,
                                             int32_t* __restrict__ num_post_pad, AlignLds& L) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const int run = ((n_slots + kAlignWaves - 1) / kAlignWaves + 63) / 64 * 64;
+  const int s0 = min(wid * run, n_slots), s1 = min(s0 + run, n_slots);
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  for (int e = tid; e < E; e += kAlignThreads) {
-    L.cnt[e] = 0;
-    L.placed[e] = 0;
-  }
   for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) L.wave_cnt[i / E][i % E] = 0;
   __syncthreads();
-  for (int f = tid; f < n_slots; f += kAlignThreads) {
-    const int e = topk_ids[f];
-    if (e >= 0 && e < E) atomicAdd(&L.cnt[e], 1);
+  // groups of kIdBatch 64-slot groups: their ids are loaded together (one
+  // memory latency per batch, not per group)
+  for (int b0 = s0; b0 < s1; b0 += 64 * kIdBatch) {
+    int ev[kIdBatch];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int f = b0 + 64 * u + lane;
+      ev[u] = (f < s1) ? topk_ids[f] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      if (b0 + 64 * u >= s1) break;  // past the run (uniform over the wave)
+      int e = ev[u];
+      const bool valid = (e >= 0 && e < E);
+      if (!valid) e = 0;
+      const unsigned long long same = match_expert(e, valid, nbits);
+      if (valid && ((same >> lane) >> 1) == 0ull) L.wave_cnt[wid][e] += __popcll(same);  // last lane of its group
+    }
   }
   __syncthreads();
 
-  // padded segment offsets (E <= 1024: one expert per thread)
-  const int my_pad = (tid < E) ? (L.cnt[tid] + block_m - 1) / block_m * block_m : 0;
+  // per expert (E <= 1024: one per thread): count, padded segment offsets
+  int my_cnt = 0;
+  if (tid < E)
+    for (int w = 0; w < kAlignWaves; ++w) my_cnt += L.wave_cnt[w][tid];
+  const int my_pad = (tid < E) ? (my_cnt + block_m - 1) / block_m * block_m : 0;
   const int my_off = block_exclusive_scan(my_pad, L.wave_tot);
-  if (tid < E) L.off[tid] = my_off;
   if (tid == E - 1) L.total = my_off + my_pad;
+  if (tid < E) {
+    // each wave's share of the segment starts after the earlier waves' shares
+    int at = my_off;
+    for (int w = 0; w < kAlignWaves; ++w) {
+      const int c = L.wave_cnt[w][tid];
+      L.wave_cnt[w][tid] = at;
+      at += c;
+    }
+  }
   __syncthreads();
   const int total = L.total;
   if (tid == 0) num_post_pad[0] = total;
@@ -287,37 +332,31 @@ __device__ __forceinline__ void align_block(const int32_t* topk_ids, int n_slots
   for (int b = total / block_m + tid; b < nblocks; b += kAlignThreads) expert_ids[b] = -1;
   // sentinel in each expert's padding and past the used length
   if (tid < E) {
-    for (int i = my_off + L.cnt[tid]; i < my_off + my_pad; ++i) sorted_ids[i] = n_slots;
+    for (int i = my_off + my_cnt; i < my_off + my_pad; ++i) sorted_ids[i] = n_slots;
   }
   for (int i = total + tid; i < cap; i += kAlignThreads) sorted_ids[i] = n_slots;
 
-  // stable placement, one 1024-slot chunk at a time
-  for (int c0 = 0; c0 < n_slots; c0 += kAlignThreads) {
-    const int f = c0 + tid;
-    int e = (f < n_slots) ? topk_ids[f] : -1;
-    const bool valid = (e >= 0 && e < E);
-    if (!valid) e = 0;
-    unsigned long long same = __ballot(valid);
-    for (int bit = 0; bit < 10; ++bit) {
-      const unsigned long long m = __ballot((e >> bit) & 1);
-      same &= ((e >> bit) & 1) ? m : ~m;
+  // stable placement: the cursor is read by every lane of a group before the
+  // group's last lane advances it (one wave's LDS accesses stay in order)
+  for (int b0 = s0; b0 < s1; b0 += 64 * kIdBatch) {
+    int ev[kIdBatch];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int f = b0 + 64 * u + lane;
+      ev[u] = (f < s1) ? topk_ids[f] : -1;
     }
-    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int rank_in_wave = __popcll(same & lt);
-    const bool leader = valid && ((same >> lane) >> 1) == 0ull;  // last lane of its group
-    if (leader) L.wave_cnt[wid][e] = __popcll(same);
-    __syncthreads();
-    if (valid) {
-      int before = L.placed[e];
-      for (int w2 = 0; w2 < wid; ++w2) before += L.wave_cnt[w2][e];
-      sorted_ids[L.off[e] + before + rank_in_wave] = f;
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      if (b0 + 64 * u >= s1) break;  // past the run (uniform over the wave)
+      const int f = b0 + 64 * u + lane;
+      int e = ev[u];
+      const bool valid = (e >= 0 && e < E);
+      if (!valid) e = 0;
+      const unsigned long long same = match_expert(e, valid, nbits);
+      const int at = L.wave_cnt[wid][e];
+      if (valid) sorted_ids[at + __popcll(same & lt)] = f;
+      if (valid && ((same >> lane) >> 1) == 0ull) L.wave_cnt[wid][e] = at + __popcll(same);
     }
-    __syncthreads();
-    if (leader) {
-      atomicAdd(&L.placed[e], __popcll(same));
-      L.wave_cnt[wid][e] = 0;
-    }
-    __syncthreads();
   }
 }
 

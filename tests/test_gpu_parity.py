@@ -89,8 +89,10 @@ def test_route_align_fused(T, E, k, kind, B):
 # -------------------------------------------------------------------- align --
 
 @pytest.mark.parametrize("T,k,E,B", [(1, 4, 32, 16), (13, 2, 8, 16), (64, 4, 32, 64), (511, 6, 128, 32),
-                                      (4096, 4, 32, 128), (8192, 4, 128, 64), (3, 3, 1024, 16)])
+                                      (4096, 4, 32, 128), (8192, 4, 128, 64), (3, 3, 1024, 16),
+                                      (3001, 7, 1000, 32), (2000, 1, 1, 16), (700, 8, 2, 64)])
 def test_align_bitexact(T, k, E, B):
+    """Ragged per-wave runs (3001 x 7 slots), a single expert, two experts."""
     rng = np.random.default_rng(T + E + B)
     ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
     if T > 3:
