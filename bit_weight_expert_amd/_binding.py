@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_scales_by_chunk.restype = i
         L.moe_nvfp4_codes_by_chunk.argtypes = [vp, i, i, i, vp, vp]
         L.moe_nvfp4_codes_by_chunk.restype = i
+        L.moe_align_large.argtypes = [vp, i, i, i, i, vp, vp, vp, vp, vp]
+        L.moe_align_large.restype = i
+        L.moe_align_large_scratch_bytes.argtypes = [i]
+        L.moe_align_large_scratch_bytes.restype = ctypes.c_size_t
         L.moe_mxfp8_quantize.argtypes = [vp, i, i, vp, vp, vp, vp]
         L.moe_mxfp8_quantize.restype = i
         L.moe_mx_gemm1.argtypes = [vp, vp, i, i, i, i, i, wq, i, f, f, f, vp, vp, vp, i, vp, vp]
@@ -222,6 +226,25 @@ def moe_align(topk_ids: torch.Tensor, E: int, block_m: int, sorted_ids=None, exp
         num_post_pad = torch.zeros((1,), dtype=torch.int32, device=dev)
     _check(lib().moe_align(_ptr(topk_ids), T, k, E, block_m, _ptr(sorted_ids), _ptr(expert_ids),
                            _ptr(num_post_pad), _stream()), "moe_align")
+    return sorted_ids, expert_ids, num_post_pad
+
+
+def moe_align_large(topk_ids: torch.Tensor, E: int, block_m: int, counts=None):
+    """The multi-workgroup sort (same outputs as moe_align) -> (sorted_ids, expert_ids,
+    num_post_pad); counts: int32 scratch of moe_align_large_scratch_bytes(E) bytes."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    cap = moe_align_capacity(T, k, E, block_m)
+    dev = topk_ids.device
+    sorted_ids = torch.empty((cap,), dtype=torch.int32, device=dev)
+    expert_ids = torch.empty((cap // block_m if block_m else 0,), dtype=torch.int32, device=dev)
+    num_post_pad = torch.zeros((1,), dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty((max(lib().moe_align_large_scratch_bytes(E) // 4, 1),),
+                             dtype=torch.int32, device=dev)
+    _check(lib().moe_align_large(_ptr(topk_ids), T, k, E, block_m, _ptr(sorted_ids),
+                                 _ptr(expert_ids), _ptr(num_post_pad), _ptr(counts), _stream()),
+           "moe_align_large")
     return sorted_ids, expert_ids, num_post_pad
 
 

@@ -12,6 +12,8 @@ extern "C" hipError_t moe_launch_route(const float*, int, int, int, int, const f
                                        int32_t*, float*, hipStream_t);
 extern "C" hipError_t moe_launch_align(const int32_t*, int, int, int, int, int32_t*, int32_t*,
                                        int32_t*, hipStream_t);
+extern "C" hipError_t moe_launch_align_large(const int32_t*, int, int, int, int, int32_t*, int32_t*,
+                                             int32_t*, int32_t*, hipStream_t);
 extern "C" hipError_t moe_launch_route_align(const float*, int, int, int, int, const float*, int,
                                              int32_t*, float*, int, int, int32_t*, int32_t*,
                                              int32_t*, hipStream_t);
@@ -122,8 +124,12 @@ int pick_block_m(int T, int top_k, int E) {
 }
 
 struct WsLayout {
-  size_t ids, w, sorted, eids, npp, act, y, total;
+  size_t ids, w, sorted, eids, npp, cnt, act, y, total;
 };
+
+// Slots from which moe_forward sorts with the multi-workgroup kernels
+// (measured: the single workgroup is as fast up to about this size).
+constexpr int kAlignLargeMin = 8192;
 
 WsLayout ws_layout(int T, int E, int top_k, int hidden, int inter, int block_m) {
   WsLayout L;
@@ -135,6 +141,7 @@ WsLayout ws_layout(int T, int E, int top_k, int hidden, int inter, int block_m) 
   L.sorted = o; o = round_up(o + cap * 4, 256);
   L.eids = o; o = round_up(o + (cap / block_m) * 4, 256);
   L.npp = o; o = round_up(o + 4, 256);
+  L.cnt = o; o = round_up(o + (size_t)moe::kAlignGroups * E * 4, 256);
   L.act = o; o = round_up(o + n * (size_t)inter * 2, 256);
   L.y = o; o = round_up(o + n * (size_t)hidden * 2, 256);
   L.total = o;
@@ -221,6 +228,41 @@ moe_status_t moe_align(const int32_t* topk_ids, int T, int top_k, int E, int blo
   const int cap = (int)moe_align_capacity(T, top_k, E, block_m);
   return hip_status(moe_launch_align(topk_ids, T * top_k, E, block_m, cap, sorted_ids, expert_ids,
                                      num_post_pad, static_cast<hipStream_t>(stream)));
+}
+
+// Routing and the sort of moe_forward: fused in one workgroup for small
+// batches, the multi-workgroup sort (counts in the workspace) for large ones.
+hipError_t route_and_sort(const float* logits, int T, int E, int top_k, int kind,
+                          const float* ebias, int renorm, int32_t* ids, float* tw, int block_m,
+                          int cap, int32_t* sorted, int32_t* eids, int32_t* npp, int32_t* counts,
+                          hipStream_t s) {
+  const int n = T * top_k;
+  if (n < kAlignLargeMin)
+    return moe_launch_route_align(logits, T, E, top_k, kind, ebias, renorm, ids, tw, block_m, cap,
+                                  sorted, eids, npp, s);
+  hipError_t e = moe_launch_route(logits, T, E, top_k, kind, ebias, renorm, ids, tw, s);
+  if (e == hipSuccess)
+    e = moe_launch_align_large(ids, n, E, block_m, cap, counts, sorted, eids, npp, s);
+  return e;
+}
+
+size_t moe_align_large_scratch_bytes(int E) {
+  return E > 0 && E <= kMaxE ? (size_t)moe::kAlignGroups * E * 4 : 0;
+}
+
+moe_status_t moe_align_large(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
+                             int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_post_pad,
+                             int32_t* counts, moe_stream_t stream) {
+  if (T < 0 || top_k < 1 || E <= 0 || E > kMaxE || !valid_block_m(block_m)) return MOE_ERR_SHAPE;
+  if ((long long)T * top_k >= (1LL << 24)) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (topk_ids == nullptr || sorted_ids == nullptr || expert_ids == nullptr ||
+      num_post_pad == nullptr || counts == nullptr)
+    return MOE_ERR_NULL;
+  const int cap = (int)moe_align_capacity(T, top_k, E, block_m);
+  return hip_status(moe_launch_align_large(topk_ids, T * top_k, E, block_m, cap, counts, sorted_ids,
+                                           expert_ids, num_post_pad,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_route_align(const float* logits, int T, int E, int top_k, moe_route_t kind,
@@ -474,9 +516,8 @@ moe_status_t moe_forward_mxfp8(const uint16_t* x, const float* logits, int T, in
   const int cap = (int)moe_align_capacity(T, top_k, E, block_m);
   const int mul = mul_topk_weights;
 
-  hipError_t e = moe_launch_route_align(logits, T, E, top_k, (int)kind, expert_bias,
-                                        renormalize ? 1 : 0, ids, tw, block_m, cap, sorted, eids,
-                                        npp, s);
+  hipError_t e = route_and_sort(logits, T, E, top_k, (int)kind, expert_bias, renormalize ? 1 : 0,
+                                ids, tw, block_m, cap, sorted, eids, npp, reinterpret_cast<int32_t*>(ws + L.base.cnt), s);
   if (block_m >= 64 && mx_fits(hidden, block_m) && mx_fits(inter, block_m)) {
     // MX-scaled MFMA: both GEMMs read e4m3 codes and e8m0 scales
     if (e == hipSuccess)
@@ -563,9 +604,8 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, i
   const int n = T * top_k;
   const int cap = (int)moe_align_capacity(T, top_k, E, block_m);
 
-  hipError_t e = moe_launch_route_align(logits, T, E, top_k, (int)kind, expert_bias,
-                                        renormalize ? 1 : 0, ids, tw, block_m, cap, sorted, eids,
-                                        npp, s);
+  hipError_t e = route_and_sort(logits, T, E, top_k, (int)kind, expert_bias, renormalize ? 1 : 0,
+                                ids, tw, block_m, cap, sorted, eids, npp, reinterpret_cast<int32_t*>(ws + L.cnt), s);
   // Act-order families: GEMM1 reads one gathered input row per slot from the
   // y buffer (free until GEMM2), in the top_k = 1 view; GEMM2's input rows are
   // permuted in place.

@@ -14,6 +14,8 @@ typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 // Weight formats and epilogues (values match the public enums).
 enum { FMT_NVFP4 = 0, FMT_MXFP4 = 1, FMT_GPTQ = 2 };
 enum { EPI_SWIGLU = 0, EPI_RELU2 = 1, EPI_NONE = 2, EPI_DOWN = 3 };
+// Workgroups of the multi-workgroup sort (its count table is kAlignGroups x E ints).
+constexpr int kAlignGroups = 16;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);

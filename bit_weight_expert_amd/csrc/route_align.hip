@@ -261,30 +261,19 @@ __device__ __forceinline__ unsigned long long match_expert(int e, bool valid, in
   return same;
 }
 
-// The sort itself, for the whole 1024-thread workgroup; topk_ids may point to
-// global memory or to LDS.  Each of the 16 waves owns one contiguous run of
-// slots.  Pass 1: the wave counts its run per expert (per 64-slot group one
-// lane per expert adds the group's count to the wave's own LDS row, so no
-// atomics).  Then per expert: the total, the padded segment offsets (a block
-// scan) and, in wave order, where each wave's share of the segment starts.
-// Pass 2: the wave walks its run again and places each slot at its expert's
-// cursor plus its rank among the group's lanes of that expert.  Runs are in
-// wave order and groups in slot order, so equal experts keep slot order.
-__device__ __forceinline__ void align_block(const int32_t* topk_ids, int n_slots, int E, int block_m,
-                                            int cap, int32_t* __restrict__ sorted_ids,
-                                            int32_t* __restrict__ expert_ids,
-                                            int32_t* __restrict__ num_post_pad, AlignLds& L) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
-  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-  const int run = ((n_slots + kAlignWaves - 1) / kAlignWaves + 63) / 64 * 64;
-  const int s0 = min(wid * run, n_slots), s1 = min(s0 + run, n_slots);
-  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+// Run of slots [s0, s1) that wave `wid` owns inside a workgroup's range [r0, r1).
+__device__ __forceinline__ void wave_run(int r0, int r1, int wid, int& s0, int& s1) {
+  const int run = ((r1 - r0 + kAlignWaves - 1) / kAlignWaves + 63) / 64 * 64;
+  s0 = min(r0 + wid * run, r1);
+  s1 = min(s0 + run, r1);
+}
 
-  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) L.wave_cnt[i / E][i % E] = 0;
-  __syncthreads();
-  // groups of kIdBatch 64-slot groups: their ids are loaded together (one
-  // memory latency per batch, not per group)
+// Pass 1: the wave counts its run per expert into its own LDS row (per
+// 64-slot group one lane per expert adds the group's count, so no atomics).
+// Ids are loaded kIdBatch groups at a time (one memory latency per batch).
+__device__ __forceinline__ void count_run(const int32_t* topk_ids, int s0, int s1, int E, int nbits,
+                                          int* row) {
+  const int lane = threadIdx.x & 63;
   for (int b0 = s0; b0 < s1; b0 += 64 * kIdBatch) {
     int ev[kIdBatch];
 #pragma unroll
@@ -299,9 +288,80 @@ __device__ __forceinline__ void align_block(const int32_t* topk_ids, int n_slots
       const bool valid = (e >= 0 && e < E);
       if (!valid) e = 0;
       const unsigned long long same = match_expert(e, valid, nbits);
-      if (valid && ((same >> lane) >> 1) == 0ull) L.wave_cnt[wid][e] += __popcll(same);  // last lane of its group
+      if (valid && ((same >> lane) >> 1) == 0ull) row[e] += __popcll(same);  // last lane of its group
     }
   }
+}
+
+// Pass 2: the wave walks its run again and places each slot at its expert's
+// cursor plus its rank among the group's lanes of that expert.  The cursor is
+// read by every lane of a group before the group's last lane advances it (one
+// wave's LDS accesses stay in order).
+__device__ __forceinline__ void place_run(const int32_t* topk_ids, int s0, int s1, int E, int nbits,
+                                          int* cursor, int32_t* __restrict__ sorted_ids) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int b0 = s0; b0 < s1; b0 += 64 * kIdBatch) {
+    int ev[kIdBatch];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int f = b0 + 64 * u + lane;
+      ev[u] = (f < s1) ? topk_ids[f] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      if (b0 + 64 * u >= s1) break;  // past the run (uniform over the wave)
+      const int f = b0 + 64 * u + lane;
+      int e = ev[u];
+      const bool valid = (e >= 0 && e < E);
+      if (!valid) e = 0;
+      const unsigned long long same = match_expert(e, valid, nbits);
+      const int at = cursor[e];
+      if (valid) sorted_ids[at + __popcll(same & lt)] = f;
+      if (valid && ((same >> lane) >> 1) == 0ull) cursor[e] = at + __popcll(same);
+    }
+  }
+}
+
+// Expert of every block (-1 past the used length) and the sentinel in each
+// expert's padding and past the used length; thread e < E holds expert e's
+// padded offset, count and padded count.
+__device__ __forceinline__ void align_tables(int n_slots, int E, int block_m, int cap, int total,
+                                             int my_off, int my_cnt, int my_pad,
+                                             int32_t* __restrict__ sorted_ids,
+                                             int32_t* __restrict__ expert_ids,
+                                             int32_t* __restrict__ num_post_pad) {
+  const int tid = threadIdx.x;
+  if (tid == 0) num_post_pad[0] = total;
+  const int nblocks = cap / block_m;
+  if (tid < E) {
+    for (int b = my_off / block_m; b < (my_off + my_pad) / block_m; ++b) expert_ids[b] = tid;
+  }
+  for (int b = total / block_m + tid; b < nblocks; b += kAlignThreads) expert_ids[b] = -1;
+  if (tid < E) {
+    for (int i = my_off + my_cnt; i < my_off + my_pad; ++i) sorted_ids[i] = n_slots;
+  }
+  for (int i = total + tid; i < cap; i += kAlignThreads) sorted_ids[i] = n_slots;
+}
+
+// The sort itself, for the whole 1024-thread workgroup; topk_ids may point to
+// global memory or to LDS.  Each of the 16 waves owns one contiguous run of
+// slots: pass 1 counts it, then per expert the total, the padded segment
+// offsets (a block scan) and, in wave order, where each wave's share of the
+// segment starts; pass 2 places.  Runs are in wave order and groups in slot
+// order, so equal experts keep slot order.
+__device__ __forceinline__ void align_block(const int32_t* topk_ids, int n_slots, int E, int block_m,
+                                            int cap, int32_t* __restrict__ sorted_ids,
+                                            int32_t* __restrict__ expert_ids,
+                                            int32_t* __restrict__ num_post_pad, AlignLds& L) {
+  const int tid = threadIdx.x, wid = tid >> 6;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  int s0, s1;
+  wave_run(0, n_slots, wid, s0, s1);
+
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) L.wave_cnt[i / E][i % E] = 0;
+  __syncthreads();
+  count_run(topk_ids, s0, s1, E, nbits, L.wave_cnt[wid]);
   __syncthreads();
 
   // per expert (E <= 1024: one per thread): count, padded segment offsets
@@ -321,43 +381,9 @@ __device__ __forceinline__ void align_block(const int32_t* topk_ids, int n_slots
     }
   }
   __syncthreads();
-  const int total = L.total;
-  if (tid == 0) num_post_pad[0] = total;
-
-  // expert of every block; -1 past the used length
-  const int nblocks = cap / block_m;
-  if (tid < E) {
-    for (int b = my_off / block_m; b < (my_off + my_pad) / block_m; ++b) expert_ids[b] = tid;
-  }
-  for (int b = total / block_m + tid; b < nblocks; b += kAlignThreads) expert_ids[b] = -1;
-  // sentinel in each expert's padding and past the used length
-  if (tid < E) {
-    for (int i = my_off + my_cnt; i < my_off + my_pad; ++i) sorted_ids[i] = n_slots;
-  }
-  for (int i = total + tid; i < cap; i += kAlignThreads) sorted_ids[i] = n_slots;
-
-  // stable placement: the cursor is read by every lane of a group before the
-  // group's last lane advances it (one wave's LDS accesses stay in order)
-  for (int b0 = s0; b0 < s1; b0 += 64 * kIdBatch) {
-    int ev[kIdBatch];
-#pragma unroll
-    for (int u = 0; u < kIdBatch; ++u) {
-      const int f = b0 + 64 * u + lane;
-      ev[u] = (f < s1) ? topk_ids[f] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kIdBatch; ++u) {
-      if (b0 + 64 * u >= s1) break;  // past the run (uniform over the wave)
-      const int f = b0 + 64 * u + lane;
-      int e = ev[u];
-      const bool valid = (e >= 0 && e < E);
-      if (!valid) e = 0;
-      const unsigned long long same = match_expert(e, valid, nbits);
-      const int at = L.wave_cnt[wid][e];
-      if (valid) sorted_ids[at + __popcll(same & lt)] = f;
-      if (valid && ((same >> lane) >> 1) == 0ull) L.wave_cnt[wid][e] = at + __popcll(same);
-    }
-  }
+  align_tables(n_slots, E, block_m, cap, L.total, my_off, my_cnt, my_pad, sorted_ids, expert_ids,
+               num_post_pad);
+  place_run(topk_ids, s0, s1, E, nbits, L.wave_cnt[wid], sorted_ids);
 }
 
 __global__ void __launch_bounds__(kAlignThreads) align_kernel(
@@ -366,6 +392,78 @@ __global__ void __launch_bounds__(kAlignThreads) align_kernel(
     int32_t* __restrict__ num_post_pad) {
   __shared__ AlignLds L;
   align_block(topk_ids, n_slots, E, block_m, cap, sorted_ids, expert_ids, num_post_pad, L);
+}
+
+// The same sort over kAlignGroups workgroups for large batches: workgroup g
+// owns the g-th contiguous range of slots (its 16 waves a run each).  The
+// count launch writes each workgroup's per-expert counts to counts[g][E]; the
+// place launch re-counts its range per wave, adds the earlier workgroups'
+// counts from the table to each cursor and places; workgroup 0 also writes
+// the block table, the sentinels and the padded length.  Same output as the
+// single workgroup (slot order is kept across ranges, waves and groups).
+__device__ __forceinline__ void group_range(int n_slots, int g, int& r0, int& r1) {
+  const int R = ((n_slots + kAlignGroups - 1) / kAlignGroups + 63) / 64 * 64;
+  r0 = min(g * R, n_slots);
+  r1 = min(r0 + R, n_slots);
+}
+
+__global__ void __launch_bounds__(kAlignThreads) align_count_kernel(
+    const int32_t* __restrict__ topk_ids, int n_slots, int E, int32_t* __restrict__ counts) {
+  __shared__ AlignLds L;
+  const int tid = threadIdx.x, wid = tid >> 6, g = blockIdx.x;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  int r0, r1, s0, s1;
+  group_range(n_slots, g, r0, r1);
+  wave_run(r0, r1, wid, s0, s1);
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) L.wave_cnt[i / E][i % E] = 0;
+  __syncthreads();
+  count_run(topk_ids, s0, s1, E, nbits, L.wave_cnt[wid]);
+  __syncthreads();
+  for (int e = tid; e < E; e += kAlignThreads) {
+    int c = 0;
+    for (int w = 0; w < kAlignWaves; ++w) c += L.wave_cnt[w][e];
+    counts[g * E + e] = c;
+  }
+}
+
+__global__ void __launch_bounds__(kAlignThreads) align_place_kernel(
+    const int32_t* __restrict__ topk_ids, int n_slots, int E, int block_m, int cap,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ num_post_pad) {
+  __shared__ AlignLds L;
+  const int tid = threadIdx.x, wid = tid >> 6, g = blockIdx.x;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  int r0, r1, s0, s1;
+  group_range(n_slots, g, r0, r1);
+  wave_run(r0, r1, wid, s0, s1);
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) L.wave_cnt[i / E][i % E] = 0;
+  __syncthreads();
+  count_run(topk_ids, s0, s1, E, nbits, L.wave_cnt[wid]);
+  // per expert: total over all ranges, and the count of the ranges before g
+  int my_cnt = 0, before = 0;
+  if (tid < E) {
+    for (int h = 0; h < kAlignGroups; ++h) {
+      const int c = counts[h * E + tid];
+      my_cnt += c;
+      before += h < g ? c : 0;
+    }
+  }
+  const int my_pad = (tid < E) ? (my_cnt + block_m - 1) / block_m * block_m : 0;
+  const int my_off = block_exclusive_scan(my_pad, L.wave_tot);  // (its barriers order pass 1 too)
+  if (tid == E - 1) L.total = my_off + my_pad;
+  if (tid < E) {
+    int at = my_off + before;
+    for (int w = 0; w < kAlignWaves; ++w) {
+      const int c = L.wave_cnt[w][tid];
+      L.wave_cnt[w][tid] = at;
+      at += c;
+    }
+  }
+  __syncthreads();
+  if (g == 0)
+    align_tables(n_slots, E, block_m, cap, L.total, my_off, my_cnt, my_pad, sorted_ids, expert_ids,
+                 num_post_pad);
+  place_run(topk_ids, s0, s1, E, nbits, L.wave_cnt[wid], sorted_ids);
 }
 
 // Routing and the sort in one workgroup (small batches): the 16 waves route
@@ -396,6 +494,15 @@ extern "C" hipError_t moe_launch_route(const float* logits, int T, int E, int to
     moe::route_kernel<0><<<grid, block, 0, stream>>>(logits, T, E, top_k, ebias, renorm, ids, w);
   else
     moe::route_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, top_k, ebias, renorm, ids, w);
+  return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_align_large(const int32_t* ids, int n_slots, int E, int block_m,
+                                             int cap, int32_t* counts, int32_t* sorted_ids,
+                                             int32_t* expert_ids, int32_t* npp, hipStream_t stream) {
+  moe::align_count_kernel<<<moe::kAlignGroups, moe::kAlignThreads, 0, stream>>>(ids, n_slots, E, counts);
+  moe::align_place_kernel<<<moe::kAlignGroups, moe::kAlignThreads, 0, stream>>>(
+      ids, n_slots, E, block_m, cap, counts, sorted_ids, expert_ids, npp);
   return hipGetLastError();
 }
 

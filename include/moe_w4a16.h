@@ -154,6 +154,19 @@ moe_status_t moe_align(const int32_t* topk_ids, int T, int top_k, int E, int blo
                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_post_pad,
                        moe_stream_t stream);
 
+/* The same sort (same outputs, bit for bit) spread over 16 workgroups, for
+ * large batches: a counting launch writes each workgroup's per-expert counts
+ * to `counts`, a placing launch reads them.  moe_forward uses it from 8192
+ * slots on, with the counts in its workspace.
+ *   counts  int32 scratch of moe_align_large_scratch_bytes(E) bytes (16*E
+ *           ints), caller-owned, overwritten; no alignment beyond 4 bytes.
+ * Other arguments and limits as moe_align. */
+moe_status_t moe_align_large(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
+                             int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_post_pad,
+                             int32_t* counts, moe_stream_t stream);
+/* Bytes of moe_align_large's counts for E experts (0 if E is out of range). */
+size_t moe_align_large_scratch_bytes(int E);
+
 /* moe_route followed by moe_align on its ids, with the same outputs as the
  * two calls (all five written).  Small batches run both steps in one launch
  * (the routed ids pass through on-chip memory); larger ones run the two

@@ -189,6 +189,18 @@ def test_mxfp8_entry_points_reject(L):
         L.moe_forward_workspace_bytes(64, 32, 4, 2880, 2880)
 
 
+def test_align_large_rejects(L):
+    f = lambda **kw: L.moe_align_large(kw.get("ids", FAKE), kw.get("T", 64), 4, kw.get("E", 32),
+                                       kw.get("B", 64), FAKE, FAKE, FAKE, kw.get("c", FAKE), None)
+    assert f(c=None) == NULL
+    assert f(ids=None) == NULL
+    assert f(E=0) == SHAPE
+    assert f(B=48) == SHAPE
+    assert f(T=0, c=None) == 0                           # empty batch: nothing to do
+    assert L.moe_align_large_scratch_bytes(32) == 16 * 32 * 4
+    assert L.moe_align_large_scratch_bytes(0) == 0
+
+
 def test_codes_by_chunk_rejects(L):
     f = lambda **kw: L.moe_nvfp4_codes_by_chunk(kw.get("q", FAKE), kw.get("E", 4), 256,
                                                 kw.get("K", 2880), kw.get("o", FAKE * 2), None)

@@ -106,15 +106,37 @@ def test_align_bitexact(T, k, E, B):
     assert int(got[2].item()) == int(ref[2])
 
 
+@pytest.mark.parametrize("T,k,E,B", [(1, 4, 32, 16), (13, 2, 8, 16), (511, 6, 128, 32),
+                                      (4096, 4, 32, 128), (8192, 4, 128, 64), (3, 3, 1024, 16),
+                                      (3001, 7, 1000, 32), (2000, 1, 1, 16), (700, 8, 2, 64),
+                                      (16383, 4, 64, 128)])
+def test_align_large_bitexact(T, k, E, B):
+    """The 16-workgroup sort: the same outputs as the oracle (and so as the
+    single workgroup), ragged ranges and runs included; counts start dirty."""
+    rng = np.random.default_rng(T + E + B + 1)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if T > 3:
+        ids[2, 0] = E + 7
+        ids[3, k - 1] = -2
+    ref = O.align(ids, E, B)
+    counts = torch.full((16 * E,), 12345, dtype=torch.int32, device="cuda")
+    got = M.moe_align_large(torch.from_numpy(ids).cuda(), E, B, counts=counts)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got[0].cpu().numpy(), ref[0])
+    np.testing.assert_array_equal(got[1].cpu().numpy(), ref[1])
+    assert int(got[2].item()) == int(ref[2])
+
+
 def test_align_skewed_routing_full_size():
     logits, _ = S.make_router_inputs(4)          # E=128, T=8192, per-expert offsets
     ids_ref, _ = O.route(logits, 4, "softmax", None, True)
     for B in (16, 64, 128):
         ref = O.align(ids_ref, 128, B)
-        got = M.moe_align(torch.from_numpy(ids_ref).cuda(), 128, B)
-        np.testing.assert_array_equal(got[0].cpu().numpy(), ref[0])
-        np.testing.assert_array_equal(got[1].cpu().numpy(), ref[1])
-        assert int(got[2].item()) == int(ref[2])
+        for sort in (M.moe_align, M.moe_align_large):
+            got = sort(torch.from_numpy(ids_ref).cuda(), 128, B)
+            np.testing.assert_array_equal(got[0].cpu().numpy(), ref[0])
+            np.testing.assert_array_equal(got[1].cpu().numpy(), ref[1])
+            assert int(got[2].item()) == int(ref[2])
 
 
 # -------------------------------------------------------------------- GEMMs --
