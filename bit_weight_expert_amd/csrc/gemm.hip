@@ -1040,6 +1040,17 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
 #pragma unroll
     for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
 
+    if (SK != 0 && n0 >= N) {
+      // every weight row of this wave lies past N (the last column tile):
+      // only its share of the copies, which leaves its SIMD to the other
+      // workgroup on the CU
+      for (int kc = 0; kc < nchunks; ++kc) {
+        wait_vmcnt<(kStages - 2) * P::kIssue>();
+        pf_barrier();
+        pf_issue<FMT, BM, NF, SK>(ring + (kc % kStages) * P::kStage, arow, brow, skc,
+                                  min(kc + kStages, nchunks - 1), wave_u, N);
+      }
+    } else
     for (int kc = 0; kc < nchunks; ++kc) {
       const uint8_t* st = smem + (kc % kStages) * P::kStage + aoff;
       // steps 0..2: each overlaps the next step's A reads and dequant
