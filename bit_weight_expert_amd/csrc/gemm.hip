@@ -703,10 +703,11 @@ __device__ __forceinline__ void pf_mfma(f32x16 (&acc)[MI][NF], const uint4 (&a)[
 }
 
 // One MFMA step (as pf_mfma) with one wave's DMA of chunk kc dealt between
-// its rows: issued back to back, a wave's 5..7 DMA instructions wait on the
-// CU's memory pipeline and hold up the MFMAs behind them; between rows the
-// pipeline drains while the matrix core works.  The A fragments serve as the
-// pins, so `a` reads as modified afterwards (callers reload it).
+// its rows.  Issued back to back, a wave's 5..7 DMA instructions sit in
+// front of the MFMAs that follow them in the wave's in-order issue; dealt
+// between rows they overlap the matrix core's work (measured ~5% faster on
+// both GEMMs).  The A fragments serve as the pins, so `a` reads as modified
+// afterwards (callers reload it).
 template <int FMT, int BM, int NF, int SK, int MI>
 __device__ __forceinline__ void pf_mfma_issue(f32x16 (&acc)[MI][NF], uint4 (&a)[MI], const bf16x8 (&b)[NF],
                                               uint32_t stage_lds,
