@@ -183,8 +183,11 @@ def mxfp8_leg(args, time_calls):
     dev = torch.device("cuda")
     copies = []
     for _ in range(max(1, min(args.copies, 3))):   # 3 x 2.4 GB: each call misses the 256 MB cache
-        copies.append(tuple(M.QuantWeights.from_arrays(w.fmt, w.group, w.N, w.K, w.qweight, w.scales,
-                                                       None, None, w.bias) for w in (L.w13, L.w2)))
+        pair = tuple(M.QuantWeights.from_arrays(w.fmt, w.group, w.N, w.K, w.qweight, w.scales,
+                                                None, None, w.bias) for w in (L.w13, L.w2))
+        for w in pair:   # the MX kernels' copy of the codes by 128-deep K chunk (load time)
+            w.qweight_kc = M.moe_mxfp4_codes_by_chunk(w)
+        copies.append(pair)
     x = torch.from_numpy(L.x.view(np.int16)).to(dev).view(torch.bfloat16)
     logits = torch.from_numpy(L.logits).to(dev)
     tmax = max(ts)

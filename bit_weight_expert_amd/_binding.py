@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_scales_by_chunk.restype = i
         L.moe_nvfp4_codes_by_chunk.argtypes = [vp, i, i, i, vp, vp]
         L.moe_nvfp4_codes_by_chunk.restype = i
+        L.moe_mxfp4_codes_by_chunk.argtypes = [vp, i, i, i, vp, vp]
+        L.moe_mxfp4_codes_by_chunk.restype = i
         L.moe_align_large.argtypes = [vp, i, i, i, i, vp, vp, vp, vp, vp]
         L.moe_align_large.restype = i
         L.moe_align_large_scratch_bytes.argtypes = [i]
@@ -149,7 +151,8 @@ class QuantWeights:
     bias: torch.Tensor | None = None
     k_perm: torch.Tensor | None = None     # GPTQ act-order, from moe_gptq_act_order_sort
     scales_kc: torch.Tensor | None = None  # NVFP4 scales by K chunk, from moe_nvfp4_scales_by_chunk
-    qweight_kc: torch.Tensor | None = None  # NVFP4 codes by K chunk (with scales_kc), moe_nvfp4_codes_by_chunk
+    qweight_kc: torch.Tensor | None = None  # codes by K chunk: moe_nvfp4_codes_by_chunk (with scales_kc)
+    #                                          or moe_mxfp4_codes_by_chunk (MX kernels)
 
     @classmethod
     def from_arrays(cls, fmt, group, N, K, qweight, scales, zeros=None, global_scale=None,
@@ -353,6 +356,19 @@ def moe_nvfp4_codes_by_chunk(w: "QuantWeights") -> torch.Tensor:
     out = torch.empty((E, w.K // 64, w.N, 32), dtype=torch.uint8, device=w.qweight.device)
     _check(lib().moe_nvfp4_codes_by_chunk(_ptr(w.qweight), E, w.N, w.K, _ptr(out), _stream()),
            "moe_nvfp4_codes_by_chunk")
+    return out
+
+
+def moe_mxfp4_codes_by_chunk(w: "QuantWeights") -> torch.Tensor:
+    """MXFP4 codes [E, N, K/2] re-laid by 128-deep K chunk -> uint8 [E, ceil(K/128), N, 64],
+    zero past K (set it as w.qweight_kc for the MXFP8-activation kernels)."""
+    if w.fmt != "mxfp4":
+        raise ValueError("this re-layout is for MXFP4 codes")
+    _dev(w.qweight, torch.uint8, "qweight")
+    E = w.qweight.shape[0]
+    out = torch.empty((E, (w.K + 127) // 128, w.N, 64), dtype=torch.uint8, device=w.qweight.device)
+    _check(lib().moe_mxfp4_codes_by_chunk(_ptr(w.qweight), E, w.N, w.K, _ptr(out), _stream()),
+           "moe_mxfp4_codes_by_chunk")
     return out
 
 

@@ -35,6 +35,8 @@ extern "C" hipError_t moe_launch_nvfp4_scales_by_chunk(const uint8_t*, int, int,
                                                        hipStream_t);
 extern "C" hipError_t moe_launch_nvfp4_codes_by_chunk(const uint8_t*, int, int, int, uint8_t*,
                                                        hipStream_t);
+extern "C" hipError_t moe_launch_mxfp4_codes_by_chunk(const uint8_t*, int, int, int, uint8_t*,
+                                                      hipStream_t);
 extern "C" hipError_t moe_launch_permute_slots(const uint16_t*, int, int, int, int, const int32_t*,
                                                const int32_t*, uint16_t*, hipStream_t);
 
@@ -88,7 +90,9 @@ moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out
     if (!aligned16(w->scales_kc)) return MOE_ERR_ALIGN;
   }
   if (w->qweight_kc != nullptr) {
-    if (w->scales_kc == nullptr) return MOE_ERR_UNSUPPORTED;  // NVFP4 and K % 64 checked above
+    // NVFP4: with scales_kc (format and K % 64 checked above); MXFP4: alone
+    if (w->fmt == MOE_W_NVFP4 ? w->scales_kc == nullptr : w->fmt != MOE_W_MXFP4)
+      return MOE_ERR_UNSUPPORTED;
     if (!aligned16(w->qweight_kc)) return MOE_ERR_ALIGN;
   }
   if (!aligned16(w->qweight) || !aligned16(w->scales)) return MOE_ERR_ALIGN;
@@ -375,6 +379,16 @@ moe_status_t moe_nvfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int 
   if (!aligned16(qweight) || !aligned16(out)) return MOE_ERR_ALIGN;
   if (out == qweight) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe_launch_nvfp4_codes_by_chunk(qweight, E, N, K, out,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_mxfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int K, uint8_t* out,
+                                      moe_stream_t stream) {
+  if (E <= 0 || E > kMaxE || N <= 0 || K <= 0 || K % 32 != 0) return MOE_ERR_SHAPE;
+  if (qweight == nullptr || out == nullptr) return MOE_ERR_NULL;
+  if (!aligned16(qweight) || !aligned16(out)) return MOE_ERR_ALIGN;
+  if (out == qweight) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe_launch_mxfp4_codes_by_chunk(qweight, E, N, K, out,
                                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -46,6 +46,24 @@ __global__ __launch_bounds__(256) void nvfp4_codes_by_chunk_kernel(const uint4* 
   dst[1] = src[1];
 }
 
+
+// MXFP4 codes by 128-deep K chunk for the MX kernel: [E][ceil(K/128)][N][64];
+// the part of the last chunk past K (K % 128 == 64) is zero.  One thread per
+// (expert, chunk, row): four 16-byte units.
+__global__ __launch_bounds__(256) void mxfp4_codes_by_chunk_kernel(const uint4* __restrict__ in,
+                                                                   int N, int K, int KC,
+                                                                   uint4* __restrict__ out) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.y;
+  const int e = blockIdx.z;
+  if (n >= N) return;
+  const int units = K / 32;  // 16-byte units per row
+  const uint4* src = in + ((size_t)e * N + n) * units;
+  uint4* dst = out + (((size_t)e * KC + c) * N + n) * 4;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) dst[u] = 4 * c + u < units ? src[4 * c + u] : make_uint4(0, 0, 0, 0);
+}
+
 }  // namespace
 
 extern "C" hipError_t moe_launch_nvfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int K,
@@ -62,5 +80,13 @@ extern "C" hipError_t moe_launch_nvfp4_codes_by_chunk(const uint8_t* qweight, in
   const int kc = K / 64;
   hipLaunchKernelGGL(nvfp4_codes_by_chunk_kernel, dim3((N + 255) / 256, kc, E), dim3(256), 0, st,
                      reinterpret_cast<const uint4*>(qweight), N, kc, reinterpret_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_mxfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int K,
+                                                      uint8_t* out, hipStream_t st) {
+  const int kc = (K + 127) / 128;
+  hipLaunchKernelGGL(mxfp4_codes_by_chunk_kernel, dim3((N + 255) / 256, kc, E), dim3(256), 0, st,
+                     reinterpret_cast<const uint4*>(qweight), N, K, kc, reinterpret_cast<uint4*>(out));
   return hipGetLastError();
 }

@@ -117,7 +117,9 @@ typedef struct {
                                  scales_kc the 64/128-row GEMM kernel streams each chunk's scales
                                  with its codes instead of holding the tile's scales for the whole
                                  K in on-chip memory, which lets two workgroups share a CU. */
-  const uint8_t* qweight_kc;  /* NVFP4 only, optional, and only together with scales_kc: the same
+  const uint8_t* qweight_kc;  /* MXFP4, optional: the codes by 128-deep K chunk from
+                                 moe_mxfp4_codes_by_chunk, read only by the MXFP8-activation (MX)
+                                 kernels.  NVFP4, optional, and only together with scales_kc: the same
                                  codes laid out by 64-deep K chunk, uint8 [E][K/64][N][32]
                                  (moe_nvfp4_codes_by_chunk), 16-byte aligned.  `qweight` stays
                                  required (the 1..64-token kernels read it); with qweight_kc the
@@ -252,6 +254,16 @@ moe_status_t moe_nvfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int 
  * K % 64 == 0; both 16-byte aligned.  Costs a second copy of the codes: the
  * 1..64-token kernels keep reading qweight. */
 moe_status_t moe_nvfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int K, uint8_t* out,
+                                      moe_stream_t stream);
+
+/* MXFP4 codes re-laid by 128-deep K chunk for the MX kernels, run once when
+ * the weights are loaded:
+ *   out[e][c][n][j] = qweight[e][n][64c + j] for 64c + j < K/2, else 0
+ *   (c < ceil(K/128), j < 64)
+ * qweight uint8 [E][N][K/2]; out uint8 [E][ceil(K/128)][N][64], a separate
+ * buffer; K % 32 == 0; both 16-byte aligned.  A second copy of the codes (the
+ * bf16-activation kernels keep reading qweight). */
+moe_status_t moe_mxfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int K, uint8_t* out,
                                       moe_stream_t stream);
 
 /* Gather of GEMM input rows through an act-order permutation, one row per

@@ -96,8 +96,8 @@ def test_gemm1_rejects(L):
     assert _g1(L, _wq(fmt=1, group=32, scales_kc=FAKE)) == UNSUP   # scales by chunk: NVFP4 only
     assert _g1(L, _wq(scales_kc=FAKE), K=2880 + 32) == SHAPE       # needs K % 64 == 0
     assert _g1(L, _wq(scales_kc=FAKE + 4)) == ALIGN
-    assert _g1(L, _wq(qweight_kc=FAKE)) == UNSUP         # codes by chunk need scales by chunk
-    assert _g1(L, _wq(fmt=1, group=32, qweight_kc=FAKE)) == UNSUP
+    assert _g1(L, _wq(qweight_kc=FAKE)) == UNSUP         # NVFP4 codes by chunk need scales by chunk
+    assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, qweight_kc=FAKE)) == UNSUP   # no GPTQ form
     assert _g1(L, _wq(scales_kc=FAKE, qweight_kc=FAKE), K=2880 + 32) == SHAPE
     assert _g1(L, _wq(scales_kc=FAKE, qweight_kc=FAKE + 4)) == ALIGN
     assert _g1(L, _wq(fmt=2, group=64)) == NULL          # zeros missing
@@ -199,6 +199,16 @@ def test_align_large_rejects(L):
     assert f(T=0, c=None) == 0                           # empty batch: nothing to do
     assert L.moe_align_large_scratch_bytes(32) == 16 * 32 * 4
     assert L.moe_align_large_scratch_bytes(0) == 0
+
+
+def test_mxfp4_codes_by_chunk_rejects(L):
+    f = lambda **kw: L.moe_mxfp4_codes_by_chunk(kw.get("q", FAKE), kw.get("E", 4), 256,
+                                                kw.get("K", 2880), kw.get("o", FAKE * 2), None)
+    assert f(K=2880 + 16) == SHAPE
+    assert f(E=0) == SHAPE
+    assert f(q=None) == NULL
+    assert f(o=FAKE) == UNSUP
+    assert f(o=FAKE * 2 + 4) == ALIGN
 
 
 def test_codes_by_chunk_rejects(L):

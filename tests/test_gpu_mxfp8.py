@@ -260,3 +260,64 @@ def test_forward_mxfp8_empty_batch():
     D = upload(L)
     out = M.moe_forward_mxfp8(D["x"][:0], D["logits"][:0], L.top_k, L.I, D["w13"], D["w2"])
     assert out.shape == (0, L.H)
+
+
+# ------------------------------------------------- MXFP4 codes by K chunk --
+
+@pytest.mark.parametrize("E,N,K", [(3, 384, 320), (2, 2880, 2880), (5, 16, 352), (2, 48, 128)])
+def test_mxfp4_codes_by_chunk_bitexact(E, N, K):
+    w = S.make_weights("mxfp4", E=E, N=N, K=K, bias=False, seed=N + K + 3)
+    Dw = M.QuantWeights.from_arrays(w.fmt, w.group, w.N, w.K, w.qweight, w.scales, None, None, None)
+    got = M.moe_mxfp4_codes_by_chunk(Dw).cpu().numpy()
+    kc = (K + 127) // 128
+    padded = np.zeros((E, N, kc * 64), np.uint8)
+    padded[:, :, : K // 2] = w.qweight
+    np.testing.assert_array_equal(got, padded.reshape(E, N, kc, 64).transpose(0, 2, 1, 3))
+
+
+@pytest.mark.parametrize("K", [320, 352, 2880])
+@pytest.mark.parametrize("B", [64, 128])
+def test_mx_gemms_codes_by_chunk(K, B):
+    """The MX kernels reading the chunked copy: bit for bit what they give on
+    the checkpoint codes (only the copy source differs), and the oracle's
+    values; K % 128 = 64 and 96 cover a partial last chunk."""
+    L = _layer(H=K, I=K, T=300 if K < 2880 else 150)
+    D = upload(L)
+    w13c = dataclasses.replace(D["w13"], qweight_kc=M.moe_mxfp4_codes_by_chunk(D["w13"]))
+    w2c = dataclasses.replace(D["w2"], qweight_kc=M.moe_mxfp4_codes_by_chunk(D["w2"]))
+    ids, w = O.route(L)
+    si, ei, npp = O.align(ids, L.E, B)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    xc, xs = F.quantize_mxfp8(F.bf16_to_f64(L.x))
+    dc, ds = _up_mx(xc, xs, K)
+    print(f"mx gemms codes by chunk K={K} B={B}", flush=True)
+    args = (L.act, L.alpha, L.beta, L.limit, t(si), t(ei), t(np.array([npp], np.int32)), B)
+    o1 = M.moe_mx_gemm1(dc, ds, L.top_k, K, D["w13"], *args)
+    o1c = M.moe_mx_gemm1(dc, ds, L.top_k, K, w13c, *args)
+    assert torch.equal(o1.view(torch.int16), o1c.view(torch.int16))
+    ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, L.act, L.alpha, L.beta, L.limit, si, ei, npp, B,
+                       act_fmt="mxfp8")
+    assert_rows_close(host_bf16(o1c), ref, rows=cov, what=f"mx gemm1 codes by chunk K{K} B{B}")
+    n = L.T * L.top_k
+    rng = np.random.default_rng(K + B)
+    a = F.bf16_round(rng.standard_normal((n, K)))
+    ac, as_ = F.quantize_mxfp8(a)
+    dc2, ds2 = _up_mx(ac, as_, K)
+    args2 = (t(w.reshape(-1).astype(np.float32)), True, t(si), t(ei), t(np.array([npp], np.int32)), B)
+    y = M.moe_mx_gemm2(dc2, ds2, K, D["w2"], *args2)
+    yc = M.moe_mx_gemm2(dc2, ds2, K, w2c, *args2)
+    assert torch.equal(y.view(torch.int16), yc.view(torch.int16))
+    ref2, cov2 = O.gemm2(a, n, L.w2, w.reshape(-1), True, si, ei, npp, B, act_fmt="mxfp8")
+    assert_rows_close(host_bf16(yc), ref2, rows=cov2, what=f"mx gemm2 codes by chunk K{K} B{B}")
+
+
+def test_forward_mxfp8_codes_by_chunk_full_size():
+    """gpt-oss-120b shape, T = 8192: the chunked copies change no output bit."""
+    L = dataclasses.replace(S.make_config(4, 8192), act_fmt="mxfp8")
+    D = upload(L)
+    out = gpu_forward_mx(L, D)
+    D["w13"] = dataclasses.replace(D["w13"], qweight_kc=M.moe_mxfp4_codes_by_chunk(D["w13"]))
+    D["w2"] = dataclasses.replace(D["w2"], qweight_kc=M.moe_mxfp4_codes_by_chunk(D["w2"]))
+    print("forward mxfp8 codes by chunk full size", flush=True)
+    outc = gpu_forward_mx(L, D)
+    assert torch.equal(out.view(torch.int16), outc.view(torch.int16))
