@@ -2190,6 +2190,15 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA m
   int sa[MI], sb[NF];
   mx_scales<MI, NF>(sa, sb, sca, ma.lds, scb, kb, rl, c, g, 0, r0);
   mx_read<MI, NF, 0>(o0, smem, P::kABytes, bpos, c, g, r0);
+  if (n0 >= N) {
+    // every weight row of this wave lies past N (the last column tile): only
+    // its share of the copies, which leaves its SIMD to the other waves
+    for (int kc = 0; kc < nchunks; ++kc) {
+      wait_vmcnt<P::kIssue>();
+      pf_barrier();
+      issue(ring + (kc % kMxStages) * P::kStage, min(kc + kMxStages, nchunks - 1));
+    }
+  } else
   for (int kc = 0; kc < nchunks; ++kc) {
     const uint8_t* stg = smem + (kc % kMxStages) * P::kStage;
     mx_read<MI, NF, 1>(o1, stg, P::kABytes, bpos, c, g, r0);
