@@ -15,6 +15,7 @@ _LIB_NAME = "libmoe_w4a16.so"
 FMT = {"nvfp4": 0, "mxfp4": 1, "gptq": 2}
 ACT = {"swigluoai": 0, "relu2": 1, "none": 2}
 ROUTE = {"softmax": 0, "sigmoid_bias": 1}
+KERNEL = {"auto": 0, "splitk": 1, "wide": 2}   # kernel for blocks of 16/32 rows
 
 
 class MoeError(RuntimeError):
@@ -62,8 +63,6 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_workspace_bytes.restype = sz
         L.moe_forward_block_m.argtypes = [i, i, i]
         L.moe_forward_block_m.restype = i
-        L.moe_set_decode_policy.argtypes = [i]
-        L.moe_set_decode_policy.restype = i
         L.moe_status_str.argtypes = [i]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_route.argtypes = [vp, i, i, i, i, vp, i, vp, vp, vp]
@@ -74,11 +73,17 @@ def lib() -> ctypes.CDLL:
         L.moe_route_align.restype = i
         L.moe_w4a16_gemm1.argtypes = [vp, i, i, i, i, i, wq, i, f, f, f, vp, i, vp, vp, vp, i, vp, vp]
         L.moe_w4a16_gemm1.restype = i
-        L.moe_w4a16_gemm2.argtypes = [vp, i, i, i, i, wq, vp, i, vp, vp, vp, i, vp, vp]
+        L.moe_w4a16_gemm1_ex.argtypes = L.moe_w4a16_gemm1.argtypes[:-1] + [i, vp]
+        L.moe_w4a16_gemm1_ex.restype = i
+        L.moe_w4a16_gemm2.argtypes = [vp, i, i, i, i, i, wq, vp, i, vp, vp, vp, i, vp, vp]
         L.moe_w4a16_gemm2.restype = i
+        L.moe_w4a16_gemm2_ex.argtypes = L.moe_w4a16_gemm2.argtypes[:-1] + [i, vp]
+        L.moe_w4a16_gemm2_ex.restype = i
         L.moe_forward.argtypes = [vp, vp, i, i, i, i, i, i, vp, i, wq, wq, i, f, f, f, i, vp, sz,
                                   vp, vp]
         L.moe_forward.restype = i
+        L.moe_forward_ex.argtypes = L.moe_forward.argtypes[:-1] + [i, vp]
+        L.moe_forward_ex.restype = i
         L.moe_gptq_act_order_sort.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, vp]
         L.moe_gptq_act_order_sort.restype = i
         L.moe_permute_slots.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
@@ -153,6 +158,7 @@ class QuantWeights:
     scales_kc: torch.Tensor | None = None  # NVFP4 scales by K chunk, from moe_nvfp4_scales_by_chunk
     qweight_kc: torch.Tensor | None = None  # codes by K chunk: moe_nvfp4_codes_by_chunk (with scales_kc)
     #                                          or moe_mxfp4_codes_by_chunk (MX kernels)
+    g_idx: torch.Tensor | None = None      # GPTQ group map int32 [E, K] (identity only, checked on device)
 
     @classmethod
     def from_arrays(cls, fmt, group, N, K, qweight, scales, zeros=None, global_scale=None,
@@ -170,19 +176,12 @@ class QuantWeights:
 
     def struct(self) -> _Wq:
         return _Wq(FMT[self.fmt], self.group, _ptr(self.qweight), _ptr(self.scales),
-                   _ptr(self.zeros), _ptr(self.global_scale), None, _ptr(self.bias),
+                   _ptr(self.zeros), _ptr(self.global_scale), _ptr(self.g_idx), _ptr(self.bias),
                    _ptr(self.k_perm), _ptr(self.scales_kc), _ptr(self.qweight_kc))
 
     @property
     def E(self) -> int:
         return self.qweight.shape[0]
-
-
-def moe_set_decode_policy(policy: str) -> str:
-    """'auto', 'splitk' or 'wide' kernel for 16/32-row blocks; returns the previous policy."""
-    names = ["auto", "splitk", "wide"]
-    old = lib().moe_set_decode_policy(names.index(policy))
-    return names[old]
 
 
 def moe_align_capacity(T: int, top_k: int, E: int, block_m: int) -> int:
@@ -275,11 +274,12 @@ def moe_route_align(logits: torch.Tensor, top_k: int, block_m: int, kind: str = 
 
 def moe_w4a16_gemm1(x: torch.Tensor, top_k: int, w13: QuantWeights, act: str, alpha: float,
                     beta: float, limit: float, sorted_ids, expert_ids, num_post_pad,
-                    block_m: int, out=None, topk_w=None):
+                    block_m: int, out=None, topk_w=None, kernel: str = "auto"):
     """x bf16 [size_m, K] -> out bf16 [size_m*top_k, N/2 (gated) or N].
 
     topk_w (fp32 [size_m*top_k]) given: each input row is scaled by its slot's
-    routing weight (the weight applied on the input)."""
+    routing weight (the weight applied on the input).  kernel: "auto", "splitk"
+    or "wide" for 16/32-row blocks (moe_w4a16_gemm1_ex)."""
     _dev(x, torch.bfloat16, "x")
     if topk_w is not None:
         _dev(topk_w, torch.float32, "topk_w")
@@ -288,26 +288,29 @@ def moe_w4a16_gemm1(x: torch.Tensor, top_k: int, w13: QuantWeights, act: str, al
     if out is None:
         out = torch.zeros((size_m * top_k, n_out), dtype=torch.bfloat16, device=x.device)
     s = w13.struct()
-    _check(lib().moe_w4a16_gemm1(_ptr(x), size_m, top_k, K, w13.N, w13.E, ctypes.byref(s),
-                                 ACT[act], alpha, beta, limit, _ptr(topk_w), int(topk_w is not None),
-                                 _ptr(sorted_ids), _ptr(expert_ids), _ptr(num_post_pad), block_m,
-                                 _ptr(out), _stream()),
-           "moe_w4a16_gemm1")
+    _check(lib().moe_w4a16_gemm1_ex(_ptr(x), size_m, top_k, K, w13.N, w13.E, ctypes.byref(s),
+                                    ACT[act], alpha, beta, limit, _ptr(topk_w),
+                                    int(topk_w is not None), _ptr(sorted_ids), _ptr(expert_ids),
+                                    _ptr(num_post_pad), block_m, _ptr(out), KERNEL[kernel],
+                                    _stream()),
+           "moe_w4a16_gemm1_ex")
     return out
 
 
 def moe_w4a16_gemm2(a: torch.Tensor, w2: QuantWeights, topk_w, mul_topk_weights: bool,
-                    sorted_ids, expert_ids, num_post_pad, block_m: int, out=None):
-    """a bf16 [size_m, K] (one row per flat slot) -> y bf16 [size_m, N]."""
+                    sorted_ids, expert_ids, num_post_pad, block_m: int, out=None,
+                    top_k: int = 1, kernel: str = "auto"):
+    """a bf16 [size_m, K] -> y bf16 [size_m*top_k, N]; row f reads A row f // top_k
+    (top_k = 1: one A row per flat slot, the layer's view)."""
     _dev(a, torch.bfloat16, "a")
     size_m, K = a.shape
     if out is None:
-        out = torch.zeros((size_m, w2.N), dtype=torch.bfloat16, device=a.device)
+        out = torch.zeros((size_m * top_k, w2.N), dtype=torch.bfloat16, device=a.device)
     s = w2.struct()
-    _check(lib().moe_w4a16_gemm2(_ptr(a), size_m, K, w2.N, w2.E, ctypes.byref(s),
-                                 _ptr(topk_w), int(bool(mul_topk_weights)), _ptr(sorted_ids),
-                                 _ptr(expert_ids), _ptr(num_post_pad), block_m, _ptr(out),
-                                 _stream()), "moe_w4a16_gemm2")
+    _check(lib().moe_w4a16_gemm2_ex(_ptr(a), size_m, top_k, K, w2.N, w2.E, ctypes.byref(s),
+                                    _ptr(topk_w), int(bool(mul_topk_weights)), _ptr(sorted_ids),
+                                    _ptr(expert_ids), _ptr(num_post_pad), block_m, _ptr(out),
+                                    KERNEL[kernel], _stream()), "moe_w4a16_gemm2_ex")
     return out
 
 
@@ -481,11 +484,12 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, top_k: int, inter: int,
                 route: str = "softmax", expert_bias=None, renormalize: bool = True,
                 alpha: float = 1.702, beta: float = 1.0, limit: float = 7.0,
                 mul_topk_weights: bool = True, workspace=None, out=None,
-                weight_on_input: bool = False):
+                weight_on_input: bool = False, kernel: str = "auto"):
     """The whole layer: x bf16 [T, hidden], logits f32 [T, E] -> out bf16 [T, hidden].
 
     weight_on_input: the routing weight scales GEMM1's input rows instead of
-    GEMM2's output rows (top_k must be 1)."""
+    GEMM2's output rows (top_k must be 1).  kernel: the kernel for 16/32-row
+    blocks, "auto", "splitk" or "wide" (moe_forward_ex)."""
     _dev(x, torch.bfloat16, "x")
     _dev(logits, torch.float32, "logits")
     T, hidden = x.shape
@@ -496,10 +500,11 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, top_k: int, inter: int,
     if out is None:
         out = torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
     s13, s2 = w13.struct(), w2.struct()
-    _check(lib().moe_forward(_ptr(x), _ptr(logits), T, E, top_k, hidden, inter, ROUTE[route],
-                             _ptr(expert_bias), int(bool(renormalize)), ctypes.byref(s13),
-                             ctypes.byref(s2), ACT[act], alpha, beta, limit,
-                             2 if weight_on_input else int(bool(mul_topk_weights)), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _ptr(out), _stream()),
-           "moe_forward")
+    _check(lib().moe_forward_ex(_ptr(x), _ptr(logits), T, E, top_k, hidden, inter, ROUTE[route],
+                                _ptr(expert_bias), int(bool(renormalize)), ctypes.byref(s13),
+                                ctypes.byref(s2), ACT[act], alpha, beta, limit,
+                                2 if weight_on_input else int(bool(mul_topk_weights)),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _ptr(out), KERNEL[kernel], _stream()),
+           "moe_forward_ex")
     return out

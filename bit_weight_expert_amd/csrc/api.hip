@@ -20,7 +20,7 @@ extern "C" hipError_t moe_launch_route_align(const float*, int, int, int, int, c
 extern "C" hipError_t moe_launch_gemm(int, int, int, int, const uint16_t*, int, int, int, int, int,
                                       const moe::WeightArgs*, const int32_t*, const int32_t*,
                                       const int32_t*, const float*, int, float, float, float,
-                                      uint16_t*, int, hipStream_t);
+                                      uint16_t*, int, int, hipStream_t);
 extern "C" hipError_t moe_launch_sum(const uint16_t*, const int32_t*, int, int, int, int,
                                      uint16_t*, hipStream_t);
 extern "C" hipError_t moe_launch_gptq_sort(const int32_t*, const int32_t*, int, int, int, int,
@@ -73,17 +73,21 @@ moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out
         return MOE_ERR_UNSUPPORTED;
       if (K % w->group_size != 0) return MOE_ERR_SHAPE;
       if (w->zeros == nullptr) return MOE_ERR_NULL;
-      if (w->g_idx != nullptr) return MOE_ERR_UNSUPPORTED;
       if (w->k_perm != nullptr) {
         if (!allow_perm) return MOE_ERR_UNSUPPORTED;
+        // group-sorted weights: their rows are already in group order
+        if (w->g_idx != nullptr) return MOE_ERR_UNSUPPORTED;
         if (K > kMaxPermK) return MOE_ERR_SHAPE;
         if (!aligned16(w->k_perm)) return MOE_ERR_ALIGN;
       }
+      // a group map is checked on the device against the identity
+      if (w->g_idx != nullptr && (reinterpret_cast<uintptr_t>(w->g_idx) & 3u)) return MOE_ERR_ALIGN;
       break;
     default:
       return MOE_ERR_UNSUPPORTED;
   }
-  if (w->fmt != MOE_W_INT4_GPTQ && w->k_perm != nullptr) return MOE_ERR_UNSUPPORTED;
+  if (w->fmt != MOE_W_INT4_GPTQ && (w->k_perm != nullptr || w->g_idx != nullptr))
+    return MOE_ERR_UNSUPPORTED;
   if (w->scales_kc != nullptr) {
     if (w->fmt != MOE_W_NVFP4) return MOE_ERR_UNSUPPORTED;
     if (K % 64 != 0) return MOE_ERR_SHAPE;
@@ -105,8 +109,13 @@ moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out
   out->bias = w->bias;
   out->scales_kc = w->scales_kc;
   out->qweight_kc = w->qweight_kc;
+  out->g_idx = w->g_idx;
   out->group = w->group_size;
   return MOE_OK;
+}
+
+bool valid_kernel(moe_kernel_t k) {
+  return k == MOE_KERNEL_AUTO || k == MOE_KERNEL_SPLITK || k == MOE_KERNEL_WIDE;
 }
 
 int epi_of(moe_act_t act) {
@@ -297,16 +306,16 @@ static moe_status_t gemm_common_checks(int size_m, int top_k, int E, int block_m
   return MOE_OK;
 }
 
-moe_status_t moe_w4a16_gemm1(const uint16_t* x, int size_m, int top_k, int K, int N, int E,
-                             const moe_wq_t* w13, moe_act_t act, float alpha, float beta,
-                             float limit, const float* topk_w, int mul_topk_weights,
-                             const int32_t* sorted_ids, const int32_t* expert_ids,
-                             const int32_t* num_post_pad, int block_m, uint16_t* out,
-                             moe_stream_t stream) {
+moe_status_t moe_w4a16_gemm1_ex(const uint16_t* x, int size_m, int top_k, int K, int N, int E,
+                                const moe_wq_t* w13, moe_act_t act, float alpha, float beta,
+                                float limit, const float* topk_w, int mul_topk_weights,
+                                const int32_t* sorted_ids, const int32_t* expert_ids,
+                                const int32_t* num_post_pad, int block_m, uint16_t* out,
+                                moe_kernel_t kernel, moe_stream_t stream) {
   moe_status_t st = gemm_common_checks(size_m, top_k, E, block_m);
   if (st != MOE_OK) return st;
   const int epi = epi_of(act);
-  if (epi < 0) return MOE_ERR_UNSUPPORTED;
+  if (epi < 0 || !valid_kernel(kernel)) return MOE_ERR_UNSUPPORTED;
   moe::WeightArgs W;
   st = check_weights(w13, N, K, &W);
   if (st != MOE_OK) return st;
@@ -322,16 +331,28 @@ moe_status_t moe_w4a16_gemm1(const uint16_t* x, int size_m, int top_k, int K, in
   return hip_status(moe_launch_gemm((int)w13->fmt, epi, block_m, cap, x, top_k, size_m * top_k, K, N, E,
                                     &W, sorted_ids, expert_ids, num_post_pad, topk_w,
                                     mul_topk_weights ? 1 : 0, alpha, beta, limit, out, out_ld,
-                                    static_cast<hipStream_t>(stream)));
+                                    (int)kernel, static_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_w4a16_gemm2(const uint16_t* a, int size_m, int K, int N, int E,
-                             const moe_wq_t* w2, const float* topk_w, int mul_topk_weights,
+moe_status_t moe_w4a16_gemm1(const uint16_t* x, int size_m, int top_k, int K, int N, int E,
+                             const moe_wq_t* w13, moe_act_t act, float alpha, float beta,
+                             float limit, const float* topk_w, int mul_topk_weights,
                              const int32_t* sorted_ids, const int32_t* expert_ids,
-                             const int32_t* num_post_pad, int block_m, uint16_t* y,
+                             const int32_t* num_post_pad, int block_m, uint16_t* out,
                              moe_stream_t stream) {
-  moe_status_t st = gemm_common_checks(size_m, 1, E, block_m);
+  return moe_w4a16_gemm1_ex(x, size_m, top_k, K, N, E, w13, act, alpha, beta, limit, topk_w,
+                            mul_topk_weights, sorted_ids, expert_ids, num_post_pad, block_m, out,
+                            MOE_KERNEL_AUTO, stream);
+}
+
+moe_status_t moe_w4a16_gemm2_ex(const uint16_t* a, int size_m, int top_k, int K, int N, int E,
+                                const moe_wq_t* w2, const float* topk_w, int mul_topk_weights,
+                                const int32_t* sorted_ids, const int32_t* expert_ids,
+                                const int32_t* num_post_pad, int block_m, uint16_t* y,
+                                moe_kernel_t kernel, moe_stream_t stream) {
+  moe_status_t st = gemm_common_checks(size_m, top_k, E, block_m);
   if (st != MOE_OK) return st;
+  if (!valid_kernel(kernel)) return MOE_ERR_UNSUPPORTED;
   moe::WeightArgs W;
   st = check_weights(w2, N, K, &W);
   if (st != MOE_OK) return st;
@@ -341,11 +362,20 @@ moe_status_t moe_w4a16_gemm2(const uint16_t* a, int size_m, int K, int N, int E,
     return MOE_ERR_NULL;
   if (mul_topk_weights && topk_w == nullptr) return MOE_ERR_NULL;
   if (!aligned16(a) || !aligned16(y)) return MOE_ERR_ALIGN;
-  const int cap = (int)moe_align_capacity(size_m, 1, E, block_m);
-  return hip_status(moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, a, 1, size_m, K, N, E, &W,
-                                    sorted_ids, expert_ids, num_post_pad, topk_w,
-                                    mul_topk_weights ? 1 : 0, 0.f, 0.f, 0.f, y, N,
+  const int cap = (int)moe_align_capacity(size_m, top_k, E, block_m);
+  return hip_status(moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, a, top_k, size_m * top_k,
+                                    K, N, E, &W, sorted_ids, expert_ids, num_post_pad, topk_w,
+                                    mul_topk_weights ? 1 : 0, 0.f, 0.f, 0.f, y, N, (int)kernel,
                                     static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_w4a16_gemm2(const uint16_t* a, int size_m, int top_k, int K, int N, int E,
+                             const moe_wq_t* w2, const float* topk_w, int mul_topk_weights,
+                             const int32_t* sorted_ids, const int32_t* expert_ids,
+                             const int32_t* num_post_pad, int block_m, uint16_t* y,
+                             moe_stream_t stream) {
+  return moe_w4a16_gemm2_ex(a, size_m, top_k, K, N, E, w2, topk_w, mul_topk_weights, sorted_ids,
+                            expert_ids, num_post_pad, block_m, y, MOE_KERNEL_AUTO, stream);
 }
 
 moe_status_t moe_gptq_act_order_sort(const int32_t* qweight, const int32_t* g_idx, int E, int K,
@@ -554,13 +584,15 @@ moe_status_t moe_forward_mxfp8(const uint16_t* x, const float* logits, int T, in
                                  yb, s);
     if (e == hipSuccess)
       e = moe_launch_gemm((int)w13->fmt, epi, block_m, cap, yb, top_k, n, hidden, n1, E, &W13,
-                          sorted, eids, npp, tw, 0, alpha, beta, limit, actb, inter, s);
+                          sorted, eids, npp, tw, 0, alpha, beta, limit, actb, inter,
+                          moe::KERNEL_AUTO, s);
     if (e == hipSuccess)
       e = moe_launch_mxfp8_quant(actb, n, inter, mx_lda(inter), mx_lds(inter), nullptr, nullptr,
                                  actb, s);
     if (e == hipSuccess)
       e = moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, actb, 1, n, inter, hidden, E,
-                          &W2, sorted, eids, npp, tw, mul, 0.f, 0.f, 0.f, yb, hidden, s);
+                          &W2, sorted, eids, npp, tw, mul, 0.f, 0.f, 0.f, yb, hidden,
+                          moe::KERNEL_AUTO, s);
   }
   if (e == hipSuccess) e = moe_launch_sum(yb, ids, T, top_k, hidden, E, out, s);
   return hip_status(e);
@@ -576,16 +608,17 @@ size_t moe_forward_workspace_bytes(int T, int E, int top_k, int hidden, int inte
   return ws_layout(T, E, top_k, hidden, inter, pick_block_m(T, top_k, E)).total;
 }
 
-moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, int top_k,
-                         int hidden, int inter, moe_route_t kind, const float* expert_bias,
-                         int renormalize, const moe_wq_t* w13, const moe_wq_t* w2, moe_act_t act,
-                         float alpha, float beta, float limit, int mul_topk_weights,
-                         void* workspace, size_t workspace_bytes, uint16_t* out,
-                         moe_stream_t stream) {
+moe_status_t moe_forward_ex(const uint16_t* x, const float* logits, int T, int E, int top_k,
+                            int hidden, int inter, moe_route_t kind, const float* expert_bias,
+                            int renormalize, const moe_wq_t* w13, const moe_wq_t* w2, moe_act_t act,
+                            float alpha, float beta, float limit, int mul_topk_weights,
+                            void* workspace, size_t workspace_bytes, uint16_t* out,
+                            moe_kernel_t kernel, moe_stream_t stream) {
   if (T < 0 || E <= 0 || E > kMaxE || top_k < 1 || top_k > E || top_k > kMaxTopK)
     return MOE_ERR_SHAPE;
   if ((long long)T * top_k >= (1LL << 24)) return MOE_ERR_SHAPE;
   if (kind != MOE_ROUTE_SOFTMAX && kind != MOE_ROUTE_SIGMOID_BIAS) return MOE_ERR_UNSUPPORTED;
+  if (!valid_kernel(kernel)) return MOE_ERR_UNSUPPORTED;
   const int epi = epi_of(act);
   if (epi != moe::EPI_SWIGLU && epi != moe::EPI_RELU2) return MOE_ERR_UNSUPPORTED;
   const int n1 = (epi == moe::EPI_SWIGLU) ? 2 * inter : inter;
@@ -634,15 +667,26 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, i
   if (e == hipSuccess)
     e = moe_launch_gemm((int)w13->fmt, epi, block_m, cap, g1_in, g1_topk, n, hidden, n1, E, &W13,
                         sorted, eids, npp, tw, mul_topk_weights == 2 ? 1 : 0, alpha, beta, limit,
-                        actb, inter, s);
+                        actb, inter, (int)kernel, s);
   if (e == hipSuccess && w2->k_perm != nullptr)
     e = moe_launch_permute_slots(actb, n, 1, inter, E, w2->k_perm, ids, actb, s);
   if (e == hipSuccess)
     e = moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, actb, 1, n, inter, hidden, E, &W2,
                         sorted, eids, npp, tw, mul_topk_weights == 1 ? 1 : 0, 0.f, 0.f, 0.f, yb,
-                        hidden, s);
+                        hidden, (int)kernel, s);
   if (e == hipSuccess) e = moe_launch_sum(yb, ids, T, top_k, hidden, E, out, s);
   return hip_status(e);
+}
+
+moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, int top_k,
+                         int hidden, int inter, moe_route_t kind, const float* expert_bias,
+                         int renormalize, const moe_wq_t* w13, const moe_wq_t* w2, moe_act_t act,
+                         float alpha, float beta, float limit, int mul_topk_weights,
+                         void* workspace, size_t workspace_bytes, uint16_t* out,
+                         moe_stream_t stream) {
+  return moe_forward_ex(x, logits, T, E, top_k, hidden, inter, kind, expert_bias, renormalize, w13,
+                        w2, act, alpha, beta, limit, mul_topk_weights, workspace, workspace_bytes,
+                        out, MOE_KERNEL_AUTO, stream);
 }
 
 }  // extern "C"

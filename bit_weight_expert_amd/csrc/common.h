@@ -48,6 +48,10 @@ struct WeightArgs {
   int group;
   const uint8_t* scales_kc;    // NVFP4 e4m3 scales by 64-deep K chunk [E][K/64][N][4], or null
   const uint8_t* qweight_kc;   // NVFP4 codes by 64-deep K chunk [E][K/64][N][32], or null (needs scales_kc)
+  const int32_t* g_idx;        // GPTQ group map [E][K], or null; only the identity is valid here
 };
+
+// Kernel choice for blocks of 16/32 rows (values match the public enum).
+enum { KERNEL_AUTO = 0, KERNEL_SPLITK = 1, KERNEL_WIDE = 2 };
 
 }  // namespace moe

@@ -69,6 +69,15 @@ struct BChunk {
   int zsh;  // GPTQ: bit offset of this column's zero point in sr[1]
 };
 
+// Scale operand of the fp4 -> bf16 convert for an e8m0 byte: the byte in the
+// fp32 exponent field.  The convert applies only that field, read as e8m0 (so
+// in-bounds probes on gfx950 found): byte 0x00 (a float 0) scales by 2^-127,
+// giving exact bf16 subnormals, and 0xFF (a float infinity) gives NaN, the
+// OCP decode of both bytes.
+__device__ __forceinline__ float e8m0_operand(uint32_t byte) {
+  return __uint_as_float((byte & 0xffu) << 23);
+}
+
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
   _Float16 v;
   __builtin_memcpy(&v, &h, 2);
@@ -189,7 +198,7 @@ __device__ __forceinline__ bf16x8 deq_step(const BChunk<FMT, C>& b, int st) {
   } else if (FMT == FMT_MXFP4) {
     const int grp = (st * 8) / 32;
     const uint32_t raw = (C == 256) ? b.sr[grp] : b.sr[0];
-    const float s = __uint_as_float((raw & 0xffu) << 23);
+    const float s = e8m0_operand(raw);
     bf16x2 p;
     p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
     __builtin_memcpy(&r.x, &p, 4);
@@ -227,6 +236,51 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
   return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
 }
 
+// The activations of the GEMM1 epilogue.  The clamps are selects, not
+// fminf/fmaxf: those return the other operand when one is NaN, which would
+// turn a NaN pre-activation (a NaN scale, say) into a finite output.  Here a
+// NaN stays NaN, as it does in the plain definition.
+// swigluoai: g = min(gate, limit), u = clamp(up, -limit, limit),
+// a = g * sigmoid(alpha * g) * (u + beta).
+__device__ __forceinline__ float act_swigluoai(float gate, float up, float alpha, float beta,
+                                               float limit) {
+  const float g = gate > limit ? limit : gate;
+  const float u = up > limit ? limit : (up < -limit ? -limit : up);
+  return g * sigmoid_fast(alpha * g) * (u + beta);
+}
+// ReLU^2: max(h, 0)^2.
+__device__ __forceinline__ float act_relu2(float h) {
+  const float r = h < 0.f ? 0.f : h;
+  return r * r;
+}
+
+// GPTQ weights passed with a group map: the kernels read groups as runs of
+// `group` consecutive rows, so only the identity map (row k in group
+// k / group) describes weights they can multiply.  Every workgroup checks its
+// expert's map after its K loop (K ints, from L2) and all its threads agree
+// on the result; any other map poisons the workgroup's outputs with NaN, a
+// visible failure instead of silently misgrouped scales.  Act-order maps go
+// through the load-time group sort instead.  Called by every thread of the
+// workgroup (the condition on g_idx is the same for all of them).
+template <int FMT>
+__device__ __forceinline__ bool gidx_bad(const WeightArgs& W, int e, int K, int tid, int nthreads) {
+  int bad = 0;
+  if (FMT == FMT_GPTQ && W.g_idx != nullptr) {
+    const int32_t* g = W.g_idx + (size_t)e * K;
+    for (int k = tid; k < K; k += nthreads) bad |= g[k] != k / W.group;
+    bad = __syncthreads_or(bad);
+  }
+  return bad != 0;
+}
+
+// Per-expert multiplier of the accumulators: the NVFP4 global scale (1 for the
+// other formats), or NaN for a poisoned tile.
+template <int FMT>
+__device__ __forceinline__ float acc_scale(const WeightArgs& W, int e, bool poison) {
+  const float g = (FMT == FMT_NVFP4) ? W.global_scale[e] : 1.f;
+  return poison ? __builtin_nanf("") : g;
+}
+
 // --------------------------------------------------------------------------
 // epilogue for one wave's fragment accumulators
 // --------------------------------------------------------------------------
@@ -258,9 +312,10 @@ __device__ __forceinline__ bool frag_on(int n0, int j, int N) {
 // acc[i][j]: rows i*16 + 4g + r, fragment j (NF fragments from weight row n0).
 template <int EPI, int FMT, int MI, int NF>
 __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiArgs& a,
-                                         const WeightArgs& W, int e, int n0, int lane) {
+                                         const WeightArgs& W, int e, int n0, int lane,
+                                         bool poison = false) {
   const int c16 = lane & 15, g = lane >> 4;
-  const float gsc = (FMT == FMT_NVFP4) ? W.global_scale[e] : 1.f;
+  const float gsc = acc_scale<FMT>(W, e, poison);
   // bias: unconditional loads (another valid word when there is none)
   const bool has_bias = W.bias != nullptr;
   const uint16_t* bbase = has_bias ? W.bias : reinterpret_cast<const uint16_t*>(W.qweight);
@@ -302,11 +357,9 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiAr
 #pragma unroll
         for (int p = 0; p < NF / 2; ++p) {
           if (!frag_on<EPI>(n0, 2 * p, a.N)) continue;
-          float gate = acc[i][2 * p][r] * gin + bias[2 * p];
-          float up = acc[i][2 * p + 1][r] * gin + bias[2 * p + 1];
-          gate = fminf(gate, a.limit);
-          up = fminf(fmaxf(up, -a.limit), a.limit);
-          const float v = gate * sigmoid_fast(a.alpha * gate) * (up + a.beta);
+          const float gate = acc[i][2 * p][r] * gin + bias[2 * p];
+          const float up = acc[i][2 * p + 1][r] * gin + bias[2 * p + 1];
+          const float v = act_swigluoai(gate, up, a.alpha, a.beta, a.limit);
           orow[n0 / 2 + 16 * p + c16] = f32_to_bf16_bits(v);
         }
       } else {
@@ -315,8 +368,7 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiAr
           if (!frag_on<EPI>(n0, j, a.N)) continue;
           float v = acc[i][j][r] * gin + bias[j];
           if (EPI == EPI_RELU2) {
-            v = fmaxf(v, 0.f);
-            v = v * v;
+            v = act_relu2(v);
           } else if (EPI == EPI_DOWN) {
             v = v * tw;
           }
@@ -671,7 +723,7 @@ __device__ __forceinline__ void pf_read_b(PfB (&b)[NF], const uint8_t* bstage, c
         b[j].s0 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 0);
         b[j].s1 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 1);
       } else {
-        b[j].s0 = __uint_as_float((uint32_t)sc[r * (K / 32) + k0 / 32 + h] << 23);
+        b[j].s0 = e8m0_operand(sc[r * (K / 32) + k0 / 32 + h]);
         b[j].s1 = 0.f;
       }
     }
@@ -763,9 +815,10 @@ __device__ __forceinline__ int frag32_row(int n0, int j, int c) {
 template <int EPI, int FMT, int MI, int NF>
 __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const EpiArgs& a,
                                            const WeightArgs& W, int e, int n0, int lane,
-                                           const int2* rows = nullptr, int rloc0 = 0) {
+                                           const int2* rows = nullptr, int rloc0 = 0,
+                                           bool poison = false) {
   const int c = lane & 31, h = lane >> 5;
-  const float gsc = (FMT == FMT_NVFP4) ? W.global_scale[e] : 1.f;
+  const float gsc = acc_scale<FMT>(W, e, poison);
   // bias: unconditional loads (another valid word when there is none)
   const bool has_bias = W.bias != nullptr;
   const uint16_t* bbase = has_bias ? W.bias : reinterpret_cast<const uint16_t*>(W.qweight);
@@ -827,11 +880,9 @@ __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const Ep
 #pragma unroll
         for (int p = 0; p < NF / 2; ++p) {
           if (!on[2 * p]) continue;
-          float gate = acc[i][2 * p][v] * gin + bias[2 * p];
-          float up = acc[i][2 * p + 1][v] * gin + bias[2 * p + 1];
-          gate = fminf(gate, a.limit);
-          up = fminf(fmaxf(up, -a.limit), a.limit);
-          const float y = gate * sigmoid_fast(a.alpha * gate) * (up + a.beta);
+          const float gate = acc[i][2 * p][v] * gin + bias[2 * p];
+          const float up = acc[i][2 * p + 1][v] * gin + bias[2 * p + 1];
+          const float y = act_swigluoai(gate, up, a.alpha, a.beta, a.limit);
           orow[n0 / 2 + 32 * p + c] = f32_to_bf16_bits(y);
         }
       } else {
@@ -840,8 +891,7 @@ __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const Ep
           if (!on[j]) continue;
           float y = acc[i][j][v] * gin + bias[j];
           if (EPI == EPI_RELU2) {
-            y = fmaxf(y, 0.f);
-            y = y * y;
+            y = act_relu2(y);
           } else if (EPI == EPI_DOWN) {
             y = y * tw;
           }
@@ -1095,6 +1145,7 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
   }
   // no DMA may land in LDS after this workgroup is gone
   wait_vmcnt<0>();
+  const bool poison = gidx_bad<FMT>(W, e, K, tid, 256 * RS * KS);
 
   const int row0 = mb * BM + rpart * MI * 32;
   if (K % kPfBK && kp == 0) pf_tail32<FMT, EPI, MI, NF>(acc, ga, W, e, row0, n0, c, h, nchunks * kPfBK);
@@ -1155,7 +1206,7 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
     if (n0 >= N) return;
     EpiArgs a = ea;
     a.row0 = row0 + kp * HM * 32;
-    epilogue32<EPI, FMT, HM, NF>(acch, a, W, e, n0, lane, rowtab, a.row0 - mb * BM);
+    epilogue32<EPI, FMT, HM, NF>(acch, a, W, e, n0, lane, rowtab, a.row0 - mb * BM, poison);
     return;
   }
 
@@ -1163,7 +1214,7 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
   if (n0 >= N) return;
   EpiArgs a = ea;
   a.row0 = row0;
-  epilogue32<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane, rowtab, row0 - mb * BM);
+  epilogue32<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane, rowtab, row0 - mb * BM, poison);
 }
 
 // --------------------------------------------------------------------------
@@ -1460,10 +1511,11 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
     if (K - k0 >= 32) dc_chunk<FMT, 32, MI, NF>(acc, W, ga, arow, nrow, rl, sc, e, k0, g);
   }
 
+  const bool poison = gidx_bad<FMT>(W, e, K, tid, 64 * nw);
   EpiArgs a = ea;
   a.row0 = mb * BM;
   if (nw == 1) {
-    epilogue<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane);
+    epilogue<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane, poison);
     return;
   }
   // add the waves' partial sums in wave order
@@ -1495,7 +1547,7 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
         fin[i][q] = sum;
       }
     // the fragment group as its own "wave" starting at weight row n0 + 16*GF*grp
-    epilogue<EPI, FMT, MI, GF>(fin, a, W, e, n0 + 16 * GF * grp, lane);
+    epilogue<EPI, FMT, MI, GF>(fin, a, W, e, n0 + 16 * GF * grp, lane, poison);
   }
 }
 
@@ -1597,11 +1649,9 @@ __device__ __forceinline__ void epilogue_pre(const f32x4 (&acc)[MI][NF], const E
 #pragma unroll
         for (int q = 0; q < NF / 2; ++q) {
           if (!frag_on<EPI>(n0, 2 * q, a.N)) continue;
-          float gate = acc[i][2 * q][r] * gin + bias[2 * q];
-          float up = acc[i][2 * q + 1][r] * gin + bias[2 * q + 1];
-          gate = fminf(gate, a.limit);
-          up = fminf(fmaxf(up, -a.limit), a.limit);
-          const float v = gate * sigmoid_fast(a.alpha * gate) * (up + a.beta);
+          const float gate = acc[i][2 * q][r] * gin + bias[2 * q];
+          const float up = acc[i][2 * q + 1][r] * gin + bias[2 * q + 1];
+          const float v = act_swigluoai(gate, up, a.alpha, a.beta, a.limit);
           orow[n0 / 2 + 16 * q + c16] = f32_to_bf16_bits(v);
         }
       } else {
@@ -1610,8 +1660,7 @@ __device__ __forceinline__ void epilogue_pre(const f32x4 (&acc)[MI][NF], const E
           if (!frag_on<EPI>(n0, j, a.N)) continue;
           float v = acc[i][j][r] * gin + bias[j];
           if (EPI == EPI_RELU2) {
-            v = fmaxf(v, 0.f);
-            v = v * v;
+            v = act_relu2(v);
           } else if (EPI == EPI_DOWN) {
             v = v * tw;
           }
@@ -1795,6 +1844,7 @@ __global__ void __launch_bounds__(256, (MI == 1 ? 4 : 3)) gemm_wide_kernel(GemmA
       pf_barrier();
     }
   }
+  if (gidx_bad<FMT>(W, e, K, tid, 256)) pre.gsc = __builtin_nanf("");
   epilogue_pre<EPI, MI, NF>(acc, pre, ep, W, n0w, lane);
 }
 
@@ -1855,17 +1905,16 @@ static inline size_t wide_lds(int fmt, int K, int group, int MI) {
 }
 constexpr size_t kWdMaxLds = 64 * 1024;
 // Wide kernel when the (expert block, 128-column tile) pairs alone give the
-// chip enough workgroups; otherwise the split-K kernel.  The process-wide
-// policy can force either (0 automatic, 1 split-K, 2 wide where its LDS fits).
+// chip enough workgroups; otherwise the split-K kernel.  The caller's kernel
+// argument can force either (KERNEL_WIDE where its LDS fits).
 constexpr long kWdMinTiles = 640;
-static int g_decode_policy = 0;
 
 template <int FMT, int EPI, int MI>
 static void launch_decode(GemmArgs ga, const WeightArgs& W, const EpiArgs& ea, int blocks_est,
-                          hipStream_t st) {
+                          int kernel, hipStream_t st) {
   const long wide_tiles = (long)blocks_est * ((ga.N + kWdCols - 1) / kWdCols);
   const size_t lds = wide_lds(FMT, ga.K, W.group, MI);
-  const bool want_wide = g_decode_policy == 2 || (g_decode_policy == 0 && wide_tiles >= kWdMinTiles);
+  const bool want_wide = kernel == KERNEL_WIDE || (kernel == KERNEL_AUTO && wide_tiles >= kWdMinTiles);
   if (want_wide && lds <= kWdMaxLds) {
     ga.n_ntiles = (ga.N + kWdCols - 1) / kWdCols;
     gemm_wide_kernel<FMT, EPI, MI>
@@ -1877,16 +1926,16 @@ static void launch_decode(GemmArgs ga, const WeightArgs& W, const EpiArgs& ea, i
 
 template <int FMT, int EPI>
 static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs& W, EpiArgs ea,
-                             hipStream_t st) {
+                             int kernel, hipStream_t st) {
   ga.n_mblocks = cap / block_m;
   if (block_m <= 32) {
     // at most one block per routed expert is expected in this regime: the
     // number of routed experts bounds the blocks that hold slots
     const int blocks_est = ga.E < ga.n_slots ? ga.E : ga.n_slots;
     if (block_m == 16)
-      launch_decode<FMT, EPI, 1>(ga, W, ea, blocks_est, st);
+      launch_decode<FMT, EPI, 1>(ga, W, ea, blocks_est, kernel, st);
     else
-      launch_decode<FMT, EPI, 2>(ga, W, ea, blocks_est, st);
+      launch_decode<FMT, EPI, 2>(ga, W, ea, blocks_est, kernel, st);
   } else {
     // widest tile whose scales fit the kernel's LDS; otherwise the split-K kernel
     if (pf_scale_bytes(FMT, ga.K, W.group, Pf<128, 2>::BN) > kPfScaleBytes ||
@@ -1895,7 +1944,7 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
       // are not 16-byte multiples: the split-K kernel over 32-row sub-blocks
       // of the aligned blocks
       ga.n_mblocks = cap / 32;
-      launch_decode<FMT, EPI, 2>(ga, W, ea, ga.n_mblocks, st);
+      launch_decode<FMT, EPI, 2>(ga, W, ea, ga.n_mblocks, kernel, st);
       return hipGetLastError();
     }
     ga.n_ntiles = (ga.N + Pf<128, 2>::BN - 1) / Pf<128, 2>::BN;
@@ -2236,12 +2285,12 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA m
 
 template <int FMT>
 static hipError_t launch_fmt(int epi, int block_m, int cap, const GemmArgs& ga, const WeightArgs& W,
-                             const EpiArgs& ea, hipStream_t st) {
+                             const EpiArgs& ea, int kernel, hipStream_t st) {
   switch (epi) {
-    case EPI_SWIGLU: return launch_epi<FMT, EPI_SWIGLU>(block_m, cap, ga, W, ea, st);
-    case EPI_RELU2: return launch_epi<FMT, EPI_RELU2>(block_m, cap, ga, W, ea, st);
-    case EPI_NONE: return launch_epi<FMT, EPI_NONE>(block_m, cap, ga, W, ea, st);
-    default: return launch_epi<FMT, EPI_DOWN>(block_m, cap, ga, W, ea, st);
+    case EPI_SWIGLU: return launch_epi<FMT, EPI_SWIGLU>(block_m, cap, ga, W, ea, kernel, st);
+    case EPI_RELU2: return launch_epi<FMT, EPI_RELU2>(block_m, cap, ga, W, ea, kernel, st);
+    case EPI_NONE: return launch_epi<FMT, EPI_NONE>(block_m, cap, ga, W, ea, kernel, st);
+    default: return launch_epi<FMT, EPI_DOWN>(block_m, cap, ga, W, ea, kernel, st);
   }
 }
 
@@ -2254,15 +2303,15 @@ extern "C" hipError_t moe_launch_gemm(int fmt, int epi, int block_m, int cap, co
                                       const moe::WeightArgs* W, const int32_t* sid,
                                       const int32_t* eid, const int32_t* npp, const float* tw,
                                       int mul, float alpha, float beta, float limit, uint16_t* out,
-                                      int out_ld, hipStream_t st) {
+                                      int out_ld, int kernel, hipStream_t st) {
   if (cap / block_m == 0) return hipSuccess;
   const uint64_t a_mul = ((1ull << 32) + (uint64_t)a_div - 1) / (uint64_t)a_div;
   moe::GemmArgs ga{A, a_div, a_mul, n_slots, K, N, E, 0, 0, 1, block_m, sid, eid, npp};
   moe::EpiArgs ea{sid, 0, n_slots, N, tw, mul, alpha, beta, limit, out, out_ld};
   switch (fmt) {
-    case moe::FMT_NVFP4: return moe::launch_fmt<moe::FMT_NVFP4>(epi, block_m, cap, ga, *W, ea, st);
-    case moe::FMT_MXFP4: return moe::launch_fmt<moe::FMT_MXFP4>(epi, block_m, cap, ga, *W, ea, st);
-    default: return moe::launch_fmt<moe::FMT_GPTQ>(epi, block_m, cap, ga, *W, ea, st);
+    case moe::FMT_NVFP4: return moe::launch_fmt<moe::FMT_NVFP4>(epi, block_m, cap, ga, *W, ea, kernel, st);
+    case moe::FMT_MXFP4: return moe::launch_fmt<moe::FMT_MXFP4>(epi, block_m, cap, ga, *W, ea, kernel, st);
+    default: return moe::launch_fmt<moe::FMT_GPTQ>(epi, block_m, cap, ga, *W, ea, kernel, st);
   }
 }
 
@@ -2300,13 +2349,6 @@ extern "C" hipError_t moe_launch_gemm_mx(int epi, int block_m, int cap, const ui
   }
 #undef MOE_MX_LAUNCH
   return hipGetLastError();
-}
-
-extern "C" int moe_set_decode_policy(int policy) {
-  if (policy < 0 || policy > 2) return -1;
-  const int old = moe::g_decode_policy;
-  moe::g_decode_policy = policy;
-  return old;
 }
 
 extern "C" hipError_t moe_launch_sum(const uint16_t* y, const int32_t* ids, int T, int top_k, int H,

@@ -28,7 +28,10 @@
  *   A non-MOE_OK status means nothing was enqueued, except MOE_ERR_HIP,
  *   which reports a launch failure (work enqueued before it may have run).
  * - Device data conventions: expert ids outside [0, E) are not routed (align
- *   gives them no slot; the sum skips them).  NaN scales propagate.
+ *   gives them no slot; the sum skips them).  NaN scales propagate to every
+ *   output they reach (e4m3 0x7F and 0xFF, e8m0 0xFF, NaN fp16 scales and
+ *   global scales); e8m0 0x00 is 2^-127.  Dequantised weights beyond the bf16
+ *   range become infinities.
  * - Sizes: K (the reduction length) must be a multiple of 32 and of the
  *   group size; N must be a multiple of 16 (32 for the gated GEMM1, whose
  *   rows pair up).  K and N tails are handled exactly: no buffer is padded
@@ -101,9 +104,16 @@ typedef struct {
                                  GPTQ: fp16 [E][K/G][N] */
   const void* zeros;          /* GPTQ: int32 [E][K/G][N/8], nibble i holds n%8 == i. Else NULL */
   const float* global_scale;  /* NVFP4: fp32 [E]. Else NULL */
-  const int32_t* g_idx;       /* GPTQ group of each row, int32 [E][K]; the GEMMs take only NULL
-                                 (group = k / group_size): act-order weights are first put
-                                 in group order by moe_gptq_act_order_sort */
+  const int32_t* g_idx;       /* GPTQ group of each row, int32 [E][K] (4-byte aligned), or NULL
+                                 for group = k / group_size.  The kernels read groups as runs
+                                 of group_size rows, so the only map they take is that
+                                 identity: each workgroup checks its expert's map on the
+                                 device, and a map that differs anywhere turns every output
+                                 that expert's weights produce into NaN (a visible failure).
+                                 Act-order maps are first put in group order by
+                                 moe_gptq_act_order_sort (whose weights come with k_perm and
+                                 g_idx = NULL; both set is MOE_ERR_UNSUPPORTED).  Other formats:
+                                 must be NULL. */
   const uint16_t* bias;       /* bf16 [E][N], or NULL for no bias */
   const int32_t* k_perm;      /* GPTQ act-order: NULL, or int32 [E][K] from moe_gptq_act_order_sort
                                  (row k of the stored weight multiplies input channel
@@ -126,6 +136,16 @@ typedef struct {
                                  64/128-row kernel copies each chunk's codes for 32 rows as one
                                  contiguous kilobyte instead of 32-byte pieces of 32 rows. */
 } moe_wq_t;
+
+/* Kernel for the grouped GEMMs over blocks of 16 or 32 rows (few tokens per
+ * expert).  AUTO: the library's choice from the launch size.  SPLITK: the
+ * split-K kernel (32 weight rows per workgroup, K split over its waves).
+ * WIDE: 128 weight rows per workgroup with the A rows shared through on-chip
+ * memory (the split-K kernel where its scale tile would not fit).  The results
+ * agree to the rounding of the fp32 accumulation order.  Blocks of 64/128 rows
+ * always run the streaming prefill kernel.  Taken by the _ex entry points; the
+ * plain ones use AUTO.  Any other value is MOE_ERR_UNSUPPORTED. */
+typedef enum { MOE_KERNEL_AUTO = 0, MOE_KERNEL_SPLITK = 1, MOE_KERNEL_WIDE = 2 } moe_kernel_t;
 
 /* Length of sorted_ids for T tokens: T*top_k + min(E, T*top_k)*(block_m-1),
  * rounded up to block_m (every expert that can receive a slot pads to
@@ -199,20 +219,37 @@ moe_status_t moe_w4a16_gemm1(const uint16_t* x, int size_m, int top_k, int K, in
                              const int32_t* num_post_pad, int block_m, uint16_t* out,
                              moe_stream_t stream);
 
-/* Grouped GEMM2 in the top_k = 1 view: A rows are already one per flat slot.
- * For every real entry f of block b (expert e):
- *   y[f][:] = (W2_e . a[f] (+ bias2_e)) * (mul_topk_weights ? topk_w[f] : 1)
- * The routing weight is read from topk_w at the row's own flat slot ("moe_wna16_marlin_gemm
- * applies wrong per-row topk weights": the fix is exactly that each row gets its
- * own weight).
- *   a      bf16 [size_m][K]         (size_m = T*top_k)
- *   topk_w fp32 [size_m]            (may be NULL when mul_topk_weights = 0)
- *   y      bf16 [size_m][N]; rows no block covers are left untouched. */
-moe_status_t moe_w4a16_gemm2(const uint16_t* a, int size_m, int K, int N, int E,
+/* Grouped GEMM2.  For every real entry f of block b (expert e):
+ *   y[f][:] = (W2_e . a[f / top_k] (+ bias2_e)) * (mul_topk_weights ? topk_w[f] : 1)
+ * The layer calls it in the top_k = 1 view (size_m = T*top_k, one A row per
+ * flat slot), as the "moe_wna16_marlin_gemm applies wrong per-row topk
+ * weights" page's repro calls its gemm2 step; top_k > 1 shares one A row
+ * between top_k slots, as GEMM1 does.  The routing weight is read from topk_w
+ * at the row's own flat slot (that page's fix: each row gets its own weight).
+ *   a      bf16 [size_m][K]
+ *   topk_w fp32 [size_m*top_k]      (may be NULL when mul_topk_weights = 0)
+ *   y      bf16 [size_m*top_k][N]; rows no block covers are left untouched.
+ * sorted_ids / expert_ids / num_post_pad come from moe_align with the same
+ * block_m, size_m and top_k (sentinel size_m*top_k). */
+moe_status_t moe_w4a16_gemm2(const uint16_t* a, int size_m, int top_k, int K, int N, int E,
                              const moe_wq_t* w2, const float* topk_w, int mul_topk_weights,
                              const int32_t* sorted_ids, const int32_t* expert_ids,
                              const int32_t* num_post_pad, int block_m, uint16_t* y,
                              moe_stream_t stream);
+
+/* moe_w4a16_gemm1 and moe_w4a16_gemm2 with the kernel for 16/32-row blocks
+ * chosen by the caller (moe_kernel_t; for tuning and for testing each kernel). */
+moe_status_t moe_w4a16_gemm1_ex(const uint16_t* x, int size_m, int top_k, int K, int N, int E,
+                                const moe_wq_t* w13, moe_act_t act, float alpha, float beta,
+                                float limit, const float* topk_w, int mul_topk_weights,
+                                const int32_t* sorted_ids, const int32_t* expert_ids,
+                                const int32_t* num_post_pad, int block_m, uint16_t* out,
+                                moe_kernel_t kernel, moe_stream_t stream);
+moe_status_t moe_w4a16_gemm2_ex(const uint16_t* a, int size_m, int top_k, int K, int N, int E,
+                                const moe_wq_t* w2, const float* topk_w, int mul_topk_weights,
+                                const int32_t* sorted_ids, const int32_t* expert_ids,
+                                const int32_t* num_post_pad, int block_m, uint16_t* y,
+                                moe_kernel_t kernel, moe_stream_t stream);
 
 /* GPTQ act-order preparation, run once when the weights are loaded.  A GPTQ
  * checkpoint quantised in activation order stores its rows in input-channel
@@ -311,6 +348,15 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, i
                          int mul_topk_weights, void* workspace, size_t workspace_bytes,
                          uint16_t* out, moe_stream_t stream);
 
+/* moe_forward with the kernel for 16/32-row blocks chosen by the caller
+ * (moe_kernel_t), for both GEMMs. */
+moe_status_t moe_forward_ex(const uint16_t* x, const float* logits, int T, int E, int top_k,
+                            int hidden, int inter, moe_route_t kind, const float* expert_bias,
+                            int renormalize, const moe_wq_t* w13, const moe_wq_t* w2,
+                            moe_act_t act, float alpha, float beta, float limit,
+                            int mul_topk_weights, void* workspace, size_t workspace_bytes,
+                            uint16_t* out, moe_kernel_t kernel, moe_stream_t stream);
+
 /* ---- MXFP8 activations (MXFP4 weights x MXFP8 activations) ----
  * The variant of the layer with MXFP8 activations ("gpt-oss-120b MXFP4 +
  * --enable-expert-parallel crashes", sections "Actual behavior" and "Why the
@@ -366,16 +412,6 @@ moe_status_t moe_forward_mxfp8(const uint16_t* x, const float* logits, int T, in
                                moe_act_t act, float alpha, float beta, float limit,
                                int mul_topk_weights, void* workspace, size_t workspace_bytes,
                                uint16_t* out, moe_stream_t stream);
-
-/* Which kernel the grouped GEMMs use for blocks of 16 or 32 rows (few tokens
- * per expert): 0 = automatic (the library's choice from the launch size),
- * 1 = split-K kernel, 2 = wide kernel (128 weight rows per workgroup, A
- * shared through LDS; falls back to split-K when its scale tile does not fit).
- * Process-wide, for tuning and testing; results are the same to rounding of
- * the fp32 accumulation order.  Returns the previous policy, or -1 for an
- * invalid value (the policy is then unchanged).  Not synchronised with calls
- * running on other threads. */
-int moe_set_decode_policy(int policy);
 
 /* Static description of a status code. */
 const char* moe_status_str(moe_status_t s);

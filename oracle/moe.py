@@ -296,15 +296,17 @@ def forward_tokens(layer, tokens, topk=None):
 
     Used to check full-size runs on sampled rows: only the experts those
     tokens route to are decoded, one at a time, so memory stays at one
-    expert's float64 weights.  Each (token, choice) row is computed on its
-    own; the rows are then summed over the choices j in ascending order.
-    Returns float64 [len(tokens), H].
+    expert's float64 weights.  The (token, choice) rows routed to an expert
+    are stacked and multiplied by its weights together (each row's result is
+    its own dot products, as one at a time); the rows are then summed over the
+    choices j in ascending order.  Returns float64 [len(tokens), H].
     """
     L = layer
     ids, w = route(L) if topk is None else topk
     tokens = list(tokens)
     x = bf16_to_f64(L.x)
     mx = getattr(L, "act_fmt", "bf16") == "mxfp8"
+    on_input = getattr(L, "weight_on_input", False)
     y = np.zeros((len(tokens), L.top_k, L.H), dtype=np.float64)
     by_expert = {}
     for i, t in enumerate(tokens):
@@ -315,19 +317,21 @@ def forward_tokens(layer, tokens, topk=None):
     for e, items in sorted(by_expert.items()):
         W13 = decode_expert(L.w13, e)
         W2 = decode_expert(L.w2, e)
-        on_input = getattr(L, "weight_on_input", False)
-        for i, t, j in items:
-            xin = x[t] * float(w[t, j]) if on_input else x[t]
-            if mx:
-                xin = mxfp8_round_trip(xin)
-            h = W13 @ xin + _bias_f64(L.w13, e)
-            a = activation(h, L.act, L.alpha, L.beta, L.limit)
-            if mx:
-                a = mxfp8_round_trip(bf16_round(a))
-            yv = W2 @ a + _bias_f64(L.w2, e)
-            if L.mul_topk_weights and not on_input:
-                yv = yv * float(w[t, j])
-            y[i, j] = yv
+        ii = np.array([it[0] for it in items])
+        tt = np.array([it[1] for it in items])
+        jj = np.array([it[2] for it in items])
+        wr = np.asarray(w, dtype=np.float64)[tt, jj]
+        xin = x[tt] * wr[:, None] if on_input else x[tt]
+        if mx:
+            xin = mxfp8_round_trip(xin)
+        h = xin @ W13.T + _bias_f64(L.w13, e)
+        a = activation(h, L.act, L.alpha, L.beta, L.limit)
+        if mx:
+            a = mxfp8_round_trip(bf16_round(a))
+        yv = a @ W2.T + _bias_f64(L.w2, e)
+        if L.mul_topk_weights and not on_input:
+            yv = yv * wr[:, None]
+        y[ii, jj] = yv
         del W13, W2
     out = np.zeros((len(tokens), L.H), dtype=np.float64)
     for j in range(L.top_k):

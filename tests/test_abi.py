@@ -90,7 +90,7 @@ def test_gemm1_rejects(L):
     assert _g1(L, _wq(group=32)) == UNSUP                # NVFP4 is group 16
     assert _g1(L, _wq(fmt=1, group=16)) == UNSUP         # MXFP4 is group 32
     assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE), K=2880 + 32) == SHAPE   # K % group
-    assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, g_idx=FAKE)) == UNSUP    # act-order
+    assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, g_idx=FAKE), x=None) == NULL  # map accepted
     assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, k_perm=FAKE)) == UNSUP   # gather first
     assert _g1(L, _wq(k_perm=FAKE)) == UNSUP             # act-order is a GPTQ form
     assert _g1(L, _wq(fmt=1, group=32, scales_kc=FAKE)) == UNSUP   # scales by chunk: NVFP4 only
@@ -113,13 +113,53 @@ def test_gemm1_rejects(L):
 
 def test_gemm2_rejects(L):
     w = _wq()
-    g2 = lambda **kw: L.moe_w4a16_gemm2(kw.get("a", FAKE), 32, 2880, 2880, 32, ctypes.byref(kw.get("w", w)),
+    g2 = lambda **kw: L.moe_w4a16_gemm2(kw.get("a", FAKE), 32, kw.get("k", 1), 2880, 2880, 32,
+                                        ctypes.byref(kw.get("w", w)),
                                         kw.get("tw", FAKE), kw.get("mul", 1), FAKE, FAKE, FAKE,
                                         kw.get("bm", 16), kw.get("y", FAKE), None)
     assert g2(tw=None) == NULL                           # weights needed when multiplying
     assert g2(bm=256) == SHAPE
     assert g2(y=None) == NULL
     assert g2(w=_wq(scales=None)) == NULL
+    assert g2(k=0) == SHAPE                              # top_k >= 1
+    assert g2(k=1 << 20) == SHAPE                        # size_m * top_k < 2^24
+
+
+def test_no_process_wide_state(L):
+    """The kernel choice is an argument of the _ex calls, not library state."""
+    assert not hasattr(L, "moe_set_decode_policy")
+
+
+def test_kernel_choice_rejects(L):
+    w = _wq()
+    g1 = lambda kern: L.moe_w4a16_gemm1_ex(FAKE, 32, 4, 2880, 5760, 32, ctypes.byref(w), 0, 1.702,
+                                           1.0, 7.0, None, 0, FAKE, FAKE, FAKE, 16, FAKE, kern, None)
+    g2 = lambda kern: L.moe_w4a16_gemm2_ex(FAKE, 32, 1, 2880, 2880, 32, ctypes.byref(w), FAKE, 1,
+                                           FAKE, FAKE, FAKE, 16, None, kern, None)
+    f = lambda kern: L.moe_forward_ex(FAKE, FAKE, 8, 32, 4, 2880, 2880, 0, None, 1,
+                                      ctypes.byref(w), ctypes.byref(w), 0, 1.702, 1.0, 7.0, 1,
+                                      FAKE * 16, 0, FAKE, kern, None)
+    for bad in (-1, 3, 17):
+        assert g1(bad) == UNSUP and g2(bad) == UNSUP and f(bad) == UNSUP
+    for good in (0, 1, 2):
+        assert g2(good) == NULL                          # accepted, then y = NULL
+        assert f(good) == WS                             # accepted, then the workspace size
+
+
+def test_g_idx_rules(L):
+    """GPTQ g_idx is accepted (checked against the identity on the device);
+    other formats take none; not together with k_perm; 4-byte alignment."""
+    g = dict(fmt=2, group=64, zeros=FAKE)
+    g1 = lambda w: L.moe_w4a16_gemm1(FAKE, 32, 4, 2880, 5760, 32, ctypes.byref(w), 0, 1.702, 1.0,
+                                     7.0, None, 0, FAKE, FAKE, FAKE, 16, None, None)
+    assert g1(_wq(g_idx=FAKE, **g)) == NULL              # accepted, then out = NULL
+    assert g1(_wq(g_idx=FAKE + 2, **g)) == ALIGN
+    assert g1(_wq(g_idx=FAKE)) == UNSUP                  # NVFP4 has no group map
+    assert g1(_wq(fmt=1, group=32, gs=None, g_idx=FAKE)) == UNSUP
+    w = _wq(g_idx=FAKE, k_perm=FAKE, **g)
+    f = L.moe_forward(FAKE, FAKE, 8, 32, 4, 2880, 2880, 0, None, 1, ctypes.byref(w),
+                      ctypes.byref(w), 0, 1.702, 1.0, 7.0, 1, FAKE * 16, 1 << 40, FAKE, None)
+    assert f == UNSUP                                    # sorted weights carry no group map
 
 
 def test_forward_rejects(L):

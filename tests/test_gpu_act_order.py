@@ -19,7 +19,7 @@ from oracle import moe as O
 pytestmark = pytest.mark.gpu
 
 M = pytest.importorskip("bit_weight_expert_amd")
-from gpu_util import (assert_rows_close, decode_policy, gpu_forward, host_bf16,  # noqa: E402
+from gpu_util import (assert_rows_close, gpu_forward, host_bf16,  # noqa: E402
                       upload)
 
 
@@ -117,8 +117,7 @@ def test_forward_act_order(act, T, which, policy):
     if L.w2.g_idx is not None:
         D["w2"] = prepare(L.w2, D["w2"])
     print(f"act-order forward {act} T={T} {which} {policy}", flush=True)
-    with decode_policy(policy):
-        out = gpu_forward(L, D)
+    out = gpu_forward(L, D, kernel=policy)
     assert_rows_close(host_bf16(out), O.forward(L)["out"], what=f"act-order {act} T{T} {which}")
 
 

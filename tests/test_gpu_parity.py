@@ -17,11 +17,11 @@ from oracle import moe as O
 pytestmark = pytest.mark.gpu
 
 M = pytest.importorskip("bit_weight_expert_amd")
-from gpu_util import (TOL, assert_rows_close, decode_policy, dev_bf16, gpu_forward,  # noqa: E402
-                      host_bf16, upload, upload_weights)
+from gpu_util import (TOL, assert_rows_close, assert_untouched, dev_bf16, gpu_forward,  # noqa: E402
+                      host_bf16, poisoned, upload, upload_weights)
 
-# "auto" takes the split-K kernel at these small sizes; "wide" forces the
-# 128-column kernel (both serve 16- and 32-row blocks).
+# The kernel for 16/32-row blocks ("auto" takes the split-K kernel at these
+# small sizes, "wide" forces the 128-column kernel).
 POLICIES = ["auto", "wide"]
 
 
@@ -140,11 +140,31 @@ def test_align_skewed_routing_full_size():
 
 
 # -------------------------------------------------------------------- GEMMs --
+# Every GEMM output starts as 0xFF bytes (bf16 NaN): covered rows must come
+# back finite and within tolerance, rows no block covers must stay untouched.
 
 def _small(fmt, act="swigluoai", E=4, k=2, H=320, I=192, T=13, seed=21, **kw):
     route = "sigmoid_bias" if act == "relu2" else "softmax"
     return S.make_layer(E=E, top_k=k, H=H, I=I, fmt=fmt, act=act, route=route, T=T, seed=seed,
                         router_bias_std=0.1 if route == "sigmoid_bias" else 0.0, **kw)
+
+
+def _dev_align(si, ei, npp):
+    return tuple(torch.from_numpy(a).cuda() for a in (si, ei, np.array([npp], np.int32)))
+
+
+def _gemm1(D, L, act, dsi, dei, dnpp, B, kernel, n_rows, topk_w=None, w13=None):
+    n_out = L.w13.N // 2 if act == "swigluoai" else L.w13.N
+    out = poisoned((n_rows, n_out))
+    return M.moe_w4a16_gemm1(D["x"], L.top_k, D["w13"] if w13 is None else w13, act, L.alpha,
+                             L.beta, L.limit, dsi, dei, dnpp, B, out=out, topk_w=topk_w,
+                             kernel=kernel)
+
+
+def _gemm2(a, w2, tw, mul, dsi, dei, dnpp, B, kernel, top_k=1):
+    out = poisoned((a.shape[0] * top_k, w2.N))
+    return M.moe_w4a16_gemm2(a, w2, tw, mul, dsi, dei, dnpp, B, out=out, top_k=top_k,
+                             kernel=kernel)
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "gptq"])
@@ -156,11 +176,9 @@ def test_gemm1_parity(fmt, act, B, policy):
     ids, w = O.route(L)
     si, ei, npp = O.align(ids, L.E, B)
     ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, act, L.alpha, L.beta, L.limit, si, ei, npp, B)
-    dsi, dei, dnpp = (torch.from_numpy(a).cuda() for a in (si, ei, np.array([npp], np.int32)))
-    with decode_policy(policy):
-        out = M.moe_w4a16_gemm1(D["x"], L.top_k, D["w13"], act, L.alpha, L.beta, L.limit, dsi,
-                                dei, dnpp, B)
+    out = _gemm1(D, L, act, *_dev_align(si, ei, npp), B, policy, L.T * L.top_k)
     assert_rows_close(host_bf16(out), ref, rows=cov, what=f"gemm1 {fmt} {act} B{B} {policy}")
+    assert_untouched(out, cov, "gemm1")
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "gptq"])
@@ -176,17 +194,38 @@ def test_gemm2_parity_and_mul_flag(fmt, B, policy):
     a_bits = S.f32_to_bf16_bits(rng.standard_normal((n, L.I)).astype(np.float32))
     tw = w.reshape(-1).astype(np.float32)
     ref1, cov = O.gemm2(a_bits, n, L.w2, tw, True, si, ei, npp, B)
-    dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
+    da = _dev_align(si, ei, npp)
     a = dev_bf16(a_bits)
     dtw = torch.from_numpy(tw).cuda()
-    with decode_policy(policy):
-        y1 = M.moe_w4a16_gemm2(a, D["w2"], dtw, True, dsi, dei, dnpp, B)
-        y0 = M.moe_w4a16_gemm2(a, D["w2"], dtw, False, dsi, dei, dnpp, B)
+    y1 = _gemm2(a, D["w2"], dtw, True, *da, B, policy)
+    y0 = _gemm2(a, D["w2"], dtw, False, *da, B, policy)
     assert_rows_close(host_bf16(y1), ref1, rows=cov, what=f"gemm2 {fmt} B{B} {policy}")
+    assert_untouched(y1, cov, "gemm2")
     # forensic check: the multiplier each row received is its own weight
     g1, g0 = host_bf16(y1), host_bf16(y0)
-    ratio = (g1 * g0).sum(1) / np.maximum((g0 * g0).sum(1), 1e-30)
-    np.testing.assert_allclose(ratio[cov], tw[cov], rtol=5e-3)
+    ratio = (g1[cov] * g0[cov]).sum(1) / np.maximum((g0[cov] * g0[cov]).sum(1), 1e-30)
+    np.testing.assert_allclose(ratio, tw[cov], rtol=5e-3)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "gptq"])
+@pytest.mark.parametrize("B,policy", [(16, "splitk"), (16, "wide"), (64, "auto")])
+def test_gemm2_top_k_shares_rows(fmt, B, policy):
+    """GEMM2 with top_k > 1: row f reads A row f // top_k (as GEMM1 does) and
+    takes its own slot's routing weight; equal to the top_k = 1 view on the
+    repeated rows."""
+    L = _small(fmt, E=5, k=3, T=17)
+    D = upload(L)
+    ids, w = O.route(L)
+    si, ei, npp = O.align(ids, L.E, B)
+    rng = np.random.default_rng(13)
+    a_bits = S.f32_to_bf16_bits(rng.standard_normal((L.T, L.I)).astype(np.float32))
+    tw = w.reshape(-1).astype(np.float32)
+    n = L.T * L.top_k
+    ref, cov = O.gemm2(np.repeat(a_bits, L.top_k, axis=0), n, L.w2, tw, True, si, ei, npp, B)
+    y = _gemm2(dev_bf16(a_bits), D["w2"], torch.from_numpy(tw).cuda(), True,
+               *_dev_align(si, ei, npp), B, policy, top_k=L.top_k)
+    assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 top_k={L.top_k} {fmt} B{B} {policy}")
+    assert_untouched(y, cov, "gemm2 top_k")
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
@@ -200,10 +239,10 @@ def test_gemm2_power_of_two_weights_bitwise(fmt):
     tw = np.ldexp(np.ones(n, np.float32), -(np.arange(n) % 5)).astype(np.float32)
     rng = np.random.default_rng(4)
     a = dev_bf16(S.f32_to_bf16_bits(rng.standard_normal((n, L.I)).astype(np.float32)))
-    dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
+    da = _dev_align(si, ei, npp)
     dtw = torch.from_numpy(tw).cuda()
-    y1 = M.moe_w4a16_gemm2(a, D["w2"], dtw, True, dsi, dei, dnpp, 16)
-    y0 = M.moe_w4a16_gemm2(a, D["w2"], dtw, False, dsi, dei, dnpp, 16)
+    y1 = _gemm2(a, D["w2"], dtw, True, *da, 16, "auto")
+    y0 = _gemm2(a, D["w2"], dtw, False, *da, 16, "auto")
     ext = (y0.float() * dtw[:, None]).to(torch.bfloat16)
     assert torch.equal(y1.view(torch.int16), ext.view(torch.int16))
 
@@ -219,10 +258,8 @@ def test_gemm1_weight_on_input(fmt, B, policy):
     si, ei, npp = O.align(ids, L.E, B)
     ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, "swigluoai", L.alpha, L.beta, L.limit, si, ei,
                        npp, B, topk_w_flat=tw)
-    dsi, dei, dnpp = (torch.from_numpy(a).cuda() for a in (si, ei, np.array([npp], np.int32)))
-    with decode_policy(policy):
-        out = M.moe_w4a16_gemm1(D["x"], L.top_k, D["w13"], "swigluoai", L.alpha, L.beta, L.limit,
-                                dsi, dei, dnpp, B, topk_w=torch.from_numpy(tw).cuda())
+    out = _gemm1(D, L, "swigluoai", *_dev_align(si, ei, npp), B, policy, L.T * L.top_k,
+                 topk_w=torch.from_numpy(tw).cuda())
     assert_rows_close(host_bf16(out), ref, rows=cov, what=f"gemm1 weight on input {fmt} B{B} {policy}")
 
 
@@ -235,8 +272,7 @@ def test_gemm1_weight_on_input(fmt, B, policy):
 def test_forward_parity_small(fmt, act, T, policy):
     L = _small(fmt, act, E=6, k=3, T=T, skew_std=1.0)
     D = upload(L)
-    with decode_policy(policy):
-        out = gpu_forward(L, D)
+    out = gpu_forward(L, D, kernel=policy)
     ref = O.forward(L)["out"]
     assert_rows_close(host_bf16(out), ref, what=f"forward {fmt} {act} T{T}")
 
@@ -256,7 +292,8 @@ def test_forward_config1_full():
     D = upload(L)
     out = gpu_forward(L, D)
     ref = O.forward(L)["out"]
-    assert_rows_close(host_bf16(out), ref, what=S.CONFIGS[1]["name"])
+    err = assert_rows_close(host_bf16(out), ref, what=S.CONFIGS[1]["name"])
+    print(f"config 1: max per-row rel err {err:.3e} over all {L.T} tokens", flush=True)
 
 
 def test_forward_deterministic_bitwise():
@@ -298,11 +335,10 @@ def test_gemm2_k_tails(K, B, policy):
     a_bits = S.f32_to_bf16_bits(rng.standard_normal((n, K)).astype(np.float32))
     tw = w.reshape(-1).astype(np.float32)
     ref, cov = O.gemm2(a_bits, n, L.w2, tw, True, si, ei, npp, B)
-    dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
-    with decode_policy(policy):
-        y = M.moe_w4a16_gemm2(dev_bf16(a_bits), D["w2"], torch.from_numpy(tw).cuda(), True, dsi,
-                              dei, dnpp, B)
+    y = _gemm2(dev_bf16(a_bits), D["w2"], torch.from_numpy(tw).cuda(), True,
+               *_dev_align(si, ei, npp), B, policy)
     assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 K={K} B{B} {policy}")
+    assert_untouched(y, cov, "gemm2 K tail")
 
 
 @pytest.mark.parametrize("fmt,K,N,group,B", [
@@ -323,8 +359,6 @@ def test_gemm2_tile_fallbacks(fmt, K, N, group, B, policy):
     n = T * k
     a_bits = S.f32_to_bf16_bits(rng.standard_normal((n, K)).astype(np.float32))
     ref, cov = O.gemm2(a_bits, n, w2, tw, True, si, ei, npp, B)
-    dsi, dei, dnpp = (torch.from_numpy(x).cuda() for x in (si, ei, np.array([npp], np.int32)))
-    with decode_policy(policy):
-        y = M.moe_w4a16_gemm2(dev_bf16(a_bits), upload_weights(w2), torch.from_numpy(tw).cuda(),
-                              True, dsi, dei, dnpp, B)
+    y = _gemm2(dev_bf16(a_bits), upload_weights(w2), torch.from_numpy(tw).cuda(), True,
+               *_dev_align(si, ei, npp), B, policy)
     assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 {fmt} K={K} N={N} B{B} {policy}")

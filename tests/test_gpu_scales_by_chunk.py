@@ -17,7 +17,8 @@ from oracle import moe as O
 pytestmark = pytest.mark.gpu
 
 M = pytest.importorskip("bit_weight_expert_amd")
-from gpu_util import assert_rows_close, gpu_forward, host_bf16, upload  # noqa: E402
+from gpu_util import (assert_rows_close, block_covering_tokens, gpu_forward,  # noqa: E402
+                      host_bf16, upload)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -126,7 +127,9 @@ def test_forward_scales_by_chunk_full_size(codes):
     out = gpu_forward(L, D)
     out2 = gpu_forward(L, D)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
-    toks = [0, 1, 7, 63, 511, 2047, 4095]
+    ids, _ = O.route(L)
+    toks = block_covering_tokens(ids, L.E, M.moe_forward_block_m(4096, L.top_k, L.E),
+                                 extra=(0, 1, 7, 63, 511, 2047, 4095))
     got = host_bf16(out)
     assert np.isfinite(got).all()
     assert_rows_close(got[toks], O.forward_tokens(L, toks), what="forward scales by chunk full size")
