@@ -13,4 +13,5 @@ from ._binding import (  # noqa: F401
     moe_forward_mxfp8, moe_forward_mxfp8_workspace_bytes, moe_mx_gemm1, moe_mx_gemm2,
     moe_mxfp8_quantize, mxfp8_lda, mxfp8_lds, moe_nvfp4_codes_by_chunk, moe_nvfp4_scales_by_chunk, moe_mxfp4_codes_by_chunk,
     moe_route, moe_route_align, moe_w4a16_gemm1, moe_w4a16_gemm2,
+    NOALLOC_SCRATCH_BYTES, moe_forward_noalloc,
 )

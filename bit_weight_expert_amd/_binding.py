@@ -84,6 +84,9 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.restype = i
         L.moe_forward_ex.argtypes = L.moe_forward.argtypes[:-1] + [i, vp]
         L.moe_forward_ex.restype = i
+        L.moe_forward_noalloc.argtypes = [vp, vp, i, i, i, i, i, i, vp, i, wq, wq, i, f, f, f, i,
+                                          vp, vp]
+        L.moe_forward_noalloc.restype = i
         L.moe_gptq_act_order_sort.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, vp]
         L.moe_gptq_act_order_sort.restype = i
         L.moe_permute_slots.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
@@ -507,4 +510,30 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, top_k: int, inter: int,
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _ptr(out), KERNEL[kernel], _stream()),
            "moe_forward_ex")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_FORWARD_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc(x: torch.Tensor, logits: torch.Tensor, top_k: int, inter: int,
+                        w13: QuantWeights, w2: QuantWeights, out: torch.Tensor,
+                        act: str = "swigluoai", route: str = "softmax", expert_bias=None,
+                        renormalize: bool = True, alpha: float = 1.702, beta: float = 1.0,
+                        limit: float = 7.0, mul_topk_weights: bool = True):
+    """moe_forward on the library's fixed per-GPU scratch (no workspace
+    argument; the library allocates nothing).  out bf16 [T, hidden] is the
+    caller's.  Raises MoeError (status 7) when the call needs more scratch
+    than NOALLOC_SCRATCH_BYTES."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(logits, torch.float32, "logits")
+    _dev(out, torch.bfloat16, "out")
+    T, hidden = x.shape
+    E = logits.shape[1]
+    s13, s2 = w13.struct(), w2.struct()
+    _check(lib().moe_forward_noalloc(_ptr(x), _ptr(logits), T, E, top_k, hidden, inter,
+                                     ROUTE[route], _ptr(expert_bias), int(bool(renormalize)),
+                                     ctypes.byref(s13), ctypes.byref(s2), ACT[act], alpha, beta,
+                                     limit, int(bool(mul_topk_weights)), _ptr(out), _stream()),
+           "moe_forward_noalloc")
     return out

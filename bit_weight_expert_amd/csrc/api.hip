@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/moe_w4a16.h"
 #include "common.h"
 
@@ -212,6 +214,7 @@ const char* moe_status_str(moe_status_t s) {
     case MOE_ERR_ALIGN: return "pointer not sufficiently aligned";
     case MOE_ERR_HIP: return "HIP launch error";
     case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_TOO_LARGE: return "problem needs more than the fixed scratch of moe_forward_noalloc";
   }
   return "unknown status";
 }
@@ -608,12 +611,15 @@ size_t moe_forward_workspace_bytes(int T, int E, int top_k, int hidden, int inte
   return ws_layout(T, E, top_k, hidden, inter, pick_block_m(T, top_k, E)).total;
 }
 
-moe_status_t moe_forward_ex(const uint16_t* x, const float* logits, int T, int E, int top_k,
-                            int hidden, int inter, moe_route_t kind, const float* expert_bias,
-                            int renormalize, const moe_wq_t* w13, const moe_wq_t* w2, moe_act_t act,
-                            float alpha, float beta, float limit, int mul_topk_weights,
-                            void* workspace, size_t workspace_bytes, uint16_t* out,
-                            moe_kernel_t kernel, moe_stream_t stream) {
+}  // extern "C"
+
+// The layer on a given workspace (moe_forward_ex, moe_forward_noalloc).
+static moe_status_t forward_run(const uint16_t* x, const float* logits, int T, int E, int top_k,
+                                int hidden, int inter, moe_route_t kind, const float* expert_bias,
+                                int renormalize, const moe_wq_t* w13, const moe_wq_t* w2,
+                                moe_act_t act, float alpha, float beta, float limit,
+                                int mul_topk_weights, void* workspace, size_t workspace_bytes,
+                                uint16_t* out, moe_kernel_t kernel, moe_stream_t stream) {
   if (T < 0 || E <= 0 || E > kMaxE || top_k < 1 || top_k > E || top_k > kMaxTopK)
     return MOE_ERR_SHAPE;
   if ((long long)T * top_k >= (1LL << 24)) return MOE_ERR_SHAPE;
@@ -676,6 +682,63 @@ moe_status_t moe_forward_ex(const uint16_t* x, const float* logits, int T, int E
                         hidden, (int)kernel, s);
   if (e == hipSuccess) e = moe_launch_sum(yb, ids, T, top_k, hidden, E, out, s);
   return hip_status(e);
+}
+
+// Fixed scratch of moe_forward_noalloc: the same workspace moe_forward takes,
+// in one array per GPU (each GPU holds its own copy, from the library's load
+// until the process ends).  On the host `scratch` only stands in for the
+// device array; its device address comes from hipGetSymbolAddress, looked up
+// once per device, with that device current, and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[MOE_FORWARD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<uint8_t*> g_scratch[kMaxDevices];  // device address of `scratch`, per device
+
+// Device address of the current device's scratch (set up on the first call on
+// that device; later calls read the kept address).
+moe_status_t scratch_of_current_device(uint8_t** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  uint8_t* a = g_scratch[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+      return MOE_ERR_HIP;
+    a = static_cast<uint8_t*>(q);
+    g_scratch[dev].store(a, std::memory_order_release);  // the same address on every lookup
+  }
+  *p = a;
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_forward_ex(const uint16_t* x, const float* logits, int T, int E, int top_k,
+                            int hidden, int inter, moe_route_t kind, const float* expert_bias,
+                            int renormalize, const moe_wq_t* w13, const moe_wq_t* w2, moe_act_t act,
+                            float alpha, float beta, float limit, int mul_topk_weights,
+                            void* workspace, size_t workspace_bytes, uint16_t* out,
+                            moe_kernel_t kernel, moe_stream_t stream) {
+  return forward_run(x, logits, T, E, top_k, hidden, inter, kind, expert_bias, renormalize, w13, w2,
+                     act, alpha, beta, limit, mul_topk_weights, workspace, workspace_bytes, out,
+                     kernel, stream);
+}
+
+moe_status_t moe_forward_noalloc(const uint16_t* x, const float* logits, int T, int E, int top_k,
+                                 int hidden, int inter, moe_route_t kind, const float* expert_bias,
+                                 int renormalize, const moe_wq_t* w13, const moe_wq_t* w2,
+                                 moe_act_t act, float alpha, float beta, float limit,
+                                 int mul_topk_weights, uint16_t* out, moe_stream_t stream) {
+  uint8_t* ws = nullptr;
+  const moe_status_t st = scratch_of_current_device(&ws);
+  if (st != MOE_OK) return st;
+  const moe_status_t r = forward_run(x, logits, T, E, top_k, hidden, inter, kind, expert_bias,
+                                     renormalize, w13, w2, act, alpha, beta, limit,
+                                     mul_topk_weights, ws, MOE_FORWARD_NOALLOC_SCRATCH_BYTES, out,
+                                     MOE_KERNEL_AUTO, stream);
+  return r == MOE_ERR_WORKSPACE ? MOE_ERR_TOO_LARGE : r;
 }
 
 moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, int top_k,

@@ -18,8 +18,9 @@
  * - Every pointer argument is device memory owned by the caller (global
  *   memory of the GPU current on the calling thread), contiguous, row-major.
  *   The library allocates nothing, never synchronises, never reads device
- *   memory from the host and keeps no state between calls: all work is
- *   enqueued on `stream` (a hipStream_t; NULL is the default stream).
+ *   memory from the host and keeps no state between calls (one exception:
+ *   moe_forward_noalloc keeps its scratch array's address per device): all
+ *   work is enqueued on `stream` (a hipStream_t; NULL is the default stream).
  * - bf16 values are passed as uint16_t bit patterns.
  * - A "flat slot" is f = t*top_k + j (token t, choice j).  The padding id in
  *   sorted_ids is the sentinel size_m*top_k.
@@ -59,7 +60,8 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = 3, /* a format / activation / option combination that is not built */
   MOE_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned */
   MOE_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
-  MOE_ERR_WORKSPACE = 6    /* workspace smaller than moe_forward_workspace_bytes() */
+  MOE_ERR_WORKSPACE = 6,   /* workspace smaller than moe_forward_workspace_bytes() */
+  MOE_ERR_TOO_LARGE = 7    /* moe_forward_noalloc: the call needs more than its fixed scratch */
 } moe_status_t;
 
 /* 4-bit weight storage formats.
@@ -347,6 +349,27 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int T, int E, i
                          moe_act_t act, float alpha, float beta, float limit,
                          int mul_topk_weights, void* workspace, size_t workspace_bytes,
                          uint16_t* out, moe_stream_t stream);
+
+/* Size of the fixed scratch of moe_forward_noalloc, per GPU (64 MiB). */
+#define MOE_FORWARD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it.  The
+ * workspace is a fixed array in the library, MOE_FORWARD_NOALLOC_SCRATCH_BYTES
+ * per GPU, held by every GPU the library runs on until the process ends; the
+ * first call on a device looks up that device's copy (hipGetSymbolAddress) and
+ * keeps its address.  Calls whose moe_forward_workspace_bytes() exceeds the
+ * scratch return MOE_ERR_TOO_LARGE before anything is enqueued (for the
+ * gpt-oss-20b shape, E=32 top-4 2880/2880, up to about 1450 tokens).  The
+ * call allocates nothing; every call on one GPU uses that GPU's one array, so
+ * calls that overlap on one GPU (other streams, other threads) race: order
+ * them.  The caller still passes x, logits and out; everything else is as
+ * moe_forward (kernel choice automatic). */
+moe_status_t moe_forward_noalloc(const uint16_t* x, const float* logits, int T, int E, int top_k,
+                                 int hidden, int inter, moe_route_t kind, const float* expert_bias,
+                                 int renormalize, const moe_wq_t* w13, const moe_wq_t* w2,
+                                 moe_act_t act, float alpha, float beta, float limit,
+                                 int mul_topk_weights, uint16_t* out, moe_stream_t stream);
 
 /* moe_forward with the kernel for 16/32-row blocks chosen by the caller
  * (moe_kernel_t), for both GEMMs. */

@@ -13,7 +13,7 @@ from bit_weight_expert_amd._binding import _Wq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_w4a16.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, HIP, WS = range(7)
+OK, NULL, SHAPE, UNSUP, ALIGN, HIP, WS, TOO_LARGE = range(8)
 
 
 def _declared_functions():
@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for s in range(7):
+    for s in range(8):
         assert len(L.moe_status_str(s)) > 0
 
 
