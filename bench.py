@@ -1,21 +1,29 @@
 #!/usr/bin/env python3
 """Throughput of the fused W4A16 MoE layer on one MI355X.
 
-Workload: the gpt-oss-20b-shaped MoE layer -- E=32 experts, top-4, hidden =
-intermediate = 2880, NVFP4 (e2m1 + e4m3 scale per 16 + fp32 global scale)
-weights, per-expert biases, swigluoai, routing weight applied in GEMM2's
-epilogue -- on synthetic inputs (seeded; see synthetic/).  One step is one
-moe_forward call (route -> align -> GEMM1 -> GEMM2 -> sum) over a batch of T
-tokens with everything already resident in HBM.  The headline line is at
-T = 4096; the same JSON line carries the other token counts of the sweep.
+Headline workload: the gpt-oss-20b-shaped MoE layer -- E=32 experts, top-4,
+hidden = intermediate = 2880, NVFP4 (e2m1 + e4m3 scale per 16 + fp32 global
+scale) weights, per-expert biases, swigluoai, routing weight applied in
+GEMM2's epilogue -- on synthetic inputs (seeded; see synthetic/).  One step is
+one moe_forward call (route -> align -> GEMM1 -> GEMM2 -> sum) over a batch
+of T tokens with everything already resident in HBM.  The headline value is
+at T = 4096; the same JSON line carries the other token counts of the sweep
+and the other four workloads ("configs": the INT4-GPTQ g64 layer at T = 2048,
+the gpt-oss-120b-shaped MXFP4 layer with skewed routing at T in {1, 16, 128,
+1024, 8192}, the Nemotron-3-Nano-shaped ReLU^2 layer at T = 2048), each row
+with its roofline bound and fraction.
 
 Weight copies are rotated between calls so that no call finds its weights in
-the 256 MB last-level cache left behind by the previous one.  The weights are
-loaded as a user of the library loads them: the checkpoint bytes plus the
-NVFP4 scales and codes re-laid by K chunk (moe_nvfp4_scales_by_chunk and
-moe_nvfp4_codes_by_chunk, done once at load time; the token counts up to 64
-read the checkpoint codes).  --checkpoint-codes runs without the codes copy,
---checkpoint-scales without either.
+the 256 MB last-level cache left behind by the previous one (enough copies
+that the touched experts of the copies together exceed it).  The weights are
+loaded as a user of the library loads them: the checkpoint bytes plus, for
+NVFP4, the scales and codes re-laid by K chunk (moe_nvfp4_scales_by_chunk and
+moe_nvfp4_codes_by_chunk, done once at load time).
+
+The dominant kernel (GEMM1 at the headline size) is timed on its own with one
+HIP event pair around each launch, on the stream it is launched on; the mean
+launch duration gives roofline.achieved (the same quantity a kernel trace
+reports as the kernel's average duration).
 
 Prints ONE JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 
@@ -34,6 +42,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -44,6 +53,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+LLC_BYTES = 256 << 20        # MI355X last-level (Infinity) cache
 
 
 def log(msg: str) -> None:
@@ -51,7 +61,7 @@ def log(msg: str) -> None:
 
 
 def alg_bytes_per_expert(L) -> int:
-    """Bytes one touched expert must stream: 4-bit codes, scales, global scale, biases."""
+    """Bytes one touched expert must stream: 4-bit codes, scales, zeros, global scale, biases."""
     tot = 0
     for w in (L.w13, L.w2):
         tot += w.qweight[0].nbytes + w.scales[0].nbytes
@@ -65,21 +75,34 @@ def alg_bytes_per_expert(L) -> int:
 
 
 def algorithmic(L, T, ids):
-    """(bytes, flops) the layer must move / compute for T tokens with routing ids."""
+    """(bytes, flops, touched experts) the layer must move / compute for T tokens
+    with routing ids: the touched experts' weights, x, out and the logits."""
     touched = len(np.unique(ids[(ids >= 0) & (ids < L.E)]))
     nbytes = touched * alg_bytes_per_expert(L) + T * L.H * 2 * 2 + T * L.E * 4
-    n1 = L.N1
-    flops = 2 * T * L.top_k * L.H * (n1 + L.I)
+    flops = 2 * T * L.top_k * L.H * (L.N1 + L.I)
     return nbytes, flops, touched
 
 
 def gemm1_alg(L, T, ids):
+    """GEMM1 alone: touched experts' w13 codes, scales, bias, global scale; x in, act out."""
     touched = len(np.unique(ids))
     w = L.w13
-    b = touched * (w.qweight[0].nbytes + w.scales[0].nbytes + 4 + (w.bias[0].nbytes if w.bias is not None else 0))
+    b = touched * (w.qweight[0].nbytes + w.scales[0].nbytes + 4 +
+                   (w.bias[0].nbytes if w.bias is not None else 0))
     b += T * L.H * 2 + T * L.top_k * L.I * 2
     f = 2 * T * L.top_k * L.H * L.N1
     return b, f
+
+
+def roofline_row(L, T, ids, ms):
+    nb, fl, touched = algorithmic(L, T, ids)
+    t_hbm = nb / (HBM_PEAK_GBS * 1e9)
+    t_mfma = fl / (BF16_PEAK_TFLOPS * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    return dict(T=T, ms=ms, tokens_per_s=T / (ms * 1e-3), touched_experts=touched,
+                alg_bytes=nb, alg_flops=fl, GBps=nb / (ms * 1e-3) / 1e9,
+                TFLOPs=fl / (ms * 1e-3) / 1e12, bound=bound,
+                roofline_frac=max(t_hbm, t_mfma) / (ms * 1e-3))
 
 
 def profiled_traffic():
@@ -100,6 +123,16 @@ def profiled_traffic():
         return int(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def act_order_leg(args, time_calls):
@@ -228,6 +261,32 @@ def mxfp8_leg(args, time_calls):
                         "skewed routing), bf16 vs MXFP8 activations", "rows": rows}
 
 
+def upload_copies(L, n, chunked=True):
+    """n device copies of the layer's two weight families (the same bytes);
+    NVFP4 families also get the load-time copies by K chunk."""
+    import bit_weight_expert_amd as M
+    copies = []
+    for _ in range(n):
+        pair = []
+        for w in (L.w13, L.w2):
+            d = M.QuantWeights.from_arrays(w.fmt, w.group, w.N, w.K, w.qweight, w.scales, w.zeros,
+                                           w.global_scale, w.bias)
+            if chunked and w.fmt == "nvfp4" and w.K % 64 == 0:
+                d.scales_kc = M.moe_nvfp4_scales_by_chunk(d)
+                d.qweight_kc = M.moe_nvfp4_codes_by_chunk(d)
+            pair.append(d)
+        copies.append(tuple(pair))
+    return copies
+
+
+def copies_for(L, ids_small) -> int:
+    """Copies whose touched experts together exceed the last-level cache at the
+    smallest batch of a sweep (so every call streams its weights from HBM)."""
+    touched = max(1, len(np.unique(ids_small)))
+    per_copy = touched * alg_bytes_per_expert(L)
+    return int(min(8, max(2, -(-2 * LLC_BYTES // per_copy))))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,12 +296,16 @@ def main() -> int:
     ap.add_argument("--sweep", default="1,8,64,512,4096")
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens the oracle is timed on")
+    ap.add_argument("--cpu-runs", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay timings")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other four workloads (GPTQ, gpt-oss-120b MXFP4, Nemotron, tiny)")
+    ap.add_argument("--configs", default="3,4,5", help="the other workloads to time")
+    ap.add_argument("--kernels", action="store_true",
+                    help="also time GEMM1 and GEMM2 alone at every T of the headline sweep")
     ap.add_argument("--checkpoint-scales", action="store_true",
                     help="run on the checkpoint layout only (no scales or codes by K chunk)")
-    ap.add_argument("--checkpoint-codes", action="store_true",
-                    help="scales by K chunk, codes in the checkpoint layout only")
     ap.add_argument("--act-order", action="store_true",
                     help="also time the GPTQ layer with act-order weights (and its gather)")
     ap.add_argument("--act-order-tokens", default="1,64,2048")
@@ -266,45 +329,10 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
-
-    sweep = sorted(set(int(t) for t in args.sweep.split(",") if t) | {args.tokens})
-    t_max = max(sweep)
-    t0 = time.time()
-    L = S.make_config(2)
-    assert L.T >= t_max
-    log(f"generated the {S.CONFIGS[2]['name']} inputs in {time.time() - t0:.1f}s")
-
     dev = torch.device("cuda")
-    x = torch.from_numpy(L.x.view(np.int16)).to(dev).view(torch.bfloat16)
-    logits = torch.from_numpy(L.logits).to(dev)
-    copies = []
-    for r in range(args.copies):
-        w13 = M.QuantWeights.from_arrays(L.w13.fmt, L.w13.group, L.w13.N, L.w13.K, L.w13.qweight,
-                                         L.w13.scales, None, L.w13.global_scale, L.w13.bias)
-        w2 = M.QuantWeights.from_arrays(L.w2.fmt, L.w2.group, L.w2.N, L.w2.K, L.w2.qweight,
-                                        L.w2.scales, None, L.w2.global_scale, L.w2.bias)
-        if not args.checkpoint_scales:
-            # the load-time layout of the NVFP4 scales by K chunk (a copy of the
-            # same bytes), which the 64/128-row GEMM kernel streams with the codes
-            w13.scales_kc = M.moe_nvfp4_scales_by_chunk(w13)
-            w2.scales_kc = M.moe_nvfp4_scales_by_chunk(w2)
-            if not args.checkpoint_codes:
-                # and the codes: a second copy, read by the same kernel
-                w13.qweight_kc = M.moe_nvfp4_codes_by_chunk(w13)
-                w2.qweight_kc = M.moe_nvfp4_codes_by_chunk(w2)
-        copies.append((w13, w2))
-    ws = torch.empty((M.moe_forward_workspace_bytes(t_max, L.E, L.top_k, L.H, L.I),),
-                     dtype=torch.uint8, device=dev)
-    out = torch.empty((t_max, L.H), dtype=torch.bfloat16, device=dev)
-    torch.cuda.synchronize()
-
-    def fwd(T, i):
-        w13, w2 = copies[i % len(copies)]
-        M.moe_forward(x[:T], logits[:T], L.top_k, L.I, w13, w2, act=L.act, route=L.route,
-                      renormalize=L.renormalize, alpha=L.alpha, beta=L.beta, limit=L.limit,
-                      mul_topk_weights=L.mul_topk_weights, workspace=ws, out=out[:T])
 
     def time_calls(fn, steps, warmup):
+        """ms per call of `steps` back-to-back calls, bracketed by synchronisation."""
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -314,11 +342,72 @@ def main() -> int:
             fn(i)
         ev1.record()
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / steps  # ms per call
+        return ev0.elapsed_time(ev1) / steps
 
-    # routing ids of the batch (for the algorithmic byte counts: touched experts)
-    ids_all = M.moe_route(logits, L.top_k, L.route, None, L.renormalize)[0].cpu().numpy()
+    def time_launches(fn, steps, warmup):
+        """Mean duration (ms) of single launches, one event pair around each on the
+        current stream (the stream the library launches on)."""
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            fn(i)
+            b.record()
+        torch.cuda.synchronize()
+        d = [a.elapsed_time(b) for a, b in evs]
+        return sum(d) / len(d), statistics.median(d)
 
+    def layer_leg(L, ts, copies, steps, graph=False, mxfp8=False):
+        """Per-T rows of moe_forward over the layer's first T tokens."""
+        x = torch.from_numpy(L.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        logits = torch.from_numpy(L.logits).to(dev)
+        eb = None if L.expert_bias is None else torch.from_numpy(L.expert_bias).to(dev)
+        ids_all = M.moe_route(logits, L.top_k, L.route, eb, L.renormalize)[0].cpu().numpy()
+        tmax = max(ts)
+        ws = torch.empty((M.moe_forward_workspace_bytes(tmax, L.E, L.top_k, L.H, L.I),),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty((tmax, L.H), dtype=torch.bfloat16, device=dev)
+        rows = []
+        for T in ts:
+            def fwd(i, T=T):
+                w13, w2 = copies[i % len(copies)]
+                M.moe_forward(x[:T], logits[:T], L.top_k, L.I, w13, w2, act=L.act, route=L.route,
+                              expert_bias=eb, renormalize=L.renormalize, alpha=L.alpha,
+                              beta=L.beta, limit=L.limit, mul_topk_weights=L.mul_topk_weights,
+                              workspace=ws, out=out[:T])
+            ms = time_calls(fwd, steps if T == tmax else max(steps, 50), args.warmup)
+            r = roofline_row(L, T, ids_all[:T], ms)
+            r["block_m"] = M.moe_forward_block_m(T, L.top_k, L.E)
+            if graph:
+                graphs = []
+                for c in range(len(copies)):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        fwd(c)
+                    graphs.append(g)
+                g_ms = time_calls(lambda i: graphs[i % len(graphs)].replay(), max(steps, 50),
+                                  args.warmup)
+                del graphs
+                r["graph_ms"] = g_ms
+                r["graph_roofline_frac"] = r["roofline_frac"] * ms / g_ms
+            rows.append(r)
+            log(f"  T={T}: {ms * 1e3:.1f} us/step, {r['tokens_per_s']:.0f} tok/s, "
+                f"{r['GBps']:.0f} GB/s, {r['TFLOPs']:.1f} TFLOP/s, {r['bound']} roofline "
+                f"{r['roofline_frac'] * 100:.1f}% (block_m {r['block_m']}, "
+                f"{r['touched_experts']} experts)")
+        return rows, (x, logits, eb, ids_all)
+
+    # ---------------------------------------------------------------- headline
+    sweep = sorted(set(int(t) for t in args.sweep.split(",") if t) | {args.tokens})
+    t0 = time.time()
+    L = S.make_config(2)
+    assert L.T >= max(sweep)
+    log(f"generated the {S.CONFIGS[2]['name']} inputs in {time.time() - t0:.1f}s")
+    copies = upload_copies(L, args.copies, chunked=not args.checkpoint_scales)
+    torch.cuda.synchronize()
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -326,63 +415,80 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    log(f"{S.CONFIGS[2]['name']}:")
+    rows, (x, logits, _, ids_all) = layer_leg(L, sweep, copies, args.steps, graph=not args.no_graph)
+    results = {r["T"]: r for r in rows}
 
-    def graph_ms(T, steps):
-        """Per-call time of moe_forward replayed from hipGraphs (one graph per weight copy)."""
-        graphs = []
-        for r in range(len(copies)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                fwd(T, r)
-            graphs.append(g)
-        ms = time_calls(lambda i: graphs[i % len(graphs)].replay(), steps, args.warmup)
-        del graphs
-        return ms
+    def gemm_alone(T, which):
+        """(mean, median) launch ms of GEMM1 or GEMM2 alone at T, rotating copies."""
+        bm = M.moe_forward_block_m(T, L.top_k, L.E)
+        ids_t, w_t = M.moe_route(logits[:T], L.top_k, L.route, None, L.renormalize)
+        si, ei, npp = M.moe_align(ids_t, L.E, bm)
+        act_buf = torch.zeros((T * L.top_k, L.I), dtype=torch.bfloat16, device=dev)
+        y_buf = torch.empty((T * L.top_k, L.H), dtype=torch.bfloat16, device=dev)
+        tw = w_t.reshape(-1).contiguous()
+        if which == 1:
+            f = lambda i: M.moe_w4a16_gemm1(x[:T], L.top_k, copies[i % len(copies)][0], L.act,
+                                            L.alpha, L.beta, L.limit, si, ei, npp, bm, out=act_buf)
+        else:
+            f = lambda i: M.moe_w4a16_gemm2(act_buf, copies[i % len(copies)][1], tw, True, si, ei,
+                                            npp, bm, out=y_buf)
+        return time_launches(f, max(args.steps, 20), args.warmup)
 
-    results = {}
-    for T in sweep:
-        steps = args.steps if T == args.tokens else max(args.steps, 50)
-        ms = time_calls(lambda i: fwd(T, i), steps, args.warmup)
-        g_ms = None if args.no_graph else graph_ms(T, steps)
-        nb, fl, touched = algorithmic(L, T, ids_all[:T])
-        t_hbm = nb / (HBM_PEAK_GBS * 1e9)
-        t_mfma = fl / (BF16_PEAK_TFLOPS * 1e12)
-        bound = "hbm" if t_hbm >= t_mfma else "mfma"
-        results[T] = dict(T=T, ms=ms, tokens_per_s=T / (ms * 1e-3), touched_experts=touched,
-                          graph_ms=g_ms,
-                          graph_roofline_frac=None if g_ms is None else max(t_hbm, t_mfma) / (g_ms * 1e-3),
-                          alg_bytes=nb, alg_flops=fl, GBps=nb / (ms * 1e-3) / 1e9,
-                          TFLOPs=fl / (ms * 1e-3) / 1e12, bound=bound,
-                          roofline_frac=max(t_hbm, t_mfma) / (ms * 1e-3))
-        log(f"T={T}: {ms * 1e3:.1f} us/step (graph {('%.1f' % (g_ms * 1e3)) if g_ms else '-'}), "
-            f"{results[T]['tokens_per_s']:.0f} tok/s, "
-            f"{results[T]['GBps']:.0f} GB/s, {results[T]['TFLOPs']:.1f} TFLOP/s, "
-            f"{bound} roofline {results[T]['roofline_frac'] * 100:.1f}%")
-
-    # dominant kernel at the headline T: GEMM1, timed alone on the same stream
+    # dominant kernel at the headline T: GEMM1, each launch timed on its stream
     T = args.tokens
-    bm = M.moe_forward_block_m(T, L.top_k, L.E)
-    ids_t, w_t = M.moe_route(logits[:T], L.top_k, L.route, None, L.renormalize)
-    si, ei, npp = M.moe_align(ids_t, L.E, bm)
-    act_buf = torch.empty((T * L.top_k, L.I), dtype=torch.bfloat16, device=dev)
-
-    def g1(i):
-        w13 = copies[i % len(copies)][0]
-        M.moe_w4a16_gemm1(x[:T], L.top_k, w13, L.act, L.alpha, L.beta, L.limit, si, ei, npp, bm,
-                          out=act_buf)
-
-    g1_ms = time_calls(g1, args.steps, args.warmup)
+    g1_mean, g1_med = gemm_alone(T, 1)
     gb, gf = gemm1_alg(L, T, ids_all[:T])
     g_bound = "hbm" if gb / (HBM_PEAK_GBS * 1e9) >= gf / (BF16_PEAK_TFLOPS * 1e12) else "mfma"
     if g_bound == "mfma":
-        achieved, peak, unit = gf / (g1_ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+        achieved, peak, unit = gf / (g1_mean * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
-        achieved, peak, unit = gb / (g1_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
-    log(f"gemm1 alone at T={T}: {g1_ms * 1e3:.1f} us, {achieved:.1f} {unit} ({achieved / peak * 100:.1f}%)")
-
-    # headline: the timed K steps at T = args.tokens, bracketed by synchronisation
+        achieved, peak, unit = gb / (g1_mean * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    log(f"gemm1 alone at T={T}: mean launch {g1_mean * 1e3:.1f} us (median {g1_med * 1e3:.1f}), "
+        f"{achieved:.1f} {unit} ({achieved / peak * 100:.1f}%)")
+    kernels = None
+    if args.kernels:
+        kernels = []
+        for t in sweep:
+            m1, _ = gemm_alone(t, 1)
+            m2, _ = gemm_alone(t, 2)
+            b1, _ = gemm1_alg(L, t, ids_all[:t])
+            touched = len(np.unique(ids_all[:t]))
+            w2 = L.w2
+            b2 = touched * (w2.qweight[0].nbytes + w2.scales[0].nbytes + 4 +
+                            (w2.bias[0].nbytes if w2.bias is not None else 0)) + \
+                t * L.top_k * (L.I + L.H) * 2
+            kernels.append(dict(T=t, gemm1_us=m1 * 1e3, gemm1_alg_bytes=b1,
+                                gemm1_GBps=b1 / (m1 * 1e-3) / 1e9, gemm2_us=m2 * 1e3,
+                                gemm2_alg_bytes=b2, gemm2_GBps=b2 / (m2 * 1e-3) / 1e9))
+            log(f"  kernels T={t}: gemm1 {m1 * 1e3:.1f} us ({b1 / (m1 * 1e-3) / 1e9:.0f} GB/s), "
+                f"gemm2 {m2 * 1e3:.1f} us ({b2 / (m2 * 1e-3) / 1e9:.0f} GB/s)")
     head = results[args.tokens]
+    del copies
+    torch.cuda.empty_cache()
 
+    # ---------------------------------------------------------- other configs
+    configs = {}
+    if not args.no_configs:
+        for cfg in [int(c) for c in args.configs.split(",") if c]:
+            c = S.CONFIGS[cfg]
+            t0 = time.time()
+            Lc = S.make_config(cfg)
+            log(f"{c['name']} (generated in {time.time() - t0:.1f}s):")
+            ts = list(c["T"])
+            # copies: enough that the smallest batch's touched experts exceed the cache
+            lg = torch.from_numpy(Lc.logits[:min(ts)]).to(dev)
+            eb = None if Lc.expert_bias is None else torch.from_numpy(Lc.expert_bias).to(dev)
+            ids_small = M.moe_route(lg, Lc.top_k, Lc.route, eb, Lc.renormalize)[0].cpu().numpy()
+            cps = upload_copies(Lc, copies_for(Lc, ids_small))
+            crow, _ = layer_leg(Lc, ts, cps, args.steps)
+            configs[f"config{cfg}"] = {"workload": c["name"], "weight_copies_rotated": len(cps),
+                                       "rows": [{k: (round(v, 6) if isinstance(v, float) else v)
+                                                 for k, v in r.items()} for r in crow]}
+            del cps, Lc
+            torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import moe as O
@@ -391,14 +497,21 @@ def main() -> int:
             blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
         except Exception:  # pragma: no cover
             blas_threads = 1
-        n = min(args.cpu_sample, T)
-        t0 = time.time()
-        O.forward(L.take(n))
-        dt = time.time() - t0
+        n = min(args.cpu_sample, args.tokens)
+        Ls = L.take(n)
+        times = []
+        for _ in range(max(1, args.cpu_runs)):
+            t0 = time.time()
+            O.forward(Ls)
+            times.append(time.time() - t0)
+        dt = statistics.median(times)
         cpu = {"value": n / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-               "sample": f"first {n} tokens of the T={T} batch, whole layer (route, align, float64 "
-                         f"dequant of every touched expert, both GEMMs, sum); {dt:.1f}s wall"}
-        log(f"oracle: {n} tokens in {dt:.1f}s")
+               "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+               "runs_s": [round(t, 3) for t in times],
+               "sample": f"first {n} tokens of the T={args.tokens} batch of the headline workload, "
+                         f"whole layer (route, align, float64 dequant of every touched expert, "
+                         f"both GEMMs, sum); median of {len(times)} runs; BLAS threads = cores"}
+        log(f"oracle: {n} tokens, median {dt:.1f}s of {len(times)} runs, {blas_threads} BLAS threads")
 
     act_order = act_order_leg(args, time_calls) if args.act_order else None
     mxfp8 = mxfp8_leg(args, time_calls) if args.mxfp8 else None
@@ -419,19 +532,23 @@ def main() -> int:
         "config": {"workload": "gpt-oss-20b-shaped MoE layer: E=32, top_k=4, hidden=2880, "
                                "intermediate=2880, NVFP4 g16 weights + bias, swigluoai, "
                                f"T={args.tokens} tokens",
-                   "tokens": args.tokens, "block_m": bm, "weight_copies_rotated": args.copies,
-                   "nvfp4_scales_by_chunk": not args.checkpoint_scales,
-                   "nvfp4_codes_by_chunk": not (args.checkpoint_scales or args.checkpoint_codes)},
-        "roofline": {"kernel": "grouped_gemm (GEMM1, w13 + swigluoai)", "bound": g_bound,
-                     "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
-                     "traffic": profiled_traffic(), "kernel_us": g1_ms * 1e3},
+                   "tokens": args.tokens, "block_m": head["block_m"],
+                   "weight_copies_rotated": args.copies,
+                   "nvfp4_by_chunk_copies": not args.checkpoint_scales},
+        "roofline": {"kernel": "grouped GEMM1 (w13 + bias + swigluoai), gemm_prefill_kernel",
+                     "bound": g_bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": profiled_traffic(),
+                     "kernel_us": g1_mean * 1e3, "kernel_us_median": g1_med * 1e3,
+                     "alg_bytes": gb, "alg_flops": gf},
         "layer_roofline": {"bound": head["bound"], "frac": head["roofline_frac"],
                            "GBps": head["GBps"], "TFLOPs": head["TFLOPs"]},
         "cpu_baseline": cpu,
-        "act_order": act_order,
-        "mxfp8": mxfp8,
         "sweep": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in results[t].items()}
                   for t in sweep],
+        "configs": configs or None,
+        "kernels": kernels,
+        "act_order": act_order,
+        "mxfp8": mxfp8,
     }
     print(json.dumps(line), flush=True)
     return 0
