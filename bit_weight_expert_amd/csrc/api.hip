@@ -22,7 +22,10 @@ extern "C" hipError_t moe_launch_route_align(const float*, int, int, int, int, c
 extern "C" hipError_t moe_launch_gemm(int, int, int, int, const uint16_t*, int, int, int, int, int,
                                       const moe::WeightArgs*, const int32_t*, const int32_t*,
                                       const int32_t*, const float*, int, float, float, float,
-                                      uint16_t*, int, int, hipStream_t);
+                                      uint16_t*, int, int, const int2*, const int32_t*, hipStream_t);
+extern "C" int moe_prefill_tiles_ok(int, int, int, int);
+extern "C" hipError_t moe_launch_tile_plan(const int32_t*, const int32_t*, int, int, int32_t*, int2*,
+                                           int32_t*, hipStream_t);
 extern "C" hipError_t moe_launch_sum(const uint16_t*, const int32_t*, int, int, int, int,
                                      uint16_t*, hipStream_t);
 extern "C" hipError_t moe_launch_gptq_sort(const int32_t*, const int32_t*, int, int, int, int,
@@ -139,12 +142,17 @@ int pick_block_m(int T, int top_k, int E) {
 }
 
 struct WsLayout {
-  size_t ids, w, sorted, eids, npp, cnt, act, y, total;
+  size_t ids, w, sorted, eids, npp, cnt, dec, tiles, ntiles, act, y, total;
 };
 
 // Slots from which moe_forward sorts with the multi-workgroup kernels
 // (measured: the single workgroup is as fast up to about this size).
 constexpr int kAlignLargeMin = 8192;
+// Mixed tiling (few slots per expert on average): from this many slots on,
+// experts' full 128-row runs go to the streaming kernel (a tile list made on
+// the device after the sort) and the rest to the 16/32-row decode kernels.
+constexpr int kMixedMinSlots = 1024;
+constexpr int kMixedMaxBlocks = 4096;  // the plan kernel's block table in LDS
 
 WsLayout ws_layout(int T, int E, int top_k, int hidden, int inter, int block_m) {
   WsLayout L;
@@ -157,6 +165,9 @@ WsLayout ws_layout(int T, int E, int top_k, int hidden, int inter, int block_m) 
   L.eids = o; o = round_up(o + (cap / block_m) * 4, 256);
   L.npp = o; o = round_up(o + 4, 256);
   L.cnt = o; o = round_up(o + (size_t)moe::kAlignGroups * E * 4, 256);
+  L.dec = o; o = round_up(o + (cap / block_m) * 4, 256);           // mixed tiling: decode blocks
+  L.tiles = o; o = round_up(o + (cap / 128 + 1) * 8, 256);         // mixed tiling: 128-row tiles
+  L.ntiles = o; o = round_up(o + 4, 256);
   L.act = o; o = round_up(o + n * (size_t)inter * 2, 256);
   L.y = o; o = round_up(o + n * (size_t)hidden * 2, 256);
   L.total = o;
@@ -334,7 +345,7 @@ moe_status_t moe_w4a16_gemm1_ex(const uint16_t* x, int size_m, int top_k, int K,
   return hip_status(moe_launch_gemm((int)w13->fmt, epi, block_m, cap, x, top_k, size_m * top_k, K, N, E,
                                     &W, sorted_ids, expert_ids, num_post_pad, topk_w,
                                     mul_topk_weights ? 1 : 0, alpha, beta, limit, out, out_ld,
-                                    (int)kernel, static_cast<hipStream_t>(stream)));
+                                    (int)kernel, nullptr, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_w4a16_gemm1(const uint16_t* x, int size_m, int top_k, int K, int N, int E,
@@ -368,7 +379,7 @@ moe_status_t moe_w4a16_gemm2_ex(const uint16_t* a, int size_m, int top_k, int K,
   const int cap = (int)moe_align_capacity(size_m, top_k, E, block_m);
   return hip_status(moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, a, top_k, size_m * top_k,
                                     K, N, E, &W, sorted_ids, expert_ids, num_post_pad, topk_w,
-                                    mul_topk_weights ? 1 : 0, 0.f, 0.f, 0.f, y, N, (int)kernel,
+                                    mul_topk_weights ? 1 : 0, 0.f, 0.f, 0.f, y, N, (int)kernel, nullptr, nullptr,
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -588,14 +599,14 @@ moe_status_t moe_forward_mxfp8(const uint16_t* x, const float* logits, int T, in
     if (e == hipSuccess)
       e = moe_launch_gemm((int)w13->fmt, epi, block_m, cap, yb, top_k, n, hidden, n1, E, &W13,
                           sorted, eids, npp, tw, 0, alpha, beta, limit, actb, inter,
-                          moe::KERNEL_AUTO, s);
+                          moe::KERNEL_AUTO, nullptr, nullptr, s);
     if (e == hipSuccess)
       e = moe_launch_mxfp8_quant(actb, n, inter, mx_lda(inter), mx_lds(inter), nullptr, nullptr,
                                  actb, s);
     if (e == hipSuccess)
       e = moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, actb, 1, n, inter, hidden, E,
                           &W2, sorted, eids, npp, tw, mul, 0.f, 0.f, 0.f, yb, hidden,
-                          moe::KERNEL_AUTO, s);
+                          moe::KERNEL_AUTO, nullptr, nullptr, s);
   }
   if (e == hipSuccess) e = moe_launch_sum(yb, ids, T, top_k, hidden, E, out, s);
   return hip_status(e);
@@ -659,6 +670,18 @@ static moe_status_t forward_run(const uint16_t* x, const float* logits, int T, i
 
   hipError_t e = route_and_sort(logits, T, E, top_k, (int)kind, expert_bias, renormalize ? 1 : 0,
                                 ids, tw, block_m, cap, sorted, eids, npp, reinterpret_cast<int32_t*>(ws + L.cnt), s);
+  // Mixed tiling: the 128-row tiles (prefill kernel, tile list) and the rest
+  // of the blocks (decode kernels, dec_eids: -1 for blocks in a tile).
+  const bool mixed = block_m <= 32 && n >= kMixedMinSlots && cap / block_m <= kMixedMaxBlocks &&
+                     moe_prefill_tiles_ok((int)w13->fmt, hidden, n1, w13->group_size) &&
+                     moe_prefill_tiles_ok((int)w2->fmt, inter, hidden, w2->group_size);
+  int32_t* dec_eids = reinterpret_cast<int32_t*>(ws + L.dec);
+  int2* tiles = reinterpret_cast<int2*>(ws + L.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
+  const int tile_cap = cap / 128 * 128;
+  if (e == hipSuccess && mixed)
+    e = moe_launch_tile_plan(eids, npp, block_m, cap / block_m, dec_eids, tiles, ntiles, s);
+  const int32_t* blk_eids = mixed ? dec_eids : eids;
   // Act-order families: GEMM1 reads one gathered input row per slot from the
   // y buffer (free until GEMM2), in the top_k = 1 view; GEMM2's input rows are
   // permuted in place.
@@ -670,16 +693,24 @@ static moe_status_t forward_run(const uint16_t* x, const float* logits, int T, i
     g1_topk = 1;
   }
   // routing weight on GEMM2's output rows (mode 1) or GEMM1's input rows (mode 2)
+  if (e == hipSuccess && mixed && tile_cap > 0)
+    e = moe_launch_gemm((int)w13->fmt, epi, 128, tile_cap, g1_in, g1_topk, n, hidden, n1, E, &W13,
+                        sorted, eids, npp, tw, mul_topk_weights == 2 ? 1 : 0, alpha, beta, limit,
+                        actb, inter, (int)kernel, tiles, ntiles, s);
   if (e == hipSuccess)
     e = moe_launch_gemm((int)w13->fmt, epi, block_m, cap, g1_in, g1_topk, n, hidden, n1, E, &W13,
-                        sorted, eids, npp, tw, mul_topk_weights == 2 ? 1 : 0, alpha, beta, limit,
-                        actb, inter, (int)kernel, s);
+                        sorted, blk_eids, npp, tw, mul_topk_weights == 2 ? 1 : 0, alpha, beta, limit,
+                        actb, inter, (int)kernel, nullptr, nullptr, s);
   if (e == hipSuccess && w2->k_perm != nullptr)
     e = moe_launch_permute_slots(actb, n, 1, inter, E, w2->k_perm, ids, actb, s);
+  if (e == hipSuccess && mixed && tile_cap > 0)
+    e = moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, 128, tile_cap, actb, 1, n, inter, hidden, E,
+                        &W2, sorted, eids, npp, tw, mul_topk_weights == 1 ? 1 : 0, 0.f, 0.f, 0.f,
+                        yb, hidden, (int)kernel, tiles, ntiles, s);
   if (e == hipSuccess)
     e = moe_launch_gemm((int)w2->fmt, moe::EPI_DOWN, block_m, cap, actb, 1, n, inter, hidden, E, &W2,
-                        sorted, eids, npp, tw, mul_topk_weights == 1 ? 1 : 0, 0.f, 0.f, 0.f, yb,
-                        hidden, (int)kernel, s);
+                        sorted, blk_eids, npp, tw, mul_topk_weights == 1 ? 1 : 0, 0.f, 0.f, 0.f, yb,
+                        hidden, (int)kernel, nullptr, nullptr, s);
   if (e == hipSuccess) e = moe_launch_sum(yb, ids, T, top_k, hidden, E, out, s);
   return hip_status(e);
 }

@@ -418,7 +418,25 @@ struct GemmArgs {
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
   const int32_t* num_post_pad;
+  // prefill kernel only, optional: a list of 128-row tiles (first row in
+  // sorted_ids, expert) with its length in n_tiles[0], instead of the
+  // aligned blocks (mixed tiling: an expert's full 128-row runs)
+  const int2* tiles;
+  const int32_t* n_tiles;
 };
+
+// First row (in sorted_ids) and expert of prefill tile mb: aligned block mb,
+// or entry mb of the tile list.
+__device__ __forceinline__ void tile_rows(const GemmArgs& ga, int mb, int bm, int& row0, int& e) {
+  if (ga.tiles != nullptr) {
+    const int2 t = ga.tiles[mb];
+    row0 = t.x;
+    e = t.y;
+  } else {
+    row0 = mb * bm;
+    e = ga.expert_ids[mb];
+  }
+}
 
 // A row of a sorted slot.  Padding slots read row 0 instead: their products
 // land only in accumulator rows that the epilogue never stores (an MFMA row
@@ -555,7 +573,7 @@ __device__ __forceinline__ void pf_barrier() {
 // same time on one XCD share both their weight tiles (the blocks of one
 // expert) and their A blocks (across column tiles) in that XCD's L2.
 __device__ __forceinline__ bool prefill_tile(const GemmArgs& a, int bm, int& mb, int& nt) {
-  const int nmb = min(a.num_post_pad[0] / bm, a.n_mblocks);
+  const int nmb = min(a.tiles != nullptr ? a.n_tiles[0] : a.num_post_pad[0] / bm, a.n_mblocks);
   const int total = nmb * a.n_ntiles;
   const int per_xcd = (total + 7) / 8;
   const int pid = blockIdx.x;
@@ -730,14 +748,21 @@ __device__ __forceinline__ void pf_read_b(PfB (&b)[NF], const uint8_t* bstage, c
   }
 }
 
+// Physical 16-byte slot of logical slot q in A row r of a 128-byte-row LDS
+// stage: q ^ ((r / 2) % 8).  A 16-byte read serves 16 lanes (16 rows) per LDS
+// cycle, and two rows fill the 64 banks; with this swizzle the 16 rows of a
+// cycle cover 16 distinct 4-bank groups (q ^ (r % 8) gave rows r and r + 8 the
+// same group: a two-way conflict on every A read).
+__device__ __forceinline__ int a_slot(int q, int r) { return q ^ ((r >> 1) & 7); }
+
 // A fragments of MFMA step s of a chunk: rows i*32 + c, k = 32h + 8s .. +8.
-// A rows are 128 bytes in LDS, 16-byte slot q of row r stored at q ^ (r % 8).
+// A rows are 128 bytes in LDS, logical 16-byte slot q of row r stored at a_slot(q, r).
 template <int MI>
 __device__ __forceinline__ void pf_read_a(uint4 (&a)[MI], const uint8_t* astage, int c, int h, int s) {
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int r = i * 32 + c;
-    a[i] = *reinterpret_cast<const uint4*>(astage + r * 128 + 16 * ((4 * h + s) ^ (r & 7)));
+    a[i] = *reinterpret_cast<const uint4*>(astage + r * 128 + 16 * a_slot(4 * h + s, r));
   }
 }
 
@@ -957,26 +982,27 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
 
   // slot ids of the A rows this lane copies, requested before anything waits:
   // DMA instruction q = 4p + wave covers rows 8q .. 8q+7, lane l row 8q + l/8
+  int rowb, e;  // the tile's first row in sorted_ids, its expert
+  tile_rows(ga, mb, BM, rowb, e);
   int sid[P::kAIssue];
 #pragma unroll
-  for (int p = 0; p < P::kAIssue; ++p) sid[p] = ga.sorted_ids[mb * BM + 8 * (4 * p + wave_u) + (lane >> 3)];
-  const int e = ga.expert_ids[mb];
+  for (int p = 0; p < P::kAIssue; ++p) sid[p] = ga.sorted_ids[rowb + 8 * (4 * p + wave_u) + (lane >> 3)];
   if (e < 0 || e >= ga.E) return;
   // slot id of block row tid, for the epilogue: requested now, first used
   // after the K loop, so its latency hides behind the loop
-  const int row_sid = ga.sorted_ids[mb * BM + min(tid, BM - 1)];
+  const int row_sid = ga.sorted_ids[rowb + min(tid, BM - 1)];
 
   const int nt0 = nt * P::BN;             // first weight row of the tile
   const int rows = min(P::BN, N - nt0);   // valid weight rows of the tile
   const int n0 = nt0 + wave_u * NF * 32;  // first weight row of this wave
 
-  // DMA sources.  A: lane l of instruction q fetches logical slot
-  // (l%8) ^ (row%8) of row 8q + l/8 (see pf_read_a).
+  // DMA sources.  A: lane l of instruction q writes physical slot l%8 of row
+  // r = 8q + l/8, so it fetches logical slot a_slot(l%8, r) (see pf_read_a).
   const uint16_t* arow[P::kAIssue];
 #pragma unroll
   for (int p = 0; p < P::kAIssue; ++p) {
     const int r = 8 * (4 * p + wave_u) + (lane >> 3);
-    arow[p] = a_row(ga, sid[p]) + 8 * ((lane & 7) ^ (r & 7));
+    arow[p] = a_row(ga, sid[p]) + 8 * a_slot(lane & 7, r);
   }
   // Weight codes.  NVFP4/MXFP4: instruction q fills 32-row block q, lane l
   // the half l/32 of tile row pf_brow(q, l) (rows past N re-read the last
@@ -1147,7 +1173,7 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
   wait_vmcnt<0>();
   const bool poison = gidx_bad<FMT>(W, e, K, tid, 256 * RS * KS);
 
-  const int row0 = mb * BM + rpart * MI * 32;
+  const int row0 = rowb + rpart * MI * 32;
   if (K % kPfBK && kp == 0) pf_tail32<FMT, EPI, MI, NF>(acc, ga, W, e, row0, n0, c, h, nchunks * kPfBK);
 
   // (slot id, routing weight) of every block row, in the last KB of LDS
@@ -1206,7 +1232,7 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
     if (n0 >= N) return;
     EpiArgs a = ea;
     a.row0 = row0 + kp * HM * 32;
-    epilogue32<EPI, FMT, HM, NF>(acch, a, W, e, n0, lane, rowtab, a.row0 - mb * BM, poison);
+    epilogue32<EPI, FMT, HM, NF>(acch, a, W, e, n0, lane, rowtab, a.row0 - rowb, poison);
     return;
   }
 
@@ -1214,7 +1240,7 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
   if (n0 >= N) return;
   EpiArgs a = ea;
   a.row0 = row0;
-  epilogue32<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane, rowtab, row0 - mb * BM, poison);
+  epilogue32<EPI, FMT, MI, NF>(acc, a, W, e, n0, lane, rowtab, row0 - rowb, poison);
 }
 
 // --------------------------------------------------------------------------
@@ -1924,6 +1950,15 @@ static void launch_decode(GemmArgs ga, const WeightArgs& W, const EpiArgs& ea, i
   launch_decode_nf<FMT, EPI, MI, 2>(ga, W, ea, (long)blocks_est * ((ga.N + 31) / 32), st);
 }
 
+// The streaming (prefill) kernel's tiles fit: the tile's scales for the whole
+// K in its LDS (the resident-scale variant), GPTQ zero-point rows in 16-byte
+// pieces.  Otherwise 64/128-row blocks run the split-K kernel on 32-row
+// sub-blocks.
+static inline bool prefill_fits(int fmt, int K, int N, int group) {
+  return pf_scale_bytes(fmt, K, group, Pf<128, 2>::BN) <= kPfScaleBytes &&
+         !(fmt == FMT_GPTQ && N % 32 != 0);
+}
+
 template <int FMT, int EPI>
 static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs& W, EpiArgs ea,
                              int kernel, hipStream_t st) {
@@ -1938,8 +1973,8 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
       launch_decode<FMT, EPI, 2>(ga, W, ea, blocks_est, kernel, st);
   } else {
     // widest tile whose scales fit the kernel's LDS; otherwise the split-K kernel
-    if (pf_scale_bytes(FMT, ga.K, W.group, Pf<128, 2>::BN) > kPfScaleBytes ||
-        (FMT == FMT_GPTQ && ga.N % 32 != 0)) {
+    if (!prefill_fits(FMT, ga.K, ga.N, W.group)) {
+      if (ga.tiles != nullptr) return hipErrorInvalidValue;
       // very long K (scales too large for LDS), or GPTQ zero-point rows that
       // are not 16-byte multiples: the split-K kernel over 32-row sub-blocks
       // of the aligned blocks
@@ -1999,7 +2034,7 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
 // Tile: BM rows x 256 weight rows, four waves side by side over the weight
 // rows (two 32-row fragments each), all BM rows per wave.  K moves in chunks
 // of 128 through a 3-deep LDS ring filled by LDS-DMA (A: 128 bytes per row,
-// 16-byte slot q of row r at q ^ (r % 8); weights: 64 bytes per row at the
+// 16-byte slot q of row r at a_slot(q, r); weights: 64 bytes per row at the
 // row's position, slot q at q ^ ((position / 4) % 4)); both scale tiles stay
 // in LDS for the whole K.
 
@@ -2077,8 +2112,8 @@ __device__ __forceinline__ void mx_read(MxOps<MI, NF>& o, const uint8_t* stg, in
   for (int i = 0; i < MI; ++i) {
     const int r = r0 + 32 * i + c;
     const uint8_t* row = stg + r * 128;
-    const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * ((4 * ST + g) ^ (r & 7)));
-    const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * ((4 * ST + 2 + g) ^ (r & 7)));
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * a_slot(4 * ST + g, r));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * a_slot(4 * ST + 2 + g, r));
     o.a[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
 }
@@ -2151,14 +2186,15 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA m
   const int rows = min(P::BN, N - nt0);
   const int n0 = nt0 + wave_u * NF * 32;
 
-  // DMA sources.  A: lane l fetches logical slot (l%8) ^ (row%8) of row 8q + l/8.
+  // DMA sources.  A: lane l writes physical slot l%8 of row r = 8q + l/8, so it
+  // fetches logical slot a_slot(l%8, r).
   const uint8_t* arow[P::kAIssue];
 #pragma unroll
   for (int p = 0; p < P::kAIssue; ++p) {
     const int r = 8 * (NW * p + wave) + (lane >> 3);
     const int s = sid[p];
     const int row = s < ga.n_slots ? (int)(((uint64_t)(uint32_t)s * ga.a_mul) >> 32) : 0;
-    arow[p] = ma.codes + (size_t)row * ma.lda + 16 * ((lane & 7) ^ (r & 7));
+    arow[p] = ma.codes + (size_t)row * ma.lda + 16 * a_slot(lane & 7, r);
   }
   // Weights: instruction q fills positions 16q .. 16q+15, lane l the physical
   // slot l%4 of position 16q + l/4 (rows past N re-read the last row; offsets
@@ -2298,15 +2334,20 @@ static hipError_t launch_fmt(int epi, int block_m, int cap, const GemmArgs& ga, 
 
 // Launch one grouped GEMM.  cap = capacity of sorted_ids (the grid covers every
 // block that could be used; blocks past num_post_pad exit at once).
+// tiles (optional, block_m = 128): the streaming kernel over a list of
+// 128-row tiles with its length in n_tiles[0] (room for cap / 128 entries)
+// instead of the aligned blocks; moe_prefill_tiles_ok must hold.
 extern "C" hipError_t moe_launch_gemm(int fmt, int epi, int block_m, int cap, const uint16_t* A,
                                       int a_div, int n_slots, int K, int N, int E,
                                       const moe::WeightArgs* W, const int32_t* sid,
                                       const int32_t* eid, const int32_t* npp, const float* tw,
                                       int mul, float alpha, float beta, float limit, uint16_t* out,
-                                      int out_ld, int kernel, hipStream_t st) {
+                                      int out_ld, int kernel, const int2* tiles,
+                                      const int32_t* n_tiles, hipStream_t st) {
   if (cap / block_m == 0) return hipSuccess;
+  if (tiles != nullptr && block_m != 128) return hipErrorInvalidValue;
   const uint64_t a_mul = ((1ull << 32) + (uint64_t)a_div - 1) / (uint64_t)a_div;
-  moe::GemmArgs ga{A, a_div, a_mul, n_slots, K, N, E, 0, 0, 1, block_m, sid, eid, npp};
+  moe::GemmArgs ga{A, a_div, a_mul, n_slots, K, N, E, 0, 0, 1, block_m, sid, eid, npp, tiles, n_tiles};
   moe::EpiArgs ea{sid, 0, n_slots, N, tw, mul, alpha, beta, limit, out, out_ld};
   switch (fmt) {
     case moe::FMT_NVFP4: return moe::launch_fmt<moe::FMT_NVFP4>(epi, block_m, cap, ga, *W, ea, kernel, st);
@@ -2349,6 +2390,10 @@ extern "C" hipError_t moe_launch_gemm_mx(int epi, int block_m, int cap, const ui
   }
 #undef MOE_MX_LAUNCH
   return hipGetLastError();
+}
+
+extern "C" int moe_prefill_tiles_ok(int fmt, int K, int N, int group) {
+  return moe::prefill_fits(fmt, K, N, group) ? 1 : 0;
 }
 
 extern "C" hipError_t moe_launch_sum(const uint16_t* y, const int32_t* ids, int T, int top_k, int H,

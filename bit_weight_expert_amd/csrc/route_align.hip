@@ -484,6 +484,139 @@ __global__ void __launch_bounds__(kAlignThreads) route_align_kernel(
   align_block(lds_ids, T * top_k, E, block_m, cap, sorted_ids, expert_ids, num_post_pad, L);
 }
 
+// Route + align for at most 16 tokens, 64 slots and 128 experts in one small
+// workgroup (one wave per token): each wave routes its token (ids into LDS),
+// then wave 0 sorts with one slot per lane -- equal ids found by ballots over the id
+// bits (lanes with an equal id agree on every bit), each group's last lane
+// writes its expert's count, the padded offsets are one wave-wide scan over
+// the experts (two per lane), and each slot lands at its expert's offset plus
+// its rank among the lanes of its group, which are in slot order.  Same
+// outputs as route_kernel + align_kernel, bit for bit (the routing is the same
+// code; the sort's result is unique).
+constexpr int kSmallSlots = 64;
+constexpr int kSmallMaxE = 128;
+
+template <int KIND>
+__global__ void __launch_bounds__(1024) route_align_small_kernel(
+    const float* __restrict__ logits, int T, int E, int top_k, const float* __restrict__ ebias,
+    int renorm, int32_t* __restrict__ ids, float* __restrict__ w, int block_m, int cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ num_post_pad) {
+  __shared__ int32_t lds_ids[kSmallSlots];
+  __shared__ int32_t cnt[kSmallMaxE];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (wid < T) route_wave<KIND>(logits, wid, E, top_k, ebias, renorm, ids, w, lds_ids);
+  if (wid == 0) {
+    cnt[lane] = 0;
+    cnt[lane + 64] = 0;
+  }
+  __syncthreads();
+  if (wid != 0) return;
+  const int n = T * top_k;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  int e = lane < n ? lds_ids[lane] : -1;
+  const bool valid = e >= 0 && e < E;
+  if (!valid) e = 0;
+  const unsigned long long same = match_expert(e, valid, nbits);
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(same & lt);
+  if (valid && ((same >> lane) >> 1) == 0ull) cnt[e] = __popcll(same);  // group's last lane
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the counts are in LDS
+  // experts lane and lane + 64: padded counts, exclusive offsets in expert order
+  const int c0 = lane < E ? cnt[lane] : 0, c1 = lane + 64 < E ? cnt[lane + 64] : 0;
+  const int p0 = (c0 + block_m - 1) / block_m * block_m, p1 = (c1 + block_m - 1) / block_m * block_m;
+  int i0 = p0, i1 = p1;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u0 = __shfl_up(i0, o), u1 = __shfl_up(i1, o);
+    if (lane >= o) {
+      i0 += u0;
+      i1 += u1;
+    }
+  }
+  const int tot0 = __shfl(i0, 63);
+  const int off0 = i0 - p0, off1 = tot0 + i1 - p1;
+  const int total = tot0 + __shfl(i1, 63);
+  __builtin_amdgcn_wave_barrier();
+  cnt[lane] = off0;  // the counts are read; the table now holds offsets
+  cnt[lane + 64] = off1;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  if (lane < n && valid) sorted_ids[cnt[e] + rank] = lane;
+  // per expert (two per lane): block table, sentinels in the padding
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int ex = lane + 64 * h;
+    const int c = h ? c1 : c0, p = h ? p1 : p0, off = h ? off1 : off0;
+    if (ex < E && p > 0) {
+      for (int b = off / block_m; b < (off + p) / block_m; ++b) expert_ids[b] = ex;
+      for (int i = off + c; i < off + p; ++i) sorted_ids[i] = n;
+    }
+  }
+  for (int b = total / block_m + lane; b < cap / block_m; b += 64) expert_ids[b] = -1;
+  for (int i = total + lane; i < cap; i += 64) sorted_ids[i] = n;
+  if (lane == 0) num_post_pad[0] = total;
+}
+
+// Tile plan of the mixed tiling (few slots per expert on average, a few
+// experts with many): over the aligned blocks of bs rows (16 or 32), every
+// expert's first floor(blocks * bs / 128) runs of 128 rows become tiles of
+// the streaming kernel, listed as (first row, expert) in block order (the
+// last run may end in the expert's padding rows); the other blocks keep
+// their expert in dec_eids for the decode kernels, the listed ones get -1
+// there.  One workgroup; the block table (sorted by expert, -1 past the used
+// length) is staged in LDS and each block finds its expert's run by binary
+// search.  tiles has room for nblocks * bs / 128 entries; n_tiles[0] = their
+// number.
+constexpr int kPlanMaxBlocks = 4096;
+
+__global__ void __launch_bounds__(kAlignThreads) tile_plan_kernel(
+    const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ num_post_pad, int bs,
+    int nblocks, int32_t* __restrict__ dec_eids, int2* __restrict__ tiles,
+    int32_t* __restrict__ n_tiles) {
+  __shared__ int32_t eid[kPlanMaxBlocks];
+  __shared__ int wave_tot[kAlignWaves];
+  __shared__ int running;
+  const int tid = threadIdx.x;
+  const int nb = min(num_post_pad[0] / bs, nblocks);  // blocks in use
+  const int per = 128 / bs;                           // blocks per tile
+  for (int b = tid; b < nb; b += kAlignThreads) eid[b] = expert_ids[b];
+  __syncthreads();
+  int carry = 0;
+  for (int b0 = 0; b0 < nblocks; b0 += kAlignThreads) {
+    const int b = b0 + tid;
+    int e = -1;
+    bool first = false, covered = false;
+    if (b < nb) {
+      e = eid[b];
+      int lo = 0, hi = b;  // first block of expert e
+      while (lo < hi) {
+        const int m = (lo + hi) >> 1;
+        if (eid[m] < e) lo = m + 1; else hi = m;
+      }
+      const int start = lo;
+      lo = b + 1;
+      hi = nb;  // one past its last block
+      while (lo < hi) {
+        const int m = (lo + hi) >> 1;
+        if (eid[m] <= e) lo = m + 1; else hi = m;
+      }
+      const int full = (lo - start) / per * per;
+      covered = b - start < full;
+      first = covered && (b - start) % per == 0;
+    }
+    if (b < nblocks) dec_eids[b] = covered ? -1 : (b < nb ? e : -1);
+    const int pos = carry + block_exclusive_scan(first ? 1 : 0, wave_tot);
+    if (first) tiles[pos] = int2{b * bs, e};
+    // the last thread's position plus its own flag is the running count
+    if (tid == kAlignThreads - 1) running = pos + (first ? 1 : 0);
+    __syncthreads();
+    carry = running;
+    __syncthreads();
+  }
+  if (tid == 0) n_tiles[0] = carry;
+}
+
 }  // namespace moe
 
 extern "C" hipError_t moe_launch_route(const float* logits, int T, int E, int top_k, int kind,
@@ -523,6 +656,16 @@ extern "C" hipError_t moe_launch_route_align(const float* logits, int T, int E, 
                                              int block_m, int cap, int32_t* sorted_ids,
                                              int32_t* expert_ids, int32_t* npp,
                                              hipStream_t stream) {
+  if (T <= moe::kAlignWaves && T * top_k <= moe::kSmallSlots && E <= moe::kSmallMaxE) {
+    const dim3 block(64 * T);  // one wave per token
+    if (kind == 0)
+      moe::route_align_small_kernel<0><<<1, block, 0, stream>>>(
+          logits, T, E, top_k, ebias, renorm, ids, w, block_m, cap, sorted_ids, expert_ids, npp);
+    else
+      moe::route_align_small_kernel<1><<<1, block, 0, stream>>>(
+          logits, T, E, top_k, ebias, renorm, ids, w, block_m, cap, sorted_ids, expert_ids, npp);
+    return hipGetLastError();
+  }
   if (T <= moe::kAlignWaves && T * top_k <= moe::kFusedMaxSlots) {
     if (kind == 0)
       moe::route_align_kernel<0><<<1, moe::kAlignThreads, 0, stream>>>(
@@ -535,4 +678,14 @@ extern "C" hipError_t moe_launch_route_align(const float* logits, int T, int E, 
   hipError_t e = moe_launch_route(logits, T, E, top_k, kind, ebias, renorm, ids, w, stream);
   if (e == hipSuccess) e = moe_launch_align(ids, T * top_k, E, block_m, cap, sorted_ids, expert_ids, npp, stream);
   return e;
+}
+
+// Tile plan of the mixed tiling (tile_plan_kernel); nblocks <= 4096.
+extern "C" hipError_t moe_launch_tile_plan(const int32_t* expert_ids, const int32_t* npp, int bs,
+                                           int nblocks, int32_t* dec_eids, int2* tiles,
+                                           int32_t* n_tiles, hipStream_t stream) {
+  if (nblocks > moe::kPlanMaxBlocks || (bs != 16 && bs != 32)) return hipErrorInvalidValue;
+  moe::tile_plan_kernel<<<1, moe::kAlignThreads, 0, stream>>>(expert_ids, npp, bs, nblocks, dec_eids,
+                                                             tiles, n_tiles);
+  return hipGetLastError();
 }

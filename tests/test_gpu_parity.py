@@ -362,3 +362,23 @@ def test_gemm2_tile_fallbacks(fmt, K, N, group, B, policy):
     y = _gemm2(dev_bf16(a_bits), upload_weights(w2), torch.from_numpy(tw).cuda(), True,
                *_dev_align(si, ei, npp), B, policy)
     assert_rows_close(host_bf16(y), ref, rows=cov, what=f"gemm2 {fmt} K={K} N={N} B{B} {policy}")
+
+
+@pytest.mark.parametrize("fmt,act", [("nvfp4", "swigluoai"), ("mxfp4", "swigluoai"),
+                                     ("gptq", "swigluoai"), ("nvfp4", "relu2")])
+@pytest.mark.parametrize("policy", ["auto", "splitk", "wide"])
+def test_forward_mixed_tiling(fmt, act, policy):
+    """Few slots per expert on average (16/32-row blocks) with a few experts
+    holding hundreds: moe_forward sends those experts' full 128-row runs to
+    the streaming kernel (a tile list built on the device) and the rest to the
+    decode kernels; the whole output against the oracle, every row."""
+    L = _small(fmt, act, E=64, k=2, T=800, skew_std=2.5, seed=77)
+    ids, _ = O.route(L)
+    cnt = np.bincount(ids.reshape(-1), minlength=L.E)
+    bm = M.moe_forward_block_m(L.T, L.top_k, L.E)
+    assert bm <= 32 and (cnt >= 128).sum() >= 2, (bm, np.sort(cnt)[-4:])
+    D = upload(L)
+    out = gpu_forward(L, D, kernel=policy)
+    err = assert_rows_close(host_bf16(out), O.forward(L)["out"], what=f"mixed tiling {fmt} {act}")
+    print(f"mixed tiling {fmt} {act} {policy}: {int((cnt // 128).sum())} tiles of 128 rows, "
+          f"max rel err {err:.3e}", flush=True)
