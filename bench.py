@@ -17,8 +17,8 @@ Weight copies are rotated between calls so that no call finds its weights in
 the 256 MB last-level cache left behind by the previous one (enough copies
 that the touched experts of the copies together exceed it).  The weights are
 loaded as a user of the library loads them: the checkpoint bytes plus, for
-NVFP4, the scales and codes re-laid by K chunk (moe_nvfp4_scales_by_chunk and
-moe_nvfp4_codes_by_chunk, done once at load time).
+NVFP4 and MXFP4, the scales and codes re-laid by K chunk (moe_*_scales_by_chunk
+and moe_*_codes_by_chunk, done once at load time).
 
 The dominant kernel (GEMM1 at the headline size) is timed on its own with one
 HIP event pair around each launch, on the stream it is launched on; the mean
@@ -274,6 +274,9 @@ def upload_copies(L, n, chunked=True):
             if chunked and w.fmt == "nvfp4" and w.K % 64 == 0:
                 d.scales_kc = M.moe_nvfp4_scales_by_chunk(d)
                 d.qweight_kc = M.moe_nvfp4_codes_by_chunk(d)
+            elif chunked and w.fmt == "mxfp4":
+                d.scales_kc = M.moe_mxfp4_scales_by_chunk(d)
+                d.qweight_kc = M.moe_mxfp4_codes_by_chunk(d)
             pair.append(d)
         copies.append(tuple(pair))
     return copies

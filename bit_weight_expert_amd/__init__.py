@@ -11,7 +11,7 @@ from ._binding import (  # noqa: F401
     moe_align, moe_align_capacity, moe_align_large, moe_forward, moe_forward_block_m,
     moe_forward_workspace_bytes, moe_gptq_act_order_sort, moe_permute_slots,
     moe_forward_mxfp8, moe_forward_mxfp8_workspace_bytes, moe_mx_gemm1, moe_mx_gemm2,
-    moe_mxfp8_quantize, mxfp8_lda, mxfp8_lds, moe_nvfp4_codes_by_chunk, moe_nvfp4_scales_by_chunk, moe_mxfp4_codes_by_chunk,
+    moe_mxfp8_quantize, mxfp8_lda, mxfp8_lds, moe_nvfp4_codes_by_chunk, moe_nvfp4_scales_by_chunk, moe_mxfp4_codes_by_chunk, moe_mxfp4_scales_by_chunk,
     moe_route, moe_route_align, moe_w4a16_gemm1, moe_w4a16_gemm2,
     NOALLOC_SCRATCH_BYTES, moe_forward_noalloc,
 )

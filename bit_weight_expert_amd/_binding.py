@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_codes_by_chunk.restype = i
         L.moe_mxfp4_codes_by_chunk.argtypes = [vp, i, i, i, vp, vp]
         L.moe_mxfp4_codes_by_chunk.restype = i
+        L.moe_mxfp4_scales_by_chunk.argtypes = [vp, i, i, i, vp, vp]
+        L.moe_mxfp4_scales_by_chunk.restype = i
         L.moe_align_large.argtypes = [vp, i, i, i, i, vp, vp, vp, vp, vp]
         L.moe_align_large.restype = i
         L.moe_align_large_scratch_bytes.argtypes = [i]
@@ -375,6 +377,20 @@ def moe_mxfp4_codes_by_chunk(w: "QuantWeights") -> torch.Tensor:
     out = torch.empty((E, (w.K + 127) // 128, w.N, 64), dtype=torch.uint8, device=w.qweight.device)
     _check(lib().moe_mxfp4_codes_by_chunk(_ptr(w.qweight), E, w.N, w.K, _ptr(out), _stream()),
            "moe_mxfp4_codes_by_chunk")
+    return out
+
+
+def moe_mxfp4_scales_by_chunk(w: "QuantWeights") -> torch.Tensor:
+    """MXFP4 e8m0 scales [E, N, K/32] re-laid by 128-deep K chunk -> uint8
+    [E, ceil(K/128), N, 4], zero past K/32 (set it as w.scales_kc for the
+    streaming 64/128-row GEMM kernel)."""
+    if w.fmt != "mxfp4":
+        raise ValueError("this re-layout is for MXFP4 scales")
+    _dev(w.scales, torch.uint8, "scales")
+    E = w.scales.shape[0]
+    out = torch.empty((E, (w.K + 127) // 128, w.N, 4), dtype=torch.uint8, device=w.scales.device)
+    _check(lib().moe_mxfp4_scales_by_chunk(_ptr(w.scales), E, w.N, w.K, _ptr(out), _stream()),
+           "moe_mxfp4_scales_by_chunk")
     return out
 
 

@@ -42,6 +42,8 @@ extern "C" hipError_t moe_launch_nvfp4_codes_by_chunk(const uint8_t*, int, int, 
                                                        hipStream_t);
 extern "C" hipError_t moe_launch_mxfp4_codes_by_chunk(const uint8_t*, int, int, int, uint8_t*,
                                                       hipStream_t);
+extern "C" hipError_t moe_launch_mxfp4_scales_by_chunk(const uint8_t*, int, int, int, uint8_t*,
+                                                       hipStream_t);
 extern "C" hipError_t moe_launch_permute_slots(const uint16_t*, int, int, int, int, const int32_t*,
                                                const int32_t*, uint16_t*, hipStream_t);
 
@@ -94,12 +96,14 @@ moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out
   if (w->fmt != MOE_W_INT4_GPTQ && (w->k_perm != nullptr || w->g_idx != nullptr))
     return MOE_ERR_UNSUPPORTED;
   if (w->scales_kc != nullptr) {
-    if (w->fmt != MOE_W_NVFP4) return MOE_ERR_UNSUPPORTED;
-    if (K % 64 != 0) return MOE_ERR_SHAPE;
+    // NVFP4 [E][K/64][N][4]; MXFP4 [E][ceil(K/128)][N][4]
+    if (w->fmt == MOE_W_INT4_GPTQ) return MOE_ERR_UNSUPPORTED;
+    if (w->fmt == MOE_W_NVFP4 && K % 64 != 0) return MOE_ERR_SHAPE;
     if (!aligned16(w->scales_kc)) return MOE_ERR_ALIGN;
   }
   if (w->qweight_kc != nullptr) {
-    // NVFP4: with scales_kc (format and K % 64 checked above); MXFP4: alone
+    // NVFP4: with scales_kc (format and K % 64 checked above); MXFP4: alone (the
+    // MX kernels) or with scales_kc (also the streaming bf16 kernel)
     if (w->fmt == MOE_W_NVFP4 ? w->scales_kc == nullptr : w->fmt != MOE_W_MXFP4)
       return MOE_ERR_UNSUPPORTED;
     if (!aligned16(w->qweight_kc)) return MOE_ERR_ALIGN;
@@ -424,6 +428,16 @@ moe_status_t moe_nvfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int 
   if (out == qweight) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe_launch_nvfp4_codes_by_chunk(qweight, E, N, K, out,
                                                     static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_mxfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int K, uint8_t* out,
+                                       moe_stream_t stream) {
+  if (E <= 0 || E > kMaxE || N <= 0 || K <= 0 || K % 32 != 0) return MOE_ERR_SHAPE;
+  if (scales == nullptr || out == nullptr) return MOE_ERR_NULL;
+  if (!aligned16(out)) return MOE_ERR_ALIGN;
+  if (out == scales) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe_launch_mxfp4_scales_by_chunk(scales, E, N, K, out,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_mxfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int K, uint8_t* out,

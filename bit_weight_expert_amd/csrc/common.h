@@ -46,8 +46,10 @@ struct WeightArgs {
   const float* global_scale;   // NVFP4 [E]
   const uint16_t* bias;        // bf16 [E][N] or null
   int group;
-  const uint8_t* scales_kc;    // NVFP4 e4m3 scales by 64-deep K chunk [E][K/64][N][4], or null
-  const uint8_t* qweight_kc;   // NVFP4 codes by 64-deep K chunk [E][K/64][N][32], or null (needs scales_kc)
+  const uint8_t* scales_kc;    // scales by K chunk, or null: NVFP4 e4m3 [E][K/64][N][4],
+                               // MXFP4 e8m0 [E][ceil(K/128)][N][4]
+  const uint8_t* qweight_kc;   // codes by K chunk, or null: NVFP4 [E][K/64][N][32] (needs
+                               // scales_kc), MXFP4 [E][ceil(K/128)][N][64]
   const int32_t* g_idx;        // GPTQ group map [E][K], or null; only the identity is valid here
 };
 

@@ -627,12 +627,16 @@ __device__ __forceinline__ void pf_issue_one(int d, uint32_t stage_lds,
     dst = stage_lds + P::kABytes + (uint32_t)(4 * p + wave_u) * 1024u;
     if (FMT == FMT_GPTQ)
       src = brow[p] + (size_t)k0 / 8 * N * 4;  // 256 words of the [8][BN] word tile
+    else if (SK == 2 && FMT == FMT_NVFP4)
+      src = brow[p] + (size_t)kc * N * 32;     // one 32-row block, codes by 64-deep chunk
     else if (SK == 2)
-      src = brow[p] + (size_t)kc * N * 32;     // one 32-row block, codes by chunk
+      src = brow[p] + (size_t)(kc >> 1) * N * 64 + 32 * (kc & 1);  // MXFP4 codes by 128-deep chunk
     else
       src = brow[p] + k0 / 2;                  // one 32-row block
   } else {
-    src = skc + (size_t)kc * N * 4;
+    // the chunk's scale words (NVFP4: one per 64-deep chunk; MXFP4: one per
+    // 128-deep chunk, fetched for both of its 64-deep halves)
+    src = skc + (size_t)(FMT == FMT_NVFP4 ? kc : kc >> 1) * N * 4;
     dst = stage_lds + P::kABytes + P::kBBytes + (uint32_t)wave_u * 256u;
   }
   const bool word = SK && d == P::kIssue - 1;
@@ -741,7 +745,8 @@ __device__ __forceinline__ void pf_read_b(PfB (&b)[NF], const uint8_t* bstage, c
         b[j].s0 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 0);
         b[j].s1 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 1);
       } else {
-        b[j].s0 = e8m0_operand(sc[r * (K / 32) + k0 / 32 + h]);
+        // SK: the stage's [BN][4] e8m0 bytes of the 128-deep chunk holding kc
+        b[j].s0 = e8m0_operand(SK ? sc[r * 4 + 2 * (kc & 1) + h] : sc[r * (K / 32) + k0 / 32 + h]);
         b[j].s1 = 0.f;
       }
     }
@@ -959,7 +964,8 @@ template <int FMT, int EPI, int BM, int NF, int RS, int KS, int SK>
 __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
   using P = Pf<BM, NF, SK>;
   constexpr int kStages = P::kStages;
-  static_assert(!SK || (RS == 1 && KS == 1 && FMT == FMT_NVFP4), "streamed scales: one wave per SIMD per workgroup, NVFP4");
+  static_assert(!SK || (RS == 1 && KS == 1 && FMT != FMT_GPTQ),
+                "streamed scales: one wave per SIMD per workgroup, NVFP4 or MXFP4");
   // RS = 2: eight waves, two per SIMD; waves w and w + 4 take the same
   // columns and one half of the rows each (both dequantise the same codes),
   // so one wave's dequant and LDS reads overlap the other's MFMAs.  Only the
@@ -1018,7 +1024,10 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
       brow[p] = W.qweight + (((size_t)e * (K / 8) + w / P::BN) * N + col) * 4;
     } else {
       const int n = min(nt0 + pf_brow<EPI>(q, lane), N - 1);
-      brow[p] = SK == 2 ? W.qweight_kc + ((size_t)e * (K / 64) * N + n) * 32 + 16 * (lane >> 5)
+      brow[p] = SK == 2 ? (FMT == FMT_NVFP4
+                               ? W.qweight_kc + ((size_t)e * (K / 64) * N + n) * 32 + 16 * (lane >> 5)
+                               : W.qweight_kc + ((size_t)e * ((K + 127) / 128) * N + n) * 64 +
+                                     16 * (lane >> 5))
                         : W.qweight + ((size_t)e * N + n) * (K / 2) + 16 * (lane >> 5);
     }
   }
@@ -1028,7 +1037,8 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
   const uint32_t ring = lds_addr(smem);
   const uint32_t sc_lds = ring + kStages * P::kStage;
   // SK: this lane's scale-run source, tile row 64*wave + lane of chunk 0
-  const uint8_t* skc = SK ? W.scales_kc + ((size_t)e * (K / 64) * N + min(nt0 + 64 * wave_u + lane, N - 1)) * 4
+  const int skc_chunks = FMT == FMT_NVFP4 ? K / 64 : (K + 127) / 128;
+  const uint8_t* skc = SK ? W.scales_kc + ((size_t)e * skc_chunks * N + min(nt0 + 64 * wave_u + lane, N - 1)) * 4
                           : nullptr;
   const int nchunks = K / kPfBK;  // (K < 64: only the 32-wide tail, no LDS)
   if (nchunks == 0 || !dma_wave || SK) {
@@ -1986,7 +1996,7 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
     ga.group_m = 4;  // measured flat between 1 and 16 at the gpt-oss-20b shape
     const dim3 grid((ga.n_mblocks * ga.n_ntiles + 7) / 8 * 8);
     constexpr int kThreads = 256 * pf_rs<FMT>() * pf_ks<FMT>();
-    if constexpr (FMT == FMT_NVFP4) {
+    if constexpr (FMT != FMT_GPTQ) {
       if (W.scales_kc != nullptr) {
         // scales (and codes) by K chunk: two 256-thread workgroups per CU
         if (W.qweight_kc != nullptr) {

@@ -1,5 +1,5 @@
-// NVFP4 scales and codes re-laid by 64-deep K chunk, once, when the weights
-// are loaded.
+// NVFP4 scales and codes re-laid by 64-deep K chunk, and MXFP4 scales and
+// codes by 128-deep K chunk, once, when the weights are loaded.
 //
 // The checkpoint layout keeps each weight row's e4m3 group scales (one per 16
 // along K) together: [E][N][K/16].  The 64/128-row GEMM kernel reads, for each
@@ -64,7 +64,34 @@ __global__ __launch_bounds__(256) void mxfp4_codes_by_chunk_kernel(const uint4* 
   for (int u = 0; u < 4; ++u) dst[u] = 4 * c + u < units ? src[4 * c + u] : make_uint4(0, 0, 0, 0);
 }
 
+// MXFP4 e8m0 scales by 128-deep K chunk: [E][ceil(K/128)][N][4], byte j of
+// row n's word of chunk c = the scale of 32-group 4c + j (0 past K/32).  One
+// thread per (expert, chunk, row); the checkpoint bytes are read one by one
+// (K/32 need not be a multiple of 4).
+__global__ __launch_bounds__(256) void mxfp4_scales_by_chunk_kernel(const uint8_t* __restrict__ in,
+                                                                    int N, int G, int KC,
+                                                                    uint32_t* __restrict__ out) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.y;
+  const int e = blockIdx.z;
+  if (n >= N) return;
+  const uint8_t* row = in + ((size_t)e * N + n) * G;
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (4 * c + j < G) w |= (uint32_t)row[4 * c + j] << (8 * j);
+  out[((size_t)e * KC + c) * N + n] = w;
+}
+
 }  // namespace
+
+extern "C" hipError_t moe_launch_mxfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int K,
+                                                       uint8_t* out, hipStream_t st) {
+  const int g = K / 32, kc = (K + 127) / 128;
+  hipLaunchKernelGGL(mxfp4_scales_by_chunk_kernel, dim3((N + 255) / 256, kc, E), dim3(256), 0, st,
+                     scales, N, g, kc, reinterpret_cast<uint32_t*>(out));
+  return hipGetLastError();
+}
 
 extern "C" hipError_t moe_launch_nvfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int K,
                                                        uint8_t* out, hipStream_t st) {

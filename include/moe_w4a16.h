@@ -123,20 +123,23 @@ typedef struct {
                                  accepts it (it gathers the GEMM inputs through it); the
                                  single GEMM calls return MOE_ERR_UNSUPPORTED: gather with
                                  moe_permute_slots and call them in the top_k = 1 view. */
-  const uint8_t* scales_kc;   /* NVFP4 only, optional: the same e4m3 scales laid out by 64-deep K
-                                 chunk, uint8 [E][K/64][N][4] (moe_nvfp4_scales_by_chunk), K a
-                                 multiple of 64, 16-byte aligned.  `scales` stays required; with
-                                 scales_kc the 64/128-row GEMM kernel streams each chunk's scales
-                                 with its codes instead of holding the tile's scales for the whole
-                                 K in on-chip memory, which lets two workgroups share a CU. */
-  const uint8_t* qweight_kc;  /* MXFP4, optional: the codes by 128-deep K chunk from
-                                 moe_mxfp4_codes_by_chunk, read only by the MXFP8-activation (MX)
-                                 kernels.  NVFP4, optional, and only together with scales_kc: the same
-                                 codes laid out by 64-deep K chunk, uint8 [E][K/64][N][32]
-                                 (moe_nvfp4_codes_by_chunk), 16-byte aligned.  `qweight` stays
-                                 required (the 1..64-token kernels read it); with qweight_kc the
-                                 64/128-row kernel copies each chunk's codes for 32 rows as one
-                                 contiguous kilobyte instead of 32-byte pieces of 32 rows. */
+  const uint8_t* scales_kc;   /* optional load-time copy of the scales laid out by K chunk, read
+                                 by the 64/128-row (streaming) GEMM kernel, which then streams
+                                 each chunk's scales with its codes instead of holding the
+                                 tile's scales for the whole K on chip, so two workgroups share
+                                 a CU.  NVFP4: uint8 [E][K/64][N][4] from moe_nvfp4_scales_by_chunk
+                                 (K a multiple of 64).  MXFP4: uint8 [E][ceil(K/128)][N][4] from
+                                 moe_mxfp4_scales_by_chunk.  16-byte aligned; `scales` stays
+                                 required (the other kernels read it).  GPTQ: must be NULL. */
+  const uint8_t* qweight_kc;  /* optional load-time copy of the codes laid out by K chunk, so the
+                                 copy of one chunk of a 32-row block is one contiguous piece
+                                 instead of 32 row pieces.  NVFP4, only together with scales_kc:
+                                 uint8 [E][K/64][N][32] (moe_nvfp4_codes_by_chunk), read by the
+                                 streaming kernel.  MXFP4: uint8 [E][ceil(K/128)][N][64]
+                                 (moe_mxfp4_codes_by_chunk), read by the MXFP8-activation (MX)
+                                 kernels and, when scales_kc is given too, by the streaming
+                                 kernel.  16-byte aligned; `qweight` stays required (the
+                                 1..64-token kernels read it). */
 } moe_wq_t;
 
 /* Kernel for the grouped GEMMs over blocks of 16 or 32 rows (few tokens per
@@ -304,6 +307,17 @@ moe_status_t moe_nvfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int 
  * bf16-activation kernels keep reading qweight). */
 moe_status_t moe_mxfp4_codes_by_chunk(const uint8_t* qweight, int E, int N, int K, uint8_t* out,
                                       moe_stream_t stream);
+
+/* MXFP4 scales re-laid by 128-deep K chunk, run once when the weights are
+ * loaded:
+ *   out[e][c][n][j] = scales[e][n][4c + j] for 4c + j < K/32, else 0
+ *   (c < ceil(K/128), j < 4)
+ * i.e. the four e8m0 group scales of each 128-deep chunk of each weight row,
+ * rows of one chunk contiguous.  scales uint8 [E][N][K/32] (the moe_wq_t MXFP4
+ * layout); out uint8 [E][ceil(K/128)][N][4], a separate buffer, 16-byte
+ * aligned; K % 32 == 0.  Pass as moe_wq_t.scales_kc. */
+moe_status_t moe_mxfp4_scales_by_chunk(const uint8_t* scales, int E, int N, int K, uint8_t* out,
+                                       moe_stream_t stream);
 
 /* Gather of GEMM input rows through an act-order permutation, one row per
  * flat slot f < size_m*top_k, permuted by the slot's own expert:

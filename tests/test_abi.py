@@ -93,7 +93,8 @@ def test_gemm1_rejects(L):
     assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, g_idx=FAKE), x=None) == NULL  # map accepted
     assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, k_perm=FAKE)) == UNSUP   # gather first
     assert _g1(L, _wq(k_perm=FAKE)) == UNSUP             # act-order is a GPTQ form
-    assert _g1(L, _wq(fmt=1, group=32, scales_kc=FAKE)) == UNSUP   # scales by chunk: NVFP4 only
+    assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, scales_kc=FAKE)) == UNSUP   # no GPTQ form
+    assert _g1(L, _wq(fmt=1, group=32, gs=None, scales_kc=FAKE), x=None) == NULL  # MXFP4: accepted
     assert _g1(L, _wq(scales_kc=FAKE), K=2880 + 32) == SHAPE       # needs K % 64 == 0
     assert _g1(L, _wq(scales_kc=FAKE + 4)) == ALIGN
     assert _g1(L, _wq(qweight_kc=FAKE)) == UNSUP         # NVFP4 codes by chunk need scales by chunk

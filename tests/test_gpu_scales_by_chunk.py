@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 M = pytest.importorskip("bit_weight_expert_amd")
 from gpu_util import (assert_rows_close, block_covering_tokens, gpu_forward,  # noqa: E402
-                      host_bf16, upload)
+                      host_bf16, poisoned, upload)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -133,3 +133,99 @@ def test_forward_scales_by_chunk_full_size(codes):
     got = host_bf16(out)
     assert np.isfinite(got).all()
     assert_rows_close(got[toks], O.forward_tokens(L, toks), what="forward scales by chunk full size")
+
+
+# ------------------------------------------------------------ MXFP4 by chunk --
+# MXFP4 on the streaming kernel: scales by 128-deep chunk (moe_mxfp4_scales_by_chunk)
+# and, optionally, the codes by 128-deep chunk that the MX kernels read too.
+
+def with_kc_mx(Dw, codes=False):
+    return dataclasses.replace(Dw, scales_kc=M.moe_mxfp4_scales_by_chunk(Dw),
+                               qweight_kc=M.moe_mxfp4_codes_by_chunk(Dw) if codes else None)
+
+
+@pytest.mark.parametrize("E,N,K", [(3, 384, 320), (2, 2880, 2880), (5, 16, 352), (2, 48, 96)])
+def test_mxfp4_scales_by_chunk_bitexact(E, N, K):
+    w = S.make_weights("mxfp4", E=E, N=N, K=K, bias=False, seed=N + K + 5)
+    Dw = M.QuantWeights.from_arrays(w.fmt, w.group, w.N, w.K, w.qweight, w.scales, None, None, None)
+    got = M.moe_mxfp4_scales_by_chunk(Dw).cpu().numpy()
+    kc = (K + 127) // 128
+    padded = np.zeros((E, N, kc * 4), np.uint8)
+    padded[:, :, :K // 32] = w.scales
+    np.testing.assert_array_equal(got, padded.reshape(E, N, kc, 4).transpose(0, 2, 1, 3))
+
+
+def _small_mx(act="swigluoai", E=4, k=2, H=320, I=192, T=300, seed=53, **kw):
+    route = "sigmoid_bias" if act == "relu2" else "softmax"
+    return S.make_layer(E=E, top_k=k, H=H, I=I, fmt="mxfp4", act=act, route=route, T=T, seed=seed,
+                        router_bias_std=0.1 if route == "sigmoid_bias" else 0.0, **kw)
+
+
+@CODES
+@pytest.mark.parametrize("act", ["none", "swigluoai", "relu2"])
+@pytest.mark.parametrize("B", [64, 128])
+@pytest.mark.parametrize("H", [320, 352, 2880])
+def test_mxfp4_gemm1_by_chunk(act, B, H, codes):
+    """K = 352: a 64-deep chunk ends the 128-deep layout's last, partial chunk,
+    then the 32-wide tail (checkpoint layout)."""
+    L = _small_mx("relu2" if act == "relu2" else "swigluoai", H=H, T=300 if H < 2880 else 150,
+                  x_std=12.0)
+    D = upload(L)
+    w13 = with_kc_mx(D["w13"], codes)
+    ids, w = O.route(L)
+    si, ei, npp = O.align(ids, L.E, B)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    print(f"mxfp4 gemm1 by chunk act={act} B={B} H={H} codes={codes}", flush=True)
+    n_out = L.w13.N // 2 if act == "swigluoai" else L.w13.N
+    out = M.moe_w4a16_gemm1(D["x"], L.top_k, w13, act, L.alpha, L.beta, L.limit, t(si), t(ei),
+                            t(np.array([npp], np.int32)), B, out=poisoned((L.T * L.top_k, n_out)))
+    ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, act, L.alpha, L.beta, L.limit, si, ei, npp, B)
+    assert_rows_close(host_bf16(out), ref, rows=cov, what=f"mxfp4 gemm1 by chunk {act} B{B} H{H}")
+
+
+@CODES
+@pytest.mark.parametrize("B", [64, 128])
+@pytest.mark.parametrize("I", [192, 224, 2880])
+def test_mxfp4_gemm2_by_chunk(B, I, codes):
+    L = _small_mx(I=I, T=300 if I < 2880 else 150)
+    D = upload(L)
+    w2 = with_kc_mx(D["w2"], codes)
+    ids, w = O.route(L)
+    si, ei, npp = O.align(ids, L.E, B)
+    n = L.T * L.top_k
+    a_bits = S.f32_to_bf16_bits(np.random.default_rng(I + B).standard_normal((n, I)).astype(np.float32))
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    print(f"mxfp4 gemm2 by chunk B={B} I={I} codes={codes}", flush=True)
+    y = M.moe_w4a16_gemm2(t(a_bits.view(np.int16)).view(torch.bfloat16), w2,
+                          t(w.reshape(-1).astype(np.float32)), True, t(si), t(ei),
+                          t(np.array([npp], np.int32)), B, out=poisoned((n, L.H)))
+    ref, cov = O.gemm2(a_bits, n, L.w2, w.reshape(-1), True, si, ei, npp, B)
+    assert_rows_close(host_bf16(y), ref, rows=cov, what=f"mxfp4 gemm2 by chunk B{B} I{I}")
+
+
+@pytest.mark.parametrize("T", [13, 600])
+def test_mxfp4_forward_by_chunk(T):
+    """T = 13: 16-row blocks (the decode kernels read the checkpoint copy);
+    T = 600: 128-row blocks on the streaming kernel reading the chunked copies."""
+    L = _small_mx(T=T, E=6)
+    D = upload(L)
+    D["w13"], D["w2"] = with_kc_mx(D["w13"], True), with_kc_mx(D["w2"], True)
+    out = gpu_forward(L, D)
+    assert_rows_close(host_bf16(out), O.forward(L)["out"], what=f"mxfp4 forward by chunk T{T}")
+
+
+def test_mxfp4_forward_by_chunk_full_size():
+    """The gpt-oss-120b MXFP4 layer at T = 8192 with the chunked copies, as
+    bench.py loads it: tokens covering every aligned block against the oracle."""
+    L = S.make_config(4, 8192)
+    D = upload(L)
+    D["w13"], D["w2"] = with_kc_mx(D["w13"], True), with_kc_mx(D["w2"], True)
+    print("mxfp4 forward by chunk full size", flush=True)
+    out = gpu_forward(L, D)
+    ids, _ = O.route(L)
+    toks = block_covering_tokens(ids, L.E, M.moe_forward_block_m(8192, L.top_k, L.E),
+                                 extra=(0, 1, 7, 63, 511, 4095, 8191))
+    got = host_bf16(out)
+    assert np.isfinite(got).all()
+    err = assert_rows_close(got[toks], O.forward_tokens(L, toks), what="mxfp4 by chunk full size")
+    print(f"mxfp4 by chunk full size: max rel err {err:.3e} over {len(toks)} tokens", flush=True)
