@@ -423,7 +423,8 @@ def main() -> int:
     results = {r["T"]: r for r in rows}
 
     def gemm_alone(T, which):
-        """(mean, median) launch ms of GEMM1 or GEMM2 alone at T, rotating copies."""
+        """(mean, median) launch ms of GEMM1 or GEMM2 alone at T, rotating copies, on
+        the aligned blocks of moe_forward's tile size."""
         bm = M.moe_forward_block_m(T, L.top_k, L.E)
         ids_t, w_t = M.moe_route(logits[:T], L.top_k, L.route, None, L.renormalize)
         si, ei, npp = M.moe_align(ids_t, L.E, bm)

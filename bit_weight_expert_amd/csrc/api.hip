@@ -136,7 +136,7 @@ int epi_of(moe_act_t act) {
   }
 }
 
-// block_m for moe_forward: the smallest tile that the average expert load fills.
+// block_m by the average expert load: the smallest tile it fills.
 int pick_block_m(int T, int top_k, int E) {
   const long avg = ((long)T * top_k + E - 1) / E;
   if (avg <= 16) return 16;
@@ -144,6 +144,13 @@ int pick_block_m(int T, int top_k, int E) {
   if (avg <= 64) return 64;
   return 128;
 }
+
+constexpr int kMixedMaxBlocks = 4096;  // the tile-plan kernel's block table in LDS
+
+// The sort granularity moe_forward uses.  (Measured: 64-row blocks for
+// uneven loads, pairs of them as 128-row tiles and the odd ones as a second,
+// 64-row launch, ran slower than 128-row blocks throughout.)
+int forward_block_m(int T, int top_k, int E) { return pick_block_m(T, top_k, E); }
 
 struct WsLayout {
   size_t ids, w, sorted, eids, npp, cnt, dec, tiles, ntiles, act, y, total;
@@ -156,7 +163,6 @@ constexpr int kAlignLargeMin = 8192;
 // experts' full 128-row runs go to the streaming kernel (a tile list made on
 // the device after the sort) and the rest to the 16/32-row decode kernels.
 constexpr int kMixedMinSlots = 1024;
-constexpr int kMixedMaxBlocks = 4096;  // the plan kernel's block table in LDS
 
 WsLayout ws_layout(int T, int E, int top_k, int hidden, int inter, int block_m) {
   WsLayout L;
@@ -628,12 +634,12 @@ moe_status_t moe_forward_mxfp8(const uint16_t* x, const float* logits, int T, in
 
 int moe_forward_block_m(int T, int top_k, int E) {
   if (T <= 0 || top_k <= 0 || E <= 0) return 16;
-  return pick_block_m(T, top_k, E);
+  return forward_block_m(T, top_k, E);
 }
 
 size_t moe_forward_workspace_bytes(int T, int E, int top_k, int hidden, int inter) {
   if (T <= 0 || E <= 0 || top_k <= 0 || hidden <= 0 || inter <= 0) return 0;
-  return ws_layout(T, E, top_k, hidden, inter, pick_block_m(T, top_k, E)).total;
+  return ws_layout(T, E, top_k, hidden, inter, forward_block_m(T, top_k, E)).total;
 }
 
 }  // extern "C"
@@ -666,7 +672,7 @@ static moe_status_t forward_run(const uint16_t* x, const float* logits, int T, i
   if (kind == MOE_ROUTE_SIGMOID_BIAS && expert_bias == nullptr) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return MOE_ERR_ALIGN;
-  const int block_m = pick_block_m(T, top_k, E);
+  const int block_m = forward_block_m(T, top_k, E);
   const WsLayout L = ws_layout(T, E, top_k, hidden, inter, block_m);
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
 

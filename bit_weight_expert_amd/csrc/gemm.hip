@@ -762,10 +762,11 @@ __device__ __forceinline__ int a_slot(int q, int r) { return q ^ ((r >> 1) & 7);
 
 // A fragments of MFMA step s of a chunk: rows i*32 + c, k = 32h + 8s .. +8.
 // A rows are 128 bytes in LDS, logical 16-byte slot q of row r stored at a_slot(q, r).
-template <int MI>
+// (MA <= MI: only the first MA fragments, the rest of a tile being padding rows.)
+template <int MI, int MA = MI>
 __device__ __forceinline__ void pf_read_a(uint4 (&a)[MI], const uint8_t* astage, int c, int h, int s) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  for (int i = 0; i < MA; ++i) {
     const int r = i * 32 + c;
     a[i] = *reinterpret_cast<const uint4*>(astage + r * 128 + 16 * a_slot(4 * h + s, r));
   }
@@ -773,10 +774,10 @@ __device__ __forceinline__ void pf_read_a(uint4 (&a)[MI], const uint8_t* astage,
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-template <int MI, int NF>
+template <int MI, int NF, int MA = MI>
 __device__ __forceinline__ void pf_mfma(f32x16 (&acc)[MI][NF], const uint4 (&a)[MI], const bf16x8 (&b)[NF]) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  for (int i = 0; i < MA; ++i) {
     const bf16x8 af = as_bf16x8(a[i]);
 #pragma unroll
     for (int j = 0; j < NF; ++j)
@@ -790,17 +791,17 @@ __device__ __forceinline__ void pf_mfma(f32x16 (&acc)[MI][NF], const uint4 (&a)[
 // between rows they overlap the matrix core's work (measured ~5% faster on
 // both GEMMs).  The A fragments serve as the pins, so `a` reads as modified
 // afterwards (callers reload it).
-template <int FMT, int BM, int NF, int SK, int MI>
+template <int FMT, int BM, int NF, int SK, int MI, int MA = MI>
 __device__ __forceinline__ void pf_mfma_issue(f32x16 (&acc)[MI][NF], uint4 (&a)[MI], const bf16x8 (&b)[NF],
                                               uint32_t stage_lds,
                                               const uint16_t* const (&arow)[Pf<BM, NF, SK>::kAIssue],
                                               const uint8_t* const (&brow)[Pf<BM, NF, SK>::kBIssue],
                                               const uint8_t* skc, int kc, int wave_u, int N) {
   using P = Pf<BM, NF, SK>;
-  constexpr int kPer = (P::kIssue + MI - 1) / MI;  // DMA instructions after each row
+  constexpr int kPer = (P::kIssue + MA - 1) / MA;  // DMA instructions after each active row
   uint32_t last = 0;
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  for (int i = 0; i < MA; ++i) {
     const bf16x8 af = as_bf16x8(a[i]);
 #pragma unroll
     for (int j = 0; j < NF; ++j)
@@ -808,7 +809,7 @@ __device__ __forceinline__ void pf_mfma_issue(f32x16 (&acc)[MI][NF], uint4 (&a)[
 #pragma unroll
     for (int d = kPer * i; d < kPer * (i + 1) && d < P::kIssue; ++d)
       pf_issue_one<FMT, BM, NF, SK, true>(d, stage_lds, arow, brow, skc, kc, wave_u, N, a[i].x,
-                                          i + 1 < MI ? a[i + 1 < MI ? i + 1 : i].x : last);
+                                          i + 1 < MA ? a[i + 1 < MA ? i + 1 : i].x : last);
   }
 }
 
@@ -990,6 +991,12 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
   // DMA instruction q = 4p + wave covers rows 8q .. 8q+7, lane l row 8q + l/8
   int rowb, e;  // the tile's first row in sorted_ids, its expert
   tile_rows(ga, mb, BM, rowb, e);
+  // 32-row fragments holding a real slot: a tile's real slots come first (the
+  // sort pads each expert's run at its end), so fragment i is live when its
+  // first slot is
+  int nact = 1;
+#pragma unroll
+  for (int i = 1; i < BM / 32; ++i) nact += ga.sorted_ids[rowb + 32 * i] < ga.n_slots ? 1 : 0;
   int sid[P::kAIssue];
 #pragma unroll
   for (int p = 0; p < P::kAIssue; ++p) sid[p] = ga.sorted_ids[rowb + 8 * (4 * p + wave_u) + (lane >> 3)];
@@ -1079,6 +1086,9 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
     for (int j = 0; j < NF; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  // live fragments among this wave's MI (wave-uniform: the slot ids are the
+  // same for all lanes)
+  const int nact_w = __builtin_amdgcn_readfirstlane(min(max(nact - rpart * MI, 0), MI));
 
   if (KS == 2 && nchunks > 0) {
     wait_vmcnt<(kStages - 1) * P::kIssue>();
@@ -1117,66 +1127,80 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
     // scales and chunk 0 have landed (chunks 1..3 may still be in flight)
     wait_vmcnt<(kStages - 1) * P::kIssue>();
     pf_barrier();
-    // chunk 0: weights, step-0 A fragments and dequant
-    PfB b[NF];
-    uint4 a0[MI], a1[MI];
-    bf16x8 q0[NF], q1[NF];
-    pf_read_b<FMT, EPI, NF, SK>(b, smem + P::kABytes, SK ? smem + P::kABytes + P::kBBytes : scale_lds, rl,
-                                0, h, K, W.group, P::BN);
-    pf_read_a<MI>(a0, smem + aoff, c, h, 0);
+    // the K loop with the wave's first MA row fragments (MA < MI: the tile's
+    // later 32-row fragments hold only padding rows, whose MFMAs and A reads
+    // are skipped); one copy of the loop per MA, chosen once per tile
+    auto kloop = [&](auto ma_tag) {
+      constexpr int MA = decltype(ma_tag)::value;
+      // chunk 0: weights, step-0 A fragments and dequant
+      PfB b[NF];
+      uint4 a0[MI], a1[MI];
+      bf16x8 q0[NF], q1[NF];
+      pf_read_b<FMT, EPI, NF, SK>(b, smem + P::kABytes, SK ? smem + P::kABytes + P::kBBytes : scale_lds, rl,
+                                  0, h, K, W.group, P::BN);
+      pf_read_a<MI, MA>(a0, smem + aoff, c, h, 0);
 #pragma unroll
-    for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
-
-    if (SK != 0 && n0 >= N) {
-      // every weight row of this wave lies past N (the last column tile):
-      // only its share of the copies, which leaves its SIMD to the other
-      // workgroup on the CU
+      for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
+      for (int kc = 0; kc < nchunks; ++kc) {
+        const uint8_t* st = smem + (kc % kStages) * P::kStage + aoff;
+        // steps 0..2: each overlaps the next step's A reads and dequant
+        pf_read_a<MI, MA>(a1, st, c, h, 1);
+#pragma unroll
+        for (int j = 0; j < NF; ++j) q1[j] = pf_deq_step<FMT>(b[j], 1);
+        pf_mfma<MI, NF, MA>(acc, a0, q0);
+        pf_read_a<MI, MA>(a0, st, c, h, 2);
+#pragma unroll
+        for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 2);
+        pf_mfma<MI, NF, MA>(acc, a1, q1);
+        pf_read_a<MI, MA>(a1, st, c, h, 3);
+#pragma unroll
+        for (int j = 0; j < NF; ++j) q1[j] = pf_deq_step<FMT>(b[j], 3);
+        pf_mfma<MI, NF, MA>(acc, a0, q0);
+        // step 3 overlaps chunk kc+1's reads: chunk kc+1 has landed (all but the
+        // two newest chunks' DMA are done) and every wave is past its reads of
+        // chunk kc, whose stage is refilled with chunk kc+4
+        wait_vmcnt<(kStages - 2) * P::kIssue>();
+        pf_barrier();
+        const uint8_t* nx = smem + ((kc + 1) % kStages) * P::kStage;
+        if constexpr (SK != 0) {
+          // every wave copies (one per SIMD): its DMA goes between step 3's rows
+          pf_read_b<FMT, EPI, NF, SK>(b, nx + P::kABytes, nx + P::kABytes + P::kBBytes, rl,
+                                      min(kc + 1, nchunks - 1), h, K, W.group, P::BN);
+          pf_read_a<MI, MA>(a0, nx + aoff, c, h, 0);
+          pf_mfma_issue<FMT, BM, NF, SK, MI, MA>(acc, a1, q1, ring + (kc % kStages) * P::kStage, arow,
+                                                 brow, skc, min(kc + kStages, nchunks - 1), wave_u, N);
+        } else {
+          if (dma_wave)
+            pf_issue<FMT, BM, NF, SK>(ring + (kc % kStages) * P::kStage, arow, brow, skc,
+                                      min(kc + kStages, nchunks - 1), wave_u, N);
+          pf_read_b<FMT, EPI, NF, SK>(b, nx + P::kABytes, scale_lds, rl, min(kc + 1, nchunks - 1), h, K,
+                                      W.group, P::BN);
+          pf_read_a<MI, MA>(a0, nx + aoff, c, h, 0);
+          pf_mfma<MI, NF, MA>(acc, a1, q1);
+        }
+#pragma unroll
+        for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
+      }
+    };
+    if ((SK != 0 && n0 >= N) || nact_w == 0) {
+      // every weight row of this wave lies past N (the last column tile), or
+      // all its rows are padding: only its share of the copies, which leaves
+      // its SIMD to the other workgroup (or wave) on it
       for (int kc = 0; kc < nchunks; ++kc) {
         wait_vmcnt<(kStages - 2) * P::kIssue>();
         pf_barrier();
-        pf_issue<FMT, BM, NF, SK>(ring + (kc % kStages) * P::kStage, arow, brow, skc,
-                                  min(kc + kStages, nchunks - 1), wave_u, N);
-      }
-    } else
-    for (int kc = 0; kc < nchunks; ++kc) {
-      const uint8_t* st = smem + (kc % kStages) * P::kStage + aoff;
-      // steps 0..2: each overlaps the next step's A reads and dequant
-      pf_read_a<MI>(a1, st, c, h, 1);
-#pragma unroll
-      for (int j = 0; j < NF; ++j) q1[j] = pf_deq_step<FMT>(b[j], 1);
-      pf_mfma<MI, NF>(acc, a0, q0);
-      pf_read_a<MI>(a0, st, c, h, 2);
-#pragma unroll
-      for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 2);
-      pf_mfma<MI, NF>(acc, a1, q1);
-      pf_read_a<MI>(a1, st, c, h, 3);
-#pragma unroll
-      for (int j = 0; j < NF; ++j) q1[j] = pf_deq_step<FMT>(b[j], 3);
-      pf_mfma<MI, NF>(acc, a0, q0);
-      // step 3 overlaps chunk kc+1's reads: chunk kc+1 has landed (all but the
-      // two newest chunks' DMA are done) and every wave is past its reads of
-      // chunk kc, whose stage is refilled with chunk kc+4
-      wait_vmcnt<(kStages - 2) * P::kIssue>();
-      pf_barrier();
-      const uint8_t* nx = smem + ((kc + 1) % kStages) * P::kStage;
-      if constexpr (SK != 0) {
-        // every wave copies (one per SIMD): its DMA goes between step 3's rows
-        pf_read_b<FMT, EPI, NF, SK>(b, nx + P::kABytes, nx + P::kABytes + P::kBBytes, rl,
-                                    min(kc + 1, nchunks - 1), h, K, W.group, P::BN);
-        pf_read_a<MI>(a0, nx + aoff, c, h, 0);
-        pf_mfma_issue<FMT, BM, NF, SK, MI>(acc, a1, q1, ring + (kc % kStages) * P::kStage, arow, brow,
-                                           skc, min(kc + kStages, nchunks - 1), wave_u, N);
-      } else {
-        if (dma_wave)
+        if (SK != 0 || dma_wave)
           pf_issue<FMT, BM, NF, SK>(ring + (kc % kStages) * P::kStage, arow, brow, skc,
                                     min(kc + kStages, nchunks - 1), wave_u, N);
-        pf_read_b<FMT, EPI, NF, SK>(b, nx + P::kABytes, scale_lds, rl, min(kc + 1, nchunks - 1), h, K,
-                                    W.group, P::BN);
-        pf_read_a<MI>(a0, nx + aoff, c, h, 0);
-        pf_mfma<MI, NF>(acc, a1, q1);
       }
-#pragma unroll
-      for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
+    } else if (nact_w >= MI) {
+      kloop(std::integral_constant<int, MI>{});
+    } else if constexpr (MI >= 2) {
+      if (nact_w == 1) kloop(std::integral_constant<int, 1>{});
+      else if constexpr (MI >= 3) {
+        if (nact_w == 2) kloop(std::integral_constant<int, 2>{});
+        else if constexpr (MI >= 4) kloop(std::integral_constant<int, 3>{});
+      }
     }
   }
   // no DMA may land in LDS after this workgroup is gone

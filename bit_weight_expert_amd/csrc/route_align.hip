@@ -558,12 +558,12 @@ __global__ void __launch_bounds__(1024) route_align_small_kernel(
   if (lane == 0) num_post_pad[0] = total;
 }
 
-// Tile plan of the mixed tiling (few slots per expert on average, a few
-// experts with many): over the aligned blocks of bs rows (16 or 32), every
+// Tile plan of the mixed tiling (uneven slots per expert): over the aligned
+// blocks of bs rows (16, 32 or 64), every
 // expert's first floor(blocks * bs / 128) runs of 128 rows become tiles of
 // the streaming kernel, listed as (first row, expert) in block order (the
 // last run may end in the expert's padding rows); the other blocks keep
-// their expert in dec_eids for the decode kernels, the listed ones get -1
+// their expert in dec_eids for the kernel of bs-row blocks, the listed ones get -1
 // there.  One workgroup; the block table (sorted by expert, -1 past the used
 // length) is staged in LDS and each block finds its expert's run by binary
 // search.  tiles has room for nblocks * bs / 128 entries; n_tiles[0] = their
@@ -684,7 +684,7 @@ extern "C" hipError_t moe_launch_route_align(const float* logits, int T, int E, 
 extern "C" hipError_t moe_launch_tile_plan(const int32_t* expert_ids, const int32_t* npp, int bs,
                                            int nblocks, int32_t* dec_eids, int2* tiles,
                                            int32_t* n_tiles, hipStream_t stream) {
-  if (nblocks > moe::kPlanMaxBlocks || (bs != 16 && bs != 32)) return hipErrorInvalidValue;
+  if (nblocks > moe::kPlanMaxBlocks || (bs != 16 && bs != 32 && bs != 64)) return hipErrorInvalidValue;
   moe::tile_plan_kernel<<<1, moe::kAlignThreads, 0, stream>>>(expert_ids, npp, bs, nblocks, dec_eids,
                                                              tiles, n_tiles);
   return hipGetLastError();

@@ -382,3 +382,4 @@ def test_forward_mixed_tiling(fmt, act, policy):
     err = assert_rows_close(host_bf16(out), O.forward(L)["out"], what=f"mixed tiling {fmt} {act}")
     print(f"mixed tiling {fmt} {act} {policy}: {int((cnt // 128).sum())} tiles of 128 rows, "
           f"max rel err {err:.3e}", flush=True)
+
