@@ -23,7 +23,7 @@ extern "C" hipError_t moe_launch_gemm(int, int, int, int, const uint16_t*, int, 
                                       const moe::WeightArgs*, const int32_t*, const int32_t*,
                                       const int32_t*, const float*, int, float, float, float,
                                       uint16_t*, int, int, const int2*, const int32_t*, hipStream_t);
-extern "C" int moe_prefill_tiles_ok(int, int, int, int);
+extern "C" int moe_prefill_tiles_ok(int, int, int, int, int);
 extern "C" hipError_t moe_launch_tile_plan(const int32_t*, const int32_t*, int, int, int32_t*, int2*,
                                            int32_t*, hipStream_t);
 extern "C" hipError_t moe_launch_sum(const uint16_t*, const int32_t*, int, int, int, int,
@@ -693,8 +693,8 @@ static moe_status_t forward_run(const uint16_t* x, const float* logits, int T, i
   // Mixed tiling: the 128-row tiles (prefill kernel, tile list) and the rest
   // of the blocks (decode kernels, dec_eids: -1 for blocks in a tile).
   const bool mixed = block_m <= 32 && n >= kMixedMinSlots && cap / block_m <= kMixedMaxBlocks &&
-                     moe_prefill_tiles_ok((int)w13->fmt, hidden, n1, w13->group_size) &&
-                     moe_prefill_tiles_ok((int)w2->fmt, inter, hidden, w2->group_size);
+                     moe_prefill_tiles_ok((int)w13->fmt, hidden, n1, w13->group_size, w13->scales_kc != nullptr) &&
+                     moe_prefill_tiles_ok((int)w2->fmt, inter, hidden, w2->group_size, w2->scales_kc != nullptr);
   int32_t* dec_eids = reinterpret_cast<int32_t*>(ws + L.dec);
   int2* tiles = reinterpret_cast<int2*>(ws + L.tiles);
   int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);

@@ -177,6 +177,23 @@ __device__ __forceinline__ void load_codes(BChunk<FMT, C>& b, const WeightArgs& 
 }
 
 // 8 dequantised bf16 weights of MFMA step st.
+// Eight GPTQ codes of one word (code i in bits 4i .. 4i+3) as code * s + zs.
+// The even codes are masked into the word's four bytes and the odd ones
+// shifted there first, so each code takes one byte-to-float convert (a
+// nibble extract and a convert otherwise); the products are exact in fp32.
+// (The masks are opaque to the compiler: knowing the bits of lo and hi, it
+// would fold each byte read back into a nibble extract.)
+__device__ __forceinline__ void gptq_deq8(uint32_t w, float s, float zs, float (&v)[8]) {
+  uint32_t lo, hi;
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w));
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w >> 4));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = fmaf((float)((lo >> (8 * j)) & 0xFFu), s, zs);
+    v[2 * j + 1] = fmaf((float)((hi >> (8 * j)) & 0xFFu), s, zs);
+  }
+}
+
 template <int FMT, int C>
 __device__ __forceinline__ bf16x8 deq_step(const BChunk<FMT, C>& b, int st) {
   const uint32_t w = b.q[st];
@@ -212,8 +229,7 @@ __device__ __forceinline__ bf16x8 deq_step(const BChunk<FMT, C>& b, int st) {
     const float s = half_bits_to_f32((uint16_t)b.sr[0]);
     const float zs = (float)((b.sr[1] >> b.zsh) & 15u) * s;
     float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = fmaf((float)((w >> (4 * i)) & 15u), s, -zs);
+    gptq_deq8(w, s, -zs, v);
     r.x = pack_bf16x2(v[0], v[1]);
     r.y = pack_bf16x2(v[2], v[3]);
     r.z = pack_bf16x2(v[4], v[5]);
@@ -605,6 +621,17 @@ __device__ __forceinline__ int pf_brow(int b, int p) {
   return 32 * b + ((EPI == EPI_SWIGLU) ? 2 * (s & 15) + (s >> 4) : s);
 }
 
+// Source of a lane's streamed scale word (SK != 0): chunk kc reads
+// p + (kc >> gsh) * stride.  NVFP4: one [N][4] row per 64-deep chunk; MXFP4:
+// one per 128-deep chunk (gsh = 1); GPTQ: the checkpoint's fp16 scale row
+// and packed zero-point row of the chunk's group (gsh = log2(group / 64)),
+// lanes 0..31 two scales each, lanes 32..39 one zero word each.
+struct SkSrc {
+  const uint8_t* p;
+  uint32_t stride;
+  int gsh;
+};
+
 // DMA instruction d (0 <= d < kIssue) of one wave's share of chunk kc, into
 // the ring stage at stage_lds: first the A rows, then the weight codes, then
 // (SK) the chunk's 4-byte scale runs of tile rows 64*wave .. 64*wave+63.
@@ -613,7 +640,7 @@ template <int FMT, int BM, int NF, int SK, bool PIN>
 __device__ __forceinline__ void pf_issue_one(int d, uint32_t stage_lds,
                                              const uint16_t* const (&arow)[Pf<BM, NF, SK>::kAIssue],
                                              const uint8_t* const (&brow)[Pf<BM, NF, SK>::kBIssue],
-                                             const uint8_t* skc, int kc, int wave_u, int N,
+                                             const SkSrc& sk, int kc, int wave_u, int N,
                                              uint32_t& after, uint32_t& before) {
   using P = Pf<BM, NF, SK>;
   const int k0 = kc * kPfBK;
@@ -634,9 +661,9 @@ __device__ __forceinline__ void pf_issue_one(int d, uint32_t stage_lds,
     else
       src = brow[p] + k0 / 2;                  // one 32-row block
   } else {
-    // the chunk's scale words (NVFP4: one per 64-deep chunk; MXFP4: one per
-    // 128-deep chunk, fetched for both of its 64-deep halves)
-    src = skc + (size_t)(FMT == FMT_NVFP4 ? kc : kc >> 1) * N * 4;
+    // the chunk's scale words (MXFP4: one row per 128-deep chunk, fetched for
+    // both of its 64-deep halves; GPTQ: one row per group)
+    src = sk.p + (size_t)(kc >> sk.gsh) * sk.stride;
     dst = stage_lds + P::kABytes + P::kBBytes + (uint32_t)wave_u * 256u;
   }
   const bool word = SK && d == P::kIssue - 1;
@@ -653,11 +680,11 @@ __device__ __forceinline__ void pf_issue_one(int d, uint32_t stage_lds,
 template <int FMT, int BM, int NF, int SK>
 __device__ __forceinline__ void pf_issue(uint32_t stage_lds, const uint16_t* const (&arow)[Pf<BM, NF, SK>::kAIssue],
                                          const uint8_t* const (&brow)[Pf<BM, NF, SK>::kBIssue],
-                                         const uint8_t* skc, int kc, int wave_u, int N) {
+                                         const SkSrc& sk, int kc, int wave_u, int N) {
   uint32_t unused = 0;
 #pragma unroll
   for (int d = 0; d < Pf<BM, NF, SK>::kIssue; ++d)
-    pf_issue_one<FMT, BM, NF, SK, false>(d, stage_lds, arow, brow, skc, kc, wave_u, N, unused, unused);
+    pf_issue_one<FMT, BM, NF, SK, false>(d, stage_lds, arow, brow, sk, kc, wave_u, N, unused, unused);
 }
 
 // Weight codes of one fragment for one chunk (one code word per MFMA step)
@@ -693,8 +720,7 @@ __device__ __forceinline__ bf16x8 pf_deq(uint32_t w, float s, float zs) {
     __builtin_memcpy(&r.w, &p, 4);
   } else {
     float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = fmaf((float)((w >> (4 * i)) & 15u), s, zs);
+    gptq_deq8(w, s, zs, v);
     r.x = pack_bf16x2(v[0], v[1]);
     r.y = pack_bf16x2(v[2], v[3]);
     r.z = pack_bf16x2(v[4], v[5]);
@@ -730,10 +756,18 @@ __device__ __forceinline__ void pf_read_b(PfB (&b)[NF], const uint8_t* bstage, c
       b[j].q.y = w[(4 * h + 1) * bn + r];
       b[j].q.z = w[(4 * h + 2) * bn + r];
       b[j].q.w = w[(4 * h + 3) * bn + r];
-      const int grp = (k0 + 32 * h) / group;
-      const float s = half_bits_to_f32(reinterpret_cast<const uint16_t*>(sc)[grp * bn + r]);
-      const uint32_t* zw = reinterpret_cast<const uint32_t*>(sc + (K / group) * bn * 2);
-      const float z = (float)((zw[grp * (bn / 8) + (r >> 3)] >> (4 * (r & 7))) & 15u);
+      float s, z;
+      if (SK) {
+        // the stage's run of wave r/64: 64 fp16 scales, then 8 zero words
+        const uint8_t* run = sc + (r >> 6) * 256;
+        s = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(run + (r & 63) * 2));
+        z = (float)((*reinterpret_cast<const uint32_t*>(run + 128 + ((r & 63) >> 3) * 4) >> (4 * (r & 7))) & 15u);
+      } else {
+        const int grp = (k0 + 32 * h) / group;
+        s = half_bits_to_f32(reinterpret_cast<const uint16_t*>(sc)[grp * bn + r]);
+        const uint32_t* zw = reinterpret_cast<const uint32_t*>(sc + (K / group) * bn * 2);
+        z = (float)((zw[grp * (bn / 8) + (r >> 3)] >> (4 * (r & 7))) & 15u);
+      }
       b[j].s0 = s;
       b[j].s1 = -z * s;
     } else {
@@ -796,7 +830,7 @@ __device__ __forceinline__ void pf_mfma_issue(f32x16 (&acc)[MI][NF], uint4 (&a)[
                                               uint32_t stage_lds,
                                               const uint16_t* const (&arow)[Pf<BM, NF, SK>::kAIssue],
                                               const uint8_t* const (&brow)[Pf<BM, NF, SK>::kBIssue],
-                                              const uint8_t* skc, int kc, int wave_u, int N) {
+                                              const SkSrc& sk, int kc, int wave_u, int N) {
   using P = Pf<BM, NF, SK>;
   constexpr int kPer = (P::kIssue + MA - 1) / MA;  // DMA instructions after each active row
   uint32_t last = 0;
@@ -808,7 +842,7 @@ __device__ __forceinline__ void pf_mfma_issue(f32x16 (&acc)[MI][NF], uint4 (&a)[
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b[j], acc[i][j], 0, 0, 0);
 #pragma unroll
     for (int d = kPer * i; d < kPer * (i + 1) && d < P::kIssue; ++d)
-      pf_issue_one<FMT, BM, NF, SK, true>(d, stage_lds, arow, brow, skc, kc, wave_u, N, a[i].x,
+      pf_issue_one<FMT, BM, NF, SK, true>(d, stage_lds, arow, brow, sk, kc, wave_u, N, a[i].x,
                                           i + 1 < MA ? a[i + 1 < MA ? i + 1 : i].x : last);
   }
 }
@@ -965,8 +999,9 @@ template <int FMT, int EPI, int BM, int NF, int RS, int KS, int SK>
 __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel(GemmArgs ga, WeightArgs W, EpiArgs ea) {
   using P = Pf<BM, NF, SK>;
   constexpr int kStages = P::kStages;
-  static_assert(!SK || (RS == 1 && KS == 1 && FMT != FMT_GPTQ),
-                "streamed scales: one wave per SIMD per workgroup, NVFP4 or MXFP4");
+  static_assert(kStages == 3 || kStages == 4, "the K loop is unrolled for 3 or 4 stages");
+  static_assert(!SK || (RS == 1 && KS == 1 && (FMT != FMT_GPTQ || SK == 1)),
+                "streamed scales: one wave per SIMD per workgroup; GPTQ codes as stored");
   // RS = 2: eight waves, two per SIMD; waves w and w + 4 take the same
   // columns and one half of the rows each (both dequantise the same codes),
   // so one wave's dequant and LDS reads overlap the other's MFMAs.  Only the
@@ -1043,10 +1078,26 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
   // 0..3 <- chunks 0..3 (chunks past the end re-read the last one)
   const uint32_t ring = lds_addr(smem);
   const uint32_t sc_lds = ring + kStages * P::kStage;
-  // SK: this lane's scale-run source, tile row 64*wave + lane of chunk 0
-  const int skc_chunks = FMT == FMT_NVFP4 ? K / 64 : (K + 127) / 128;
-  const uint8_t* skc = SK ? W.scales_kc + ((size_t)e * skc_chunks * N + min(nt0 + 64 * wave_u + lane, N - 1)) * 4
-                          : nullptr;
+  // SK: this lane's scale-run source for chunk 0 (the wave's tile rows
+  // 64*wave .. 64*wave+63; rows past N re-read the last row)
+  SkSrc skc{nullptr, 0u, 0};
+  if constexpr (SK != 0 && FMT == FMT_GPTQ) {
+    const int ng = K / W.group, c0 = nt0 + 64 * wave_u;
+    skc.gsh = 31 - __builtin_clz((unsigned)(W.group / 64));
+    if (lane < 32) {
+      skc.p = W.scales + ((size_t)e * ng * N + min(c0 + 2 * lane, N - 2)) * 2;
+      skc.stride = (uint32_t)N * 2;
+    } else {
+      skc.p = reinterpret_cast<const uint8_t*>(W.zeros) +
+              ((size_t)e * ng * (N / 8) + min(c0 / 8 + min(lane - 32, 7), N / 8 - 1)) * 4;
+      skc.stride = (uint32_t)N / 2;
+    }
+  } else if constexpr (SK != 0) {
+    const int chunks = FMT == FMT_NVFP4 ? K / 64 : (K + 127) / 128;
+    skc.p = W.scales_kc + ((size_t)e * chunks * N + min(nt0 + 64 * wave_u + lane, N - 1)) * 4;
+    skc.stride = (uint32_t)N * 4;
+    skc.gsh = FMT == FMT_NVFP4 ? 0 : 1;
+  }
   const int nchunks = K / kPfBK;  // (K < 64: only the 32-wide tail, no LDS)
   if (nchunks == 0 || !dma_wave || SK) {
   } else if (FMT == FMT_NVFP4) {
@@ -1141,8 +1192,11 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
       pf_read_a<MI, MA>(a0, smem + aoff, c, h, 0);
 #pragma unroll
       for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
-      for (int kc = 0; kc < nchunks; ++kc) {
-        const uint8_t* st = smem + (kc % kStages) * P::kStage + aoff;
+      // one chunk, in ring stage ST = kc % kStages (a constant, so every LDS
+      // read of the chunk is a lane offset plus an immediate)
+      auto chunk = [&](int kc, auto st_tag) {
+        constexpr int ST = decltype(st_tag)::value, NX = (ST + 1) % kStages;
+        const uint8_t* st = smem + ST * P::kStage + aoff;
         // steps 0..2: each overlaps the next step's A reads and dequant
         pf_read_a<MI, MA>(a1, st, c, h, 1);
 #pragma unroll
@@ -1158,20 +1212,20 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
         pf_mfma<MI, NF, MA>(acc, a0, q0);
         // step 3 overlaps chunk kc+1's reads: chunk kc+1 has landed (all but the
         // two newest chunks' DMA are done) and every wave is past its reads of
-        // chunk kc, whose stage is refilled with chunk kc+4
+        // chunk kc, whose stage is refilled with chunk kc+kStages
         wait_vmcnt<(kStages - 2) * P::kIssue>();
         pf_barrier();
-        const uint8_t* nx = smem + ((kc + 1) % kStages) * P::kStage;
+        const uint8_t* nx = smem + NX * P::kStage;
         if constexpr (SK != 0) {
           // every wave copies (one per SIMD): its DMA goes between step 3's rows
           pf_read_b<FMT, EPI, NF, SK>(b, nx + P::kABytes, nx + P::kABytes + P::kBBytes, rl,
                                       min(kc + 1, nchunks - 1), h, K, W.group, P::BN);
           pf_read_a<MI, MA>(a0, nx + aoff, c, h, 0);
-          pf_mfma_issue<FMT, BM, NF, SK, MI, MA>(acc, a1, q1, ring + (kc % kStages) * P::kStage, arow,
-                                                 brow, skc, min(kc + kStages, nchunks - 1), wave_u, N);
+          pf_mfma_issue<FMT, BM, NF, SK, MI, MA>(acc, a1, q1, ring + ST * P::kStage, arow, brow, skc,
+                                                 min(kc + kStages, nchunks - 1), wave_u, N);
         } else {
           if (dma_wave)
-            pf_issue<FMT, BM, NF, SK>(ring + (kc % kStages) * P::kStage, arow, brow, skc,
+            pf_issue<FMT, BM, NF, SK>(ring + ST * P::kStage, arow, brow, skc,
                                       min(kc + kStages, nchunks - 1), wave_u, N);
           pf_read_b<FMT, EPI, NF, SK>(b, nx + P::kABytes, scale_lds, rl, min(kc + 1, nchunks - 1), h, K,
                                       W.group, P::BN);
@@ -1180,7 +1234,19 @@ __global__ void __launch_bounds__(256 * RS * KS, SK ? 2 : 1) gemm_prefill_kernel
         }
 #pragma unroll
         for (int j = 0; j < NF; ++j) q0[j] = pf_deq_step<FMT>(b[j], 0);
+      };
+      // kStages chunks per trip, then the last nchunks % kStages
+      int kc = 0;
+      for (; kc + kStages <= nchunks; kc += kStages) {
+        chunk(kc, std::integral_constant<int, 0>{});
+        chunk(kc + 1, std::integral_constant<int, 1>{});
+        chunk(kc + 2, std::integral_constant<int, 2>{});
+        if constexpr (kStages == 4) chunk(kc + 3, std::integral_constant<int, 3 % kStages>{});
       }
+      if (kc < nchunks) chunk(kc++, std::integral_constant<int, 0>{});
+      if (kc < nchunks) chunk(kc++, std::integral_constant<int, 1>{});
+      if constexpr (kStages == 4)
+        if (kc < nchunks) chunk(kc++, std::integral_constant<int, 2>{});
     };
     if ((SK != 0 && n0 >= N) || nact_w == 0) {
       // every weight row of this wave lies past N (the last column tile), or
@@ -1984,13 +2050,20 @@ static void launch_decode(GemmArgs ga, const WeightArgs& W, const EpiArgs& ea, i
   launch_decode_nf<FMT, EPI, MI, 2>(ga, W, ea, (long)blocks_est * ((ga.N + 31) / 32), st);
 }
 
-// The streaming (prefill) kernel's tiles fit: the tile's scales for the whole
-// K in its LDS (the resident-scale variant), GPTQ zero-point rows in 16-byte
-// pieces.  Otherwise 64/128-row blocks run the split-K kernel on 32-row
-// sub-blocks.
-static inline bool prefill_fits(int fmt, int K, int N, int group) {
-  return pf_scale_bytes(fmt, K, group, Pf<128, 2>::BN) <= kPfScaleBytes &&
-         !(fmt == FMT_GPTQ && N % 32 != 0);
+// The streaming (prefill) kernel reads each chunk's scales with its codes
+// (no resident scale tile, any K): NVFP4/MXFP4 given the scales by K chunk,
+// GPTQ with groups of 64 * 2^j rows (a chunk then lies in one group, whose
+// scale and zero-point rows the checkpoint stores contiguous over N).
+static inline bool prefill_streams(int fmt, int group, bool scales_kc) {
+  return fmt == FMT_GPTQ ? group >= 64 && (group & (group - 1)) == 0 : scales_kc;
+}
+// The streaming kernel's tiles fit: scales streamed, or the tile's scales for
+// the whole K in its LDS (the resident-scale variant); GPTQ zero-point rows in
+// 16-byte pieces.  Otherwise 64/128-row blocks run the split-K kernel on
+// 32-row sub-blocks.
+static inline bool prefill_fits(int fmt, int K, int N, int group, bool streams) {
+  if (fmt == FMT_GPTQ && N % 32 != 0) return false;
+  return streams || pf_scale_bytes(fmt, K, group, Pf<128, 2>::BN) <= kPfScaleBytes;
 }
 
 template <int FMT, int EPI>
@@ -2007,7 +2080,8 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
       launch_decode<FMT, EPI, 2>(ga, W, ea, blocks_est, kernel, st);
   } else {
     // widest tile whose scales fit the kernel's LDS; otherwise the split-K kernel
-    if (!prefill_fits(FMT, ga.K, ga.N, W.group)) {
+    const bool streams = prefill_streams(FMT, W.group, W.scales_kc != nullptr);
+    if (!prefill_fits(FMT, ga.K, ga.N, W.group, streams)) {
       if (ga.tiles != nullptr) return hipErrorInvalidValue;
       // very long K (scales too large for LDS), or GPTQ zero-point rows that
       // are not 16-byte multiples: the split-K kernel over 32-row sub-blocks
@@ -2020,8 +2094,17 @@ static hipError_t launch_epi(int block_m, int cap, GemmArgs ga, const WeightArgs
     ga.group_m = 4;  // measured flat between 1 and 16 at the gpt-oss-20b shape
     const dim3 grid((ga.n_mblocks * ga.n_ntiles + 7) / 8 * 8);
     constexpr int kThreads = 256 * pf_rs<FMT>() * pf_ks<FMT>();
-    if constexpr (FMT != FMT_GPTQ) {
-      if (W.scales_kc != nullptr) {
+    if constexpr (FMT == FMT_GPTQ) {
+      if (streams) {
+        // scale and zero-point rows streamed: two 256-thread workgroups per CU
+        if (block_m == 64)
+          gemm_prefill_kernel<FMT, EPI, 64, 2, 1, 1, 1><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+        else
+          gemm_prefill_kernel<FMT, EPI, 128, 2, 1, 1, 1><<<grid, dim3(256), 0, st>>>(ga, W, ea);
+        return hipGetLastError();
+      }
+    } else {
+      if (streams) {
         // scales (and codes) by K chunk: two 256-thread workgroups per CU
         if (W.qweight_kc != nullptr) {
           if (block_m == 64)
@@ -2426,8 +2509,8 @@ extern "C" hipError_t moe_launch_gemm_mx(int epi, int block_m, int cap, const ui
   return hipGetLastError();
 }
 
-extern "C" int moe_prefill_tiles_ok(int fmt, int K, int N, int group) {
-  return moe::prefill_fits(fmt, K, N, group) ? 1 : 0;
+extern "C" int moe_prefill_tiles_ok(int fmt, int K, int N, int group, int scales_kc) {
+  return moe::prefill_fits(fmt, K, N, group, moe::prefill_streams(fmt, group, scales_kc != 0)) ? 1 : 0;
 }
 
 extern "C" hipError_t moe_launch_sum(const uint16_t* y, const int32_t* ids, int T, int top_k, int H,

@@ -343,7 +343,9 @@ def test_gemm2_k_tails(K, B, policy):
 
 @pytest.mark.parametrize("fmt,K,N,group,B", [
     ("nvfp4", 12320, 96, None, 64),    # scales too long for LDS: split-K kernel on 32-row sub-blocks
-    ("gptq", 2560, 128, 32, 128),      # GPTQ group 32: narrow (128-column) prefill tiles
+    ("gptq", 2560, 128, 32, 128),      # GPTQ group 32: scales resident in LDS, K split over 8 waves
+    ("gptq", 2560, 96, 128, 128),      # group 128: scale rows streamed, one per two chunks; ragged N
+    ("gptq", 12288, 64, 128, 64),      # K too long for resident scales: streamed
     ("gptq", 256, 80, 64, 64),         # N % 32 != 0: split-K kernel on 32-row sub-blocks
     ("mxfp4", 2880, 320, None, 128),   # MXFP4 at the gpt-oss K, ragged last column tile
 ])
