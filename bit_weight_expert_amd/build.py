@@ -13,6 +13,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_w4a16.so")
 SOURCES = ["api.hip", "route_align.hip", "gemm.hip", "act_order.hip", "mxfp8.hip", "nvfp4_chunk.hip"]
+# gemm_inst.hip is built once per (weight format, epilogue) pair: formats
+# NVFP4 / MXFP4 / GPTQ = 0 / 1 / 2, epilogues swigluoai / ReLU^2 / none /
+# down projection = 0 / 1 / 2 / 3.
+INSTANCES = [(f, e) for f in range(3) for e in range(4)]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [
@@ -23,8 +27,8 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, obj: str, defines=()) -> None:
+    cmd = [HIPCC, *FLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -34,9 +38,15 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source and link the shared library; returns its path."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        list(ex.map(_compile, SOURCES, objs))
+    jobs = [(s, os.path.join(objdir, s.replace(".hip", ".o")), ()) for s in SOURCES]
+    jobs += [("gemm_inst.hip", os.path.join(objdir, f"gemm_inst_{f}_{e}.o"),
+              (f"-DMOE_FMT={f}", f"-DMOE_EPI={e}")) for f, e in INSTANCES]
+    objs = [j[1] for j in jobs]
+    # the instantiation units first: they take the longest
+    jobs.sort(key=lambda j: j[0] != "gemm_inst.hip")
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda j: _compile(*j), jobs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -229,3 +229,32 @@ def test_mxfp4_forward_by_chunk_full_size():
     assert np.isfinite(got).all()
     err = assert_rows_close(got[toks], O.forward_tokens(L, toks), what="mxfp4 by chunk full size")
     print(f"mxfp4 by chunk full size: max rel err {err:.3e} over {len(toks)} tokens", flush=True)
+
+
+# ------------------------------------------------------------ uneven loads --
+# 128-row blocks on the streamed-scale kernels with experts of 1 to 5 blocks.
+
+@pytest.mark.parametrize("fmt,act", [("nvfp4", "swigluoai"), ("nvfp4", "relu2"),
+                                     ("mxfp4", "swigluoai"), ("gptq", "swigluoai"),
+                                     ("gptq", "relu2")])
+@pytest.mark.parametrize("H,I", [(320, 192), (2880, 384)])
+def test_forward_uneven_loads(fmt, act, H, I):
+    """Uneven loads over 5 experts (from one 128-row block to five, odd and
+    even counts); every output row against the oracle."""
+    route = "sigmoid_bias" if act == "relu2" else "softmax"
+    L = S.make_layer(E=5, top_k=2, H=H, I=I, fmt=fmt, act=act, route=route, T=700, seed=61,
+                     skew_std=0.8, router_bias_std=0.1 if route == "sigmoid_bias" else 0.0)
+    ids, _ = O.route(L)
+    blocks = -(-np.bincount(ids.reshape(-1), minlength=L.E) // 128)
+    assert M.moe_forward_block_m(L.T, L.top_k, L.E) == 128
+    assert (blocks % 2 == 1).any() and (blocks >= 4).any(), blocks
+    D = upload(L)
+    if fmt == "nvfp4":
+        D["w13"], D["w2"] = with_kc(D["w13"], True), with_kc(D["w2"], True)
+    elif fmt == "mxfp4":
+        D["w13"], D["w2"] = with_kc_mx(D["w13"], True), with_kc_mx(D["w2"], True)
+    print(f"uneven loads {fmt} {act} H={H} I={I} blocks={blocks.tolist()}", flush=True)
+    out = gpu_forward(L, D)
+    got = host_bf16(out)
+    assert np.isfinite(got).all()
+    assert_rows_close(got, O.forward(L)["out"], what=f"uneven loads {fmt} {act} H{H} I{I}")
