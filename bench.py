@@ -16,9 +16,12 @@ with its roofline bound and fraction.
 Weight copies are rotated between calls so that no call finds its weights in
 the 256 MB last-level cache left behind by the previous one (enough copies
 that the touched experts of the copies together exceed it).  The weights are
-loaded as a user of the library loads them: the checkpoint bytes plus, for
-NVFP4 and MXFP4, the scales and codes re-laid by K chunk (moe_*_scales_by_chunk
-and moe_*_codes_by_chunk, done once at load time).
+loaded as a user of the library loads them: NVFP4 and MXFP4 families are
+re-laid by K chunk once at load time (moe_*_scales_by_chunk and
+moe_*_codes_by_chunk) and the checkpoint layout is then dropped, so one copy
+of the codes stays on the device and every kernel reads that layout
+(--no-codes-by-chunk keeps the checkpoint codes beside the scales by chunk,
+--checkpoint-scales the checkpoint layout alone); GPTQ has one layout.
 
 The dominant kernel (GEMM1 at the headline size) is timed on its own with one
 HIP event pair around each launch, on the stream it is launched on; the mean
@@ -216,11 +219,11 @@ def mxfp8_leg(args, time_calls):
     dev = torch.device("cuda")
     copies = []
     for _ in range(max(1, min(args.copies, 3))):   # 3 x 2.4 GB: each call misses the 256 MB cache
-        pair = tuple(M.QuantWeights.from_arrays(w.fmt, w.group, w.N, w.K, w.qweight, w.scales,
-                                                None, None, w.bias) for w in (L.w13, L.w2))
-        for w in pair:   # the MX kernels' copy of the codes by 128-deep K chunk (load time)
-            w.qweight_kc = M.moe_mxfp4_codes_by_chunk(w)
-        copies.append(pair)
+        # chunked-only families, as the bf16 legs hold them (the MX kernels read
+        # the codes and scales by 128-deep K chunk)
+        copies.append(tuple(M.QuantWeights.from_arrays(w.fmt, w.group, w.N, w.K, w.qweight,
+                                                       w.scales, None, None, w.bias).chunked_only()
+                            for w in (L.w13, L.w2)))
     x = torch.from_numpy(L.x.view(np.int16)).to(dev).view(torch.bfloat16)
     logits = torch.from_numpy(L.logits).to(dev)
     tmax = max(ts)
@@ -261,9 +264,10 @@ def mxfp8_leg(args, time_calls):
                         "skewed routing), bf16 vs MXFP8 activations", "rows": rows}
 
 
-def upload_copies(L, n, chunked=True):
+def upload_copies(L, n, chunked=True, codes=True):
     """n device copies of the layer's two weight families (the same bytes);
-    NVFP4 families also get the load-time copies by K chunk."""
+    NVFP4 and MXFP4 families also get the load-time scales by K chunk and,
+    with `codes`, the codes by K chunk."""
     import bit_weight_expert_amd as M
     copies = []
     for _ in range(n):
@@ -271,12 +275,12 @@ def upload_copies(L, n, chunked=True):
         for w in (L.w13, L.w2):
             d = M.QuantWeights.from_arrays(w.fmt, w.group, w.N, w.K, w.qweight, w.scales, w.zeros,
                                            w.global_scale, w.bias)
-            if chunked and w.fmt == "nvfp4" and w.K % 64 == 0:
-                d.scales_kc = M.moe_nvfp4_scales_by_chunk(d)
-                d.qweight_kc = M.moe_nvfp4_codes_by_chunk(d)
-            elif chunked and w.fmt == "mxfp4":
-                d.scales_kc = M.moe_mxfp4_scales_by_chunk(d)
-                d.qweight_kc = M.moe_mxfp4_codes_by_chunk(d)
+            kc_ok = w.fmt == "mxfp4" or (w.fmt == "nvfp4" and w.K % 64 == 0)
+            if chunked and kc_ok and codes:
+                d = d.chunked_only()            # the checkpoint copy is freed here
+            elif chunked and kc_ok:
+                d.scales_kc = (M.moe_nvfp4_scales_by_chunk(d) if w.fmt == "nvfp4"
+                               else M.moe_mxfp4_scales_by_chunk(d))
             pair.append(d)
         copies.append(tuple(pair))
     return copies
@@ -309,6 +313,8 @@ def main() -> int:
                     help="also time GEMM1 and GEMM2 alone at every T of the headline sweep")
     ap.add_argument("--checkpoint-scales", action="store_true",
                     help="run on the checkpoint layout only (no scales or codes by K chunk)")
+    ap.add_argument("--no-codes-by-chunk", action="store_true",
+                    help="scales by K chunk only: the codes stay in the checkpoint layout")
     ap.add_argument("--act-order", action="store_true",
                     help="also time the GPTQ layer with act-order weights (and its gather)")
     ap.add_argument("--act-order-tokens", default="1,64,2048")
@@ -409,7 +415,8 @@ def main() -> int:
     L = S.make_config(2)
     assert L.T >= max(sweep)
     log(f"generated the {S.CONFIGS[2]['name']} inputs in {time.time() - t0:.1f}s")
-    copies = upload_copies(L, args.copies, chunked=not args.checkpoint_scales)
+    copies = upload_copies(L, args.copies, chunked=not args.checkpoint_scales,
+                           codes=not args.no_codes_by_chunk)
     torch.cuda.synchronize()
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -484,7 +491,8 @@ def main() -> int:
             lg = torch.from_numpy(Lc.logits[:min(ts)]).to(dev)
             eb = None if Lc.expert_bias is None else torch.from_numpy(Lc.expert_bias).to(dev)
             ids_small = M.moe_route(lg, Lc.top_k, Lc.route, eb, Lc.renormalize)[0].cpu().numpy()
-            cps = upload_copies(Lc, copies_for(Lc, ids_small))
+            cps = upload_copies(Lc, copies_for(Lc, ids_small), chunked=not args.checkpoint_scales,
+                                codes=not args.no_codes_by_chunk)
             crow, _ = layer_leg(Lc, ts, cps, args.steps)
             configs[f"config{cfg}"] = {"workload": c["name"], "weight_copies_rotated": len(cps),
                                        "rows": [{k: (round(v, 6) if isinstance(v, float) else v)
@@ -538,7 +546,9 @@ def main() -> int:
                                f"T={args.tokens} tokens",
                    "tokens": args.tokens, "block_m": head["block_m"],
                    "weight_copies_rotated": args.copies,
-                   "nvfp4_by_chunk_copies": not args.checkpoint_scales},
+                   "scales_by_chunk": not args.checkpoint_scales,
+                   "codes_by_chunk": not (args.checkpoint_scales or args.no_codes_by_chunk),
+                   "checkpoint_codes_resident": args.checkpoint_scales or args.no_codes_by_chunk},
         "roofline": {"kernel": "grouped GEMM1 (w13 + bias + swigluoai), gemm_prefill_kernel",
                      "bound": g_bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": profiled_traffic(),

@@ -154,8 +154,8 @@ class QuantWeights:
     group: int
     N: int
     K: int
-    qweight: torch.Tensor
-    scales: torch.Tensor
+    qweight: torch.Tensor | None          # None in a chunked-only family (see chunked_only)
+    scales: torch.Tensor | None
     zeros: torch.Tensor | None = None
     global_scale: torch.Tensor | None = None
     bias: torch.Tensor | None = None
@@ -186,7 +186,27 @@ class QuantWeights:
 
     @property
     def E(self) -> int:
-        return self.qweight.shape[0]
+        return (self.qweight if self.qweight is not None else self.qweight_kc).shape[0]
+
+    def chunked_only(self) -> "QuantWeights":
+        """NVFP4/MXFP4: the same family holding only the copies by K chunk
+        (codes and scales; made here if absent), which every kernel reads
+        instead of the checkpoint layout: one copy of the codes on the device."""
+        import dataclasses
+        if self.fmt not in ("nvfp4", "mxfp4"):
+            raise ValueError("only NVFP4 and MXFP4 have a layout by K chunk")
+        kc = self
+        if self.fmt == "nvfp4":
+            if kc.scales_kc is None:
+                kc = dataclasses.replace(kc, scales_kc=moe_nvfp4_scales_by_chunk(kc))
+            if kc.qweight_kc is None:
+                kc = dataclasses.replace(kc, qweight_kc=moe_nvfp4_codes_by_chunk(kc))
+        else:
+            if kc.scales_kc is None:
+                kc = dataclasses.replace(kc, scales_kc=moe_mxfp4_scales_by_chunk(kc))
+            if kc.qweight_kc is None:
+                kc = dataclasses.replace(kc, qweight_kc=moe_mxfp4_codes_by_chunk(kc))
+        return dataclasses.replace(kc, qweight=None, scales=None)
 
 
 def moe_align_capacity(T: int, top_k: int, E: int, block_m: int) -> int:
@@ -355,8 +375,8 @@ def moe_nvfp4_scales_by_chunk(w: "QuantWeights") -> torch.Tensor:
 
 def moe_nvfp4_codes_by_chunk(w: "QuantWeights") -> torch.Tensor:
     """NVFP4 codes [E, N, K/2] re-laid by 64-deep K chunk -> uint8 [E, K/64, N, 32]
-    (set it as w.qweight_kc, together with w.scales_kc, for the 64/128-row GEMM kernel;
-    it is a second copy of the codes: the 1..64-token kernels keep reading w.qweight)."""
+    (set it as w.qweight_kc, together with w.scales_kc: every kernel then reads it in
+    place of w.qweight, which may be dropped, see QuantWeights.chunked_only)."""
     if w.fmt != "nvfp4":
         raise ValueError("codes by chunk are an NVFP4 layout")
     _dev(w.qweight, torch.uint8, "qweight")
@@ -369,7 +389,7 @@ def moe_nvfp4_codes_by_chunk(w: "QuantWeights") -> torch.Tensor:
 
 def moe_mxfp4_codes_by_chunk(w: "QuantWeights") -> torch.Tensor:
     """MXFP4 codes [E, N, K/2] re-laid by 128-deep K chunk -> uint8 [E, ceil(K/128), N, 64],
-    zero past K (set it as w.qweight_kc for the MXFP8-activation kernels)."""
+    zero past K (set it as w.qweight_kc: every kernel then reads it in place of w.qweight)."""
     if w.fmt != "mxfp4":
         raise ValueError("this re-layout is for MXFP4 codes")
     _dev(w.qweight, torch.uint8, "qweight")
@@ -382,8 +402,8 @@ def moe_mxfp4_codes_by_chunk(w: "QuantWeights") -> torch.Tensor:
 
 def moe_mxfp4_scales_by_chunk(w: "QuantWeights") -> torch.Tensor:
     """MXFP4 e8m0 scales [E, N, K/32] re-laid by 128-deep K chunk -> uint8
-    [E, ceil(K/128), N, 4], zero past K/32 (set it as w.scales_kc for the
-    streaming 64/128-row GEMM kernel)."""
+    [E, ceil(K/128), N, 4], zero past K/32 (set it as w.scales_kc: every kernel
+    then reads it in place of w.scales)."""
     if w.fmt != "mxfp4":
         raise ValueError("this re-layout is for MXFP4 scales")
     _dev(w.scales, torch.uint8, "scales")

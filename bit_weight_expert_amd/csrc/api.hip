@@ -65,7 +65,11 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ER
 // allow_perm: the caller gathers the GEMM input through w->k_perm itself.
 moe_status_t check_weights(const moe_wq_t* w, int N, int K, moe::WeightArgs* out,
                            bool allow_perm = false) {
-  if (w == nullptr || w->qweight == nullptr || w->scales == nullptr) return MOE_ERR_NULL;
+  if (w == nullptr) return MOE_ERR_NULL;
+  // chunked-only NVFP4/MXFP4 family: both copies by K chunk and no checkpoint layout
+  const bool kc_only = (w->fmt == MOE_W_NVFP4 || w->fmt == MOE_W_MXFP4) && w->qweight == nullptr &&
+                       w->scales == nullptr && w->qweight_kc != nullptr && w->scales_kc != nullptr;
+  if (!kc_only && (w->qweight == nullptr || w->scales == nullptr)) return MOE_ERR_NULL;
   if (K <= 0 || N <= 0 || K % 32 != 0 || N % 16 != 0) return MOE_ERR_SHAPE;
   switch (w->fmt) {
     case MOE_W_NVFP4:

@@ -170,15 +170,24 @@ __device__ __forceinline__ void mx_mfma(f32x16e (&acc)[MI][NF], const MxOps<MI, 
 
 // Scale words of chunk kc: A dword of blocks 4kc..4kc+3 shifted so bytes 0 / 2
 // are this lane's blocks of steps 0 / 1; weight bytes likewise (blocks past
-// K/32 read as 2^0: their A codes are zero).
+// K/32 read as 2^0: their A codes are zero).  kcs: the weight scale tile is
+// [chunk][256 rows][4] (scales by K chunk; blocks past K/32 are zero bytes,
+// a finite 2^-127 against zero A codes).
 template <int MI, int NF>
 __device__ __forceinline__ void mx_scales(int (&sa)[MI], int (&sb)[NF], const uint8_t* sca, int lds,
                                           const uint8_t* scb, int kb, const int (&rl)[NF], int c,
-                                          int g, int kc, int r0) {
+                                          int g, int kc, int r0, bool kcs) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
     sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sca + (r0 + 32 * i + c) * lds + 4 * kc) >> (8 * g));
   const int b0 = 4 * kc + g, b1 = 4 * kc + 2 + g;
+  if (kcs) {
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+      sb[j] = (int)((*reinterpret_cast<const uint32_t*>(scb + kc * 1024 + rl[j] * 4) >> (8 * g)) &
+                    0x00FF00FFu);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     const uint8_t* sr = scb + rl[j] * kb;
@@ -259,9 +268,16 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA m
   const uint8_t* sca = scb + scb_bytes;
   const int nchunks = (K + kMxBK - 1) / kMxBK;
 
-  // weight scales of the tile rows (contiguous), then the A scale rows
+  // weight scales of the tile rows (contiguous; by K chunk: one kilobyte,
+  // [256 rows][4], per 128-deep chunk), then the A scale rows
+  const bool kcs = W.scales_kc != nullptr;
+  if (kcs) {
+    const uint8_t* src = W.scales_kc + ((size_t)e * nchunks * N + nt0) * 4;
+    for (int q = wave; q < nchunks; q += NW)
+      if (16 * lane < 4 * rows) dma16(src + (size_t)q * N * 4 + 16 * lane, scb_lds + q * 1024);
+  }
   {
-    const int nb = rows * kb;   // a multiple of 16 (N % 16 == 0)
+    const int nb = kcs ? 0 : rows * kb;   // a multiple of 16 (N % 16 == 0)
     const uint8_t* src = W.scales + ((size_t)e * N + nt0) * kb;
     for (int q = wave; q * 1024 < nb; q += NW)
       if (q * 1024 + 16 * lane < nb) dma16(src + q * 1024 + 16 * lane, scb_lds + q * 1024);
@@ -311,7 +327,7 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA m
   pf_barrier();
   MxOps<MI, NF> o0, o1;
   int sa[MI], sb[NF];
-  mx_scales<MI, NF>(sa, sb, sca, ma.lds, scb, kb, rl, c, g, 0, r0);
+  mx_scales<MI, NF>(sa, sb, sca, ma.lds, scb, kb, rl, c, g, 0, r0, kcs);
   mx_read<MI, NF, 0>(o0, smem, P::kABytes, bpos, c, g, r0);
   if (n0 >= N) {
     // every weight row of this wave lies past N (the last column tile): only
@@ -333,7 +349,7 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA m
     issue(ring + (kc % kMxStages) * P::kStage, min(kc + kMxStages, nchunks - 1));
     int na_[MI], nb_[NF];
     const int kn = min(kc + 1, nchunks - 1);
-    mx_scales<MI, NF>(na_, nb_, sca, ma.lds, scb, kb, rl, c, g, kn, r0);
+    mx_scales<MI, NF>(na_, nb_, sca, ma.lds, scb, kb, rl, c, g, kn, r0, kcs);
     mx_read<MI, NF, 0>(o0, smem + (kn % kMxStages) * P::kStage, P::kABytes, bpos, c, g, r0);
     mx_mfma<MI, NF, 1>(acc, o1, sa, sb);
 #pragma unroll

@@ -94,14 +94,40 @@ __device__ __forceinline__ void zero_chunk(BChunk<FMT, C>& b) {
   b.zsh = 0;
 }
 
+// Codes and scale bytes of weight row n of expert e from k = kl on (NVFP4 and
+// MXFP4), in whichever layout the family holds: the checkpoint rows ([E][N][K/2]
+// codes, [E][N][K/G] scales) or the copies by K chunk ([E][KC][N][CH/2] codes,
+// [E][KC][N][4] scales, CH = 64 for NVFP4 and 128 for MXFP4, KC = ceil(K/CH)).
+// A lane's range never crosses a chunk: it is at most 64 deep and aligned.
+template <int FMT>
+__device__ __forceinline__ const uint8_t* codes_at(const WeightArgs& W, int e, int n, int N, int K,
+                                                   int kl) {
+  if (W.qweight_kc != nullptr) {
+    constexpr int CH = FMT == FMT_NVFP4 ? 64 : 128;
+    const int kcn = (K + CH - 1) / CH;
+    return W.qweight_kc + (((size_t)e * kcn + kl / CH) * N + n) * (CH / 2) + (kl % CH) / 2;
+  }
+  return W.qweight + ((size_t)e * N + n) * (size_t)(K / 2) + kl / 2;
+}
+template <int FMT>
+__device__ __forceinline__ const uint8_t* scales_at(const WeightArgs& W, int e, int n, int N, int K,
+                                                    int kl) {
+  constexpr int G = FMT == FMT_NVFP4 ? 16 : 32;
+  if (W.scales_kc != nullptr) {
+    constexpr int CH = 4 * G;
+    const int kcn = (K + CH - 1) / CH;
+    return W.scales_kc + (((size_t)e * kcn + kl / CH) * N + n) * 4 + (kl % CH) / G;
+  }
+  return W.scales + ((size_t)e * N + n) * (size_t)(K / G) + kl / G;
+}
+
 // Load the lane's k range [kl, kl + C/4) of weight row n of expert e.
 template <int FMT, int C>
 __device__ __forceinline__ void load_chunk(BChunk<FMT, C>& b, const WeightArgs& W, int e, int n,
                                            int N, int K, int kl) {
   constexpr int S = BChunk<FMT, C>::kSteps;
   if (FMT == FMT_NVFP4 || FMT == FMT_MXFP4) {
-    const size_t row = (size_t)e * N + n;
-    const uint8_t* p = W.qweight + row * (size_t)(K / 2) + kl / 2;
+    const uint8_t* p = codes_at<FMT>(W, e, n, N, K, kl);
     if (S >= 4) {
 #pragma unroll
       for (int v = 0; v < S / 4; ++v) {
@@ -118,9 +144,9 @@ __device__ __forceinline__ void load_chunk(BChunk<FMT, C>& b, const WeightArgs& 
     } else {
       b.q[0] = *reinterpret_cast<const uint32_t*>(p);
     }
+    const uint8_t* sp = scales_at<FMT>(W, e, n, N, K, kl);
     if (FMT == FMT_NVFP4) {
       // K % 32 == 0 makes K/16 even, so scale pairs are 2-byte aligned
-      const uint8_t* sp = W.scales + row * (size_t)(K / 16) + kl / 16;
       if (C == 256) {
         b.sr[0] = *reinterpret_cast<const uint16_t*>(sp);
         b.sr[1] = *reinterpret_cast<const uint16_t*>(sp + 2);
@@ -130,7 +156,6 @@ __device__ __forceinline__ void load_chunk(BChunk<FMT, C>& b, const WeightArgs& 
         b.sr[0] = *sp;
       }
     } else {
-      const uint8_t* sp = W.scales + row * (size_t)(K / 32) + kl / 32;
       b.sr[0] = sp[0];
       if (C == 256) b.sr[1] = sp[1];
     }
@@ -152,7 +177,7 @@ __device__ __forceinline__ void load_codes(BChunk<FMT, C>& b, const WeightArgs& 
                                            int N, int K, int kl) {
   constexpr int S = BChunk<FMT, C>::kSteps;
   if (FMT == FMT_NVFP4 || FMT == FMT_MXFP4) {
-    const uint8_t* p = W.qweight + ((size_t)e * N + n) * (size_t)(K / 2) + kl / 2;
+    const uint8_t* p = codes_at<FMT>(W, e, n, N, K, kl);
     if (S >= 4) {
 #pragma unroll
       for (int v = 0; v < S / 4; ++v) {
@@ -335,7 +360,7 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[MI][NF], const EpiAr
   const float gsc = acc_scale<FMT>(W, e, poison);
   // bias: unconditional loads (another valid word when there is none)
   const bool has_bias = W.bias != nullptr;
-  const uint16_t* bbase = has_bias ? W.bias : reinterpret_cast<const uint16_t*>(W.qweight);
+  const uint16_t* bbase = has_bias ? W.bias : reinterpret_cast<const uint16_t*>(W.qweight != nullptr ? W.qweight : W.qweight_kc);
   const int bmul = has_bias ? 1 : 0;
   float bias[NF];
 #pragma unroll
@@ -892,7 +917,7 @@ __device__ __forceinline__ void epilogue32(const f32x16 (&acc)[MI][NF], const Ep
   const float gsc = acc_scale<FMT>(W, e, poison);
   // bias: unconditional loads (another valid word when there is none)
   const bool has_bias = W.bias != nullptr;
-  const uint16_t* bbase = has_bias ? W.bias : reinterpret_cast<const uint16_t*>(W.qweight);
+  const uint16_t* bbase = has_bias ? W.bias : reinterpret_cast<const uint16_t*>(W.qweight != nullptr ? W.qweight : W.qweight_kc);
   const int bmul = has_bias ? 1 : 0;
   float bias[NF];
   bool on[NF];
@@ -1370,10 +1395,13 @@ constexpr int kDcBK = 128;    // K chunk
 constexpr int kDcDepth = 4;   // chunks in flight per wave
 // LDS scale tile of one workgroup of R weight rows: NVFP4 [R rows][K/16]
 // e4m3 bytes, MXFP4 [R rows][K/32] e8m0 bytes, GPTQ [K/G][R columns] fp16
-// scales followed by [K/G][R/8] packed zero-point words.
+// scales followed by [K/G][R/8] packed zero-point words.  With the scales by
+// K chunk the NVFP4/MXFP4 tile keeps that layout, [KC][R rows][4 bytes]
+// (64-deep chunks for NVFP4, 128-deep for MXFP4), so it copies in runs of
+// 4R bytes; the MXFP4 size covers both layouts.
 __host__ __device__ inline int dc_scale_bytes(int fmt, int K, int group, int R) {
   if (fmt == FMT_NVFP4) return R * (K / 16);
-  if (fmt == FMT_MXFP4) return R * (K / 32);
+  if (fmt == FMT_MXFP4) return 4 * R * ((K + 127) / 128);
   return (K / group) * (R * 2 + R / 2);
 }
 
@@ -1382,7 +1410,18 @@ template <int FMT, int R>
 __device__ __forceinline__ void dc_stage_scales(uint8_t* sc, const WeightArgs& W, int e, int n0,
                                                 int N, int K, int tid, int nthreads) {
   const int rows = min(R, N - n0);  // a multiple of 16
-  if (FMT == FMT_NVFP4 || FMT == FMT_MXFP4) {
+  if ((FMT == FMT_NVFP4 || FMT == FMT_MXFP4) && W.scales_kc != nullptr) {
+    // [KC][R][4]: chunk c's 4 * rows bytes from its [N][4] row run
+    constexpr int CH = FMT == FMT_NVFP4 ? 64 : 128;
+    const int kcn = (K + CH - 1) / CH;
+    const uint8_t* src = W.scales_kc + ((size_t)e * kcn * N + n0) * 4;
+    for (int u = tid; u < kcn * (R / 4); u += nthreads) {
+      const int c = u / (R / 4), x = 16 * (u % (R / 4));
+      if (x < 4 * rows)
+        *reinterpret_cast<uint4*>(sc + c * 4 * R + x) =
+            *reinterpret_cast<const uint4*>(src + (size_t)c * N * 4 + x);
+    }
+  } else if (FMT == FMT_NVFP4 || FMT == FMT_MXFP4) {
     const int per_row = (FMT == FMT_NVFP4) ? K / 16 : K / 32;
     const uint8_t* src = W.scales + ((size_t)e * N + n0) * per_row;
     const int units = rows * per_row / 16;  // rows * per_row is a multiple of 16
@@ -1409,9 +1448,24 @@ __device__ __forceinline__ void dc_stage_scales(uint8_t* sc, const WeightArgs& W
 // that its loads go out ahead of the weight stream and need no registers;
 // the kernel waits for them with wait_vmcnt, counting the loads it issued
 // after them.
-template <int FMT>
+template <int FMT, int R>
 __device__ __forceinline__ void dc_dma_scales(uint8_t* sc, const WeightArgs& W, int e, int n0,
                                               int N, int K, int rows, int wave, int nw, int lane) {
+  if (W.scales_kc != nullptr) {
+    // [KC][R][4] (see dc_scale_bytes): 16-byte piece o of the tile is chunk
+    // o / 4R, bytes o % 4R of its row run (rows past N left unfilled)
+    constexpr int CH = FMT == FMT_NVFP4 ? 64 : 128;
+    const int kcn = (K + CH - 1) / CH;
+    const uint8_t* src = W.scales_kc + ((size_t)e * kcn * N + n0) * 4;
+    const int bytes = kcn * 4 * R;
+    const uint32_t base = lds_addr(sc);
+    for (int q = __builtin_amdgcn_readfirstlane(wave); q * 1024 < bytes; q += nw) {
+      const int o = q * 1024 + 16 * lane;
+      const int c = o / (4 * R), x = o % (4 * R);
+      if (o < bytes && x < 4 * rows) dma16(src + (size_t)c * N * 4 + x, base + q * 1024);
+    }
+    return;
+  }
   const int per_row = (FMT == FMT_NVFP4) ? K / 16 : K / 32;
   const uint8_t* src = W.scales + ((size_t)e * N + n0) * per_row;
   const int bytes = rows * per_row;  // a multiple of 16
@@ -1428,12 +1482,13 @@ __host__ __device__ inline int dc_scale_region(int fmt, int K, int group, int R)
 }
 
 // Raw scale words of one fragment for the lane's k range [kl, kl + C/4), from
-// the LDS tile (r = the fragment row's index inside the tile).
+// the LDS tile (r = the fragment row's index inside the tile; kc: the tile
+// has the by-chunk layout).
 template <int FMT, int C, int R>
 __device__ __forceinline__ void dc_fill_scales(BChunk<FMT, C>& b, const uint8_t* sc, int r, int K,
-                                               int group, int kl) {
+                                               int group, int kl, bool kc) {
   if (FMT == FMT_NVFP4) {
-    const uint8_t* sp = sc + r * (K / 16) + kl / 16;
+    const uint8_t* sp = kc ? sc + ((kl / 64) * R + r) * 4 + (kl % 64) / 16 : sc + r * (K / 16) + kl / 16;
     if (C == 256) {
       b.sr[0] = *reinterpret_cast<const uint16_t*>(sp);
       b.sr[1] = *reinterpret_cast<const uint16_t*>(sp + 2);
@@ -1443,7 +1498,7 @@ __device__ __forceinline__ void dc_fill_scales(BChunk<FMT, C>& b, const uint8_t*
       b.sr[0] = *sp;
     }
   } else if (FMT == FMT_MXFP4) {
-    const uint8_t* sp = sc + r * (K / 32) + kl / 32;
+    const uint8_t* sp = kc ? sc + ((kl / 128) * R + r) * 4 + (kl % 128) / 32 : sc + r * (K / 32) + kl / 32;
     b.sr[0] = sp[0];
     if (C == 256) b.sr[1] = sp[1];
   } else {
@@ -1494,12 +1549,13 @@ __device__ __forceinline__ void dc_load_a(DcA<C, MI>& d, const uint16_t* const (
 template <int FMT, int C, int MI, int NF, int R = 16 * NF>
 __device__ __forceinline__ void dc_compute(f32x4 (&acc)[MI][NF], const DcB<FMT, C, NF>& db,
                                            const DcA<C, MI>& da, const uint8_t* sc,
-                                           const int (&rl)[NF], int K, int group, int g, int k0) {
+                                           const int (&rl)[NF], int K, int group, int g, int k0,
+                                           bool kc) {
   BChunk<FMT, C> b[NF];
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     b[j] = db.b[j];
-    dc_fill_scales<FMT, C, R>(b[j], sc, rl[j], K, group, k0 + g * (C / 4));
+    dc_fill_scales<FMT, C, R>(b[j], sc, rl[j], K, group, k0 + g * (C / 4), kc);
   }
 #pragma unroll
   for (int s = 0; s < C / 32; ++s) {
@@ -1526,7 +1582,7 @@ __device__ __forceinline__ void dc_chunk(f32x4 (&acc)[MI][NF], const WeightArgs&
   DcA<C, MI> da;
   dc_load_b(db, W, ga, nrow, e, k0, g);
   dc_load_a(da, arow, k0, g);
-  dc_compute<FMT, C, MI, NF, R>(acc, db, da, sc, rl, ga.K, W.group, g, k0);
+  dc_compute<FMT, C, MI, NF, R>(acc, db, da, sc, rl, ga.K, W.group, g, k0, W.scales_kc != nullptr);
 }
 
 template <int FMT, int EPI, int MI, int NF>
@@ -1577,7 +1633,7 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
   if (n > 0 && FMT != FMT_GPTQ) {
     // (n is the same on all lanes of a wave, and every wave reaches exactly
     // one of the two barriers)
-    dc_dma_scales<FMT>(sc, W, e, n0, ga.N, K, srows, wave, nw, lane);
+    dc_dma_scales<FMT, 16 * NF>(sc, W, e, n0, ga.N, K, srows, wave, nw, lane);
     dc_load_b(b0, W, ga, nrow, e, c0 * kDcBK, g);
     dc_load_a(a0, arow, c0 * kDcBK, g);
     dc_load_b(b1, W, ga, nrow, e, min(c0 + 1, last) * kDcBK, g);
@@ -1606,6 +1662,7 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
     __syncthreads();
   }
   const int group = W.group;
+  const bool kc = W.scales_kc != nullptr;  // scale tile in the by-chunk layout
   // groups of four chunks in straight-line code (no exit between the
   // phases, so every prefetch is issued where it is written); chunk
   // c0 + i + d sits in b<d> and a<d % kADepth>; once multiplied its slots
@@ -1615,7 +1672,7 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
   for (int i = 0; i < n4; i += kDcDepth) {
 #define MOE_DC_PHASE(D, BS, AS)                                                                    \
     {                                                                                              \
-      dc_compute(acc, BS, AS, sc, rl, K, group, g, (c0 + i + D) * kDcBK);                          \
+      dc_compute(acc, BS, AS, sc, rl, K, group, g, (c0 + i + D) * kDcBK, kc);                      \
       dc_load_b(BS, W, ga, nrow, e, min(c0 + i + D + 4, last) * kDcBK, g);                         \
       dc_load_a(AS, arow, min(c0 + i + D + kADepth, last) * kDcBK, g);                             \
     }
@@ -1628,11 +1685,12 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmArgs ga, WeightArg
   // the run's last n % 4 chunks are already in the ring
   const int rem = n - n4;
   if (rem > 0) {
-    dc_compute(acc, b0, a0, sc, rl, K, group, g, (c0 + n4) * kDcBK);
+    dc_compute(acc, b0, a0, sc, rl, K, group, g, (c0 + n4) * kDcBK, kc);
     if (kADepth == 2 && rem > 2) dc_load_a(a0, arow, (c0 + n4 + 2) * kDcBK, g);
   }
-  if (rem > 1) dc_compute(acc, b1, a1, sc, rl, K, group, g, (c0 + n4 + 1) * kDcBK);
-  if (rem > 2) dc_compute(acc, b2, (kADepth == 4 ? a2 : a0), sc, rl, K, group, g, (c0 + n4 + 2) * kDcBK);
+  if (rem > 1) dc_compute(acc, b1, a1, sc, rl, K, group, g, (c0 + n4 + 1) * kDcBK, kc);
+  if (rem > 2)
+    dc_compute(acc, b2, (kADepth == 4 ? a2 : a0), sc, rl, K, group, g, (c0 + n4 + 2) * kDcBK, kc);
   // K tail (K % 128: a 64- and/or a 32-wide piece) on the last wave
   if (wave == nw - 1) {
     int k0 = nfull * kDcBK;
@@ -1733,7 +1791,7 @@ __device__ __forceinline__ void epi_prefetch_ids(EpiPre<MI, NF>& p, const EpiArg
   const int c16 = lane & 15, g = lane >> 4;
   p.gsc = (FMT == FMT_NVFP4) ? W.global_scale[e] : 1.f;
   const bool has_bias = W.bias != nullptr;
-  const uint16_t* bbase = has_bias ? W.bias : reinterpret_cast<const uint16_t*>(W.qweight);
+  const uint16_t* bbase = has_bias ? W.bias : reinterpret_cast<const uint16_t*>(W.qweight != nullptr ? W.qweight : W.qweight_kc);
   const int bmul = has_bias ? 1 : 0;
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
@@ -1844,12 +1902,12 @@ template <int FMT, int MI, int NF>
 __device__ __forceinline__ void wd_compute(f32x4 (&acc)[MI][NF], const DcB<FMT, kWdBK, NF>& db,
                                            const uint8_t* stage, const uint8_t* sc,
                                            const int (&rl)[NF], int K, int group, int g, int c16,
-                                           int kl) {
+                                           int kl, bool kc) {
   BChunk<FMT, kWdBK> b[NF];
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     b[j] = db.b[j];
-    dc_fill_scales<FMT, kWdBK, kWdCols>(b[j], sc, rl[j], K, group, kl);
+    dc_fill_scales<FMT, kWdBK, kWdCols>(b[j], sc, rl[j], K, group, kl, kc);
   }
 #pragma unroll
   for (int s = 0; s < kWdBK / 32; ++s) {
@@ -1899,7 +1957,8 @@ __global__ void __launch_bounds__(256, (MI == 1 ? 4 : 3)) gemm_wide_kernel(GemmA
   // slot ids and the epilogue's metadata, the codes of chunks 0 .. D-1, then
   // (once the slot ids are in -- which, loads retiring in order, also means
   // the DMA has landed) the A pieces of chunks 0 .. D-1.
-  if (FMT != FMT_GPTQ) dc_dma_scales<FMT>(sc, W, e, n0, ga.N, K, srows, wave, 4, lane);
+  if (FMT != FMT_GPTQ) dc_dma_scales<FMT, kWdCols>(sc, W, e, n0, ga.N, K, srows, wave, 4, lane);
+  const bool kc = W.scales_kc != nullptr;  // scale tile in the by-chunk layout
   int psid[MI];  // slots of the A rows this thread copies
 #pragma unroll
   for (int q = 0; q < MI; ++q) psid[q] = ga.sorted_ids[mb * BM + 16 * q + (tid >> 4)];
@@ -1948,7 +2007,7 @@ __global__ void __launch_bounds__(256, (MI == 1 ? 4 : 3)) gemm_wide_kernel(GemmA
 #define MOE_WD_PHASE(c, d)                                                                         \
   {                                                                                                \
     wd_compute<FMT, MI, NF>(acc, b[d], stages + ((c) & 1) * kStage, sc, rl, K, group, g, c16,      \
-                            min((c) * C + g * (C / 4), kmax));                                     \
+                            min((c) * C + g * (C / 4), kmax), kc);                                 \
     dc_load_b(b[d], W, ga, nrow, e, min(min((c) + D, last) * C + g * (C / 4), kmax));              \
     wd_load_a(r[d], prow, min((c) + D, last) * C, slot, K);                                        \
     asm volatile("" ::: "memory"); /* the loads above go out before the store waits */             \
@@ -1971,7 +2030,7 @@ __global__ void __launch_bounds__(256, (MI == 1 ? 4 : 3)) gemm_wide_kernel(GemmA
     if (nd + d < n) {  // the same for the whole workgroup
       const int c = nd + d;
       wd_compute<FMT, MI, NF>(acc, b[d], stages + (c & 1) * kStage, sc, rl, K, group, g, c16,
-                              min(c * C + g * (C / 4), kmax));
+                              min(c * C + g * (C / 4), kmax), kc);
       wd_store_a(stages + ((c + 1) & 1) * kStage, r[(d + 1) % D], tid, (c + 1) * C, K);
       pf_barrier();
     }

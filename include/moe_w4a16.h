@@ -101,9 +101,13 @@ typedef struct {
   moe_wfmt_t fmt;
   int group_size;             /* NVFP4: 16, MXFP4: 32, GPTQ: 32/64/128; must divide K */
   const void* qweight;        /* NVFP4/MXFP4: uint8 [E][N][K/2], even k in the low nibble.
-                                 GPTQ: int32 [E][K/8][N], nibble i holds k%8 == i */
+                                 GPTQ: int32 [E][K/8][N], nibble i holds k%8 == i.
+                                 NVFP4/MXFP4 may pass NULL here and in `scales` when both
+                                 copies by K chunk (qweight_kc, scales_kc) are given: every
+                                 kernel then reads those, so a caller holds one copy of the
+                                 codes ("chunked-only" family).  Otherwise required. */
   const void* scales;         /* NVFP4: e4m3fn uint8 [E][N][K/16]; MXFP4: e8m0 uint8 [E][N][K/32];
-                                 GPTQ: fp16 [E][K/G][N] */
+                                 GPTQ: fp16 [E][K/G][N].  NULL only in a chunked-only family */
   const void* zeros;          /* GPTQ: int32 [E][K/G][N/8], nibble i holds n%8 == i. Else NULL */
   const float* global_scale;  /* NVFP4: fp32 [E]. Else NULL */
   const int32_t* g_idx;       /* GPTQ group of each row, int32 [E][K] (4-byte aligned), or NULL
@@ -123,23 +127,22 @@ typedef struct {
                                  accepts it (it gathers the GEMM inputs through it); the
                                  single GEMM calls return MOE_ERR_UNSUPPORTED: gather with
                                  moe_permute_slots and call them in the top_k = 1 view. */
-  const uint8_t* scales_kc;   /* optional load-time copy of the scales laid out by K chunk, read
-                                 by the 64/128-row (streaming) GEMM kernel, which then streams
-                                 each chunk's scales with its codes instead of holding the
-                                 tile's scales for the whole K on chip, so two workgroups share
-                                 a CU.  NVFP4: uint8 [E][K/64][N][4] from moe_nvfp4_scales_by_chunk
-                                 (K a multiple of 64).  MXFP4: uint8 [E][ceil(K/128)][N][4] from
-                                 moe_mxfp4_scales_by_chunk.  16-byte aligned; `scales` stays
-                                 required (the other kernels read it).  GPTQ: must be NULL. */
+  const uint8_t* scales_kc;   /* optional load-time copy of the scales laid out by K chunk.  The
+                                 64/128-row (streaming) GEMM kernel then streams each chunk's
+                                 scales with its codes instead of holding the tile's scales
+                                 for the whole K on chip, so two workgroups share a CU; every
+                                 other kernel reads it in place of `scales` too.  NVFP4: uint8
+                                 [E][K/64][N][4] from moe_nvfp4_scales_by_chunk (K a multiple of
+                                 64).  MXFP4: uint8 [E][ceil(K/128)][N][4] from
+                                 moe_mxfp4_scales_by_chunk.  16-byte aligned.  GPTQ: must be
+                                 NULL. */
   const uint8_t* qweight_kc;  /* optional load-time copy of the codes laid out by K chunk, so the
                                  copy of one chunk of a 32-row block is one contiguous piece
-                                 instead of 32 row pieces.  NVFP4, only together with scales_kc:
-                                 uint8 [E][K/64][N][32] (moe_nvfp4_codes_by_chunk), read by the
-                                 streaming kernel.  MXFP4: uint8 [E][ceil(K/128)][N][64]
-                                 (moe_mxfp4_codes_by_chunk), read by the MXFP8-activation (MX)
-                                 kernels and, when scales_kc is given too, by the streaming
-                                 kernel.  16-byte aligned; `qweight` stays required (the
-                                 1..64-token kernels read it). */
+                                 instead of 32 row pieces; every kernel reads it in place of
+                                 `qweight` when given.  NVFP4, only together with scales_kc:
+                                 uint8 [E][K/64][N][32] (moe_nvfp4_codes_by_chunk).  MXFP4: uint8
+                                 [E][ceil(K/128)][N][64] (moe_mxfp4_codes_by_chunk), alone or
+                                 with scales_kc.  16-byte aligned. */
 } moe_wq_t;
 
 /* Kernel for the grouped GEMMs over blocks of 16 or 32 rows (few tokens per

@@ -101,6 +101,17 @@ def test_gemm1_rejects(L):
     assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, qweight_kc=FAKE)) == UNSUP   # no GPTQ form
     assert _g1(L, _wq(scales_kc=FAKE, qweight_kc=FAKE), K=2880 + 32) == SHAPE
     assert _g1(L, _wq(scales_kc=FAKE, qweight_kc=FAKE + 4)) == ALIGN
+    # chunked-only NVFP4/MXFP4 families: no checkpoint layout, both copies by chunk
+    kc = dict(qweight=None, scales=None, scales_kc=FAKE, qweight_kc=FAKE)
+    assert _g1(L, _wq(**kc), x=None) == NULL                          # accepted (x checked next)
+    assert _g1(L, _wq(fmt=1, group=32, gs=None, **kc), x=None) == NULL  # MXFP4 too
+    assert _g1(L, _wq(**kc), K=2880 + 32) == SHAPE                    # NVFP4 by chunk: K % 64
+    assert _g1(L, _wq(qweight=None, scales_kc=FAKE, qweight_kc=FAKE)) == NULL  # scales left over
+    assert _g1(L, _wq(scales=None, scales_kc=FAKE, qweight_kc=FAKE)) == NULL   # codes left over
+    assert _g1(L, _wq(qweight=None, scales=None, scales_kc=FAKE)) == NULL      # no codes at all
+    assert _g1(L, _wq(fmt=1, group=32, gs=None, qweight=None, scales=None,
+                      qweight_kc=FAKE)) == NULL                       # MXFP4: scales by chunk too
+    assert _g1(L, _wq(fmt=2, group=64, zeros=FAKE, **kc)) == NULL     # GPTQ has one layout
     assert _g1(L, _wq(fmt=2, group=64)) == NULL          # zeros missing
     assert _g1(L, _wq(gs=None)) == NULL                  # NVFP4 global scale missing
     assert _g1(L, _wq(fmt=9)) == UNSUP
