@@ -116,8 +116,8 @@ def profiled_traffic():
     returned.
     """
     import hashlib
-    path = os.path.join(ROOT, "profiles", "gemm1_nvfp4_e32_t4096_traffic.md")
-    src = os.path.join(ROOT, "bit_weight_expert_amd", "csrc", "gemm.hip")
+    path = os.path.join(ROOT, "profiles", "gemm_nvfp4_e32_traffic.md")
+    src = os.path.join(ROOT, "bit_weight_expert_amd", "csrc", "gemm_impl.h")
     try:
         fields = dict(ln.split(":", 1) for ln in open(path) if ln.startswith(("traffic_", "kernel_")))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
