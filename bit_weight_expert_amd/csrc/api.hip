@@ -140,21 +140,25 @@ int epi_of(moe_act_t act) {
   }
 }
 
-// block_m by the average expert load: the smallest tile it fills.
-int pick_block_m(int T, int top_k, int E) {
-  const long avg = ((long)T * top_k + E - 1) / E;
-  if (avg <= 16) return 16;
-  if (avg <= 32) return 32;
-  if (avg <= 64) return 64;
-  return 128;
-}
-
 constexpr int kMixedMaxBlocks = 4096;  // the tile-plan kernel's block table in LDS
 
-// The sort granularity moe_forward uses.  (Measured: 64-row blocks for
-// uneven loads, pairs of them as 128-row tiles and the odd ones as a second,
-// 64-row launch, ran slower than 128-row blocks throughout.)
-int forward_block_m(int T, int top_k, int E) { return pick_block_m(T, top_k, E); }
+// The sort granularity moe_forward (and moe_forward_mxfp8) uses, by the
+// average slots per expert.
+// The streaming kernel's 64-row tiles beat the 16/32-row decode kernels from
+// 9 slots per expert on (measured at the gpt-oss-20b shape: T = 128 160 ->
+// 127 us, T = 256 193 -> 147 us; the gpt-oss-120b skewed layer at T = 1024,
+// 32 per expert, 416 -> 381 us against the mixed tiling), and 128-row tiles
+// beat 64-row ones from 57 on (T = 512, 64 per expert: 212 -> 197 us; at 56
+// the 64-row tiles are 8% faster).  Up to 8 the decode kernels, which split K,
+// keep the chip busy where the tiles would be too few.  (Also measured: 64-row
+// blocks for uneven loads, pairs of them as 128-row tiles and the odd ones as
+// a second, 64-row launch, ran slower than 128-row blocks throughout.)
+int forward_block_m(int T, int top_k, int E) {
+  const long avg = ((long)T * top_k + E - 1) / E;
+  if (avg <= 8) return 16;
+  if (avg <= 56) return 64;
+  return 128;
+}
 
 struct WsLayout {
   size_t ids, w, sorted, eids, npp, cnt, dec, tiles, ntiles, act, y, total;
@@ -548,7 +552,7 @@ moe_status_t moe_mx_gemm2(const uint8_t* a_codes, const uint8_t* a_scales, int s
 
 size_t moe_forward_mxfp8_workspace_bytes(int T, int E, int top_k, int hidden, int inter) {
   if (T <= 0 || E <= 0 || top_k <= 0 || hidden <= 0 || inter <= 0) return 0;
-  return mx_ws_layout(T, E, top_k, hidden, inter, pick_block_m(T, top_k, E)).total;
+  return mx_ws_layout(T, E, top_k, hidden, inter, forward_block_m(T, top_k, E)).total;
 }
 
 moe_status_t moe_forward_mxfp8(const uint16_t* x, const float* logits, int T, int E, int top_k,
@@ -577,7 +581,7 @@ moe_status_t moe_forward_mxfp8(const uint16_t* x, const float* logits, int T, in
   if (kind == MOE_ROUTE_SIGMOID_BIAS && expert_bias == nullptr) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return MOE_ERR_ALIGN;
-  const int block_m = pick_block_m(T, top_k, E);
+  const int block_m = forward_block_m(T, top_k, E);
   const MxWsLayout L = mx_ws_layout(T, E, top_k, hidden, inter, block_m);
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
 

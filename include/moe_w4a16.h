@@ -335,9 +335,10 @@ moe_status_t moe_permute_slots(const uint16_t* src, int size_m, int top_k, int K
                                const int32_t* k_perm, const int32_t* topk_ids, uint16_t* dst,
                                moe_stream_t stream);
 
-/* The block_m moe_forward uses for T tokens (the smallest of 16/32/64/128
- * that covers the average number of slots per expert, T*top_k/E); callers
- * that run the steps one by one can use it to get the same tiling. */
+/* The block_m moe_forward uses for T tokens, from the average number of slots
+ * per expert a = T*top_k/E: 16 for a <= 8 (the decode kernels), 64 for
+ * a <= 56, else 128 (the streaming kernel); callers that run the steps one by
+ * one can use it to get the same tiling. */
 int moe_forward_block_m(int T, int top_k, int E);
 
 /* Bytes of scratch moe_forward needs (routing results, align metadata and

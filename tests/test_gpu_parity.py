@@ -370,11 +370,12 @@ def test_gemm2_tile_fallbacks(fmt, K, N, group, B, policy):
                                      ("gptq", "swigluoai"), ("nvfp4", "relu2")])
 @pytest.mark.parametrize("policy", ["auto", "splitk", "wide"])
 def test_forward_mixed_tiling(fmt, act, policy):
-    """Few slots per expert on average (16/32-row blocks) with a few experts
-    holding hundreds: moe_forward sends those experts' full 128-row runs to
-    the streaming kernel (a tile list built on the device) and the rest to the
-    decode kernels; the whole output against the oracle, every row."""
-    L = _small(fmt, act, E=64, k=2, T=800, skew_std=2.5, seed=77)
+    """Few slots per expert on average (16-row blocks: 8 per expert over 128
+    experts) with a few experts holding hundreds: moe_forward sends those
+    experts' full 128-row runs to the streaming kernel (a tile list built on
+    the device) and the rest to the decode kernels; the whole output against
+    the oracle, every row."""
+    L = _small(fmt, act, E=128, k=2, T=512, skew_std=2.5, seed=77)
     ids, _ = O.route(L)
     cnt = np.bincount(ids.reshape(-1), minlength=L.E)
     bm = M.moe_forward_block_m(L.T, L.top_k, L.E)
