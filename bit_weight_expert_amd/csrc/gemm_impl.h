@@ -205,19 +205,27 @@ __device__ __forceinline__ void load_codes(BChunk<FMT, C>& b, const WeightArgs& 
 // 8 dequantised bf16 weights of MFMA step st.
 // Eight GPTQ codes of one word (code i in bits 4i .. 4i+3) as code * s + zs.
 // The even codes are masked into the word's four bytes and the odd ones
-// shifted there first, so each code takes one byte-to-float convert (a
-// nibble extract and a convert otherwise); the products are exact in fp32.
-// (The masks are opaque to the compiler: knowing the bits of lo and hi, it
-// would fold each byte read back into a nibble extract.)
+// shifted there first.  A byte 0..15 read as e4m3 is that integer times 2^-9
+// (subnormals up to 7, then the first binade), so one scaled fp8 convert
+// with scale 2^9 turns two bytes into two exact integer floats; the products
+// are exact in fp32.  (The masks are opaque to the compiler: knowing the
+// bits of lo and hi, it would fold each byte read back into a nibble extract.)
 __device__ __forceinline__ void gptq_deq8(uint32_t w, float s, float zs, float (&v)[8]) {
   uint32_t lo, hi;
   asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w));
   asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w >> 4));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v[2 * j] = fmaf((float)((lo >> (8 * j)) & 0xFFu), s, zs);
-    v[2 * j + 1] = fmaf((float)((hi >> (8 * j)) & 0xFFu), s, zs);
-  }
+  const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, false);  // codes 0, 2
+  const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, true);   // codes 4, 6
+  const f32x2 o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, false);  // codes 1, 3
+  const f32x2 o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, true);   // codes 5, 7
+  v[0] = fmaf(e0[0], s, zs);
+  v[1] = fmaf(o0[0], s, zs);
+  v[2] = fmaf(e0[1], s, zs);
+  v[3] = fmaf(o0[1], s, zs);
+  v[4] = fmaf(e1[0], s, zs);
+  v[5] = fmaf(o1[0], s, zs);
+  v[6] = fmaf(e1[1], s, zs);
+  v[7] = fmaf(o1[1], s, zs);
 }
 
 template <int FMT, int C>

@@ -9,11 +9,12 @@
 //                score = sigmoid + bias in float, weights = selected unbiased
 //                sigmoids renormalised; n_group = 1 makes the grouped top-k a
 //                plain top-k (Nemotron-3-Nano page, Analysis item 3).
-// For E <= 128 (one or two scores per lane) each score's rank is counted
-// directly against every other score, broadcast one lane at a time with
-// v_readlane: no cross-lane shuffles at all, and the rank is the output
-// position.  Larger E (up to 1024) keeps up to 16 scores per lane and finds
-// the k winners by k rounds of a wave-wide argmax.
+// Each lane holds up to 16 scores (E <= 1024; one or two for E <= 128) and
+// the k winners come out of k rounds of a wave-wide argmax, in output order.
+// The wave-wide max, sum and argmax are butterflies whose first four steps
+// are DPP moves inside rows of 16 lanes (a rank count over broadcast scores,
+// one v_readlane per expert, took 15-20 us per token at E = 128: a serial
+// chain of lane reads).
 //
 // Align: one workgroup of 1024 threads.  Pads each expert's count to block_m
 // and places every slot at
@@ -38,6 +39,56 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Value held by this lane's partner in step S of a wave-wide all-reduce:
+// steps 0, 1 swap lanes within a quad (lane ^ 1, lane ^ 2), steps 2, 3
+// mirror within 8 and 16 lanes (each pairs two groups already reduced), all
+// four as DPP moves; steps 4, 5 are lane ^ 16 and lane ^ 32.
+template <int S>
+__device__ __forceinline__ int wave_partner(int v) {
+  if (S == 0) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  if (S == 1) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  if (S == 2) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  if (S == 3) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  return __shfl_xor(v, S == 4 ? 16 : 32);
+}
+
+template <int S>
+__device__ __forceinline__ float wave_partner_f(float v) {
+  return __int_as_float(wave_partner<S>(__float_as_int(v)));
+}
+
+#define MOE_WAVE_STEPS(X) X(0) X(1) X(2) X(3) X(4) X(5)
+
+__device__ __forceinline__ float wave_max(float v) {
+#define MOE_STEP(S) v = fmaxf(v, wave_partner_f<S>(v));
+  MOE_WAVE_STEPS(MOE_STEP)
+#undef MOE_STEP
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#define MOE_STEP(S) v = v + wave_partner_f<S>(v);
+  MOE_WAVE_STEPS(MOE_STEP)
+#undef MOE_STEP
+  return v;
+}
+
+// (value, expert id) of the best entry over the wave, on every lane (the
+// order of better() is total on distinct ids, so all lanes agree)
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+#define MOE_STEP(S)                                                \
+  {                                                                \
+    const float ov = wave_partner_f<S>(bv);                        \
+    const int oi = wave_partner<S>(bi);                            \
+    if (better(ov, oi, bv, bi)) {                                  \
+      bv = ov;                                                     \
+      bi = oi;                                                     \
+    }                                                              \
+  }
+  MOE_WAVE_STEPS(MOE_STEP)
+#undef MOE_STEP
 }
 
 // Score used for selection and the weight basis of expert e's logit l.
@@ -73,60 +124,59 @@ __device__ __forceinline__ void route_wave(const float* __restrict__ logits, int
       bs[c] = -INFINITY;
       if (e < E) route_score<KIND>(row[e], ebias, e, sc[c], bs[c]);
     }
-    // softmax denominator over all E in fp32 (fixed order: max, then the sum
-    // of exp over experts 0, 1, ..., E-1 accumulated lane by lane)
+    // softmax denominator over all E in fp32: per-lane pair sums, then a
+    // butterfly (both partners of a step add the same two values, so every
+    // lane ends with the same bits)
     float denom = 1.f, lmax = -INFINITY;
     if (KIND == 0) {
-      for (int o = 0; o < 64 && o < E; ++o) lmax = fmaxf(lmax, readlane_f(bs[0], o));
-      for (int o = 0; o + 64 < E; ++o) lmax = fmaxf(lmax, readlane_f(bs[1], o));
-      float ex0 = (lane < E) ? expf(bs[0] - lmax) : 0.f;
-      float ex1 = (64 + lane < E) ? expf(bs[1] - lmax) : 0.f;
-      float s = 0.f;
-      for (int o = 0; o < 64 && o < E; ++o) s += readlane_f(ex0, o);
-      for (int o = 0; o + 64 < E; ++o) s += readlane_f(ex1, o);
-      denom = s;
+      lmax = wave_max(fmaxf(bs[0], bs[1]));
+      const float ex0 = (lane < E) ? expf(bs[0] - lmax) : 0.f;
+      const float ex1 = (64 + lane < E) ? expf(bs[1] - lmax) : 0.f;
+      denom = wave_sum(ex0 + ex1);
     }
-    // rank of each of the lane's scores among all E
-    int rk[2] = {0, 0};
-    for (int o = 0; o < 64 && o < E; ++o) {
-      const float so = readlane_f(sc[0], o);
+    // top_k rounds of a wave-wide argmax: round r finds output position r
+    // (the r-th best score, ties to the lower expert id); lane r keeps it
+    unsigned taken = 0;  // bit c: entry c of this lane already selected
+    int my_id = -1;
+    float my_base = 0.f;
+    for (int r = 0; r < top_k; ++r) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) rk[c] += better(so, o, sc[c], c * 64 + lane) ? 1 : 0;
+      for (int c = 0; c < 2; ++c) {
+        const int e = c * 64 + lane;
+        if (e < E && !((taken >> c) & 1u) && better(sc[c], e, bv, bi)) {
+          bv = sc[c];
+          bi = e;
+        }
+      }
+      wave_argmax(bv, bi);
+      const int win = __builtin_amdgcn_readfirstlane(bi);
+      const int owner = win & 63, oc = win >> 6;
+      float sel = 0.f;
+      if (lane == owner) {
+        taken |= 1u << oc;
+        sel = oc ? bs[1] : bs[0];
+      }
+      sel = readlane_f(sel, owner);
+      if (lane == r) {
+        my_id = win;
+        my_base = sel;
+      }
     }
-    for (int o = 0; o + 64 < E; ++o) {
-      const float so = readlane_f(sc[1], o);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) rk[c] += better(so, 64 + o, sc[c], c * 64 + lane) ? 1 : 0;
-    }
-    // weights of the selected experts, renormalised over the k of them
-    float p[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bool sel = (c * 64 + lane < E) && rk[c] < top_k;
-      p[c] = !sel ? 0.f : (KIND == 0) ? expf(bs[c] - lmax) / denom : bs[c];
-    }
+    const float p = lane >= top_k ? 0.f : (KIND == 0) ? expf(my_base - lmax) / denom : my_base;
     float norm = 1.f;
     if (renorm) {
-      // sum in output order (rank 0 .. k-1) so it does not depend on expert ids' lanes
+      // sum in output order (position 0 .. k-1)
       float s = 0.f;
-      for (int r = 0; r < top_k; ++r) {
-        // the (unique) lane/slot holding rank r
-        const unsigned long long m0 = __ballot((lane < E) && rk[0] == r);
-        const unsigned long long m1 = __ballot((64 + lane < E) && rk[1] == r);
-        if (m0) s += readlane_f(p[0], __builtin_ctzll(m0));
-        else s += readlane_f(p[1], __builtin_ctzll(m1));
-      }
+      for (int r = 0; r < top_k; ++r) s += readlane_f(p, r);
       norm = s;
     }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int e = c * 64 + lane;
-      if (e < E && rk[c] < top_k) {
-        const size_t f = (size_t)t * top_k + rk[c];
-        ids[f] = e;
-        w[f] = renorm ? p[c] / norm : p[c];
-        if (lds_ids != nullptr) lds_ids[f] = e;
-      }
+    if (lane < top_k) {
+      const size_t f = (size_t)t * top_k + lane;
+      ids[f] = my_id;
+      w[f] = renorm ? p / norm : p;
+      if (lds_ids != nullptr) lds_ids[f] = my_id;
     }
     return;
   }
@@ -146,16 +196,15 @@ __device__ __forceinline__ void route_wave(const float* __restrict__ logits, int
     base[c] = v;
   }
 
-  // softmax denominator over all E (fp32; fixed shuffle order -> deterministic)
+  // softmax denominator over all E (fp32; fixed butterfly -> deterministic)
   float denom = 1.f;
   if (KIND == 0) {
-    for (int o = 32; o > 0; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
+    lmax = wave_max(lmax);
     float s = 0.f;
 #pragma unroll
     for (int c = 0; c < kRouteMaxPerLane; ++c)
       if (c * 64 + lane < E) s += expf(base[c] - lmax);
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    denom = s;
+    denom = wave_sum(s);
   }
 
   unsigned taken = 0;  // bit c: entry c of this lane already selected
@@ -172,14 +221,7 @@ __device__ __forceinline__ void route_wave(const float* __restrict__ logits, int
         bi = e;
       }
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_argmax(bv, bi);
     // owner marks it taken and broadcasts the weight basis
     float sel_base = 0.f;
     const int owner = bi & 63, oc = bi >> 6;
