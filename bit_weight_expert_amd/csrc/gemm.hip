@@ -71,10 +71,12 @@ __global__ void __launch_bounds__(256) moe_sum_kernel(const uint16_t* __restrict
 //
 // Tile: BM rows x 256 weight rows, four waves side by side over the weight
 // rows (two 32-row fragments each), all BM rows per wave.  K moves in chunks
-// of 128 through a 3-deep LDS ring filled by LDS-DMA (A: 128 bytes per row,
+// of 128 through an LDS ring filled by LDS-DMA (A: 128 bytes per row,
 // 16-byte slot q of row r at a_slot(q, r); weights: 64 bytes per row at the
-// row's position, slot q at q ^ ((position / 4) % 4)); both scale tiles stay
-// in LDS for the whole K.
+// row's position, slot q at q ^ ((position / 4) % 4)).  With the weight
+// scales by K chunk both scale tiles stream with the chunks (2-deep ring, two
+// workgroups per CU); otherwise they stay in LDS for the whole K (3-deep
+// ring, eight waves, one workgroup per CU).
 
 struct MxA {
   const uint8_t* codes;   // e4m3 [rows][lda]
@@ -89,8 +91,12 @@ constexpr int kMxScaleIssue = 6;  // A-scale DMA instructions per wave (BM * lds
 
 // RS = 2: eight waves, waves w and w + 4 take the same weight rows and one
 // half of the A rows each, so one wave's LDS reads and waits overlap the
-// other's MFMAs on the same SIMD.
-template <int BM, int RS = 1>
+// other's MFMAs on the same SIMD.  NS: ring stages.  SS: both scale tiles
+// stream with the chunks instead of staying resident (weights by K chunk:
+// each stage holds the chunk's [BN][4] weight scale bytes and [BM][4] A
+// scale bytes), so the workgroup waits for nothing but its first chunk and
+// takes far less LDS.
+template <int BM, int RS = 1, int NS = kMxStages, bool SS = false>
 struct Mx {
   static constexpr int NW = 4 * RS;                   // waves
   static constexpr int MI = BM / 32 / RS;             // 32-row tiles per wave
@@ -98,13 +104,16 @@ struct Mx {
   static constexpr int BN = 4 * NF * 32;
   static constexpr int kABytes = BM * kMxBK;
   static constexpr int kBBytes = BN * kMxBK / 2;
+  static constexpr int kWsBytes = SS ? BN * 4 : 0;    // streamed weight scales of one chunk
+  static constexpr int kAsBytes = SS ? 128 * 4 : 0;   // streamed A scales (room for 128 rows)
   static constexpr int kAIssue = kABytes / 1024 / NW;  // DMA instructions per wave per chunk
   static constexpr int kBIssue = kBBytes / 1024 / NW;
-  static constexpr int kSIssue = (4 * kMxScaleIssue + NW - 1) / NW;  // A-scale DMA per wave
-  static constexpr int kIssue = kAIssue + kBIssue;
-  static constexpr int kStage = kABytes + kBBytes;
-  static constexpr int kLds = kMxStages * kStage + kMxScaleBytes;
+  static constexpr int kSIssue = SS ? 0 : (4 * kMxScaleIssue + NW - 1) / NW;  // A-scale DMA per wave
+  static constexpr int kIssue = kAIssue + kBIssue + (SS ? 1 : 0);  // SS: one scale piece per wave
+  static constexpr int kStage = kABytes + kBBytes + kWsBytes + kAsBytes;
+  static constexpr int kLds = NS * kStage + (SS ? 0 : kMxScaleBytes);
   static_assert(kAIssue >= 1 && kBIssue >= 1, "tile too small for the DMA split");
+  static_assert(NS >= 2 && (NS - 1) * kIssue < 64, "ring depth / vmcnt range");
   static_assert(kLds <= 160 * 1024, "LDS");
 };
 
@@ -197,9 +206,10 @@ __device__ __forceinline__ void mx_scales(int (&sa)[MI], int (&sb)[NF], const ui
   }
 }
 
-template <int EPI, int BM, int RS>
-__global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA ma, WeightArgs W, EpiArgs ea) {
-  using P = Mx<BM, RS>;
+template <int EPI, int BM, int RS, int NS, bool SS>
+__global__ void __launch_bounds__(256 * RS, SS && RS == 1 ? 2 : 1)
+    gemm_mx_kernel(GemmArgs ga, MxA ma, WeightArgs W, EpiArgs ea) {
+  using P = Mx<BM, RS, NS, SS>;
   constexpr int MI = P::MI, NF = P::NF, NW = P::NW;
   __shared__ __attribute__((aligned(16))) uint8_t smem[P::kLds];
 
@@ -213,18 +223,23 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA m
   const int K = ga.K, N = ga.N, kb = K / 32;
 
   // slot ids of the A rows this lane copies (instruction q = NW*p + wave covers
-  // rows 8q .. 8q+7) and of the A scale rows (instruction q = NW*i + wave
-  // covers 16-byte pieces 64q .. 64q+63 of the [BM][lds] tile), all requested
-  // before anything waits
+  // rows 8q .. 8q+7) and of the A scale rows (resident tile: instruction
+  // q = NW*i + wave covers 16-byte pieces 64q .. 64q+63 of the [BM][lds] tile;
+  // streamed: waves 1 and 2 (mod 4) copy rows 0..63 and 64..127, one 4-byte
+  // piece per lane), all requested before anything waits
   const int parts = ma.lds / 16;
   const int na = BM * parts;
-  int sid[P::kAIssue], ssid[P::kSIssue];
+  int sid[P::kAIssue], ssid[SS ? 1 : P::kSIssue];
 #pragma unroll
   for (int p = 0; p < P::kAIssue; ++p) sid[p] = ga.sorted_ids[mb * BM + 8 * (NW * p + wave) + (lane >> 3)];
+  if constexpr (SS) {
+    ssid[0] = ga.sorted_ids[mb * BM + min((wave_u == 2 ? 64 : 0) + lane, BM - 1)];
+  } else {
 #pragma unroll
-  for (int i = 0; i < P::kSIssue; ++i) {
-    const int pc = min((NW * i + wave) * 64 + lane, na - 1);  // lanes past the end repeat the last piece
-    ssid[i] = ga.sorted_ids[mb * BM + pc / parts];
+    for (int i = 0; i < P::kSIssue; ++i) {
+      const int pc = min((NW * i + wave) * 64 + lane, na - 1);  // lanes past the end repeat the last piece
+      ssid[i] = ga.sorted_ids[mb * BM + pc / parts];
+    }
   }
   const int e = ga.expert_ids[mb];
   if (e < 0 || e >= ga.E) return;
@@ -232,6 +247,7 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA m
   const int nt0 = nt * P::BN;
   const int rows = min(P::BN, N - nt0);
   const int n0 = nt0 + wave_u * NF * 32;
+  const int nchunks = (K + kMxBK - 1) / kMxBK;
 
   // DMA sources.  A: lane l writes physical slot l%8 of row r = 8q + l/8, so it
   // fetches logical slot a_slot(l%8, r).
@@ -255,28 +271,48 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA m
   for (int p = 0; p < P::kBIssue; ++p) {
     const int pos = 16 * (NW * p + wave) + (lane >> 2);
     const int n = min(nt0 + pf_brow<EPI>(pos >> 5, pos & 31), N - 1);
-    brow[p] = ck ? W.qweight_kc + ((size_t)e * ((K + 127) / 128) * N + n) * 64
+    brow[p] = ck ? W.qweight_kc + ((size_t)e * nchunks * N + n) * 64
                  : W.qweight + ((size_t)e * N + n) * (K / 2);
     bls[p] = 16 * ((lane & 3) ^ ((pos >> 2) & 3));
   }
-
+  // Streamed scales (SS): this wave's piece of each chunk's scales.  Waves 0
+  // and 3 (mod 4): the weight scales of all 256 tile rows, 16 bytes (four
+  // rows) per lane (rows past N re-read the last four; the two waves write the
+  // same bytes); waves 1 and 2: A rows 0..63 / 64..127, 4 bytes per lane
+  // (rows past the tile re-read its last row).  Eight waves copy it twice.
+  const uint8_t* ssrc = nullptr;
+  uint32_t sdst = 0, sstride = 0;
   const uint32_t ring = lds_addr(smem);
-  const uint32_t scb_lds = ring + kMxStages * P::kStage;                  // weight scales
-  const int scb_bytes = (256 * kb + 1023) / 1024 * 1024;
-  const uint32_t sca_lds = scb_lds + scb_bytes;                           // A scales
-  const uint8_t* scb = smem + kMxStages * P::kStage;
-  const uint8_t* sca = scb + scb_bytes;
-  const int nchunks = (K + kMxBK - 1) / kMxBK;
-
-  // weight scales of the tile rows (contiguous; by K chunk: one kilobyte,
-  // [256 rows][4], per 128-deep chunk), then the A scale rows
-  const bool kcs = W.scales_kc != nullptr;
-  if (kcs) {
-    const uint8_t* src = W.scales_kc + ((size_t)e * nchunks * N + nt0) * 4;
-    for (int q = wave; q < nchunks; q += NW)
-      if (16 * lane < 4 * rows) dma16(src + (size_t)q * N * 4 + 16 * lane, scb_lds + q * 1024);
+  if constexpr (SS) {
+    if (wave_u == 0 || wave_u == 3) {
+      const int r = min(nt0 + 4 * lane, N - 4);
+      ssrc = W.scales_kc + ((size_t)e * nchunks * N + r) * 4;
+      sstride = (uint32_t)N * 4;
+      sdst = P::kABytes + P::kBBytes;
+    } else {
+      const int s = ssid[0];
+      const int row = s < ga.n_slots ? (int)(((uint64_t)(uint32_t)s * ga.a_mul) >> 32) : 0;
+      ssrc = ma.scales + (size_t)row * ma.lds;
+      sstride = 4;
+      sdst = P::kABytes + P::kBBytes + P::kWsBytes + (wave_u == 2 ? 256 : 0);
+    }
   }
-  {
+
+  const uint8_t* scb = smem + NS * P::kStage;
+  const int scb_bytes = SS ? 0 : (256 * kb + 1023) / 1024 * 1024;
+  const uint8_t* sca = scb + scb_bytes;
+  const bool kcs = W.scales_kc != nullptr;
+  if constexpr (!SS) {
+    // resident scale tiles: the weight scales of the tile rows (contiguous;
+    // by K chunk: one kilobyte, [256 rows][4], per 128-deep chunk), then the
+    // A scale rows
+    const uint32_t scb_lds = ring + NS * P::kStage;
+    const uint32_t sca_lds = scb_lds + scb_bytes;
+    if (kcs) {
+      const uint8_t* src = W.scales_kc + ((size_t)e * nchunks * N + nt0) * 4;
+      for (int q = wave; q < nchunks; q += NW)
+        if (16 * lane < 4 * rows) dma16(src + (size_t)q * N * 4 + 16 * lane, scb_lds + q * 1024);
+    }
     const int nb = kcs ? 0 : rows * kb;   // a multiple of 16 (N % 16 == 0)
     const uint8_t* src = W.scales + ((size_t)e * N + nt0) * kb;
     for (int q = wave; q * 1024 < nb; q += NW)
@@ -299,9 +335,15 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA m
     for (int p = 0; p < P::kBIssue; ++p)
       dma16(brow[p] + (ck ? (size_t)kc * N * 64 + bls[p] : (size_t)min(kc * (kMxBK / 2) + bls[p], K / 2 - 16)),
             stage + P::kABytes + (uint32_t)(NW * p + wave) * 1024u);
+    if constexpr (SS) {
+      if (wave_u == 0 || wave_u == 3)
+        dma16(ssrc + (size_t)kc * sstride, stage + sdst);
+      else
+        dma4(ssrc + (size_t)kc * sstride, stage + sdst);
+    }
   };
 #pragma unroll
-  for (int s = 0; s < kMxStages; ++s) issue(ring + s * P::kStage, min(s, nchunks - 1));
+  for (int s = 0; s < NS; ++s) issue(ring + s * P::kStage, min(s, nchunks - 1));
 
   // this lane's weight positions and scale rows
   int bpos[NF], rl[NF];
@@ -320,37 +362,53 @@ __global__ void __launch_bounds__(256 * RS, 1) gemm_mx_kernel(GemmArgs ga, MxA m
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // scale words of chunk kc (from its stage, or the resident tiles)
+  auto scales = [&](int (&sa)[MI], int (&sb)[NF], int kc) {
+    if constexpr (SS) {
+      const uint8_t* st = smem + (kc % NS) * P::kStage + P::kABytes + P::kBBytes;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        sa[i] = (int)(*reinterpret_cast<const uint32_t*>(st + P::kWsBytes + (r0 + 32 * i + c) * 4) >> (8 * g));
+#pragma unroll
+      for (int j = 0; j < NF; ++j)
+        sb[j] = (int)((*reinterpret_cast<const uint32_t*>(st + rl[j] * 4) >> (8 * g)) & 0x00FF00FFu);
+    } else {
+      mx_scales<MI, NF>(sa, sb, sca, ma.lds, scb, kb, rl, c, g, kc, r0, kcs);
+    }
+  };
+
   // scales and chunk 0 have landed.  Both 64-deep steps of every chunk run
   // (past K the A codes are zero), so the loop has no branch; each step's
   // LDS reads are issued while the other step's MFMAs run.
-  wait_vmcnt<(kMxStages - 1) * P::kIssue>();
+  wait_vmcnt<(NS - 1) * P::kIssue>();
   pf_barrier();
   MxOps<MI, NF> o0, o1;
   int sa[MI], sb[NF];
-  mx_scales<MI, NF>(sa, sb, sca, ma.lds, scb, kb, rl, c, g, 0, r0, kcs);
+  scales(sa, sb, 0);
   mx_read<MI, NF, 0>(o0, smem, P::kABytes, bpos, c, g, r0);
   if (n0 >= N) {
     // every weight row of this wave lies past N (the last column tile): only
     // its share of the copies, which leaves its SIMD to the other waves
     for (int kc = 0; kc < nchunks; ++kc) {
-      wait_vmcnt<P::kIssue>();
+      wait_vmcnt<(NS - 2) * P::kIssue>();
       pf_barrier();
-      issue(ring + (kc % kMxStages) * P::kStage, min(kc + kMxStages, nchunks - 1));
+      issue(ring + (kc % NS) * P::kStage, min(kc + NS, nchunks - 1));
     }
   } else
   for (int kc = 0; kc < nchunks; ++kc) {
-    const uint8_t* stg = smem + (kc % kMxStages) * P::kStage;
+    const uint8_t* stg = smem + (kc % NS) * P::kStage;
     mx_read<MI, NF, 1>(o1, stg, P::kABytes, bpos, c, g, r0);
     mx_mfma<MI, NF, 0>(acc, o0, sa, sb);
-    // chunk kc+1 has landed (only chunk kc+2 may be in flight) and every wave
-    // is past its reads of chunk kc, whose stage takes chunk kc+3
-    wait_vmcnt<P::kIssue>();
+    // chunk kc+1 has landed (only the NS-2 younger chunks may be in flight)
+    // and every wave is past its reads of chunk kc, whose stage takes chunk
+    // kc+NS
+    wait_vmcnt<(NS - 2) * P::kIssue>();
     pf_barrier();
-    issue(ring + (kc % kMxStages) * P::kStage, min(kc + kMxStages, nchunks - 1));
+    issue(ring + (kc % NS) * P::kStage, min(kc + NS, nchunks - 1));
     int na_[MI], nb_[NF];
     const int kn = min(kc + 1, nchunks - 1);
-    mx_scales<MI, NF>(na_, nb_, sca, ma.lds, scb, kb, rl, c, g, kn, r0, kcs);
-    mx_read<MI, NF, 0>(o0, smem + (kn % kMxStages) * P::kStage, P::kABytes, bpos, c, g, r0);
+    scales(na_, nb_, kn);
+    mx_read<MI, NF, 0>(o0, smem + (kn % NS) * P::kStage, P::kABytes, bpos, c, g, r0);
     mx_mfma<MI, NF, 1>(acc, o1, sa, sb);
 #pragma unroll
     for (int i = 0; i < MI; ++i) sa[i] = na_[i];
@@ -419,8 +477,13 @@ extern "C" hipError_t moe_launch_gemm_mx(int epi, int block_m, int cap, const ui
                                          const float* tw, int mul, float alpha, float beta,
                                          float limit, uint16_t* out, int out_ld, hipStream_t st) {
   if (cap / block_m == 0) return hipSuccess;
-  if (moe::mx_scale_bytes(K, block_m, lds) > moe::kMxScaleBytes ||
-      block_m * (lds / 16) > 4 * moe::kMxScaleIssue * 64)
+  // the weight scales by K chunk stream with the chunks; otherwise both scale
+  // tiles stay resident and must fit
+  const bool ss = W->scales_kc != nullptr;
+  const int nchunks = (K + moe::kMxBK - 1) / moe::kMxBK;
+  if (ss ? (lds % 4 != 0 || lds < 4 * nchunks)
+         : (moe::mx_scale_bytes(K, block_m, lds) > moe::kMxScaleBytes ||
+            block_m * (lds / 16) > 4 * moe::kMxScaleIssue * 64))
     return hipErrorInvalidValue;
   const uint64_t a_mul = ((1ull << 32) + (uint64_t)a_div - 1) / (uint64_t)a_div;
   moe::GemmArgs ga{nullptr, a_div, a_mul, n_slots, K, N, E, cap / block_m, 0, 4, block_m, sid, eid, npp};
@@ -428,13 +491,22 @@ extern "C" hipError_t moe_launch_gemm_mx(int epi, int block_m, int cap, const ui
   moe::MxA ma{a_codes, a_scales, lda, lds};
   moe::EpiArgs ea{sid, 0, n_slots, N, tw, mul, alpha, beta, limit, out, out_ld};
   const dim3 grid((ga.n_mblocks * ga.n_ntiles + 7) / 8 * 8);
+  // resident scales: eight waves, one workgroup per CU (152 KB of LDS).
+  // Streamed scales: four waves and a 2-deep ring, 67 KB, two workgroups per
+  // CU (measured at the gpt-oss-120b shape, T = 8192: MX GEMM1 795 -> 655 us;
+  // eight waves with 3 stages 799 us, four waves with 3 stages 838 us)
   constexpr int kMxRS = 2;
-#define MOE_MX_LAUNCH(EPI)                                                                  \
-  do {                                                                                      \
-    if (block_m == 64)                                                                      \
-      moe::gemm_mx_kernel<EPI, 64, kMxRS><<<grid, dim3(256 * kMxRS), 0, st>>>(ga, ma, *W, ea); \
-    else                                                                                    \
-      moe::gemm_mx_kernel<EPI, 128, kMxRS><<<grid, dim3(256 * kMxRS), 0, st>>>(ga, ma, *W, ea); \
+  constexpr int kSsRS = 1, kSsNS = 2;
+#define MOE_MX_LAUNCH(EPI)                                                                       \
+  do {                                                                                           \
+    if (ss && block_m == 64)                                                                     \
+      moe::gemm_mx_kernel<EPI, 64, kSsRS, kSsNS, true><<<grid, dim3(256 * kSsRS), 0, st>>>(ga, ma, *W, ea); \
+    else if (ss)                                                                                 \
+      moe::gemm_mx_kernel<EPI, 128, kSsRS, kSsNS, true><<<grid, dim3(256 * kSsRS), 0, st>>>(ga, ma, *W, ea); \
+    else if (block_m == 64)                                                                      \
+      moe::gemm_mx_kernel<EPI, 64, kMxRS, moe::kMxStages, false><<<grid, dim3(256 * kMxRS), 0, st>>>(ga, ma, *W, ea); \
+    else                                                                                         \
+      moe::gemm_mx_kernel<EPI, 128, kMxRS, moe::kMxStages, false><<<grid, dim3(256 * kMxRS), 0, st>>>(ga, ma, *W, ea); \
   } while (0)
   switch (epi) {
     case moe::EPI_SWIGLU: MOE_MX_LAUNCH(moe::EPI_SWIGLU); break;
