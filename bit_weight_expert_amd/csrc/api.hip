@@ -199,7 +199,11 @@ int mx_lds(int K) { return (K / 32 + 15) / 16 * 16; }
 
 // Scale tiles of the MX GEMM kernel must fit its LDS (56 KB), and the A
 // scale tile its 4 x 6 DMA instructions of 64 16-byte pieces.
-bool mx_fits(int K, int block_m) {
+// The MX kernel takes this family at this K: its weight scales by K chunk
+// stream with the chunks (any K); otherwise both scale tiles must fit the
+// kernel's 56 KB of resident LDS.
+bool mx_fits(const moe::WeightArgs& W, int K, int block_m) {
+  if (W.scales_kc != nullptr) return true;
   const int b = (256 * (K / 32) + 1023) / 1024 * 1024;
   return b + (block_m * mx_lds(K) + 1023) / 1024 * 1024 <= 56 * 1024 &&
          block_m * (mx_lds(K) / 16) <= 4 * 6 * 64;
@@ -497,7 +501,7 @@ static moe_status_t mx_gemm_checks(const moe_wq_t* w, int N, int K, int block_m,
   if (st != MOE_OK) return st;
   if (w->fmt != MOE_W_MXFP4) return MOE_ERR_UNSUPPORTED;
   if (block_m != 64 && block_m != 128) return MOE_ERR_UNSUPPORTED;
-  if (!mx_fits(K, block_m)) return MOE_ERR_UNSUPPORTED;
+  if (!mx_fits(*W, K, block_m)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -604,7 +608,7 @@ moe_status_t moe_forward_mxfp8(const uint16_t* x, const float* logits, int T, in
 
   hipError_t e = route_and_sort(logits, T, E, top_k, (int)kind, expert_bias, renormalize ? 1 : 0,
                                 ids, tw, block_m, cap, sorted, eids, npp, reinterpret_cast<int32_t*>(ws + L.base.cnt), s);
-  if (block_m >= 64 && mx_fits(hidden, block_m) && mx_fits(inter, block_m)) {
+  if (block_m >= 64 && mx_fits(W13, hidden, block_m) && mx_fits(W2, inter, block_m)) {
     // MX-scaled MFMA: both GEMMs read e4m3 codes and e8m0 scales
     if (e == hipSuccess)
       e = moe_launch_mxfp8_quant(x, T, hidden, mx_lda(hidden), mx_lds(hidden), xq, xs, nullptr, s);

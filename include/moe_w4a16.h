@@ -420,9 +420,11 @@ moe_status_t moe_mxfp8_quantize(const uint16_t* x, int rows, int K, uint8_t* cod
 /* moe_w4a16_gemm1 with the input rows in MXFP8 ([size_m] rows in the layout
  * above) and MXFP4 weights, on the MX-scaled matrix cores (e4m3 x e2m1 with
  * both e8m0 scales applied per 32-deep block, fp32 accumulate).  block_m must
- * be 64 or 128, and both scale tiles must fit the kernel's 56 KB of LDS
- * (256*K/32 + block_m*lds bytes, each rounded up to 1 KB; K <= ~4600), else
- * MOE_ERR_UNSUPPORTED.  No routing weight on the input. */
+ * be 64 or 128.  With the weight scales by K chunk (scales_kc) both scale
+ * tiles stream with the K chunks and any K is taken; otherwise both must fit
+ * the kernel's 56 KB of resident LDS (256*K/32 + block_m*lds bytes, each
+ * rounded up to 1 KB; K <= ~4600), else MOE_ERR_UNSUPPORTED.  No routing
+ * weight on the input. */
 moe_status_t moe_mx_gemm1(const uint8_t* x_codes, const uint8_t* x_scales, int size_m, int top_k,
                           int K, int N, int E, const moe_wq_t* w13, moe_act_t act, float alpha,
                           float beta, float limit, const int32_t* sorted_ids,

@@ -122,6 +122,10 @@ def test_mx_gemm1_parity(act, H, B):
     ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, act, L.alpha, L.beta, L.limit, si, ei, npp, B,
                        act_fmt="mxfp8")
     assert_rows_close(host_bf16(out), ref, rows=cov, what=f"mx gemm1 {act} H{H} B{B}")
+    # scales by K chunk: the streamed-scale kernel, the same bits
+    outs = M.moe_mx_gemm1(dc, ds, L.top_k, H, D["w13"].chunked_only(), act, L.alpha, L.beta,
+                          L.limit, t(si), t(ei), t(np.array([npp], np.int32)), B)
+    assert torch.equal(out.view(torch.int16), outs.view(torch.int16)), "streamed scales"
 
 
 @pytest.mark.parametrize("I", [192, 224, 2880])
@@ -143,6 +147,9 @@ def test_mx_gemm2_parity(I, B, mul):
                        t(np.array([npp], np.int32)), B)
     ref, cov = O.gemm2(a, n, L.w2, w.reshape(-1), mul, si, ei, npp, B, act_fmt="mxfp8")
     assert_rows_close(host_bf16(y), ref, rows=cov, what=f"mx gemm2 I{I} B{B}")
+    ys = M.moe_mx_gemm2(dc, ds, I, D["w2"].chunked_only(), t(w.reshape(-1).astype(np.float32)),
+                        mul, t(si), t(ei), t(np.array([npp], np.int32)), B)
+    assert torch.equal(y.view(torch.int16), ys.view(torch.int16)), "streamed scales"
 
 
 def gpu_forward_mx(L, D):
@@ -353,6 +360,25 @@ def test_mx_gemm1_longest_k_that_fits():
     assert_rows_close(host_bf16(out), ref, rows=cov, what="mx gemm1 K=4608")
 
 
+def test_mx_gemm1_long_k_streamed_scales():
+    """K = 6144: beyond the resident scale tiles (the checkpoint family is
+    refused); the chunked-only family streams them with the chunks."""
+    L = _layer("swigluoai", E=3, H=6144, I=64, T=100)
+    D = upload(L)
+    ids, w = O.route(L)
+    si, ei, npp = O.align(ids, L.E, 128)
+    xc, xs = F.quantize_mxfp8(F.bf16_to_f64(L.x))
+    dc, ds = _up_mx(xc, xs, L.H)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    args = ("swigluoai", L.alpha, L.beta, L.limit, t(si), t(ei), t(np.array([npp], np.int32)), 128)
+    with pytest.raises(RuntimeError):
+        M.moe_mx_gemm1(dc, ds, L.top_k, L.H, D["w13"], *args)
+    out = M.moe_mx_gemm1(dc, ds, L.top_k, L.H, D["w13"].chunked_only(), *args)
+    ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, "swigluoai", L.alpha, L.beta, L.limit, si, ei,
+                       npp, 128, act_fmt="mxfp8")
+    assert_rows_close(host_bf16(out), ref, rows=cov, what="mx gemm1 K=6144 streamed scales")
+
+
 def test_forward_mxfp8_empty_batch():
     L = _layer(T=4)
     D = upload(L)
@@ -378,7 +404,9 @@ def test_mxfp4_codes_by_chunk_bitexact(E, N, K):
 def test_mx_gemms_codes_by_chunk(K, B):
     """The MX kernels reading the chunked copy: bit for bit what they give on
     the checkpoint codes (only the copy source differs), and the oracle's
-    values; K % 128 = 64 and 96 cover a partial last chunk."""
+    values; K % 128 = 64 and 96 cover a partial last chunk.  The chunked-only
+    family (scales by K chunk too) runs the kernel whose scale tiles stream
+    with the chunks: bit for bit the same again."""
     L = _layer(H=K, I=K, T=300 if K < 2880 else 150)
     D = upload(L)
     w13c = dataclasses.replace(D["w13"], qweight_kc=M.moe_mxfp4_codes_by_chunk(D["w13"]))
@@ -393,6 +421,8 @@ def test_mx_gemms_codes_by_chunk(K, B):
     o1 = M.moe_mx_gemm1(dc, ds, L.top_k, K, D["w13"], *args)
     o1c = M.moe_mx_gemm1(dc, ds, L.top_k, K, w13c, *args)
     assert torch.equal(o1.view(torch.int16), o1c.view(torch.int16))
+    o1s = M.moe_mx_gemm1(dc, ds, L.top_k, K, D["w13"].chunked_only(), *args)
+    assert torch.equal(o1.view(torch.int16), o1s.view(torch.int16)), "streamed scales"
     ref, cov = O.gemm1(L.x, L.T, L.top_k, L.w13, L.act, L.alpha, L.beta, L.limit, si, ei, npp, B,
                        act_fmt="mxfp8")
     assert_rows_close(host_bf16(o1c), ref, rows=cov, what=f"mx gemm1 codes by chunk K{K} B{B}")
@@ -405,12 +435,15 @@ def test_mx_gemms_codes_by_chunk(K, B):
     y = M.moe_mx_gemm2(dc2, ds2, K, D["w2"], *args2)
     yc = M.moe_mx_gemm2(dc2, ds2, K, w2c, *args2)
     assert torch.equal(y.view(torch.int16), yc.view(torch.int16))
+    ys = M.moe_mx_gemm2(dc2, ds2, K, D["w2"].chunked_only(), *args2)
+    assert torch.equal(y.view(torch.int16), ys.view(torch.int16)), "streamed scales"
     ref2, cov2 = O.gemm2(a, n, L.w2, w.reshape(-1), True, si, ei, npp, B, act_fmt="mxfp8")
     assert_rows_close(host_bf16(yc), ref2, rows=cov2, what=f"mx gemm2 codes by chunk K{K} B{B}")
 
 
 def test_forward_mxfp8_codes_by_chunk_full_size():
-    """gpt-oss-120b shape, T = 8192: the chunked copies change no output bit."""
+    """gpt-oss-120b shape, T = 8192: the chunked copies (codes, then codes and
+    scales) change no output bit."""
     L = dataclasses.replace(S.make_config(4, 8192), act_fmt="mxfp8")
     D = upload(L)
     out = gpu_forward_mx(L, D)
@@ -419,3 +452,7 @@ def test_forward_mxfp8_codes_by_chunk_full_size():
     print("forward mxfp8 codes by chunk full size", flush=True)
     outc = gpu_forward_mx(L, D)
     assert torch.equal(out.view(torch.int16), outc.view(torch.int16))
+    # chunked-only families: the MX kernels stream both scale tiles
+    D["w13"], D["w2"] = D["w13"].chunked_only(), D["w2"].chunked_only()
+    outs = gpu_forward_mx(L, D)
+    assert torch.equal(out.view(torch.int16), outs.view(torch.int16)), "streamed scales"
