@@ -138,7 +138,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def act_order_leg(args, time_calls):
+def act_order_leg(args, time_calls, time_launches):
     """GPTQ g64 layer (E=32, top-4, 2880/2880): plain vs act-order weights."""
     import torch
     import synthetic as S
@@ -187,8 +187,10 @@ def act_order_leg(args, time_calls):
         ids = M.moe_route(logits[:T], Lp.top_k, Lp.route, None, Lp.renormalize)[0].reshape(-1)
         kp = fams["act_order"][0].k_perm
         xp = torch.empty((T * Lp.top_k, Lp.H), dtype=torch.bfloat16, device=dev)
-        g_ms = time_calls(lambda i: M.moe_permute_slots(x[:T], Lp.top_k, kp, ids, out=xp),
-                          max(args.steps, 20), args.warmup)
+        # (one event pair around each launch: back to back, the binding's host
+        # time per call would exceed the few microseconds of the kernel)
+        g_ms = time_launches(lambda i: M.moe_permute_slots(x[:T], Lp.top_k, kp, ids, out=xp),
+                             max(args.steps, 20), args.warmup)[0]
         touched = len(set(ids.cpu().numpy().tolist()))
         nb = T * Lp.H * 2 + T * Lp.top_k * Lp.H * 2 + touched * Lp.H * 4
         r.update(gather_us=g_ms * 1e3, gather_alg_bytes=nb,
@@ -525,7 +527,7 @@ def main() -> int:
                          f"both GEMMs, sum); median of {len(times)} runs; BLAS threads = cores"}
         log(f"oracle: {n} tokens, median {dt:.1f}s of {len(times)} runs, {blas_threads} BLAS threads")
 
-    act_order = act_order_leg(args, time_calls) if args.act_order else None
+    act_order = act_order_leg(args, time_calls, time_launches) if args.act_order else None
     mxfp8 = mxfp8_leg(args, time_calls) if args.mxfp8 else None
 
     line = {
