@@ -13,8 +13,8 @@
 // the k winners come out of k rounds of a wave-wide argmax, in output order.
 // The wave-wide max, sum and argmax are butterflies whose first four steps
 // are DPP moves inside rows of 16 lanes (a rank count over broadcast scores,
-// one v_readlane per expert, took 15-20 us per token at E = 128: a serial
-// chain of lane reads).
+// one v_readlane per expert and score, made each wave a serial chain of ~500
+// lane reads at E = 128: 15-24 us per launch).
 //
 // Align: one workgroup of 1024 threads.  Pads each expert's count to block_m
 // and places every slot at
