@@ -47,13 +47,23 @@ def test_route_bitexact_full_size(cfg):
 
 
 @pytest.mark.parametrize("E,k,kind,renorm", [(8, 2, "softmax", False), (130, 5, "sigmoid_bias", True),
-                                             (1024, 16, "softmax", True), (3, 3, "softmax", True)])
+                                             (1024, 16, "softmax", True), (3, 3, "softmax", True),
+                                             (1, 1, "softmax", True), (2, 2, "sigmoid_bias", False),
+                                             (64, 8, "softmax", True), (65, 7, "sigmoid_bias", True),
+                                             (127, 16, "softmax", False), (128, 1, "softmax", True)])
 def test_route_shapes(E, k, kind, renorm):
+    """Ties, one and two scores per lane (E = 64 / 65 / 127 / 128), k up to 16,
+    the single-expert layer; row 1 ties experts 5 and 69 (the two entries of
+    one lane) at the top, which the lower id must win."""
     rng = np.random.default_rng(E)
     T = 37
     logits = rng.standard_normal((T, E)).astype(np.float32)
     logits[0, :] = 0.25                       # all tied: lowest ids win
+    if E > 64 + 5:
+        logits[1, 5] = logits[1, 64 + 5] = 9.0  # one lane's two entries tied at the top
     bias = (rng.standard_normal(E) * 0.1).astype(np.float32) if kind == "sigmoid_bias" else None
+    if bias is not None and E > 64 + 5:
+        bias[5] = bias[64 + 5] = 0.0
     ids_ref, w_ref = O.route(logits, k, kind, bias, renorm)
     ids, w = M.moe_route(torch.from_numpy(logits).cuda(), k, kind,
                          None if bias is None else torch.from_numpy(bias).cuda(), renorm)
