@@ -315,6 +315,41 @@ def test_forward_deterministic_bitwise():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("fmt,act,E,k", [("nvfp4", "swigluoai", 6, 3), ("gptq", "swigluoai", 32, 4),
+                                         ("mxfp4", "relu2", 9, 1), ("nvfp4", "relu2", 40, 6)])
+@pytest.mark.parametrize("T", [1, 2, 16, 64, 65])
+@pytest.mark.parametrize("policy", POLICIES)
+def test_forward_sum_equals_steps_bitwise(fmt, act, E, k, T, policy):
+    """moe_forward equals its steps through the public entry points -- route and
+    sort, GEMM1, GEMM2 -- followed by each token's k-row sum in float32, j
+    ascending, rounded once to bf16, bit for bit, on 16-, 32- and 64-row blocks
+    and both decode kernels.  Two more calls on one workspace (poisoned once,
+    then left with the previous call's contents) give the same bits."""
+    L = _small(fmt, act, E=E, k=k, T=T, skew_std=1.0)
+    D = upload(L)
+    out = gpu_forward(L, D, kernel=policy)
+    B = M.moe_forward_block_m(T, k, E)
+    _, tw, si, ei, npp = M.moe_route_align(D["logits"], k, B, L.route, D["expert_bias"],
+                                           L.renormalize)
+    act_rows = _gemm1(D, L, act, si, ei, npp, B, policy, T * k)
+    y = _gemm2(act_rows, D["w2"], tw.reshape(-1), L.mul_topk_weights, si, ei, npp, B, policy)
+    yh = y.float().cpu().numpy().reshape(T, k, L.H)
+    acc = np.zeros((T, L.H), np.float32)
+    for j in range(k):
+        acc += yh[:, j]
+    ref = torch.from_numpy(acc).to(torch.bfloat16)
+    assert torch.equal(out.cpu().view(torch.int16), ref.view(torch.int16)), (
+        f"forward {fmt} {act} E{E} k{k} T{T} B{B} {policy}: differs from its steps")
+    ws = poisoned((M.moe_forward_workspace_bytes(T, E, k, L.H, L.I),), torch.uint8)
+    kw = dict(act=L.act, route=L.route, expert_bias=D["expert_bias"], renormalize=L.renormalize,
+              alpha=L.alpha, beta=L.beta, limit=L.limit, mul_topk_weights=L.mul_topk_weights,
+              workspace=ws, kernel=policy)
+    for _ in range(2):
+        again = M.moe_forward(D["x"], D["logits"], k, L.I, D["w13"], D["w2"], out=poisoned((T, L.H)),
+                              **kw)
+        assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+
+
 def test_forward_t0_is_noop():
     L = _small("nvfp4", T=4)
     D = upload(L)
