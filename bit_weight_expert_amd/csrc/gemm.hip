@@ -144,8 +144,9 @@ struct MxOps {
   i32x8 b[NF];
 };
 
-// LDS reads of step ST (0 or 1) of the chunk in stage `stg` (A rows from r0).
-template <int MI, int NF, int ST>
+// LDS reads of step ST (0 or 1) of the chunk in stage `stg` (A rows from r0;
+// only the first MA row tiles: the rest hold padding rows only).
+template <int MI, int NF, int ST, int MA = MI>
 __device__ __forceinline__ void mx_read(MxOps<MI, NF>& o, const uint8_t* stg, int abytes,
                                         const int (&bpos)[NF], int c, int g, int r0) {
 #pragma unroll
@@ -156,7 +157,7 @@ __device__ __forceinline__ void mx_read(MxOps<MI, NF>& o, const uint8_t* stg, in
     o.b[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
   }
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  for (int i = 0; i < MA; ++i) {
     const int r = r0 + 32 * i + c;
     const uint8_t* row = stg + r * 128;
     const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * a_slot(4 * ST + g, r));
@@ -165,12 +166,13 @@ __device__ __forceinline__ void mx_read(MxOps<MI, NF>& o, const uint8_t* stg, in
   }
 }
 
-// The MI x NF MFMAs of one step; byte 2*ST of each scale word is the lane's block.
-template <int MI, int NF, int ST>
+// The MA x NF MFMAs of one step (the live row tiles); byte 2*ST of each scale
+// word is the lane's block.
+template <int MI, int NF, int ST, int MA = MI>
 __device__ __forceinline__ void mx_mfma(f32x16e (&acc)[MI][NF], const MxOps<MI, NF>& o,
                                         const int (&sa)[MI], const int (&sb)[NF]) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < MA; ++i)
 #pragma unroll
     for (int j = 0; j < NF; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[i], o.b[j], acc[i][j], 0, 4,
@@ -241,8 +243,15 @@ __global__ void __launch_bounds__(256 * RS, SS && RS == 1 ? 2 : 1)
       ssid[i] = ga.sorted_ids[mb * BM + pc / parts];
     }
   }
+  // 32-row tiles holding a real slot: a block's real slots come first (the
+  // sort pads each expert's run at its end), so tile i is live when its first
+  // slot is; this wave's live tiles among its MI (wave-uniform)
+  int nact = 1;
+#pragma unroll
+  for (int i = 1; i < BM / 32; ++i) nact += ga.sorted_ids[mb * BM + 32 * i] < ga.n_slots ? 1 : 0;
   const int e = ga.expert_ids[mb];
   if (e < 0 || e >= ga.E) return;
+  const int nact_w = __builtin_amdgcn_readfirstlane(min(max(nact - r0 / 32, 0), MI));
 
   const int nt0 = nt * P::BN;
   const int rows = min(P::BN, N - nt0);
@@ -379,41 +388,55 @@ __global__ void __launch_bounds__(256 * RS, SS && RS == 1 ? 2 : 1)
 
   // scales and chunk 0 have landed.  Both 64-deep steps of every chunk run
   // (past K the A codes are zero), so the loop has no branch; each step's
-  // LDS reads are issued while the other step's MFMAs run.
+  // LDS reads are issued while the other step's MFMAs run.  Only the wave's
+  // first MA row tiles are multiplied (MA < MI: the later 32-row tiles hold
+  // only padding rows); one copy of the loop per MA, chosen once per tile.
   wait_vmcnt<(NS - 1) * P::kIssue>();
   pf_barrier();
-  MxOps<MI, NF> o0, o1;
-  int sa[MI], sb[NF];
-  scales(sa, sb, 0);
-  mx_read<MI, NF, 0>(o0, smem, P::kABytes, bpos, c, g, r0);
-  if (n0 >= N) {
-    // every weight row of this wave lies past N (the last column tile): only
-    // its share of the copies, which leaves its SIMD to the other waves
+  auto kloop = [&](auto ma_tag) {
+    constexpr int MA = decltype(ma_tag)::value;
+    MxOps<MI, NF> o0, o1;
+    int sa[MI], sb[NF];
+    scales(sa, sb, 0);
+    mx_read<MI, NF, 0, MA>(o0, smem, P::kABytes, bpos, c, g, r0);
+    for (int kc = 0; kc < nchunks; ++kc) {
+      const uint8_t* stg = smem + (kc % NS) * P::kStage;
+      mx_read<MI, NF, 1, MA>(o1, stg, P::kABytes, bpos, c, g, r0);
+      mx_mfma<MI, NF, 0, MA>(acc, o0, sa, sb);
+      // chunk kc+1 has landed (only the NS-2 younger chunks may be in flight)
+      // and every wave is past its reads of chunk kc, whose stage takes chunk
+      // kc+NS
+      wait_vmcnt<(NS - 2) * P::kIssue>();
+      pf_barrier();
+      issue(ring + (kc % NS) * P::kStage, min(kc + NS, nchunks - 1));
+      int na_[MI], nb_[NF];
+      const int kn = min(kc + 1, nchunks - 1);
+      scales(na_, nb_, kn);
+      mx_read<MI, NF, 0, MA>(o0, smem + (kn % NS) * P::kStage, P::kABytes, bpos, c, g, r0);
+      mx_mfma<MI, NF, 1, MA>(acc, o1, sa, sb);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) sa[i] = na_[i];
+#pragma unroll
+      for (int j = 0; j < NF; ++j) sb[j] = nb_[j];
+    }
+  };
+  if (n0 >= N || nact_w == 0) {
+    // every weight row of this wave lies past N (the last column tile), or
+    // all its rows are padding: only its share of the copies, which leaves
+    // its SIMD to the other waves
     for (int kc = 0; kc < nchunks; ++kc) {
       wait_vmcnt<(NS - 2) * P::kIssue>();
       pf_barrier();
       issue(ring + (kc % NS) * P::kStage, min(kc + NS, nchunks - 1));
     }
-  } else
-  for (int kc = 0; kc < nchunks; ++kc) {
-    const uint8_t* stg = smem + (kc % NS) * P::kStage;
-    mx_read<MI, NF, 1>(o1, stg, P::kABytes, bpos, c, g, r0);
-    mx_mfma<MI, NF, 0>(acc, o0, sa, sb);
-    // chunk kc+1 has landed (only the NS-2 younger chunks may be in flight)
-    // and every wave is past its reads of chunk kc, whose stage takes chunk
-    // kc+NS
-    wait_vmcnt<(NS - 2) * P::kIssue>();
-    pf_barrier();
-    issue(ring + (kc % NS) * P::kStage, min(kc + NS, nchunks - 1));
-    int na_[MI], nb_[NF];
-    const int kn = min(kc + 1, nchunks - 1);
-    scales(na_, nb_, kn);
-    mx_read<MI, NF, 0>(o0, smem + (kn % NS) * P::kStage, P::kABytes, bpos, c, g, r0);
-    mx_mfma<MI, NF, 1>(acc, o1, sa, sb);
-#pragma unroll
-    for (int i = 0; i < MI; ++i) sa[i] = na_[i];
-#pragma unroll
-    for (int j = 0; j < NF; ++j) sb[j] = nb_[j];
+  } else if (nact_w >= MI) {
+    kloop(std::integral_constant<int, MI>{});
+  } else if constexpr (MI >= 2) {
+    if (nact_w == 1) kloop(std::integral_constant<int, 1>{});
+    else if constexpr (MI >= 3) {
+      if (nact_w == 2) kloop(std::integral_constant<int, 2>{});
+      else if constexpr (MI >= 4) kloop(std::integral_constant<int, 3>{});
+    }
   }
   // no DMA may land in LDS after this workgroup is gone
   wait_vmcnt<0>();
