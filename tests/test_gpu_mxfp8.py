@@ -128,6 +128,38 @@ def test_mx_gemm1_parity(act, H, B):
     assert torch.equal(out.view(torch.int16), outs.view(torch.int16)), "streamed scales"
 
 
+def _live_tile_ids(counts, seed):
+    """top_k = 1 routing with the given slot count per expert, tokens shuffled."""
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    return np.random.default_rng(seed).permutation(ids).reshape(-1, 1)
+
+
+@pytest.mark.parametrize("act", ["swigluoai", "relu2"])
+def test_mx_gemm1_live_row_tiles(act):
+    """128-row blocks holding 1, 33, 65, 97 and 129 slots: one to four live 32-row
+    tiles (the kernel multiplies only those) and a full block followed by a
+    one-row block; every row (the output starts as NaN bytes) matches the
+    oracle, and the streamed-scale kernel gives the same bits."""
+    counts = [1, 33, 65, 97, 129]
+    T = sum(counts)
+    L = _layer(act, E=len(counts), k=1, H=352, T=T, seed=7)
+    D = upload(L)
+    ids = _live_tile_ids(counts, 5)
+    si, ei, npp = O.align(ids, L.E, 128)
+    xc, xs = F.quantize_mxfp8(F.bf16_to_f64(L.x))
+    dc, ds = _up_mx(xc, xs, L.H)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    args = (L.alpha, L.beta, L.limit, t(si), t(ei), t(np.array([npp], np.int32)), 128)
+    n_out = L.w13.N // 2 if act == "swigluoai" else L.w13.N
+    out = M.moe_mx_gemm1(dc, ds, 1, L.H, D["w13"], act, *args, out=poisoned((T, n_out)))
+    ref, cov = O.gemm1(L.x, T, 1, L.w13, act, L.alpha, L.beta, L.limit, si, ei, npp, 128,
+                       act_fmt="mxfp8")
+    assert cov.all()
+    assert_rows_close(host_bf16(out), ref, what=f"mx gemm1 live tiles {act}")
+    outs = M.moe_mx_gemm1(dc, ds, 1, L.H, D["w13"].chunked_only(), act, *args)
+    assert torch.equal(out.view(torch.int16), outs.view(torch.int16)), "streamed scales"
+
+
 @pytest.mark.parametrize("I", [192, 224, 2880])
 @pytest.mark.parametrize("B", [64, 128])
 @pytest.mark.parametrize("mul", [True, False])

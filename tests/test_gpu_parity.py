@@ -191,6 +191,26 @@ def test_gemm1_parity(fmt, act, B, policy):
     assert_untouched(out, cov, "gemm1")
 
 
+@pytest.mark.parametrize("fmt,act", [("nvfp4", "swigluoai"), ("mxfp4", "relu2"), ("gptq", "swigluoai")])
+@pytest.mark.parametrize("B", [64, 128])
+def test_gemm1_live_row_tiles(fmt, act, B):
+    """Streaming-kernel blocks with one to four live 32-row tiles (slot counts
+    1, 33, 65, 97 and 129 per expert, top_k = 1, tokens shuffled): the kernel
+    multiplies only the live tiles; every row (the output starts as NaN bytes)
+    matches the oracle."""
+    counts = [1, 33, 65, 97, 129]
+    T = sum(counts)
+    L = _small(fmt, act, E=len(counts), k=1, T=T, seed=8)
+    D = upload(L)
+    ids = np.random.default_rng(6).permutation(
+        np.repeat(np.arange(len(counts), dtype=np.int32), counts)).reshape(-1, 1)
+    si, ei, npp = O.align(ids, L.E, B)
+    ref, cov = O.gemm1(L.x, T, 1, L.w13, act, L.alpha, L.beta, L.limit, si, ei, npp, B)
+    assert cov.all()
+    out = _gemm1(D, L, act, *_dev_align(si, ei, npp), B, "auto", T)
+    assert_rows_close(host_bf16(out), ref, what=f"gemm1 live tiles {fmt} {act} B{B}")
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "gptq"])
 @pytest.mark.parametrize("B,policy", [(16, "auto"), (32, "auto"), (16, "wide"), (32, "wide"),
                                       (128, "auto")])
