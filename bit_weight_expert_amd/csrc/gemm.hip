@@ -96,12 +96,13 @@ constexpr int kMxScaleIssue = 6;  // A-scale DMA instructions per wave (BM * lds
 // each stage holds the chunk's [BN][4] weight scale bytes and [BM][4] A
 // scale bytes), so the workgroup waits for nothing but its first chunk and
 // takes far less LDS.
-template <int BM, int RS = 1, int NS = kMxStages, bool SS = false>
+template <int BM, int RS = 1, int NS = kMxStages, bool SS = false, int WR = 1>
 struct Mx {
   static constexpr int NW = 4 * RS;                   // waves
-  static constexpr int MI = BM / 32 / RS;             // 32-row tiles per wave
-  static constexpr int NF = 2;
-  static constexpr int BN = 4 * NF * 32;
+  static constexpr int MI = BM / 32 / RS / WR;        // 32-row tiles per wave
+  static constexpr int NF = 2 * WR;                   // 32-row weight fragments per wave
+  static constexpr int BN = 4 / WR * NF * 32;
+  static_assert(RS == 1 || WR == 1, "row split or a 2 x 2 wave grid, not both");
   static constexpr int kABytes = BM * kMxBK;
   static constexpr int kBBytes = BN * kMxBK / 2;
   static constexpr int kWsBytes = SS ? BN * 4 : 0;    // streamed weight scales of one chunk
@@ -208,10 +209,10 @@ __device__ __forceinline__ void mx_scales(int (&sa)[MI], int (&sb)[NF], const ui
   }
 }
 
-template <int EPI, int BM, int RS, int NS, bool SS>
+template <int EPI, int BM, int RS, int NS, bool SS, int WR = 1>
 __global__ void __launch_bounds__(256 * RS, SS && RS == 1 ? 2 : 1)
     gemm_mx_kernel(GemmArgs ga, MxA ma, WeightArgs W, EpiArgs ea) {
-  using P = Mx<BM, RS, NS, SS>;
+  using P = Mx<BM, RS, NS, SS, WR>;
   constexpr int MI = P::MI, NF = P::NF, NW = P::NW;
   __shared__ __attribute__((aligned(16))) uint8_t smem[P::kLds];
 
@@ -220,8 +221,13 @@ __global__ void __launch_bounds__(256 * RS, SS && RS == 1 ? 2 : 1)
   const int tid = threadIdx.x, lane = tid & 63;
   const int c = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // DMA share (0 .. NW-1)
-  const int wave_u = wave & 3;                                 // weight-row group
-  const int r0 = (wave >> 2) * MI * 32;                        // this wave's first A row
+  const int wave_u = wave & 3;                                 // DMA role
+  // WR = 1: the four waves side by side over the weight rows; WR = 2: a 2 x 2
+  // grid (half the A rows x half the weight rows each), so each A and each
+  // weight fragment is read from LDS by two waves instead of A by four
+  const int wave_r = WR == 2 ? (wave & 1) : 0;
+  const int wave_c = WR == 2 ? (wave_u >> 1) : wave_u;          // weight-row group
+  const int r0 = ((wave >> 2) * WR + wave_r) * MI * 32;        // this wave's first A row
   const int K = ga.K, N = ga.N, kb = K / 32;
 
   // slot ids of the A rows this lane copies (instruction q = NW*p + wave covers
@@ -255,7 +261,7 @@ __global__ void __launch_bounds__(256 * RS, SS && RS == 1 ? 2 : 1)
 
   const int nt0 = nt * P::BN;
   const int rows = min(P::BN, N - nt0);
-  const int n0 = nt0 + wave_u * NF * 32;
+  const int n0 = nt0 + wave_c * NF * 32;
   const int nchunks = (K + kMxBK - 1) / kMxBK;
 
   // DMA sources.  A: lane l writes physical slot l%8 of row r = 8q + l/8, so it
@@ -525,7 +531,7 @@ extern "C" hipError_t moe_launch_gemm_mx(int epi, int block_m, int cap, const ui
     if (ss && block_m == 64)                                                                     \
       moe::gemm_mx_kernel<EPI, 64, kSsRS, kSsNS, true><<<grid, dim3(256 * kSsRS), 0, st>>>(ga, ma, *W, ea); \
     else if (ss)                                                                                 \
-      moe::gemm_mx_kernel<EPI, 128, kSsRS, kSsNS, true><<<grid, dim3(256 * kSsRS), 0, st>>>(ga, ma, *W, ea); \
+      moe::gemm_mx_kernel<EPI, 128, kSsRS, kSsNS, true, 2><<<grid, dim3(256 * kSsRS), 0, st>>>(ga, ma, *W, ea); \
     else if (block_m == 64)                                                                      \
       moe::gemm_mx_kernel<EPI, 64, kMxRS, moe::kMxStages, false><<<grid, dim3(256 * kMxRS), 0, st>>>(ga, ma, *W, ea); \
     else                                                                                         \
