@@ -358,6 +358,63 @@ def test_forward_mxfp8(act, T):
     _check_layer(L, D, got, act_gpu)
 
 
+def _steps_mx_small(L, D, policy="auto"):
+    """moe_forward_mxfp8's result at 16/32-row blocks from the public steps:
+    route and sort, the quantiser's dequantised MXFP8 values of x, the bf16
+    GEMM1, the same for its output, the bf16 GEMM2, and each token's k-row sum
+    in float32 (j ascending, one bf16 rounding) on the host."""
+    T, k = D["x"].shape[0], L.top_k
+    bm = M.moe_forward_block_m(T, k, L.E)
+    assert bm <= 32
+    _, tw, si, ei, npp = M.moe_route_align(D["logits"], k, bm, L.route, D["expert_bias"],
+                                           L.renormalize)
+    _, _, xd = M.moe_mxfp8_quantize(D["x"], codes=False, dequant=True)
+    act = M.moe_w4a16_gemm1(xd, k, D["w13"], L.act, L.alpha, L.beta, L.limit, si, ei, npp, bm,
+                            kernel=policy)
+    _, _, ad = M.moe_mxfp8_quantize(act, codes=False, dequant=True)
+    y = M.moe_w4a16_gemm2(ad, D["w2"], tw.reshape(-1), L.mul_topk_weights, si, ei, npp, bm,
+                          kernel=policy)
+    yh = y.float().cpu().numpy().reshape(T, k, L.H)
+    acc = np.zeros((T, L.H), np.float32)
+    for j in range(k):
+        acc += yh[:, j]
+    return torch.from_numpy(acc).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", ["E6_T1", "E6_T13_nan", "cfg4_T1", "cfg4_T16"])
+def test_forward_mxfp8_small_blocks_equal_steps(case):
+    """At 16/32-row blocks the layer equals its public steps -- the quantiser's
+    dequantised MXFP8 values of x and of the activation around the bf16 GEMMs
+    -- bit for bit.  cfg4_T16 runs the 128-column kernel (enough column
+    tiles), the others the split-K one; a NaN in one 32-block of x makes that
+    token's rows NaN on both sides."""
+    if case.startswith("cfg4"):
+        T = int(case.split("_T")[1])
+        L = dataclasses.replace(S.make_config(4, T), act_fmt="mxfp8")
+    else:
+        T = 13 if "T13" in case else 1
+        L = _layer("relu2" if "nan" in case else "swigluoai", T=T, E=6, k=3 if "nan" in case else 2)
+    D = upload(L)
+    if "nan" in case:
+        xb = D["x"].clone()
+        xb[2, 40] = float("nan")
+        D = dict(D, x=xb)
+    print(f"mxfp8 small blocks {case} block_m={M.moe_forward_block_m(T, L.top_k, L.E)}", flush=True)
+    out = gpu_forward_mx(L, D)
+    ref = _steps_mx_small(L, D)
+    # bit for bit, except the payload of a NaN (the steps' sum runs on the host)
+    a, b = out.cpu().float().numpy(), ref.float().numpy()
+    nan = np.isnan(a)
+    assert (nan == np.isnan(b)).all(), "NaN positions differ"
+    diff = out.cpu().view(torch.int16).numpy()[~nan] != ref.view(torch.int16).numpy()[~nan]
+    assert not diff.any(), f"{int(diff.sum())} of {int((~nan).sum())} values differ"
+    got = host_bf16(out)
+    if "nan" in case:
+        assert np.isnan(got[2]).all() and np.isfinite(np.delete(got, 2, axis=0)).all()
+    else:
+        assert np.isfinite(got).all()
+
+
 @pytest.mark.parametrize("T", [1024, 8192])
 def test_forward_mxfp8_full_size(T):
     """The gpt-oss-120b MXFP4 layer (E=128, top-4, 2880/2880, skewed routing)
