@@ -28,7 +28,7 @@ HIP event pair around each launch, on the stream it is launched on; the mean
 launch duration gives roofline.achieved (the same quantity a kernel trace
 reports as the kernel's average duration).
 
-Prints ONE JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+Prints ONE JSON line.  --gpus N > 1 is refused: the library runs the layer on one GPU.
 
 --act-order adds a leg on the INT4-GPTQ g64 layer of the same shape: the layer
 with plain (group-ordered) weights against the same layer quantised in
@@ -329,7 +329,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer "
-              "is not sharded across GPUs in this build.", file=sys.stderr)
+              "is not sharded across GPUs by this library.", file=sys.stderr)
         return 2
 
     import torch
