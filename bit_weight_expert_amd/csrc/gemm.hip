@@ -70,7 +70,9 @@ __global__ void __launch_bounds__(256) moe_sum_kernel(const uint16_t* __restrict
 // The accumulators have the layout of the bf16 32x32 MFMA (epilogue32).
 //
 // Tile: BM rows x 256 weight rows, four waves side by side over the weight
-// rows (two 32-row fragments each), all BM rows per wave.  K moves in chunks
+// rows (two 32-row fragments each), all BM rows per wave -- or, for 128-row
+// blocks with streamed scales, a 2 x 2 grid of 64 rows x 128 weight rows per
+// wave (each fragment then read from LDS by two waves).  K moves in chunks
 // of 128 through an LDS ring filled by LDS-DMA (A: 128 bytes per row,
 // 16-byte slot q of row r at a_slot(q, r); weights: 64 bytes per row at the
 // row's position, slot q at q ^ ((position / 4) % 4)).  With the weight
