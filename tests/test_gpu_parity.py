@@ -370,6 +370,19 @@ def test_forward_sum_equals_steps_bitwise(fmt, act, E, k, T, policy):
         assert torch.equal(again.view(torch.int16), out.view(torch.int16))
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "gptq"])
+@pytest.mark.parametrize("T", [5, 300, 600])
+def test_forward_max_experts_and_top_k(fmt, T):
+    """The largest routing the ABI takes, E = 1024 and top_k = 16, through the
+    whole layer: one launch for route and sort (T = 5), the routing kernel and
+    the one-workgroup sort with mixed-tiling planning (T = 300), the
+    16-workgroup sort into 64-row streaming tiles (T = 600)."""
+    L = _small(fmt, E=1024, k=16, H=128, I=64, T=T, seed=31)
+    D = upload(L)
+    out = gpu_forward(L, D)
+    assert_rows_close(host_bf16(out), O.forward(L)["out"], what=f"forward E1024 k16 {fmt} T{T}")
+
+
 def test_forward_t0_is_noop():
     L = _small("nvfp4", T=4)
     D = upload(L)
