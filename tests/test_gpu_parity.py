@@ -383,6 +383,19 @@ def test_forward_max_experts_and_top_k(fmt, T):
     assert_rows_close(host_bf16(out), O.forward(L)["out"], what=f"forward E1024 k16 {fmt} T{T}")
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("E,k,H,I,T", [(1, 1, 128, 64, 1), (1, 1, 128, 64, 200),
+                                       (4, 2, 32, 32, 3), (4, 2, 32, 32, 150)])
+def test_forward_degenerate_shapes(fmt, E, k, H, I, T):
+    """One expert taking every token (the dense layer), and hidden = intermediate =
+    32: both GEMMs are a single 32-deep K tail with no full chunk, over one or
+    two 16/32-column weight fragments; decode and streaming kernels."""
+    L = _small(fmt, E=E, k=k, H=H, I=I, T=T, seed=33)
+    D = upload(L)
+    out = gpu_forward(L, D)
+    assert_rows_close(host_bf16(out), O.forward(L)["out"], what=f"forward E{E} k{k} H{H} I{I} T{T}")
+
+
 def test_forward_t0_is_noop():
     L = _small("nvfp4", T=4)
     D = upload(L)
