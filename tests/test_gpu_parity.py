@@ -396,6 +396,17 @@ def test_forward_degenerate_shapes(fmt, E, k, H, I, T):
     assert_rows_close(host_bf16(out), O.forward(L)["out"], what=f"forward E{E} k{k} H{H} I{I} T{T}")
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "gptq"])
+@pytest.mark.parametrize("T", [1, 13, 300])
+def test_forward_without_routing_weights(fmt, T):
+    """mul_topk_weights = False: the k rows are summed unweighted (16-row decode
+    blocks and 64/128-row streaming tiles)."""
+    L = _small(fmt, E=6, k=3, T=T, seed=35, mul_topk_weights=False)
+    D = upload(L)
+    out = gpu_forward(L, D)
+    assert_rows_close(host_bf16(out), O.forward(L)["out"], what=f"forward unweighted {fmt} T{T}")
+
+
 def test_forward_t0_is_noop():
     L = _small("nvfp4", T=4)
     D = upload(L)
